@@ -1,0 +1,269 @@
+"""fp64 CPU oracle of the lightning-indexer selection path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.  Plain definitions, no
+blocking, fusion or reordering beyond what each definition states.
+
+Sources (the pages this follows, cited by title and section):
+
+* "nemo_automodel.components.models.deepseek_v4.kernels.tilelang_indexer"
+  (NeMo AutoModel API page; "V4IndexerFunction" and "v4_lighting_indexer"):
+  SBHD tensor contracts - index_q [seqlen, batch, heads, dim] bf16,
+  index_k [seqlen_kv, batch, dim] bf16, weights [seqlen, batch, heads] fp32,
+  compress_ratio (4 for C4 layers), topk, result [batch, seqlen, topk].
+  The module summary says the indexer applies causal masking.
+* "Module glm5next_dsa" (metrale API page): "Shape of the pipeline"
+  (kpool_compress -> index_scores -> topk_pools -> expand_selection),
+  "Checkpoint and kernel facts the code depends on" (slot-axis softmax per
+  channel, pooling starts at first_key, a pool counts only if all of its
+  slots are valid, expand writes -1 over the row before any index), the
+  config invariants (index_topk a nonzero multiple of index_kpool,
+  index_kpool at most KERNEL_MAX_KPOOL = 8).
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* Score: I[t,s] = sum_h w[t,h] * ReLU(q[t,h,:] . k[s,:]) - ReLU per head,
+  then the fp32 per-head weights reduce over heads; no extra scale.
+* Causal mask under compression: key s is visible to query t (0-based)
+  iff s < n_t = min(Skv, floor((t+1)/r)).
+* Top-k order: score descending, lower key index first on equal scores
+  (+0.0 and -0.0 are equal); rows with fewer visible keys than topk are
+  padded with index -1 and score -inf.
+* kpool: logits gate[tok,c] + ape[j,c] for slot j; softmax over the slots
+  per channel; pool key = softmax-weighted sum of the slots' k_normed,
+  rounded to bf16 (nearest even); pool p covers tokens
+  first_key + p*KP ... first_key + p*KP + KP - 1, and P = floor(max(0, N -
+  first_key) / KP) so a trailing partial pool is not a pool.
+* Pooled scores use the same formula over pool keys, with no causal mask
+  (the cache precedes the decode query) and invalid pools excluded;
+  select_k = index_topk / KP pools per row, ties to the lower pool id.
+* expand: slot i*KP + j of a row holds first_key + p_i*KP + j for the i-th
+  selected pool p_i, and -1 where the pool id is -1.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------------------
+# Unpooled lightning indexer (tilelang_indexer page)
+# ---------------------------------------------------------------------------
+
+def visible_keys(t: int, Skv: int, compress_ratio: int) -> int:
+    """Number of keys query position t may see: min(Skv, floor((t+1)/r)).
+
+    Causal masking (tilelang_indexer module summary) under the compression
+    ratio (v4_lighting_indexer parameter compress_ratio, 4 for C4 layers):
+    a compressed key summarises r consecutive tokens, so it is visible once
+    all r of them are at or before t.  r = 1 is the plain causal mask s <= t.
+    """
+    return min(Skv, (t + 1) // compress_ratio)
+
+
+def _dot_products(q_row: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """[H, n]: q_row [H, D] times keys [n, D] transposed, in fp64."""
+    return q_row @ keys.T
+
+
+def _relu(x: np.ndarray) -> np.ndarray:
+    return np.maximum(x, 0.0)
+
+
+def _weighted_head_sum(w_row: np.ndarray, per_head: np.ndarray) -> np.ndarray:
+    """sum_h w[h] * per_head[h, :] in fp64 -> [n]."""
+    return (w_row[:, None] * per_head).sum(axis=0)
+
+
+def head_scores(q_row: np.ndarray, keys: np.ndarray, w_row: np.ndarray) -> np.ndarray:
+    """Index scores of one query row against `keys`.
+
+    I[s] = sum_h w[h] * ReLU(q[h,:] . k[s,:]): per-head dot products of the
+    bf16 index query with each bf16 index key, ReLU per head, then the fp32
+    per-head weights reduce over heads (v4_lighting_indexer: index_q, index_k,
+    weights [seqlen, batch, heads] fp32).
+    q_row [H, D], keys [n, D], w_row [H]; all converted to fp64.
+    """
+    q64 = np.asarray(q_row, dtype=np.float64)
+    k64 = np.asarray(keys, dtype=np.float64).reshape(-1, q64.shape[1])
+    w64 = np.asarray(w_row, dtype=np.float64)
+    if k64.shape[0] == 0:
+        return np.zeros(0, dtype=np.float64)
+    return _weighted_head_sum(w64, _relu(_dot_products(q64, k64)))
+
+
+def rank_desc(scores: np.ndarray) -> np.ndarray:
+    """Positions of `scores` ordered by (score descending, position ascending).
+
+    A stable lexicographic sort; +0.0 and -0.0 compare equal.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    return np.lexsort((np.arange(scores.shape[0]), -scores))
+
+
+def select_topk(scores: np.ndarray, topk: int):
+    """First `topk` of rank_desc(scores); pad with (-1, -inf).
+
+    Returns (idx int32 [topk], vals float64 [topk]).
+    """
+    order = rank_desc(scores)[:topk]
+    idx = np.full(topk, -1, dtype=np.int32)
+    vals = np.full(topk, NEG_INF, dtype=np.float64)
+    idx[: order.shape[0]] = order
+    vals[: order.shape[0]] = np.asarray(scores, dtype=np.float64)[order]
+    return idx, vals
+
+
+def score_topk(q: np.ndarray, k: np.ndarray, w: np.ndarray, compress_ratio: int, topk: int,
+               rows=None, row_values=False):
+    """Top-k key indices and scores per query (v4_lighting_indexer forward).
+
+    q [S, B, H, D], k [Skv, B, D], w [S, B, H] (SBHD layout) as float arrays
+    holding the bf16 / fp32 input values.  Returns (idx int32 [B, S, topk],
+    vals float64 [B, S, topk]).
+
+    If `rows` (a sequence of query positions t) is given, q and w hold only
+    those rows, in that order ([len(rows), B, ...]); the result is then
+    [B, len(rows), topk].  With `row_values=True` the full score rows are
+    also returned (a list over (b, row) of fp64 arrays of length n_t).
+    """
+    R, B = q.shape[0], q.shape[1]
+    Skv = k.shape[0]
+    positions = list(range(R)) if rows is None else [int(t) for t in rows]
+    assert len(positions) == R
+    idx = np.empty((B, R, topk), dtype=np.int32)
+    vals = np.empty((B, R, topk), dtype=np.float64)
+    full = []
+    for b in range(B):
+        for i, t in enumerate(positions):
+            n_t = visible_keys(t, Skv, compress_ratio)
+            s = head_scores(q[i, b], k[:n_t, b], w[i, b])
+            idx[b, i], vals[b, i] = select_topk(s, topk)
+            if row_values:
+                full.append(s)
+    if row_values:
+        return idx, vals, full
+    return idx, vals
+
+
+# ---------------------------------------------------------------------------
+# Pooled decode selection (glm5next_dsa page)
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(x: np.ndarray):
+    """Round fp64 values to bf16, nearest with ties to even, directly.
+
+    bf16 keeps 8 significant bits.  Writing x = m * 2**e with 0.5 <= |m| < 1,
+    the rounded value is rint(m * 256) * 2**(e - 8), where rint rounds half
+    to even and every step is exact in fp64 (no double rounding through
+    fp32).  Returns (values fp64, bits uint16).  Inputs are finite and far
+    from the bf16 subnormal range.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    bits = (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return r, bits
+
+
+def _slot_softmax(logits: np.ndarray) -> np.ndarray:
+    """Softmax over the pool-slot axis (axis 0) of [KP, D] logits, per channel,
+    with the per-channel maximum subtracted first (exact shift invariance)."""
+    ex = np.exp(logits - logits.max(axis=0, keepdims=True))
+    return ex / ex.sum(axis=0, keepdims=True)
+
+
+def pool_count(N: int, first_key: int, kpool: int) -> int:
+    """P = floor(max(0, N - first_key) / KP): pooling starts at first_key and a
+    trailing partial pool is not a pool (glm5next_dsa, kernel facts)."""
+    return max(0, N - first_key) // kpool
+
+
+def kpool_compress(k_normed: np.ndarray, gate: np.ndarray, valid: np.ndarray,
+                   ape: np.ndarray, first_key: int, kpool: int):
+    """Compress index keys into pool keys (glm5next_dsa: kpool_compress).
+
+    For pool p (tokens tok_j = first_key + p*KP + j, j < KP) and channel c:
+      logits lg_j = gate[tok_j, c] + ape[j, c]
+      a_j = softmax over the slot axis j of lg (per channel)
+      pool_k[p, c] = bf16( sum_j a_j * k_normed[tok_j, c] )
+    pool_valid[p] = all(valid[tok_j]);  pool_tok[p] = tok_0.
+
+    k_normed [N, D] (bf16 values), gate [N, D] fp32, valid [N] (0/1),
+    ape [KP, D] fp32.  Returns dict with pool_k_f64 [P, D] (before rounding),
+    pool_k [P, D] (bf16 values as fp64), pool_k_bits [P, D] uint16,
+    pool_tok [P] int32, pool_valid [P] uint8.
+    """
+    N, D = k_normed.shape
+    KP = kpool
+    P = pool_count(N, first_key, KP)
+    kn = np.asarray(k_normed, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    a = np.asarray(ape, dtype=np.float64)
+    pk = np.empty((P, D), dtype=np.float64)
+    pv = np.empty(P, dtype=np.uint8)
+    pt = np.empty(P, dtype=np.int32)
+    for p in range(P):
+        toks = first_key + p * KP + np.arange(KP)
+        lg = g[toks, :] + a[:KP, :]      # [KP, D] slot logits
+        wts = _slot_softmax(lg)
+        pk[p] = (wts * kn[toks, :]).sum(axis=0)
+        pv[p] = 1 if np.all(np.asarray(valid)[toks] != 0) else 0
+        pt[p] = toks[0]
+    rv, rb = round_to_bf16(pk)
+    return {"pool_k_f64": pk, "pool_k": rv, "pool_k_bits": rb,
+            "pool_tok": pt, "pool_valid": pv}
+
+
+def pooled_index_scores(q: np.ndarray, w: np.ndarray, pool_k: np.ndarray,
+                        pool_valid: np.ndarray) -> np.ndarray:
+    """[Q, P] scores of decode queries against pool keys (glm5next_dsa: index_scores).
+
+    S[q, p] = sum_h w[q, h] * ReLU(q[q, h, :] . pool_k[p, :]) for valid pools;
+    -inf marks an invalid candidate.  No causal mask.
+    q [Q, H, D], w [Q, H], pool_k [P, D], pool_valid [P].
+    """
+    Q = q.shape[0]
+    P = pool_k.shape[0]
+    out = np.empty((Q, P), dtype=np.float64)
+    for i in range(Q):
+        out[i] = head_scores(q[i], pool_k, w[i])
+    out[:, np.asarray(pool_valid) == 0] = NEG_INF
+    return out
+
+
+def topk_pools(scores: np.ndarray, select_k: int):
+    """Keep select_k pool ids per row (glm5next_dsa: topk_pools).
+
+    Valid pools (score > -inf) ranked by (score desc, pool id asc); rows with
+    fewer valid pools are padded with (-1, -inf).  Returns (ids int32
+    [Q, select_k], vals float64 [Q, select_k]).
+    """
+    Q = scores.shape[0]
+    ids = np.full((Q, select_k), -1, dtype=np.int32)
+    vals = np.full((Q, select_k), NEG_INF, dtype=np.float64)
+    for i in range(Q):
+        cand = np.nonzero(np.isfinite(scores[i]))[0]
+        order = cand[rank_desc(scores[i][cand])][:select_k]
+        ids[i, : order.shape[0]] = order
+        vals[i, : order.shape[0]] = scores[i][order]
+    return ids, vals
+
+
+def expand_selection(pool_ids: np.ndarray, first_key: int, kpool: int) -> np.ndarray:
+    """Pool ids -> token ids (glm5next_dsa: expand_selection).
+
+    The row is first filled with -1 (every slot written); then for each
+    selected pool p_i != -1, slots i*KP + j receive first_key + p_i*KP + j.
+    pool_ids [Q, select_k] -> [Q, select_k * KP] int32.
+    """
+    Q, K = pool_ids.shape
+    out = np.full((Q, K * kpool), -1, dtype=np.int32)
+    for q in range(Q):
+        for i in range(K):
+            p = int(pool_ids[q, i])
+            if p != -1:
+                for j in range(kpool):
+                    out[q, i * kpool + j] = first_key + p * kpool + j
+    return out
