@@ -1,0 +1,188 @@
+/*
+ * dsai.h - C ABI of the MI355X (gfx950) DSA lightning-indexer selection library.
+ *
+ * The library computes the DeepSeek-Sparse-Attention indexer's token
+ * selection with hand-written HIP kernels:
+ *
+ *   - dsai_score_topk: per-head index scores of bf16 index_q against bf16
+ *     index_k, ReLU per head, fp32 per-head weights reducing over heads,
+ *     the causal mask under compress_ratio, and a per-query top-k, fused in
+ *     one kernel so the [S, Skv] score matrix never reaches device memory.
+ *     Contract from the NeMo AutoModel page
+ *     "nemo_automodel.components.models.deepseek_v4.kernels.tilelang_indexer"
+ *     (V4IndexerFunction / v4_lighting_indexer: SBHD layout, index_q
+ *     [seqlen, batch, heads, dim] bf16, index_k [seqlen_kv, batch, dim] bf16,
+ *     weights [seqlen, batch, heads] fp32, compress_ratio, topk, result
+ *     [batch, seqlen, topk]).
+ *   - the pooled decode pipeline of the page "Module glm5next_dsa"
+ *     ("Shape of the pipeline"): dsai_kpool_compress -> dsai_index_scores ->
+ *     dsai_topk_pools -> dsai_expand (dsai_select runs the middle two).
+ *
+ * Conventions for every call:
+ *   - Pointers to tensors are DEVICE pointers, owned by the caller; the
+ *     library never keeps them past the call and never allocates device
+ *     memory inside a compute call.  bf16 tensors are passed as `const void*`
+ *     to 2-byte bfloat16 elements.  All tensors are dense, row-major
+ *     (last index fastest), with the shapes given per call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
+ *     only enqueue work on it and return; results are ready when the stream
+ *     reaches that point.
+ *   - Calls return a dsai status (DSAI_OK = 0, negative on error).  When a
+ *     call returns an error before any launch, nothing was enqueued; on
+ *     DSAI_ERR_HIP a launch failed and the HIP error code is kept in the
+ *     handle (dsai_last_hip_error).  No C++ exception crosses the ABI.
+ *   - A handle is used by one host thread at a time.  Calls that share
+ *     output buffers on one stream are ordered by that stream.
+ *   - Argument validation runs on the host before any HIP call, so every
+ *     error code below can be raised without a GPU.
+ */
+#ifndef DSAI_H_
+#define DSAI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define DSAI_OK 0
+#define DSAI_ERR_INVALID_ARG (-1) /* a size, ratio, topk or config value out of range */
+#define DSAI_ERR_UNSUPPORTED (-2) /* a legal request this build does not implement   */
+#define DSAI_ERR_WORKSPACE (-3)   /* workspace pointer NULL or smaller than required   */
+#define DSAI_ERR_NULLPTR (-4)     /* a required pointer is NULL                        */
+#define DSAI_ERR_HIP (-5)         /* a HIP call or kernel launch failed                */
+
+/* Most pool slots kpool_compress holds (the "Module glm5next_dsa" page,
+ * constant KERNEL_MAX_KPOOL: larger index_kpool values are refused at
+ * configuration time instead of silently dropping slots). */
+#define DSAI_MAX_KPOOL 8
+/* Largest topk / select_k the fused selection supports (LDS capacity). */
+#define DSAI_MAX_TOPK 8192
+/* Heads and head dims the kernels are compiled for: heads 1..64
+ * (zero-padded to 16, 32 or 64 on the matrix cores), dim 32, 64 or 128. */
+#define DSAI_MAX_HEADS 64
+
+/* ---- configuration / handle -------------------------------------------- */
+typedef struct dsai_config {
+  int heads;      /* H, index heads per query, 1..64                          */
+  int dim;        /* D, index head dim: 32, 64 or 128                          */
+  int kpool;      /* index_kpool: token slots per pool, 1..DSAI_MAX_KPOOL      */
+  int index_topk; /* tokens selected per pooled row: a nonzero multiple of
+                     kpool (config invariant on the "Module glm5next_dsa"
+                     page); select_k = index_topk / kpool pools per row       */
+  int first_key;  /* first cached token that pools (>= 0)                      */
+  int chunk_rows; /* query rows per dsai_score_topk launch; 0 = one launch     */
+} dsai_config;
+
+typedef struct dsai_context* dsai_handle;
+
+/* Validate `cfg` and create a handle in *out.  Refuses (DSAI_ERR_INVALID_ARG)
+ * kpool outside 1..8, index_topk not a positive multiple of kpool,
+ * index_topk / kpool > DSAI_MAX_TOPK, heads < 1, first_key < 0,
+ * chunk_rows < 0; DSAI_ERR_UNSUPPORTED for heads > 64 or dim not 32/64/128;
+ * DSAI_ERR_NULLPTR for a NULL cfg or out.  Makes no HIP call. */
+int dsai_create(const dsai_config* cfg, dsai_handle* out);
+
+/* Release a handle (NULL is accepted).  Waits for nothing. */
+int dsai_destroy(dsai_handle h);
+
+/* Static text for a status code (never NULL). */
+const char* dsai_status_string(int status);
+
+/* HIP error code (hipError_t value) of the last failed launch on `h`, 0 if none. */
+int dsai_last_hip_error(dsai_handle h);
+
+/* ---- unpooled lightning indexer ---------------------------------------- */
+/* Fused score + causal/compressed mask + top-k (v4_lighting_indexer forward).
+ *
+ *   index_q  [S, B, H, D]  bf16   (SBHD: query position, batch, head, dim)
+ *   index_k  [Skv, B, D]   bf16
+ *   weights  [S, B, H]     fp32
+ *   out_idx  [B, S, topk]  int32  written
+ *   out_score[B, S, topk]  fp32   written
+ *
+ * Score of key s for query position t in batch b:
+ *   I = sum_h weights[t,b,h] * max(0, sum_d index_q[t,b,h,d] * index_k[s,b,d])
+ * (products accumulated in fp32 on the matrix cores).  Key s is visible iff
+ * s < min(Skv, floor((t+1) / compress_ratio)).  Each output row lists the
+ * visible keys with the `topk` largest scores, by score descending and the
+ * lower key index first among equal scores (+0 and -0 are equal); rows with
+ * fewer visible keys are padded with index -1 and score -inf.  Every output
+ * element is written.
+ *
+ * S, Skv, B >= 0 (S == 0 or B == 0: nothing is written or launched);
+ * Skv < 2^31; compress_ratio >= 1; 1 <= topk <= DSAI_MAX_TOPK
+ * (DSAI_ERR_INVALID_ARG otherwise).  topk_indices must be NULL: scoring at
+ * caller-supplied indices returns DSAI_ERR_UNSUPPORTED.  Query rows are
+ * processed in launches of cfg.chunk_rows rows (all rows if 0); no scratch
+ * memory is used. */
+int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
+                    const float* weights, int64_t S, int64_t Skv, int64_t B,
+                    int compress_ratio, int topk, const int32_t* topk_indices,
+                    int32_t* out_idx, float* out_score, void* stream);
+
+/* ---- pooled decode pipeline ("Module glm5next_dsa") -------------------- */
+/* P = floor(max(0, N - first_key) / kpool): the number of pools of a cache
+ * of N tokens (pooling starts at first_key; a trailing partial pool is not a
+ * pool).  Host-only. */
+int dsai_pool_count(dsai_handle h, int64_t N, int64_t* P);
+
+/* kpool_compress: pool p covers tokens first_key + p*KP + j, j < KP.
+ *   k_normed  [N, D] bf16, gate [N, D] fp32, valid [N] uint8 (0 = invalid),
+ *   ape       [KP, D] fp32
+ *   pool_k    [P, D] bf16 written: per channel c, softmax over the slots j
+ *             of (gate[tok_j,c] + ape[j,c]) weighting k_normed[tok_j,c],
+ *             computed in fp32 and rounded to bf16 (nearest even)
+ *   pool_tok  [P] int32 written: first token of the pool
+ *   pool_valid[P] uint8 written: 1 iff every slot's token is valid
+ * N >= 0; nothing is launched when P == 0. */
+int dsai_kpool_compress(dsai_handle h, const void* k_normed, const float* gate,
+                        const uint8_t* valid, const float* ape, int64_t N,
+                        void* pool_k, int32_t* pool_tok, uint8_t* pool_valid,
+                        void* stream);
+
+/* index_scores: [Q, P] fp32 scores of decode queries against pool keys.
+ *   q [Q, H, D] bf16, w [Q, H] fp32, pool_k [P, D] bf16, pool_valid [P] uint8
+ *   scores[q, p] = sum_h w[q,h] * max(0, q[q,h,:] . pool_k[p,:]) if
+ *   pool_valid[p], else -inf (an invalid candidate).  No causal mask.
+ * Q, P >= 0; P < 2^31. */
+int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                      const uint8_t* pool_valid, int64_t Q, int64_t P, float* scores,
+                      void* stream);
+
+/* topk_pools: per row of scores [Q, P] (from dsai_index_scores), the
+ * select_k = index_topk / kpool pools with the largest finite scores, by
+ * score descending and the lower pool id first among equal scores; -inf
+ * marks an invalid pool, which is never selected.  Rows with fewer valid
+ * pools are padded with id -1 / score -inf.
+ *   pool_ids [Q, select_k] int32 written, pool_scores [Q, select_k] fp32 written. */
+int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P,
+                    int32_t* pool_ids, float* pool_scores, void* stream);
+
+/* Bytes of workspace dsai_select needs for Q rows and P pools (the [Q, P]
+ * fp32 score matrix).  Host-only. */
+int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* bytes);
+
+/* dsai_index_scores followed by dsai_topk_pools on one stream, with the
+ * [Q, P] scores held in the caller's `workspace` (at least
+ * dsai_select_workspace_size bytes, 256-byte aligned; DSAI_ERR_WORKSPACE
+ * otherwise).  The workspace is free again once the stream passes the call. */
+int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
+                float* pool_scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* expand_selection: pool ids [Q, select_k] int32 (each -1 or a pool id in
+ * [0, P)) -> token ids [Q, index_topk] int32 (index_topk = select_k *
+ * kpool).  Slot i*kpool + j receives first_key + pool_ids[q,i]*kpool + j,
+ * or -1 when pool_ids[q,i] is negative; every slot is written exactly once.
+ * Q >= 0. */
+int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSAI_H_ */

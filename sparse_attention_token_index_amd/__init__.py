@@ -1,0 +1,306 @@
+"""MI355X (gfx950) DSA lightning-indexer token selection.
+
+A thin ctypes binding over the C ABI in ``include/dsai.h`` (``libdsai.so``,
+built in-tree by ``python -m sparse_attention_token_index_amd.build``).  This
+module only checks and marshals arguments: every step of the selection path
+runs in the library's HIP kernels, on the current PyTorch stream.  PyTorch
+provides device memory and streams.  There is no CPU fallback: without the
+built library, or without tensors on a ROCm GPU, every call raises.
+
+Names follow the C entry points: ``score_topk`` (lightning-indexer score +
+causal/compressed mask + top-k), and the pooled decode pipeline
+``kpool_compress`` -> ``index_scores`` -> ``topk_pools`` -> ``expand``
+(``select`` = ``index_scores`` + ``topk_pools``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["DsaiError", "Indexer", "load_library", "library_path", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdsai.so")
+
+# Every symbol include/dsai.h declares.
+EXPORTS = (
+    "dsai_create", "dsai_destroy", "dsai_status_string", "dsai_last_hip_error",
+    "dsai_score_topk", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
+    "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
+)
+
+DSAI_OK = 0
+DSAI_MAX_KPOOL = 8
+DSAI_MAX_TOPK = 8192
+
+
+class DsaiError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {detail} (status {status})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int), ("dim", ctypes.c_int), ("kpool", ctypes.c_int),
+                ("index_topk", ctypes.c_int), ("first_key", ctypes.c_int),
+                ("chunk_rows", ctypes.c_int)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libdsai.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise DsaiError(-2, "libdsai.so is not built",
+                        f"{p} missing; run `python -m sparse_attention_token_index_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "dsai_create": [ctypes.POINTER(_Config), ctypes.POINTER(vp)],
+        "dsai_destroy": [vp],
+        "dsai_status_string": [c_int],
+        "dsai_last_hip_error": [vp],
+        "dsai_score_topk": [vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, vp, vp, vp],
+        "dsai_pool_count": [vp, i64, ctypes.POINTER(i64)],
+        "dsai_kpool_compress": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp],
+        "dsai_index_scores": [vp, vp, vp, vp, vp, i64, i64, vp, vp],
+        "dsai_topk_pools": [vp, vp, i64, i64, vp, vp, vp],
+        "dsai_select_workspace_size": [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "dsai_select": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp],
+        "dsai_expand": [vp, vp, i64, vp, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "dsai_status_string" else c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise DsaiError(-2, name, "must be a GPU tensor (the HIP path has no CPU fallback)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+class Indexer:
+    """One configured handle of the selection library (dsai_create)."""
+
+    def __init__(self, heads: int, dim: int, kpool: int = 1, index_topk: int = 1,
+                 first_key: int = 0, chunk_rows: int = 0):
+        self._lib = load_library()
+        self.cfg = _Config(heads, dim, kpool, index_topk, first_key, chunk_rows)
+        h = ctypes.c_void_p()
+        st = self._lib.dsai_create(ctypes.byref(self.cfg), ctypes.byref(h))
+        self._check(st, "dsai_create")
+        self._h = h
+
+    # -- plumbing ---------------------------------------------------------
+    def _check(self, st: int, what: str):
+        if st != DSAI_OK:
+            msg = self._lib.dsai_status_string(st).decode()
+            if st == -5 and getattr(self, "_h", None):
+                msg += f" (hipError {self._lib.dsai_last_hip_error(self._h)})"
+            raise DsaiError(st, what, msg)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.dsai_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def heads(self):
+        return self.cfg.heads
+
+    @property
+    def dim(self):
+        return self.cfg.dim
+
+    @property
+    def select_k(self):
+        return self.cfg.index_topk // self.cfg.kpool
+
+    # -- unpooled lightning indexer ----------------------------------------
+    def score_topk(self, index_q: torch.Tensor, index_k: torch.Tensor, weights: torch.Tensor,
+                   compress_ratio: int, topk: int, topk_indices=None,
+                   out_idx: Optional[torch.Tensor] = None,
+                   out_score: Optional[torch.Tensor] = None):
+        """index_q [S,B,H,D] bf16, index_k [Skv,B,D] bf16, weights [S,B,H] fp32 ->
+        (idx [B,S,topk] int32, score [B,S,topk] fp32)."""
+        S, B = index_q.shape[0], index_q.shape[1]
+        Skv = index_k.shape[0]
+        H, D = self.cfg.heads, self.cfg.dim
+        dev = index_q.device
+        _need(index_q, "index_q", torch.bfloat16, (S, B, H, D))
+        _need(index_k, "index_k", torch.bfloat16, (Skv, B, D), dev)
+        _need(weights, "weights", torch.float32, (S, B, H), dev)
+        if out_idx is None:
+            out_idx = torch.empty((B, S, topk), dtype=torch.int32, device=dev)
+        if out_score is None:
+            out_score = torch.empty((B, S, topk), dtype=torch.float32, device=dev)
+        _need(out_idx, "out_idx", torch.int32, (B, S, topk), dev)
+        _need(out_score, "out_score", torch.float32, (B, S, topk), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_score_topk(self._h, _ptr(index_q), _ptr(index_k), _ptr(weights),
+                                           S, Skv, B, int(compress_ratio), int(topk),
+                                           _ptr(topk_indices), _ptr(out_idx), _ptr(out_score),
+                                           _stream(dev))
+        self._check(st, "dsai_score_topk")
+        return out_idx, out_score
+
+    # -- pooled decode pipeline ---------------------------------------------
+    def pool_count(self, N: int) -> int:
+        P = ctypes.c_int64()
+        self._check(self._lib.dsai_pool_count(self._h, int(N), ctypes.byref(P)), "dsai_pool_count")
+        return P.value
+
+    def kpool_compress(self, k_normed, gate, valid, ape, pool_k=None, pool_tok=None,
+                       pool_valid=None):
+        """k_normed [N,D] bf16, gate [N,D] fp32, valid [N] bool/uint8, ape [KP,D] fp32 ->
+        (pool_k [P,D] bf16, pool_tok [P] int32, pool_valid [P] uint8)."""
+        N, D, KP = k_normed.shape[0], self.cfg.dim, self.cfg.kpool
+        dev = k_normed.device
+        if valid.dtype == torch.bool:
+            valid = valid.view(torch.uint8)
+        _need(k_normed, "k_normed", torch.bfloat16, (N, D))
+        _need(gate, "gate", torch.float32, (N, D), dev)
+        _need(valid, "valid", torch.uint8, (N,), dev)
+        _need(ape, "ape", torch.float32, (KP, D), dev)
+        P = self.pool_count(N)
+        if pool_k is None:
+            pool_k = torch.empty((P, D), dtype=torch.bfloat16, device=dev)
+        if pool_tok is None:
+            pool_tok = torch.empty((P,), dtype=torch.int32, device=dev)
+        if pool_valid is None:
+            pool_valid = torch.empty((P,), dtype=torch.uint8, device=dev)
+        _need(pool_k, "pool_k", torch.bfloat16, (P, D), dev)
+        _need(pool_tok, "pool_tok", torch.int32, (P,), dev)
+        _need(pool_valid, "pool_valid", torch.uint8, (P,), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_kpool_compress(self._h, _ptr(k_normed), _ptr(gate), _ptr(valid),
+                                               _ptr(ape), N, _ptr(pool_k), _ptr(pool_tok),
+                                               _ptr(pool_valid), _stream(dev))
+        self._check(st, "dsai_kpool_compress")
+        return pool_k, pool_tok, pool_valid
+
+    def index_scores(self, q, w, pool_k, pool_valid, out=None):
+        """q [Q,H,D] bf16, w [Q,H] fp32, pool_k [P,D] bf16, pool_valid [P] uint8 -> [Q,P] fp32."""
+        Q, P = q.shape[0], pool_k.shape[0]
+        H, D = self.cfg.heads, self.cfg.dim
+        dev = q.device
+        if pool_valid.dtype == torch.bool:
+            pool_valid = pool_valid.view(torch.uint8)
+        _need(q, "q", torch.bfloat16, (Q, H, D))
+        _need(w, "w", torch.float32, (Q, H), dev)
+        _need(pool_k, "pool_k", torch.bfloat16, (P, D), dev)
+        _need(pool_valid, "pool_valid", torch.uint8, (P,), dev)
+        if out is None:
+            out = torch.empty((Q, P), dtype=torch.float32, device=dev)
+        _need(out, "scores", torch.float32, (Q, P), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_index_scores(self._h, _ptr(q), _ptr(w), _ptr(pool_k),
+                                             _ptr(pool_valid), Q, P, _ptr(out), _stream(dev))
+        self._check(st, "dsai_index_scores")
+        return out
+
+    def topk_pools(self, scores, pool_ids=None, pool_scores=None):
+        """scores [Q,P] fp32 -> (pool_ids [Q,select_k] int32, pool_scores [Q,select_k] fp32)."""
+        Q, P = scores.shape
+        dev = scores.device
+        K = self.select_k
+        _need(scores, "scores", torch.float32, (Q, P))
+        if pool_ids is None:
+            pool_ids = torch.empty((Q, K), dtype=torch.int32, device=dev)
+        if pool_scores is None:
+            pool_scores = torch.empty((Q, K), dtype=torch.float32, device=dev)
+        _need(pool_ids, "pool_ids", torch.int32, (Q, K), dev)
+        _need(pool_scores, "pool_scores", torch.float32, (Q, K), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_topk_pools(self._h, _ptr(scores), Q, P, _ptr(pool_ids),
+                                           _ptr(pool_scores), _stream(dev))
+        self._check(st, "dsai_topk_pools")
+        return pool_ids, pool_scores
+
+    def select_workspace_size(self, Q: int, P: int) -> int:
+        n = ctypes.c_size_t()
+        self._check(self._lib.dsai_select_workspace_size(self._h, int(Q), int(P), ctypes.byref(n)),
+                    "dsai_select_workspace_size")
+        return n.value
+
+    def select(self, q, w, pool_k, pool_valid, workspace=None, pool_ids=None, pool_scores=None):
+        """index_scores + topk_pools with the [Q,P] scores in `workspace` (uint8 tensor)."""
+        Q, P = q.shape[0], pool_k.shape[0]
+        H, D = self.cfg.heads, self.cfg.dim
+        dev = q.device
+        K = self.select_k
+        if pool_valid.dtype == torch.bool:
+            pool_valid = pool_valid.view(torch.uint8)
+        _need(q, "q", torch.bfloat16, (Q, H, D))
+        _need(w, "w", torch.float32, (Q, H), dev)
+        _need(pool_k, "pool_k", torch.bfloat16, (P, D), dev)
+        _need(pool_valid, "pool_valid", torch.uint8, (P,), dev)
+        need = self.select_workspace_size(Q, P)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        if pool_ids is None:
+            pool_ids = torch.empty((Q, K), dtype=torch.int32, device=dev)
+        if pool_scores is None:
+            pool_scores = torch.empty((Q, K), dtype=torch.float32, device=dev)
+        _need(pool_ids, "pool_ids", torch.int32, (Q, K), dev)
+        _need(pool_scores, "pool_scores", torch.float32, (Q, K), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_select(self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid),
+                                       Q, P, _ptr(pool_ids), _ptr(pool_scores), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev))
+        self._check(st, "dsai_select")
+        return pool_ids, pool_scores
+
+    def expand(self, pool_ids, tokens=None):
+        """pool_ids [Q,select_k] int32 -> token ids [Q, select_k*kpool] int32 (-1 = invalid)."""
+        Q = pool_ids.shape[0]
+        dev = pool_ids.device
+        K, KP = self.select_k, self.cfg.kpool
+        _need(pool_ids, "pool_ids", torch.int32, (Q, K))
+        if tokens is None:
+            tokens = torch.empty((Q, K * KP), dtype=torch.int32, device=dev)
+        _need(tokens, "tokens", torch.int32, (Q, K * KP), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_expand(self._h, _ptr(pool_ids), Q, _ptr(tokens), _stream(dev))
+        self._check(st, "dsai_expand")
+        return tokens

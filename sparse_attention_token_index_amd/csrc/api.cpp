@@ -1,0 +1,220 @@
+// C ABI of the selection library: configuration validation, argument checks
+// (all on the host, before any HIP call) and dispatch to the kernels.
+#include "dsai.h"
+
+#include <new>
+
+#include "internal.h"
+
+struct dsai_context {
+  dsai_config cfg;
+  int last_hip_error = 0;
+  int device = -1;           // device the cached limits belong to
+  size_t lds_limit = 0;      // max LDS bytes per workgroup on that device
+};
+
+namespace {
+
+constexpr size_t kAlign = 16;
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+int select_k(const dsai_config& c) { return c.index_topk / c.kpool; }
+
+// Config invariants: "Module glm5next_dsa" page (index_topk a nonzero
+// multiple of index_kpool; index_kpool at most KERNEL_MAX_KPOOL, refused
+// rather than truncated) plus the head/dim range the kernels are built for.
+int check_config(const dsai_config& c) {
+  if (c.heads < 1) return DSAI_ERR_INVALID_ARG;
+  if (c.kpool < 1 || c.kpool > DSAI_MAX_KPOOL) return DSAI_ERR_INVALID_ARG;
+  if (c.index_topk < 1 || c.index_topk % c.kpool != 0) return DSAI_ERR_INVALID_ARG;
+  if (select_k(c) > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
+  if (c.first_key < 0 || c.chunk_rows < 0) return DSAI_ERR_INVALID_ARG;
+  if (c.heads > DSAI_MAX_HEADS) return DSAI_ERR_UNSUPPORTED;
+  if (c.dim != 32 && c.dim != 64 && c.dim != 128) return DSAI_ERR_UNSUPPORTED;
+  return DSAI_OK;
+}
+
+int hip_status(dsai_context* h, hipError_t e) {
+  if (e == hipSuccess) return DSAI_OK;
+  h->last_hip_error = (int)e;
+  return DSAI_ERR_HIP;
+}
+
+// LDS limit of the current device, queried once per device.
+hipError_t device_limits(dsai_context* h) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev == h->device) return hipSuccess;
+  int lds = 0;
+  e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  h->device = dev;
+  h->lds_limit = (size_t)lds;
+  return hipSuccess;
+}
+
+constexpr int64_t kI32 = 2147483647;
+
+}  // namespace
+
+extern "C" {
+
+int dsai_create(const dsai_config* cfg, dsai_handle* out) {
+  if (!cfg || !out) return DSAI_ERR_NULLPTR;
+  *out = nullptr;
+  const int st = check_config(*cfg);
+  if (st != DSAI_OK) return st;
+  dsai_context* h = new (std::nothrow) dsai_context;
+  if (!h) return DSAI_ERR_INVALID_ARG;
+  h->cfg = *cfg;
+  *out = h;
+  return DSAI_OK;
+}
+
+int dsai_destroy(dsai_handle h) {
+  delete h;
+  return DSAI_OK;
+}
+
+const char* dsai_status_string(int status) {
+  switch (status) {
+    case DSAI_OK: return "ok";
+    case DSAI_ERR_INVALID_ARG: return "invalid argument";
+    case DSAI_ERR_UNSUPPORTED: return "unsupported";
+    case DSAI_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSAI_ERR_NULLPTR: return "null pointer";
+    case DSAI_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int dsai_last_hip_error(dsai_handle h) { return h ? h->last_hip_error : 0; }
+
+int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, const float* weights,
+                    int64_t S, int64_t Skv, int64_t B, int compress_ratio, int topk,
+                    const int32_t* topk_indices, int32_t* out_idx, float* out_score,
+                    void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (S < 0 || Skv < 0 || B < 0 || compress_ratio < 1) return DSAI_ERR_INVALID_ARG;
+  if (topk < 1 || topk > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
+  if (S > kI32 || Skv > kI32 || B > kI32 || S * B > kI32) return DSAI_ERR_INVALID_ARG;
+  if (topk_indices) return DSAI_ERR_UNSUPPORTED;
+  if (S == 0 || B == 0) return DSAI_OK;
+  if (!index_q || !weights || !out_idx || !out_score) return DSAI_ERR_NULLPTR;
+  if (Skv > 0 && !index_k) return DSAI_ERR_NULLPTR;
+  if (!aligned(index_q) || !aligned(index_k) || !aligned(out_idx) || !aligned(out_score))
+    return DSAI_ERR_INVALID_ARG;
+  hipError_t e = device_limits(h);
+  if (e != hipSuccess) return hip_status(h, e);
+  const int R = dsai::score_topk_rows_per_block(h->cfg.dim, topk, h->lds_limit);
+  if (R < 1) return DSAI_ERR_UNSUPPORTED;
+  dsai::ScoreTopkArgs a;
+  a.q = static_cast<const uint16_t*>(index_q);
+  a.k = static_cast<const uint16_t*>(index_k);
+  a.w = weights;
+  a.S = S; a.Skv = Skv; a.B = B;
+  a.H = h->cfg.heads; a.D = h->cfg.dim; a.ratio = compress_ratio; a.topk = topk;
+  a.chunk_rows = h->cfg.chunk_rows;
+  a.out_idx = out_idx; a.out_score = out_score;
+  return hip_status(h, dsai::launch_score_topk(a, R, static_cast<hipStream_t>(stream)));
+}
+
+int dsai_pool_count(dsai_handle h, int64_t N, int64_t* P) {
+  if (!h || !P) return DSAI_ERR_NULLPTR;
+  if (N < 0) return DSAI_ERR_INVALID_ARG;
+  const int64_t avail = N - h->cfg.first_key;
+  *P = avail > 0 ? avail / h->cfg.kpool : 0;
+  return DSAI_OK;
+}
+
+int dsai_kpool_compress(dsai_handle h, const void* k_normed, const float* gate,
+                        const uint8_t* valid, const float* ape, int64_t N, void* pool_k,
+                        int32_t* pool_tok, uint8_t* pool_valid, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (N < 0 || N > kI32) return DSAI_ERR_INVALID_ARG;
+  int64_t P = 0;
+  dsai_pool_count(h, N, &P);
+  if (P == 0) return DSAI_OK;
+  if (!k_normed || !gate || !valid || !ape || !pool_k || !pool_tok || !pool_valid)
+    return DSAI_ERR_NULLPTR;
+  if (!aligned(k_normed) || !aligned(gate) || !aligned(ape) || !aligned(pool_k))
+    return DSAI_ERR_INVALID_ARG;
+  dsai::KpoolArgs a;
+  a.k_normed = static_cast<const uint16_t*>(k_normed);
+  a.gate = gate; a.valid = valid; a.ape = ape;
+  a.D = h->cfg.dim; a.KP = h->cfg.kpool; a.first_key = h->cfg.first_key; a.P = P;
+  a.pool_k = static_cast<uint16_t*>(pool_k); a.pool_tok = pool_tok; a.pool_valid = pool_valid;
+  return hip_status(h, dsai::launch_kpool(a, static_cast<hipStream_t>(stream)));
+}
+
+int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                      const uint8_t* pool_valid, int64_t Q, int64_t P, float* scores,
+                      void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Q == 0 || P == 0) return DSAI_OK;
+  if (!q || !w || !pool_k || !pool_valid || !scores) return DSAI_ERR_NULLPTR;
+  if (!aligned(q) || !aligned(pool_k)) return DSAI_ERR_INVALID_ARG;
+  dsai::PooledScoresArgs a;
+  a.q = static_cast<const uint16_t*>(q); a.w = w;
+  a.pool_k = static_cast<const uint16_t*>(pool_k); a.pool_valid = pool_valid;
+  a.Q = Q; a.P = P; a.H = h->cfg.heads; a.D = h->cfg.dim; a.scores = scores;
+  return hip_status(h, dsai::launch_pooled_scores(a, static_cast<hipStream_t>(stream)));
+}
+
+int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, int32_t* pool_ids,
+                    float* pool_scores, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Q == 0) return DSAI_OK;
+  if (!pool_ids || !pool_scores || (P > 0 && !scores)) return DSAI_ERR_NULLPTR;
+  hipError_t e = device_limits(h);
+  if (e != hipSuccess) return hip_status(h, e);
+  if (dsai::topk_rows_lds_bytes(select_k(h->cfg)) > h->lds_limit) return DSAI_ERR_UNSUPPORTED;
+  dsai::TopkPoolsArgs a;
+  a.scores = scores; a.Q = Q; a.P = P; a.sel = select_k(h->cfg);
+  a.pool_ids = pool_ids; a.pool_scores = pool_scores;
+  return hip_status(h, dsai::launch_topk_pools(a, static_cast<hipStream_t>(stream)));
+}
+
+int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* bytes) {
+  if (!h || !bytes) return DSAI_ERR_NULLPTR;
+  if (Q < 0 || P < 0) return DSAI_ERR_INVALID_ARG;
+  *bytes = (size_t)Q * (size_t)P * sizeof(float);
+  return DSAI_OK;
+}
+
+int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
+                float* pool_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Q == 0) return DSAI_OK;
+  size_t need = 0;
+  dsai_select_workspace_size(h, Q, P, &need);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return DSAI_ERR_WORKSPACE;
+  int st = dsai_index_scores(h, q, w, pool_k, pool_valid, Q, P, static_cast<float*>(workspace),
+                             stream);
+  if (st != DSAI_OK) return st;
+  return dsai_topk_pools(h, static_cast<const float*>(workspace), Q, P, pool_ids, pool_scores,
+                         stream);
+}
+
+int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,
+                void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (Q < 0 || Q > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Q == 0) return DSAI_OK;
+  if (!pool_ids || !tokens) return DSAI_ERR_NULLPTR;
+  if (!aligned(tokens)) return DSAI_ERR_INVALID_ARG;
+  dsai::ExpandArgs a;
+  a.pool_ids = pool_ids; a.Q = Q; a.sel = select_k(h->cfg); a.KP = h->cfg.kpool;
+  a.first_key = h->cfg.first_key; a.tokens = tokens;
+  return hip_status(h, dsai::launch_expand(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

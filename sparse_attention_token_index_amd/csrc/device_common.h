@@ -1,0 +1,98 @@
+// Device helpers shared by the selection kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsai {
+
+constexpr int kWave = 64;
+
+// Pointers into LDS carry the LDS address space so helpers that are not
+// inlined still compile to ds_* instructions.
+#define DSAI_LDS __attribute__((address_space(3)))
+typedef DSAI_LDS uint32_t lds_u32;
+typedef DSAI_LDS char lds_char;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Make LDS writes of this wave visible to its other lanes and keep the
+// compiler from moving LDS accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Order-preserving map of an fp32 score to uint32: a > b as floats iff
+// key(a) > key(b); -0 is mapped like +0 so the two compare equal.  Inputs
+// are finite or -inf (never NaN).
+__device__ __forceinline__ uint32_t ord_key(float s) {
+  uint32_t b = __float_as_uint(s);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float ord_to_float(uint32_t u) {
+  uint32_t b = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(b);
+}
+
+// Inclusive sum over lanes [0, lane].
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t y = __shfl_up(x, off);
+    if (l >= off) x += y;
+  }
+  return x;
+}
+
+// Inclusive sum over lanes [lane, 63].
+__device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t y = __shfl_down(x, off);
+    if (l + off < kWave) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_and(uint32_t x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x &= __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x |= __shfl_xor(x, off);
+  return x;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+}  // namespace dsai

@@ -1,0 +1,267 @@
+// Pooled decode selection: kpool_compress -> index_scores -> topk_pools ->
+// expand_selection (page "Module glm5next_dsa", "Shape of the pipeline").
+#include "internal.h"
+#include "score_tile.h"
+#include "topk_wave.h"
+
+namespace dsai {
+
+// ---------------------------------------------------------------------------
+// kpool_compress (glm5next_dsa: kernel facts - the pool softmax runs over the
+// pool-slot axis, per channel; pooling starts at first_key; a pool counts only
+// if all of its slots are valid).  Streaming: one thread per (pool, 8-channel
+// group); each reads KP x (32 B gate + 16 B keys) with 16-byte loads,
+// consecutive threads covering consecutive channels of a token row.
+// ---------------------------------------------------------------------------
+template <int KP>
+__global__ __launch_bounds__(256) void kpool_kernel(
+    const uint16_t* __restrict__ kn, const float* __restrict__ gate,
+    const uint8_t* __restrict__ valid, const float* __restrict__ ape, int D, int64_t first_key,
+    int64_t P, int groups_log2, uint16_t* __restrict__ pool_k, int32_t* __restrict__ pool_tok,
+    uint8_t* __restrict__ pool_valid) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t p = tid >> groups_log2;
+  if (p >= P) return;
+  const int cg = (int)(tid & ((1 << groups_log2) - 1));
+  const int c0 = cg * 8;
+  const int64_t tok0 = first_key + p * KP;
+
+  float lg[KP][8];
+  float kv[KP][8];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const int64_t row = (tok0 + j) * D + c0;
+    const float4 g0 = *reinterpret_cast<const float4*>(gate + row);
+    const float4 g1 = *reinterpret_cast<const float4*>(gate + row + 4);
+    const float4 a0 = *reinterpret_cast<const float4*>(ape + j * D + c0);
+    const float4 a1 = *reinterpret_cast<const float4*>(ape + j * D + c0 + 4);
+    const uint4 kk = *reinterpret_cast<const uint4*>(kn + row);
+    lg[j][0] = g0.x + a0.x; lg[j][1] = g0.y + a0.y; lg[j][2] = g0.z + a0.z; lg[j][3] = g0.w + a0.w;
+    lg[j][4] = g1.x + a1.x; lg[j][5] = g1.y + a1.y; lg[j][6] = g1.z + a1.z; lg[j][7] = g1.w + a1.w;
+    const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kv[j][2 * i] = __uint_as_float(kw[i] << 16);
+      kv[j][2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
+    }
+  }
+  uint32_t outw[4];
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    float r[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int c = i + cc;
+      float mx = lg[0][c];
+#pragma unroll
+      for (int j = 1; j < KP; ++j) mx = fmaxf(mx, lg[j][c]);
+      float den = 0.f, num = 0.f;
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        const float e = expf(lg[j][c] - mx);
+        den += e;
+        num = fmaf(e, kv[j][c], num);
+      }
+      r[cc] = num / den;
+    }
+    outw[i / 2] = (uint32_t)f32_to_bf16_rne(r[0]) | ((uint32_t)f32_to_bf16_rne(r[1]) << 16);
+  }
+  *reinterpret_cast<uint4*>(pool_k + p * D + c0) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  if (cg == 0) {
+    uint8_t all = 1;
+#pragma unroll
+    for (int j = 0; j < KP; ++j) all &= (valid[tok0 + j] != 0) ? 1 : 0;
+    pool_valid[p] = all;
+    pool_tok[p] = (int32_t)tok0;
+  }
+}
+
+hipError_t launch_kpool(const KpoolArgs& a, hipStream_t st) {
+  if (a.P <= 0) return hipSuccess;
+  const int groups = a.D / 8;
+  int glog = 0;
+  while ((1 << glog) < groups) ++glog;
+  const int64_t threads = a.P << glog;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+#define DSAI_KP(kp)                                                                             \
+  case kp:                                                                                      \
+    hipLaunchKernelGGL(kpool_kernel<kp>, dim3(blocks), dim3(256), 0, st, a.k_normed, a.gate,    \
+                       a.valid, a.ape, a.D, a.first_key, a.P, glog, a.pool_k, a.pool_tok,       \
+                       a.pool_valid);                                                           \
+    break;
+  switch (a.KP) {
+    DSAI_KP(1) DSAI_KP(2) DSAI_KP(3) DSAI_KP(4) DSAI_KP(5) DSAI_KP(6) DSAI_KP(7) DSAI_KP(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef DSAI_KP
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// index_scores: [Q, P] scores of decode queries against pool keys, -inf for
+// invalid candidates (glm5next_dsa: "[Q, P] scores + candidate validity").
+// Grid (pool blocks, row blocks of 4); each block stages its pool keys in
+// 64-key LDS tiles shared by its 4 query rows (one per wavefront).
+// ---------------------------------------------------------------------------
+constexpr int kPoolTilesPerBlock = 4;
+
+template <int HP, int D>
+__global__ __launch_bounds__(256) void pooled_scores_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint16_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_valid, int Q, int P,
+    int H, int pool_blocks, float* __restrict__ scores) {
+  using G = TileGeom<D>;
+  __shared__ __align__(16) char tile_raw[G::kTileBytes];
+  lds_char* tile = (lds_char*)tile_raw;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int pb = blockIdx.x % pool_blocks;
+  const int row = (blockIdx.x / pool_blocks) * 4 + wave;
+  const bool active = row < Q;
+  TileScorer<HP, D> sc;
+  sc.load_query(q + (int64_t)(active ? row : 0) * H * D, w + (int64_t)(active ? row : 0) * H, H,
+                active);
+  const int p0 = pb * kPoolTilesPerBlock * G::kTileKeys;
+  int ntiles = (P - p0 + G::kTileKeys - 1) / G::kTileKeys;
+  if (ntiles > kPoolTilesPerBlock) ntiles = kPoolTilesPerBlock;
+  TileLoader<D, 256> ld;
+  ld.load(pool_k, D, p0, P);
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    ld.store(tile);
+    __syncthreads();
+    if (it + 1 < ntiles) ld.load(pool_k, D, p0 + (it + 1) * G::kTileKeys, P);
+    if (active) {
+      const float s = sc.score(tile);
+      const int p = p0 + it * G::kTileKeys + lane;
+      if (p < P) scores[(int64_t)row * P + p] = pool_valid[p] ? s : -__builtin_inff();
+    }
+  }
+}
+
+template <int HP, int D>
+static hipError_t launch_scores_t(const PooledScoresArgs& a, hipStream_t st) {
+  const int per_block = kPoolTilesPerBlock * 64;
+  const int64_t pool_blocks = (a.P + per_block - 1) / per_block;
+  const int64_t blocks = pool_blocks * ((a.Q + 3) / 4);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((pooled_scores_kernel<HP, D>), dim3((unsigned)blocks), dim3(256), 0, st, a.q,
+                     a.w, a.pool_k, a.pool_valid, (int)a.Q, (int)a.P, a.H, (int)pool_blocks,
+                     a.scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_pooled_scores(const PooledScoresArgs& a, hipStream_t st) {
+  if (a.Q <= 0 || a.P <= 0) return hipSuccess;
+  const int HP = a.H <= 16 ? 16 : (a.H <= 32 ? 32 : 64);
+#define DSAI_CASE(hp, d) \
+  if (HP == hp && a.D == d) return launch_scores_t<hp, d>(a, st);
+  DSAI_CASE(16, 32) DSAI_CASE(16, 64) DSAI_CASE(16, 128)
+  DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
+  DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)
+#undef DSAI_CASE
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// topk_pools: one wavefront per row streams the row's P scores through the
+// same threshold filter / radix select / stable sort as the fused indexer.
+// -inf marks an invalid candidate and never enters the store.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ scores, int Q,
+                                                        int P, int sel, int cap,
+                                                        int32_t* __restrict__ ids,
+                                                        float* __restrict__ out_scores) {
+  extern __shared__ __align__(16) char smem_raw[];
+  lds_char* smem = (lds_char*)smem_raw;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int row = blockIdx.x * 4 + wave;
+  const size_t per_wave = (size_t)2 * cap * 4 + 1024 + 16 * kWave * 4;
+  lds_char* mine = smem + wave * per_wave;
+  lds_u32* key = (lds_u32*)mine;
+  const RowStore rs{key, key + cap, key + 2 * cap};
+  lds_u32* cnt = key + 2 * cap + 256;
+  if (row >= Q) return;
+  const float* srow = scores + (int64_t)row * P;
+  uint32_t count = 0u, tau = 0u;
+  for (int base = 0; base < P; base += kWave) {
+    const int p = base + lane;
+    const float s = p < P ? srow[p] : -__builtin_inff();
+    const uint32_t u = ord_key(s);
+    const bool pass = (p < P) && (s != -__builtin_inff()) && (u > tau);
+    wave_append(rs, count, pass, u, (uint32_t)p);
+    if (count > (uint32_t)(cap - kWave)) count = wave_keep_topk(rs, count, sel, &tau);
+  }
+  wave_lds_sync();
+  count = wave_keep_topk(rs, count, sel, &tau);
+  const SortedView sv = wave_sort_desc(rs, count, (uint32_t)sel + 64u, cnt);
+  wave_write_row(sv, count, sel, ids + (int64_t)row * sel, out_scores + (int64_t)row * sel);
+}
+
+size_t topk_rows_lds_bytes(int sel) {
+  const int cap = 2 * sel + 128;
+  return 4 * ((size_t)2 * cap * 4 + 1024 + 16 * kWave * 4);
+}
+
+hipError_t launch_topk_pools(const TopkPoolsArgs& a, hipStream_t st) {
+  if (a.Q <= 0) return hipSuccess;
+  const int cap = 2 * a.sel + 128;
+  const size_t lds = topk_rows_lds_bytes(a.sel);
+  hipError_t e = hipFuncSetAttribute((const void*)topk_rows_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((a.Q + 3) / 4)), dim3(256), lds, st,
+                     a.scores, (int)a.Q, (int)a.P, a.sel, cap, a.pool_ids, a.pool_scores);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// expand_selection (glm5next_dsa: writes -1 over the whole index row before
+// any index, so every slot is written).  One thread per (row, selected pool)
+// writes the pool's KP slots: -1 for a missing pool, else the pool's token
+// ids; each output slot is written exactly once, coalesced.
+// ---------------------------------------------------------------------------
+template <int KP>
+__global__ __launch_bounds__(256) void expand_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                     int first_key, int32_t* __restrict__ tok) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const int32_t p = ids[e];
+  int32_t v[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) v[j] = (p < 0) ? -1 : first_key + p * KP + j;
+  int32_t* o = tok + e * KP;
+  if constexpr (KP == 4) {
+    *reinterpret_cast<int4*>(o) = make_int4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (KP == 8) {
+    reinterpret_cast<int4*>(o)[0] = make_int4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<int4*>(o)[1] = make_int4(v[4], v[5], v[6], v[7]);
+  } else if constexpr (KP == 2) {
+    *reinterpret_cast<int2*>(o) = make_int2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KP; ++j) o[j] = v[j];
+  }
+}
+
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t st) {
+  const int64_t n = a.Q * a.sel;
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+#define DSAI_KP(kp)                                                                           \
+  case kp:                                                                                    \
+    hipLaunchKernelGGL(expand_kernel<kp>, dim3(blocks), dim3(256), 0, st, a.pool_ids, n,      \
+                       a.first_key, a.tokens);                                                \
+    break;
+  switch (a.KP) {
+    DSAI_KP(1) DSAI_KP(2) DSAI_KP(3) DSAI_KP(4) DSAI_KP(5) DSAI_KP(6) DSAI_KP(7) DSAI_KP(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef DSAI_KP
+  return hipGetLastError();
+}
+
+}  // namespace dsai

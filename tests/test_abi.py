@@ -1,0 +1,180 @@
+"""Host-side checks of the C ABI (CPU only: no compute call reaches the GPU).
+
+The library must load, export every entry point include/dsai.h declares, and
+refuse bad configurations and arguments with the documented status codes
+before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsai.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, NULLPTR = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import sparse_attention_token_index_amd as dsai
+    if not os.path.exists(dsai.library_path()):
+        import sparse_attention_token_index_amd.build as b
+        b.build()
+    return dsai.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsai_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    import sparse_attention_token_index_amd as dsai
+    assert declared_symbols() == sorted(dsai.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_exports_are_c_symbols():
+    import subprocess
+    import sparse_attention_token_index_amd as dsai
+    out = subprocess.run(["nm", "-D", "--defined-only", dsai.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dsai_[a-z_]+)\b", out))
+    assert set(declared_symbols()) <= exported
+
+
+def _cfg(heads=64, dim=128, kpool=4, index_topk=512, first_key=0, chunk_rows=0):
+    import sparse_attention_token_index_amd as dsai
+    return dsai._Config(heads, dim, kpool, index_topk, first_key, chunk_rows)
+
+
+def _create(lib, **kw):
+    h = ctypes.c_void_p()
+    st = lib.dsai_create(ctypes.byref(_cfg(**kw)), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, OK),
+    ({"heads": 4, "dim": 32, "kpool": 1, "index_topk": 1}, OK),
+    ({"kpool": 8, "index_topk": 8}, OK),
+    ({"kpool": 0}, INVALID),
+    ({"kpool": 9, "index_topk": 18}, INVALID),            # above KERNEL_MAX_KPOOL: refused
+    ({"kpool": 4, "index_topk": 510}, INVALID),           # not a multiple of kpool
+    ({"kpool": 4, "index_topk": 0}, INVALID),             # zero is not allowed
+    ({"kpool": 1, "index_topk": 8193}, INVALID),          # select_k above the max
+    ({"heads": 0}, INVALID),
+    ({"first_key": -1}, INVALID),
+    ({"chunk_rows": -5}, INVALID),
+    ({"heads": 65}, UNSUPPORTED),
+    ({"dim": 96}, UNSUPPORTED),
+    ({"dim": 256}, UNSUPPORTED),
+])
+def test_create_validation(lib, kw, status):
+    st, h = _create(lib, **kw)
+    assert st == status
+    if st == OK:
+        assert h.value
+        assert lib.dsai_destroy(h) == OK
+    else:
+        assert not h.value
+
+
+def test_create_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.dsai_create(None, ctypes.byref(h)) == NULLPTR
+    assert lib.dsai_create(ctypes.byref(_cfg()), None) == NULLPTR
+    assert lib.dsai_destroy(None) == OK
+
+
+def test_status_strings(lib):
+    for st in (OK, INVALID, UNSUPPORTED, WORKSPACE, NULLPTR, -5, 42):
+        assert isinstance(lib.dsai_status_string(st), bytes)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def test_score_topk_argument_errors(lib):
+    st, h = _create(lib)
+    assert st == OK
+    call = lambda S=8, Skv=8, B=1, r=1, topk=4, tki=None, q=FAKE, k=FAKE, w=FAKE, oi=FAKE, os_=FAKE: \
+        lib.dsai_score_topk(h, q, k, w, S, Skv, B, r, topk, tki, oi, os_, None)
+    assert call(S=-1) == INVALID
+    assert call(Skv=-1) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(r=0) == INVALID
+    assert call(topk=0) == INVALID
+    assert call(topk=8193) == INVALID
+    assert call(S=2 ** 31) == INVALID
+    assert call(tki=FAKE) == UNSUPPORTED          # supplied indices: not built
+    assert call(S=0) == OK                        # empty: nothing launched
+    assert call(B=0) == OK
+    assert call(q=None) == NULLPTR
+    assert call(w=None) == NULLPTR
+    assert call(oi=None) == NULLPTR
+    assert call(os_=None) == NULLPTR
+    assert call(k=None) == NULLPTR                # Skv > 0 needs keys
+    assert call(q=ctypes.c_void_p(0x10002)) == INVALID  # misaligned
+    assert lib.dsai_score_topk(None, FAKE, FAKE, FAKE, 8, 8, 1, 1, 4, None, FAKE, FAKE, None) == NULLPTR
+    lib.dsai_destroy(h)
+
+
+def test_pooled_argument_errors(lib):
+    st, h = _create(lib, kpool=4, index_topk=512, first_key=3)
+    assert st == OK
+    P = ctypes.c_int64()
+    assert lib.dsai_pool_count(h, 65536, ctypes.byref(P)) == OK and P.value == (65536 - 3) // 4
+    assert lib.dsai_pool_count(h, 2, ctypes.byref(P)) == OK and P.value == 0
+    assert lib.dsai_pool_count(h, 6, ctypes.byref(P)) == OK and P.value == 0   # partial pool only
+    assert lib.dsai_pool_count(h, 7, ctypes.byref(P)) == OK and P.value == 1
+    assert lib.dsai_pool_count(h, -1, ctypes.byref(P)) == INVALID
+    assert lib.dsai_pool_count(h, 5, None) == NULLPTR
+    # kpool_compress
+    kp = lambda N=64, *ptrs: lib.dsai_kpool_compress(h, *(ptrs or (FAKE,) * 4), N, FAKE, FAKE, FAKE, None)
+    assert kp(-1) == INVALID
+    assert kp(3) == OK                                 # no pool: nothing launched
+    assert lib.dsai_kpool_compress(h, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == NULLPTR
+    assert lib.dsai_kpool_compress(h, FAKE, FAKE, FAKE, FAKE, 64, None, FAKE, FAKE, None) == NULLPTR
+    # index_scores
+    assert lib.dsai_index_scores(h, FAKE, FAKE, FAKE, FAKE, -1, 5, FAKE, None) == INVALID
+    assert lib.dsai_index_scores(h, FAKE, FAKE, FAKE, FAKE, 0, 5, FAKE, None) == OK
+    assert lib.dsai_index_scores(h, None, FAKE, FAKE, FAKE, 2, 5, FAKE, None) == NULLPTR
+    # topk_pools
+    assert lib.dsai_topk_pools(h, FAKE, -2, 5, FAKE, FAKE, None) == INVALID
+    assert lib.dsai_topk_pools(h, FAKE, 0, 5, FAKE, FAKE, None) == OK
+    assert lib.dsai_topk_pools(h, FAKE, 2, 5, None, FAKE, None) == NULLPTR
+    # select: workspace
+    need = ctypes.c_size_t()
+    assert lib.dsai_select_workspace_size(h, 64, 16384, ctypes.byref(need)) == OK
+    assert need.value == 64 * 16384 * 4
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, 64, 16384, FAKE, FAKE, None, 0, None) == WORKSPACE
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, 64, 16384, FAKE, FAKE, FAKE, need.value - 1,
+                           None) == WORKSPACE
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, 64, 16384, FAKE, FAKE,
+                           ctypes.c_void_p(0x10010), need.value, None) == WORKSPACE   # not 256-aligned
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, -1, 16384, FAKE, FAKE, FAKE, 0, None) == INVALID
+    # expand
+    assert lib.dsai_expand(h, FAKE, -1, FAKE, None) == INVALID
+    assert lib.dsai_expand(h, FAKE, 0, FAKE, None) == OK
+    assert lib.dsai_expand(h, None, 3, FAKE, None) == NULLPTR
+    assert lib.dsai_expand(h, FAKE, 3, None, None) == NULLPTR
+    lib.dsai_destroy(h)
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import sparse_attention_token_index_amd as dsai
+    ix = dsai.Indexer(heads=4, dim=32)
+    q = torch.zeros(8, 1, 4, 32, dtype=torch.bfloat16)
+    k = torch.zeros(8, 1, 32, dtype=torch.bfloat16)
+    w = torch.zeros(8, 1, 4)
+    with pytest.raises(dsai.DsaiError):
+        ix.score_topk(q, k, w, 1, 4)

@@ -1,0 +1,205 @@
+"""GPU parity of the fused score + mask + top-k kernel against the CPU oracle.
+
+Every case runs the HIP path through the C ABI (Python binding) on seeded
+synthetic inputs and compares with the fp64 oracle under the rules in
+tests/parity.py; integer-valued cases (exact in fp32) must match bit for
+bit, ties and order included.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as SY
+from parity import check_topk_rows, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsai():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import sparse_attention_token_index_amd as m
+    m.load_library()
+    return m
+
+
+def to_gpu_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_gpu(dsai, case, inp, chunk_rows=None, out=None):
+    ix = dsai.Indexer(heads=case.H, dim=case.D,
+                      chunk_rows=case.chunk_rows if chunk_rows is None else chunk_rows)
+    q = to_gpu_bf16(inp["q_bits"])
+    k = to_gpu_bf16(inp["k_bits"])
+    w = torch.from_numpy(inp["w"]).cuda()
+    oi, os_ = (None, None) if out is None else out
+    idx, sc = ix.score_topk(q, k, w, case.compress_ratio, case.topk, out_idx=oi, out_score=os_)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def oracle_rows(case, rows, q_bits_rows, k_bits, w_rows):
+    q = SY.bf16_bits_to_f32(q_bits_rows).astype(np.float64)
+    k = SY.bf16_bits_to_f32(k_bits).astype(np.float64)
+    return oracle.score_topk(q, k, w_rows.astype(np.float64), case.compress_ratio, case.topk,
+                             rows=rows, row_values=True)
+
+
+def compare(case, gidx, gsc, rows, full):
+    labels, gi, gs = [], [], []
+    for b in range(case.B):
+        for t in rows:
+            labels.append(f"{case.name} b={b} t={t}")
+            gi.append(gidx[b, t])
+            gs.append(gsc[b, t])
+    check_topk_rows(np.array(gi), np.array(gs), full, case.topk, labels)
+
+
+MEDIUM = [
+    SY.IndexerCase("h64d128_r1_k100", B=2, S=700, Skv=700, H=64, D=128, compress_ratio=1,
+                   topk=100, w_var=1 / 64, seed=11),
+    SY.IndexerCase("h32d64_r3_k64", B=1, S=1000, Skv=300, H=32, D=64, compress_ratio=3,
+                   topk=64, w_var=1 / 32, seed=12),
+    SY.IndexerCase("h4d32_r1_k16_compactions", B=1, S=1500, Skv=1500, H=4, D=32,
+                   compress_ratio=1, topk=16, w_var=1 / 4, seed=13),
+    SY.IndexerCase("h64d128_k2048_sortall", B=1, S=2300, Skv=2300, H=64, D=128,
+                   compress_ratio=1, topk=2048, w_var=1 / 64, seed=14),
+    SY.IndexerCase("h20d128_r4_pad_heads", B=3, S=900, Skv=200, H=20, D=128, compress_ratio=4,
+                   topk=37, w_var=1 / 20, seed=15),
+    SY.IndexerCase("topk_gt_skv", B=1, S=130, Skv=100, H=64, D=128, compress_ratio=1,
+                   topk=200, w_var=1 / 64, seed=16),
+    SY.IndexerCase("h64d32_k1", B=1, S=333, Skv=333, H=64, D=32, compress_ratio=1, topk=1,
+                   w_var=1 / 64, seed=17),
+    SY.IndexerCase("h16d64_r2_k300", B=2, S=777, Skv=500, H=16, D=64, compress_ratio=2,
+                   topk=300, w_var=1 / 16, seed=18),
+    SY.IndexerCase("h64d128_k4096", B=1, S=4200, Skv=4200, H=64, D=128, compress_ratio=1,
+                   topk=4096, w_var=1 / 64, seed=19),
+]
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=[c.name for c in MEDIUM])
+def test_medium_parity(dsai, case):
+    log(f"[gpu] medium parity {case}")
+    inp = SY.indexer_inputs(case)
+    gidx, gsc = run_gpu(dsai, case, inp)
+    rows = list(range(case.S))
+    if case.S * case.B > 1500:  # keep the oracle to seconds: every row near the ends, a sample inside
+        rng = np.random.default_rng(case.seed)
+        rows = sorted(set(range(0, 40)) | set(range(case.S - 40, case.S)) |
+                      set(rng.choice(case.S, 300, replace=False).tolist()))
+    _, _, full = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
+    compare(case, gidx, gsc, rows, full)
+
+
+INTEGER = [
+    SY.IndexerCase("int_h64d128_r1", B=1, S=600, Skv=600, H=64, D=128, compress_ratio=1,
+                   topk=50, w_var=0, integer=True, seed=21),
+    SY.IndexerCase("int_h4d32_r2", B=2, S=400, Skv=300, H=4, D=32, compress_ratio=2, topk=40,
+                   w_var=0, integer=True, seed=22),
+    SY.IndexerCase("int_h32d128_k700", B=1, S=900, Skv=900, H=32, D=128, compress_ratio=1,
+                   topk=700, w_var=0, integer=True, seed=23),
+]
+
+
+@pytest.mark.parametrize("case", INTEGER, ids=[c.name for c in INTEGER])
+def test_integer_inputs_bit_exact(dsai, case):
+    """Small-integer q, k and power-of-two weights: every fp32 step on the GPU
+    is exact, so indices, order, ties and scores must equal the oracle's."""
+    log(f"[gpu] integer bit-exact {case}")
+    inp = SY.indexer_inputs(case)
+    gidx, gsc = run_gpu(dsai, case, inp)
+    oidx, ovals, _ = oracle_rows(case, list(range(case.S)), inp["q_bits"], inp["k_bits"], inp["w"])
+    assert np.array_equal(gidx, oidx), np.argwhere(gidx != oidx)[:10]
+    assert np.array_equal(gsc.astype(np.float64), ovals)   # -0.0 == +0.0
+
+
+def test_chunked_launches_match_single_launch(dsai):
+    case = MEDIUM[0]
+    log("[gpu] chunking")
+    inp = SY.indexer_inputs(case)
+    a = run_gpu(dsai, case, inp, chunk_rows=0)
+    b = run_gpu(dsai, case, inp, chunk_rows=64)
+    c = run_gpu(dsai, case, inp, chunk_rows=1)
+    for x in (b, c):
+        assert np.array_equal(a[0], x[0])
+        assert np.array_equal(a[1].view(np.uint32), x[1].view(np.uint32))
+
+
+def test_deterministic_and_every_slot_written(dsai):
+    case = MEDIUM[3]
+    log("[gpu] determinism + sentinel")
+    inp = SY.indexer_inputs(case)
+    shape = (case.B, case.S, case.topk)
+    oi = torch.full(shape, -12345, dtype=torch.int32, device="cuda")
+    os_ = torch.full(shape, 0, dtype=torch.int32, device="cuda").fill_(0x7FBFFFFF).view(torch.float32)
+    a = run_gpu(dsai, case, inp, out=(oi, os_))
+    assert not np.any(a[0] == -12345)
+    assert not np.any(a[1].view(np.uint32) == 0x7FBFFFFF)
+    b = run_gpu(dsai, case, inp)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_empty_and_degenerate_shapes(dsai):
+    log("[gpu] degenerate shapes")
+    ix = dsai.Indexer(heads=64, dim=128)
+    dev = "cuda"
+    # S == 0: nothing to do
+    idx, sc = ix.score_topk(torch.zeros(0, 1, 64, 128, dtype=torch.bfloat16, device=dev),
+                            torch.zeros(5, 1, 128, dtype=torch.bfloat16, device=dev),
+                            torch.zeros(0, 1, 64, device=dev), 1, 8)
+    assert idx.shape == (1, 0, 8)
+    # Skv == 0: every row padded
+    idx, sc = ix.score_topk(torch.ones(7, 2, 64, 128, dtype=torch.bfloat16, device=dev),
+                            torch.zeros(0, 2, 128, dtype=torch.bfloat16, device=dev),
+                            torch.ones(7, 2, 64, device=dev), 1, 5)
+    torch.cuda.synchronize()
+    assert (idx == -1).all() and torch.isneginf(sc).all()
+    # rows t < r - 1 see nothing; r larger than S: every row empty
+    case = SY.IndexerCase("r_large", B=1, S=20, Skv=20, H=64, D=128, compress_ratio=64, topk=4,
+                          w_var=1 / 64, seed=30)
+    gidx, gsc = run_gpu(dsai, case, SY.indexer_inputs(case))
+    assert (gidx == -1).all() and np.isneginf(gsc).all()
+    # all-zero queries: every visible score is 0 -> ties resolve to the lowest indices
+    case = SY.IndexerCase("zeros", B=1, S=300, Skv=300, H=64, D=128, compress_ratio=1, topk=10,
+                          w_var=1 / 64, seed=31)
+    inp = SY.indexer_inputs(case)
+    inp["q_bits"] = np.zeros_like(inp["q_bits"])
+    gidx, gsc = run_gpu(dsai, case, inp)
+    for t in range(case.S):
+        m = min(10, t + 1)
+        assert gidx[0, t, :m].tolist() == list(range(m)), t
+        assert np.all(gsc[0, t, :m] == 0.0)
+
+
+def _sample_rows(case, extra=24, seed=0):
+    rng = np.random.default_rng(seed + 1000)
+    r, S, k = case.compress_ratio, case.S, case.topk
+    cross = r * (k + 1) - 1   # first row with more than topk visible keys
+    rows = {0, 1, 2, 3, r - 1, r, S - 1, S - 2, S // 2,
+            max(0, cross - 1), min(S - 1, cross), min(S - 1, cross + 1)}
+    rows |= set(rng.choice(S, extra, replace=False).tolist())
+    return sorted(t for t in rows if 0 <= t < S)
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "c4", "long"])
+def test_config_parity(dsai, name):
+    """The workloads at their full sizes, in the bench's launch configuration;
+    the oracle checks all rows of the tiny case and sampled rows of the rest."""
+    case = SY.CASES[name]
+    log(f"[gpu] config parity {name}: generating inputs")
+    inp = SY.indexer_inputs(case)
+    log(f"[gpu] config parity {name}: running")
+    gidx, gsc = run_gpu(dsai, case, inp)
+    rows = list(range(case.S)) if name == "tiny" else _sample_rows(case)
+    log(f"[gpu] config parity {name}: oracle on {len(rows)} rows x {case.B} batches")
+    _, _, full = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
+    compare(case, gidx, gsc, rows, full)
+    # properties that hold for every row: padding exactly where the row is short
+    for b in range(case.B):
+        n = np.minimum(case.Skv, (np.arange(case.S) + 1) // case.compress_ratio)
+        npad = (gidx[b] == -1).sum(axis=1)
+        assert np.array_equal(npad, np.maximum(0, case.topk - n))
+        assert np.all(gidx[b] < n[:, None])

@@ -1,0 +1,194 @@
+"""GPU parity of the pooled decode path (kpool_compress, index_scores,
+topk_pools, select, expand) against the CPU oracle.
+
+Integer outputs (pool_tok, pool_valid, pool ids from exact fp32 inputs,
+expanded token ids) must match bit for bit.  pool_k must match bit for bit
+except where the oracle's fp64 value lies within 2^-16 (relative) of a bf16
+rounding midpoint, where one bf16 ulp is allowed (fp32 on the GPU and fp64
+in the oracle cannot agree on which side such a value falls).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as SY
+from parity import check_topk_rows, log, tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsai():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import sparse_attention_token_index_amd as m
+    m.load_library()
+    return m
+
+
+def bf16_gpu(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bits_of(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f64(bits):
+    return SY.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def check_pool_k(gpu_bits, oracle_f64):
+    _, ob = oracle.round_to_bf16(oracle_f64)
+    diff = gpu_bits != ob
+    if not np.any(diff):
+        return
+    x = oracle_f64[diff]
+    m, e = np.frexp(x)
+    scaled = np.abs(np.ldexp(m, 8))
+    frac = scaled - np.floor(scaled)
+    near_mid = np.abs(frac - 0.5) <= scaled * 2.0 ** -16
+    g = f64(gpu_bits[diff])
+    ulp = np.ldexp(1.0, e - 8)
+    within_ulp = np.abs(g - x) <= ulp
+    assert np.all(near_mid & within_ulp), (
+        f"{int(np.sum(~(near_mid & within_ulp)))} pool_k elements differ away from a rounding midpoint")
+
+
+def pooled_case_inputs(case):
+    inp = SY.pooled_inputs(case)
+    return inp
+
+
+POOL_CASES = [
+    SY.POOLED_CASES["pooled_decode"],
+    SY.PooledCase("kp1_fk5_d64", N=3001, D=64, KP=1, first_key=5, H=16, Q=7, index_topk=40),
+    SY.PooledCase("kp3_fk2_d32_h4", N=2000, D=32, KP=3, first_key=2, H=4, Q=9, index_topk=30),
+    SY.PooledCase("kp8_d128_h64", N=5000, D=128, KP=8, first_key=0, H=64, Q=5, index_topk=64,
+                  valid_p=0.999),
+    SY.PooledCase("kp2_fk1_tail", N=1001, D=128, KP=2, first_key=1, H=32, Q=3, index_topk=2000,
+                  valid_p=0.7, invalid_tail=100),   # select_k > valid pools: -1 padding
+    SY.PooledCase("kp5_d64_h20", N=4099, D=64, KP=5, first_key=7, H=20, Q=66, index_topk=55),
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=[c.name for c in POOL_CASES])
+def test_kpool_compress(dsai, case):
+    log(f"[gpu] kpool {case}")
+    inp = pooled_case_inputs(case)
+    ix = dsai.Indexer(heads=case.H, dim=case.D, kpool=case.KP, index_topk=case.index_topk,
+                      first_key=case.first_key)
+    pk, pt, pv = ix.kpool_compress(bf16_gpu(inp["k_normed_bits"]), torch.from_numpy(inp["gate"]).cuda(),
+                                   torch.from_numpy(inp["valid"]).cuda(),
+                                   torch.from_numpy(inp["ape"]).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.kpool_compress(f64(inp["k_normed_bits"]), inp["gate"], inp["valid"], inp["ape"],
+                                case.first_key, case.KP)
+    assert pk.shape[0] == ref["pool_k"].shape[0] == oracle.pool_count(case.N, case.first_key, case.KP)
+    assert np.array_equal(pt.cpu().numpy(), ref["pool_tok"])
+    assert np.array_equal(pv.cpu().numpy(), ref["pool_valid"])
+    check_pool_k(bits_of(pk), ref["pool_k_f64"])
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=[c.name for c in POOL_CASES])
+def test_index_scores_elementwise(dsai, case):
+    """Stage-isolated: the GPU scores the oracle's own pool keys."""
+    log(f"[gpu] index_scores {case}")
+    inp = pooled_case_inputs(case)
+    ref = oracle.kpool_compress(f64(inp["k_normed_bits"]), inp["gate"], inp["valid"], inp["ape"],
+                                case.first_key, case.KP)
+    ix = dsai.Indexer(heads=case.H, dim=case.D, kpool=case.KP, index_topk=case.index_topk,
+                      first_key=case.first_key)
+    sc = ix.index_scores(bf16_gpu(inp["q_bits"]), torch.from_numpy(inp["w"]).cuda(),
+                         bf16_gpu(ref["pool_k_bits"]), torch.from_numpy(ref["pool_valid"]).cuda())
+    torch.cuda.synchronize()
+    g = sc.cpu().numpy().astype(np.float64)
+    o = oracle.pooled_index_scores(f64(inp["q_bits"]), inp["w"], ref["pool_k"], ref["pool_valid"])
+    inv = ~np.isfinite(o)
+    assert np.array_equal(np.isneginf(g), inv)
+    assert np.all(np.abs(g[~inv] - o[~inv]) <= tol(o[~inv]))
+
+
+def test_topk_pools_exact_on_fp32_scores(dsai):
+    """topk_pools selects on the fp32 values it is given: with the oracle run on
+    the same fp32 values, ids, order and scores must match exactly."""
+    log("[gpu] topk_pools exact")
+    rng = np.random.default_rng(41)
+    Q, P, KP, index_topk = 70, 16384, 4, 512
+    s = rng.standard_normal((Q, P)).astype(np.float32)
+    s[rng.random((Q, P)) < 0.08] = -np.inf                   # invalid candidates
+    s[5:15] = np.round(s[5:15] * 2).astype(np.float32)        # many exact ties
+    s[20, :] = 0.0                                            # one big tie
+    s[21, :] = -np.inf                                        # no valid pool
+    s[22, :] = -np.inf
+    s[22, [7, 99, 3000]] = [1.0, 2.0, 1.0]                   # fewer valid than select_k
+    s[23] = -np.abs(s[23])                                    # all negative
+    s[24, ::2] = -0.0                                         # signed zeros tie with +0
+    s[24, 1::2] = 0.0
+    ix = dsai.Indexer(heads=32, dim=128, kpool=KP, index_topk=index_topk)
+    ids, vals = ix.topk_pools(torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    oids, ovals = oracle.topk_pools(s.astype(np.float64), index_topk // KP)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(vals.cpu().numpy().astype(np.float64), ovals)
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=[c.name for c in POOL_CASES])
+def test_select_and_expand_pipeline(dsai, case):
+    """kpool -> select -> expand on the GPU; the oracle scores the GPU's pool
+    keys (stage isolation) and expands the GPU's pool ids."""
+    log(f"[gpu] select+expand {case}")
+    inp = pooled_case_inputs(case)
+    ix = dsai.Indexer(heads=case.H, dim=case.D, kpool=case.KP, index_topk=case.index_topk,
+                      first_key=case.first_key)
+    pk, pt, pv = ix.kpool_compress(bf16_gpu(inp["k_normed_bits"]), torch.from_numpy(inp["gate"]).cuda(),
+                                   torch.from_numpy(inp["valid"]).cuda(),
+                                   torch.from_numpy(inp["ape"]).cuda())
+    q = bf16_gpu(inp["q_bits"])
+    w = torch.from_numpy(inp["w"]).cuda()
+    ids, vals = ix.select(q, w, pk, pv)
+    tok = ix.expand(ids)
+    torch.cuda.synchronize()
+    gids, gvals, gtok = ids.cpu().numpy(), vals.cpu().numpy(), tok.cpu().numpy()
+    pk64, pvv = f64(bits_of(pk)), pv.cpu().numpy()
+    o = oracle.pooled_index_scores(f64(inp["q_bits"]), inp["w"], pk64, pvv)
+    sel = case.index_topk // case.KP
+    valid_idx = np.nonzero(pvv)[0]
+    # parity rules over the valid pools (ids mapped into the valid subset)
+    rows_scores = [o[i][valid_idx] for i in range(case.Q)]
+    pos = -np.ones(max(1, o.shape[1]), dtype=np.int64)
+    pos[valid_idx] = np.arange(len(valid_idx))
+    mapped = np.where(gids >= 0, pos[np.maximum(gids, 0)], -1)
+    assert np.all((gids < 0) | (pvv[np.maximum(gids, 0)] == 1)), "invalid pool selected"
+    check_topk_rows(mapped, gvals, rows_scores, sel, [f"{case.name} q={i}" for i in range(case.Q)])
+    assert np.array_equal(gtok, oracle.expand_selection(gids, case.first_key, case.KP))
+    # the split calls give the same result as select
+    sc = ix.index_scores(q, w, pk, pv)
+    ids2, vals2 = ix.topk_pools(sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids2.cpu().numpy(), gids)
+
+
+@pytest.mark.parametrize("KP", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_expand_bit_exact(dsai, KP):
+    log(f"[gpu] expand KP={KP}")
+    sel, Q, P, fk = 96, 37, 5000, 11
+    ids = SY.random_pool_ids(KP, Q, sel, P, missing_frac=0.2)
+    ix = dsai.Indexer(heads=32, dim=128, kpool=KP, index_topk=sel * KP, first_key=fk)
+    out = torch.full((Q, sel * KP), -777, dtype=torch.int32, device="cuda")
+    tok = ix.expand(torch.from_numpy(ids).cuda(), tokens=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), oracle.expand_selection(ids, fk, KP))
+
+
+def test_pooled_decode_full_size_counts(dsai):
+    """The pooled decode workload: 16384 pools, the last 10 invalid."""
+    case = SY.POOLED_CASES["pooled_decode"]
+    inp = pooled_case_inputs(case)
+    ix = dsai.Indexer(heads=case.H, dim=case.D, kpool=case.KP, index_topk=case.index_topk)
+    _, _, pv = ix.kpool_compress(bf16_gpu(inp["k_normed_bits"]), torch.from_numpy(inp["gate"]).cuda(),
+                                 torch.from_numpy(inp["valid"]).cuda(), torch.from_numpy(inp["ape"]).cuda())
+    torch.cuda.synchronize()
+    pvv = pv.cpu().numpy()
+    assert pvv.shape == (16384,)
+    assert not pvv[16374:].any()
