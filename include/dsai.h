@@ -64,6 +64,10 @@ extern "C" {
  * (zero-padded to 16, 32 or 64 on the matrix cores), dim 32, 64 or 128. */
 #define DSAI_MAX_HEADS 64
 
+/* Order of the entries of a top-k row (dsai_config.order). */
+#define DSAI_ORDER_SCORE 0 /* score descending, lower index first among equal scores */
+#define DSAI_ORDER_INDEX 1 /* ascending index (the same set, no sorting pass)          */
+
 /* ---- configuration / handle -------------------------------------------- */
 typedef struct dsai_config {
   int heads;      /* H, index heads per query, 1..64                          */
@@ -74,6 +78,9 @@ typedef struct dsai_config {
                      page); select_k = index_topk / kpool pools per row       */
   int first_key;  /* first cached token that pools (>= 0)                      */
   int chunk_rows; /* query rows per dsai_score_topk launch; 0 = one launch     */
+  int order;      /* DSAI_ORDER_SCORE (default 0) or DSAI_ORDER_INDEX: order of
+                     the entries of each dsai_score_topk / dsai_topk_pools /
+                     dsai_select row (padding is always at the tail)         */
 } dsai_config;
 
 typedef struct dsai_context* dsai_handle;
@@ -81,7 +88,8 @@ typedef struct dsai_context* dsai_handle;
 /* Validate `cfg` and create a handle in *out.  Refuses (DSAI_ERR_INVALID_ARG)
  * kpool outside 1..8, index_topk not a positive multiple of kpool,
  * index_topk / kpool > DSAI_MAX_TOPK, heads < 1, first_key < 0,
- * chunk_rows < 0; DSAI_ERR_UNSUPPORTED for heads > 64 or dim not 32/64/128;
+ * chunk_rows < 0, order not DSAI_ORDER_SCORE / DSAI_ORDER_INDEX;
+ * DSAI_ERR_UNSUPPORTED for heads > 64 or dim not 32/64/128;
  * DSAI_ERR_NULLPTR for a NULL cfg or out.  Makes no HIP call. */
 int dsai_create(const dsai_config* cfg, dsai_handle* out);
 
@@ -107,10 +115,11 @@ int dsai_last_hip_error(dsai_handle h);
  *   I = sum_h weights[t,b,h] * max(0, sum_d index_q[t,b,h,d] * index_k[s,b,d])
  * (products accumulated in fp32 on the matrix cores).  Key s is visible iff
  * s < min(Skv, floor((t+1) / compress_ratio)).  Each output row lists the
- * visible keys with the `topk` largest scores, by score descending and the
- * lower key index first among equal scores (+0 and -0 are equal); rows with
- * fewer visible keys are padded with index -1 and score -inf.  Every output
- * element is written.
+ * visible keys with the `topk` largest scores (ties at the boundary go to
+ * the lower key index; +0 and -0 are equal), ordered by score descending and
+ * the lower index first among equal scores (cfg.order DSAI_ORDER_SCORE) or
+ * by ascending index (DSAI_ORDER_INDEX); rows with fewer visible keys are
+ * padded with index -1 and score -inf.  Every output element is written.
  *
  * S, Skv, B >= 0 (S == 0 or B == 0: nothing is written or launched);
  * Skv < 2^31; compress_ratio >= 1; 1 <= topk <= DSAI_MAX_TOPK

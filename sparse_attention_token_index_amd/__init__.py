@@ -33,6 +33,8 @@ EXPORTS = (
 )
 
 DSAI_OK = 0
+DSAI_ORDER_SCORE = 0  # rows by score descending, lower index first on ties
+DSAI_ORDER_INDEX = 1  # rows by ascending index (same set, no sorting pass)
 DSAI_MAX_KPOOL = 8
 DSAI_MAX_TOPK = 8192
 
@@ -46,7 +48,7 @@ class DsaiError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int), ("dim", ctypes.c_int), ("kpool", ctypes.c_int),
                 ("index_topk", ctypes.c_int), ("first_key", ctypes.c_int),
-                ("chunk_rows", ctypes.c_int)]
+                ("chunk_rows", ctypes.c_int), ("order", ctypes.c_int)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -117,9 +119,9 @@ class Indexer:
     """One configured handle of the selection library (dsai_create)."""
 
     def __init__(self, heads: int, dim: int, kpool: int = 1, index_topk: int = 1,
-                 first_key: int = 0, chunk_rows: int = 0):
+                 first_key: int = 0, chunk_rows: int = 0, order: int = DSAI_ORDER_SCORE):
         self._lib = load_library()
-        self.cfg = _Config(heads, dim, kpool, index_topk, first_key, chunk_rows)
+        self.cfg = _Config(heads, dim, kpool, index_topk, first_key, chunk_rows, order)
         h = ctypes.c_void_p()
         st = self._lib.dsai_create(ctypes.byref(self.cfg), ctypes.byref(h))
         self._check(st, "dsai_create")

@@ -30,6 +30,7 @@ int check_config(const dsai_config& c) {
   if (c.index_topk < 1 || c.index_topk % c.kpool != 0) return DSAI_ERR_INVALID_ARG;
   if (select_k(c) > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
   if (c.first_key < 0 || c.chunk_rows < 0) return DSAI_ERR_INVALID_ARG;
+  if (c.order != DSAI_ORDER_SCORE && c.order != DSAI_ORDER_INDEX) return DSAI_ERR_INVALID_ARG;
   if (c.heads > DSAI_MAX_HEADS) return DSAI_ERR_UNSUPPORTED;
   if (c.dim != 32 && c.dim != 64 && c.dim != 128) return DSAI_ERR_UNSUPPORTED;
   return DSAI_OK;
@@ -108,8 +109,9 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
     return DSAI_ERR_INVALID_ARG;
   hipError_t e = device_limits(h);
   if (e != hipSuccess) return hip_status(h, e);
-  const int R = dsai::score_topk_rows_per_block(h->cfg.dim, topk, h->lds_limit);
-  if (R < 1) return DSAI_ERR_UNSUPPORTED;
+  const dsai::ScoreSelectPlan plan =
+      dsai::plan_score_select(h->cfg.dim, topk, Skv, h->lds_limit);
+  if (plan.rows_per_block < 1) return DSAI_ERR_UNSUPPORTED;
   dsai::ScoreTopkArgs a;
   a.q = static_cast<const uint16_t*>(index_q);
   a.k = static_cast<const uint16_t*>(index_k);
@@ -117,8 +119,9 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   a.S = S; a.Skv = Skv; a.B = B;
   a.H = h->cfg.heads; a.D = h->cfg.dim; a.ratio = compress_ratio; a.topk = topk;
   a.chunk_rows = h->cfg.chunk_rows;
+  a.sort = h->cfg.order == DSAI_ORDER_SCORE;
   a.out_idx = out_idx; a.out_score = out_score;
-  return hip_status(h, dsai::launch_score_topk(a, R, static_cast<hipStream_t>(stream)));
+  return hip_status(h, dsai::launch_score_topk(a, plan, static_cast<hipStream_t>(stream)));
 }
 
 int dsai_pool_count(dsai_handle h, int64_t N, int64_t* P) {
@@ -172,11 +175,12 @@ int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, in
   if (!pool_ids || !pool_scores || (P > 0 && !scores)) return DSAI_ERR_NULLPTR;
   hipError_t e = device_limits(h);
   if (e != hipSuccess) return hip_status(h, e);
-  if (dsai::topk_rows_lds_bytes(select_k(h->cfg)) > h->lds_limit) return DSAI_ERR_UNSUPPORTED;
+  const dsai::TopkRowsPlan plan = dsai::plan_topk_rows(select_k(h->cfg), P, h->lds_limit);
+  if (plan.waves < 1) return DSAI_ERR_UNSUPPORTED;
   dsai::TopkPoolsArgs a;
   a.scores = scores; a.Q = Q; a.P = P; a.sel = select_k(h->cfg);
   a.pool_ids = pool_ids; a.pool_scores = pool_scores;
-  return hip_status(h, dsai::launch_topk_pools(a, static_cast<hipStream_t>(stream)));
+  return hip_status(h, dsai::launch_topk_pools(a, plan, static_cast<hipStream_t>(stream)));
 }
 
 int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* bytes) {

@@ -14,8 +14,17 @@ struct ScoreTopkArgs {
   int64_t S, Skv, B;
   int H, D, ratio, topk;
   int64_t chunk_rows;  // 0: all rows in one launch
+  bool sort;           // score-descending rows (else ascending index order)
   int32_t* out_idx;    // [B, S, topk]
   float* out_score;    // [B, S, topk]
+};
+
+// Launch geometry of the fused score + select kernel.
+struct ScoreSelectPlan {
+  int rows_per_block;  // 0: the request does not fit in LDS
+  int cap;             // candidate-store entries per row
+  int idx_bytes;       // 2 (Skv <= 65536) or 4
+  size_t lds_bytes;
 };
 
 struct KpoolArgs {
@@ -55,15 +64,23 @@ struct ExpandArgs {
   int32_t* tokens;  // [Q, sel * KP]
 };
 
-// Rows per workgroup of the fused kernel for this head dim / topk within
-// `lds_limit` bytes of LDS (0: does not fit).
-int score_topk_rows_per_block(int D, int topk, size_t lds_limit);
-size_t topk_rows_lds_bytes(int sel);
+// Launch geometry of the pooled top-k kernel.
+struct TopkRowsPlan {
+  int waves;  // wavefronts per row (0: does not fit)
+  int cap;    // candidate-store entries per wavefront
+  size_t lds_bytes;
+};
 
-hipError_t launch_score_topk(const ScoreTopkArgs& a, int rows_per_block, hipStream_t st);
+ScoreSelectPlan plan_score_select(int D, int topk, int64_t Skv, size_t lds_limit);
+TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit);
+
+hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st);
+// Stable sort of `rows` rows of `topk` (idx, score) pairs, each in ascending
+// index order with -1 padding at the tail, into score-descending order.
+hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st);
 hipError_t launch_kpool(const KpoolArgs& a, hipStream_t st);
 hipError_t launch_pooled_scores(const PooledScoresArgs& a, hipStream_t st);
-hipError_t launch_topk_pools(const TopkPoolsArgs& a, hipStream_t st);
+hipError_t launch_topk_pools(const TopkPoolsArgs& a, const TopkRowsPlan& pl, hipStream_t st);
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t st);
 
 }  // namespace dsai

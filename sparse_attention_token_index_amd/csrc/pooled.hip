@@ -165,56 +165,104 @@ hipError_t launch_pooled_scores(const PooledScoresArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// topk_pools: one wavefront per row streams the row's P scores through the
-// same threshold filter / radix select / stable sort as the fused indexer.
-// -inf marks an invalid candidate and never enters the store.
+// topk_pools: one workgroup per row, NW wavefronts each streaming a
+// contiguous slice of the row's P scores through the threshold filter and
+// radix select of the fused indexer (-inf marks an invalid candidate and never
+// enters a store).  The slices' survivors are concatenated in slice order
+// (= index order) and one wavefront selects the row's top select_k from them;
+// the row sort then orders them by score.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ scores, int Q,
-                                                        int P, int sel, int cap,
-                                                        int32_t* __restrict__ ids,
-                                                        float* __restrict__ out_scores) {
+constexpr int kLoadBatch = 4;
+
+__global__ __launch_bounds__(1024) void topk_rows_kernel(const float* __restrict__ scores, int P,
+                                                         int sel, int cap, int NW,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ out_scores) {
   extern __shared__ __align__(16) char smem_raw[];
   lds_char* smem = (lds_char*)smem_raw;
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int row = blockIdx.x * 4 + wave;
-  const size_t per_wave = (size_t)2 * cap * 4 + 1024 + 16 * kWave * 4;
+  const int row = blockIdx.x;
+  const size_t per_wave = (size_t)cap * 8 + 1024;
   lds_char* mine = smem + wave * per_wave;
-  lds_u32* key = (lds_u32*)mine;
-  const RowStore rs{key, key + cap, key + 2 * cap};
-  lds_u32* cnt = key + 2 * cap + 256;
-  if (row >= Q) return;
+  const RowStore<uint32_t> rs{(lds_u32*)mine, (lds_u32*)mine + cap, (lds_u32*)mine + 2 * cap};
+  lds_u32* merged = (lds_u32*)(smem + NW * per_wave);   // [NW * sel] keys, then indices
+  lds_u32* counts = merged + 2 * NW * sel;              // [NW]
+
   const float* srow = scores + (int64_t)row * P;
+  const int per = ((P + NW - 1) / NW + kWave - 1) / kWave * kWave;
+  const int p0 = wave * per;
+  const int p1 = min(P, p0 + per);
   uint32_t count = 0u, tau = 0u;
-  for (int base = 0; base < P; base += kWave) {
-    const int p = base + lane;
-    const float s = p < P ? srow[p] : -__builtin_inff();
-    const uint32_t u = ord_key(s);
-    const bool pass = (p < P) && (s != -__builtin_inff()) && (u > tau);
-    wave_append(rs, count, pass, u, (uint32_t)p);
-    if (count > (uint32_t)(cap - kWave)) count = wave_keep_topk(rs, count, sel, &tau);
+  for (int base = p0; base < p1; base += kWave * kLoadBatch) {
+    float v[kLoadBatch];
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      const int p = base + j * kWave + lane;
+      v[j] = p < p1 ? srow[p] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      const int p = base + j * kWave + lane;
+      const uint32_t u = ord_key(v[j]);
+      wave_append(rs, count, p < p1 && v[j] != -__builtin_inff() && u > tau, u, (uint32_t)p);
+      if (count > (uint32_t)(cap - kWave)) count = wave_keep_topk(rs, count, sel, &tau);
+    }
   }
-  wave_lds_sync();
+  int32_t* orow = ids + (int64_t)row * sel;
+  float* osc = out_scores + (int64_t)row * sel;
+  if (NW == 1) {
+    wave_finish_row(rs, count, sel, orow, osc);
+    return;
+  }
   count = wave_keep_topk(rs, count, sel, &tau);
-  const SortedView sv = wave_sort_desc(rs, count, (uint32_t)sel + 64u, cnt);
-  wave_write_row(sv, count, sel, ids + (int64_t)row * sel, out_scores + (int64_t)row * sel);
+  if (lane == 0) counts[wave] = count;
+  __syncthreads();
+  uint32_t off = 0u, total = 0u;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = counts[w];
+    if (w < wave) off += c;
+    total += c;
+  }
+  for (uint32_t i = lane; i < count; i += kWave) {
+    merged[off + i] = rs.key[i];
+    merged[NW * sel + off + i] = rs.idx[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const RowStore<uint32_t> all{merged, merged + NW * sel, rs.hist};
+    wave_finish_row(all, uniform(total), sel, orow, osc);
+  }
 }
 
-size_t topk_rows_lds_bytes(int sel) {
-  const int cap = 2 * sel + 128;
-  return 4 * ((size_t)2 * cap * 4 + 1024 + 16 * kWave * 4);
+// Waves per row and store capacity for select_k = sel within `lds_limit`.
+TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit) {
+  TopkRowsPlan pl{};
+  const int cap = ((sel + 4 * kWave) + kWave - 1) / kWave * kWave;
+  for (int NW = 16; NW >= 1; NW /= 2) {
+    if (NW > 1 && (int64_t)NW * kWave * 2 > P) continue;  // at least two loads per lane
+    const size_t lds = (size_t)NW * ((size_t)cap * 8 + 1024) +
+                       (NW > 1 ? (size_t)NW * sel * 8 + 16 * 4 : 0);
+    if (lds <= lds_limit) {
+      pl.waves = NW;
+      pl.cap = cap;
+      pl.lds_bytes = lds;
+      return pl;
+    }
+  }
+  return pl;
 }
 
-hipError_t launch_topk_pools(const TopkPoolsArgs& a, hipStream_t st) {
+hipError_t launch_topk_pools(const TopkPoolsArgs& a, const TopkRowsPlan& pl, hipStream_t st) {
   if (a.Q <= 0) return hipSuccess;
-  const int cap = 2 * a.sel + 128;
-  const size_t lds = topk_rows_lds_bytes(a.sel);
   hipError_t e = hipFuncSetAttribute((const void*)topk_rows_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((a.Q + 3) / 4)), dim3(256), lds, st,
-                     a.scores, (int)a.Q, (int)a.P, a.sel, cap, a.pool_ids, a.pool_scores);
-  return hipGetLastError();
+  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)a.Q), dim3(pl.waves * kWave), pl.lds_bytes,
+                     st, a.scores, (int)a.P, a.sel, pl.cap, pl.waves, a.pool_ids, a.pool_scores);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sort_rows(a.pool_ids, a.pool_scores, a.Q, a.sel, st);
 }
 
 // ---------------------------------------------------------------------------

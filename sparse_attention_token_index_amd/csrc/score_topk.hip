@@ -1,4 +1,5 @@
-// Fused lightning-indexer score + causal/compressed mask + per-query top-k.
+// Fused lightning-indexer score + causal/compressed mask + per-query top-k
+// selection.
 //
 // Contract: NeMo AutoModel page
 // "nemo_automodel.components.models.deepseek_v4.kernels.tilelang_indexer"
@@ -14,9 +15,10 @@
 // the matrix cores (TileScorer) and appends the keys that beat its running
 // threshold to its LDS candidate store.  When the store fills, a radix select
 // cuts it to the top k and raises the threshold.  After the last tile the
-// row's top k is sorted (stable LSD radix) and written.  No score ever goes to
-// device memory.  Blocks are numbered heaviest (largest t) first so the
-// causal imbalance is absorbed by the dispatcher.
+// row's top k is written in ascending index order; no score ever goes to
+// device memory.  (Score-descending order is produced by the row sort.)
+// Blocks are numbered heaviest (largest t) first so the causal imbalance is
+// absorbed by the dispatcher.
 #include "internal.h"
 #include "score_tile.h"
 #include "topk_wave.h"
@@ -26,8 +28,8 @@ namespace dsai {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-template <int HP, int D>
-__global__ __launch_bounds__(kThreads) void score_topk_kernel(
+template <int HP, int D, typename IdxT>
+__global__ __launch_bounds__(kThreads, 2) void score_select_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int stage_bytes, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
@@ -37,11 +39,12 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
 
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
+  const int row_bytes = cap * 4 + ((cap * (int)sizeof(IdxT) + 15) & ~15);
 
   lds_char* tile = smem;
-  lds_u32* hist = (lds_u32*)(smem + stage_bytes) + wave * 256;
-  lds_u32* rowkey = (lds_u32*)(smem + stage_bytes + R * 1024) + (size_t)wave * 2 * cap;
-  const RowStore rs{rowkey, rowkey + cap, hist};
+  lds_char* mine = smem + stage_bytes + R * 1024 + wave * row_bytes;
+  const RowStore<IdxT> rs{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4),
+                          (lds_u32*)(smem + stage_bytes) + wave * 256};
 
   const int nrow = row_end - row_begin;
   const int nrb = (nrow + R - 1) / R;
@@ -78,62 +81,83 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
       if (count > (uint32_t)(cap - G::kTileKeys)) count = wave_keep_topk(rs, count, topk, &tau);
     }
   }
-  __syncthreads();  // the tile region now holds the sort counters
   if (!active) return;
-  wave_lds_sync();
-  count = wave_keep_topk(rs, count, topk, &tau);
-  lds_u32* cnt = (lds_u32*)smem + wave * 16 * kWave;
-  const SortedView sv = wave_sort_desc(rs, count, (uint32_t)topk + 64u, cnt);
   const int64_t orow = ((int64_t)b * S + t) * topk;
-  wave_write_row(sv, count, topk, out_idx + orow, out_score + orow);
+  wave_finish_row(rs, count, topk, out_idx + orow, out_score + orow);
 }
 
-// Candidate store entries per row: room for the top k plus at least one
-// tile of new candidates, and for the sort's two padded halves.
-static int store_cap(int topk) { return 2 * topk + 128; }
+namespace {
 
-static size_t lds_bytes(int D, int R, int topk, int* stage_out) {
-  const int row_bytes = 2 * D + 16;
-  int stage = 64 * row_bytes;
-  if (stage < R * 16 * kWave * 4) stage = R * 16 * kWave * 4;  // sort counters reuse it
-  stage = (stage + 15) & ~15;
-  if (stage_out) *stage_out = stage;
-  return (size_t)stage + (size_t)R * 1024 + (size_t)R * store_cap(topk) * 8;
+int store_row_bytes(int cap, int idx_bytes) { return cap * 4 + ((cap * idx_bytes + 15) & ~15); }
+
+int stage_bytes_for(int D) { return 64 * (2 * D + 16); }
+
+// Largest candidate-store capacity (a multiple of 64) for R rows in `budget`
+// bytes of LDS.
+int cap_for(int D, int R, int idx_bytes, size_t budget) {
+  const long fixed = stage_bytes_for(D) + R * 1024;
+  long per_row = ((long)budget - fixed) / R;
+  if (per_row <= 0) return 0;
+  int cap = (int)(per_row / (4 + idx_bytes)) & ~63;
+  while (cap > 0 && store_row_bytes(cap, idx_bytes) > per_row) cap -= 64;
+  return cap;
 }
 
-int score_topk_rows_per_block(int D, int topk, size_t lds_limit) {
-  for (int R = kWaves; R >= 1; --R)
-    if (lds_bytes(D, R, topk, nullptr) <= lds_limit) return R;
-  return 0;
+}  // namespace
+
+// Pick rows per block and store capacity: prefer 4 rows and two blocks per
+// CU (half the LDS each); the store must hold the top k plus room for at
+// least 4 tiles of new candidates.  It never needs more than every visible
+// key plus one tile.
+ScoreSelectPlan plan_score_select(int D, int topk, int64_t Skv, size_t lds_limit) {
+  ScoreSelectPlan p{};
+  const int idx_bytes = Skv <= 65536 ? 2 : 4;
+  const int need = topk + 4 * 64;
+  const int64_t useful = ((Skv + 63) / 64) * 64 + 64;
+  const size_t budgets[2] = {lds_limit / 2, lds_limit};
+  for (size_t budget : budgets) {
+    for (int R = kWaves; R >= 1; --R) {
+      int cap = cap_for(D, R, idx_bytes, budget);
+      if (cap < need) continue;
+      if (cap > useful) cap = (int)useful;
+      if (cap < need) cap = need;
+      p.rows_per_block = R;
+      p.cap = cap;
+      p.idx_bytes = idx_bytes;
+      p.lds_bytes = (size_t)stage_bytes_for(D) + R * 1024 + (size_t)R * store_row_bytes(cap, idx_bytes);
+      return p;
+    }
+  }
+  return p;  // rows_per_block == 0: does not fit
 }
 
-template <int HP, int D>
-static hipError_t launch_t(const ScoreTopkArgs& a, int R, hipStream_t st) {
-  int stage = 0;
-  const size_t lds = lds_bytes(D, R, a.topk, &stage);
-  auto kern = score_topk_kernel<HP, D>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+template <int HP, int D, typename IdxT>
+static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
+  auto kern = score_select_kernel<HP, D, IdxT>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)p.lds_bytes);
   if (e != hipSuccess) return e;
-  const int cap = store_cap(a.topk);
+  const int R = p.rows_per_block;
   const int64_t chunk = a.chunk_rows > 0 ? a.chunk_rows : a.S;
   for (int64_t r0 = 0; r0 < a.S; r0 += chunk) {
     const int64_t r1 = (r0 + chunk < a.S) ? r0 + chunk : a.S;
-    const int64_t nrb = (r1 - r0 + R - 1) / R;
-    const int64_t blocks = nrb * a.B;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, st, a.q, a.k, a.w,
-                       (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio, a.topk, (int)r0, (int)r1, R,
-                       cap, stage, a.out_idx, a.out_score);
+    const int64_t blocks = ((r1 - r0 + R - 1) / R) * a.B;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), p.lds_bytes, st, a.q, a.k,
+                       a.w, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio, a.topk, (int)r0,
+                       (int)r1, R, p.cap, stage_bytes_for(D), a.out_idx, a.out_score);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.sort) return launch_sort_rows(a.out_idx, a.out_score, a.B * a.S, a.topk, st);
   return hipSuccess;
 }
 
-hipError_t launch_score_topk(const ScoreTopkArgs& a, int R, hipStream_t st) {
+hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
   const int HP = a.H <= 16 ? 16 : (a.H <= 32 ? 32 : 64);
-#define DSAI_CASE(hp, d) \
-  if (HP == hp && a.D == d) return launch_t<hp, d>(a, R, st);
+#define DSAI_CASE(hp, d)                                                       \
+  if (HP == hp && a.D == d)                                                    \
+    return p.idx_bytes == 2 ? launch_t<hp, d, uint16_t>(a, p, st)              \
+                            : launch_t<hp, d, uint32_t>(a, p, st);
   DSAI_CASE(16, 32) DSAI_CASE(16, 64) DSAI_CASE(16, 128)
   DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
   DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)

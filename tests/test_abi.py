@@ -50,9 +50,9 @@ def test_exports_are_c_symbols():
     assert set(declared_symbols()) <= exported
 
 
-def _cfg(heads=64, dim=128, kpool=4, index_topk=512, first_key=0, chunk_rows=0):
+def _cfg(heads=64, dim=128, kpool=4, index_topk=512, first_key=0, chunk_rows=0, order=0):
     import sparse_attention_token_index_amd as dsai
-    return dsai._Config(heads, dim, kpool, index_topk, first_key, chunk_rows)
+    return dsai._Config(heads, dim, kpool, index_topk, first_key, chunk_rows, order)
 
 
 def _create(lib, **kw):
@@ -73,6 +73,9 @@ def _create(lib, **kw):
     ({"heads": 0}, INVALID),
     ({"first_key": -1}, INVALID),
     ({"chunk_rows": -5}, INVALID),
+    ({"order": 1}, OK),
+    ({"order": 2}, INVALID),
+    ({"order": -1}, INVALID),
     ({"heads": 65}, UNSUPPORTED),
     ({"dim": 96}, UNSUPPORTED),
     ({"dim": 256}, UNSUPPORTED),

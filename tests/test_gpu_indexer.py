@@ -203,3 +203,31 @@ def test_config_parity(dsai, name):
         npad = (gidx[b] == -1).sum(axis=1)
         assert np.array_equal(npad, np.maximum(0, case.topk - n))
         assert np.all(gidx[b] < n[:, None])
+
+
+@pytest.mark.parametrize("case", [MEDIUM[0], MEDIUM[2], MEDIUM[3], MEDIUM[8]],
+                         ids=lambda c: c.name)
+def test_index_order_mode_and_row_sort(dsai, case):
+    """order=DSAI_ORDER_INDEX returns the same top-k set in ascending index
+    order; sorting it on the host by (score desc, index asc) must give the
+    score-ordered output bit for bit (pins the row-sort kernel)."""
+    log(f"[gpu] index-order mode {case.name}")
+    inp = SY.indexer_inputs(case)
+    q, k = to_gpu_bf16(inp["q_bits"]), to_gpu_bf16(inp["k_bits"])
+    w = torch.from_numpy(inp["w"]).cuda()
+    out = {}
+    for order in (dsai.DSAI_ORDER_SCORE, dsai.DSAI_ORDER_INDEX):
+        ix = dsai.Indexer(heads=case.H, dim=case.D, order=order)
+        i, s = ix.score_topk(q, k, w, case.compress_ratio, case.topk)
+        torch.cuda.synchronize()
+        out[order] = (i.cpu().numpy(), s.cpu().numpy())
+    si, ss = out[dsai.DSAI_ORDER_SCORE]
+    ii, isc = out[dsai.DSAI_ORDER_INDEX]
+    for b in range(case.B):
+        for t in range(case.S):
+            m = int((ii[b, t] >= 0).sum())
+            assert np.all(ii[b, t, m:] == -1) and np.all(np.isneginf(isc[b, t, m:]))
+            assert np.all(np.diff(ii[b, t, :m]) > 0), (b, t)
+            order = np.lexsort((ii[b, t, :m], -isc[b, t, :m].astype(np.float64)))
+            assert np.array_equal(ii[b, t, :m][order], si[b, t, :m]), (b, t)
+            assert np.array_equal(isc[b, t, :m][order].view(np.uint32), ss[b, t, :m].view(np.uint32))
