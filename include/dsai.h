@@ -123,7 +123,8 @@ int dsai_last_hip_error(dsai_handle h);
  *
  * S, Skv, B >= 0 (S == 0 or B == 0: nothing is written or launched);
  * Skv < 2^31; compress_ratio >= 1; 1 <= topk <= DSAI_MAX_TOPK
- * (DSAI_ERR_INVALID_ARG otherwise).  topk_indices must be NULL: scoring at
+ * (DSAI_ERR_INVALID_ARG otherwise); index_k must span < 4 GiB
+ * (Skv * B * D * 2 bytes; DSAI_ERR_UNSUPPORTED otherwise).  topk_indices must be NULL: scoring at
  * caller-supplied indices returns DSAI_ERR_UNSUPPORTED.  Query rows are
  * processed in launches of cfg.chunk_rows rows (all rows if 0); no scratch
  * memory is used. */

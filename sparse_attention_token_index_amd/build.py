@@ -18,9 +18,11 @@ LIB = os.path.join(PKG, "libdsai.so")
 SOURCES = ["api.cpp", "score_topk.hip", "sort_rows.hip", "pooled.hip"]
 
 # Packed-fp32 VALU forms are kept out of the device code: plain fp32 ops only.
+# No value the kernels handle is ever NaN (finite inputs; -inf only as padding),
+# so NaN-preserving canonicalization (an extra VALU op per ReLU) is dropped.
 HIP_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function"]
+             "-fno-honor-nans", "-Wall", "-Wno-unused-function"]
 
 
 def hipcc() -> str:

@@ -102,6 +102,8 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   if (topk < 1 || topk > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
   if (S > kI32 || Skv > kI32 || B > kI32 || S * B > kI32) return DSAI_ERR_INVALID_ARG;
   if (topk_indices) return DSAI_ERR_UNSUPPORTED;
+  // keys of one batch are addressed with 32-bit byte offsets
+  if (Skv * B * h->cfg.dim * 2 > (int64_t)0xFFFFFFFF) return DSAI_ERR_UNSUPPORTED;
   if (S == 0 || B == 0) return DSAI_OK;
   if (!index_q || !weights || !out_idx || !out_score) return DSAI_ERR_NULLPTR;
   if (Skv > 0 && !index_k) return DSAI_ERR_NULLPTR;
@@ -158,6 +160,7 @@ int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* 
   if (!h) return DSAI_ERR_NULLPTR;
   if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
   if (Q == 0 || P == 0) return DSAI_OK;
+  if (P * h->cfg.dim * 2 > (int64_t)0xFFFFFFFF) return DSAI_ERR_UNSUPPORTED;  // 32-bit offsets
   if (!q || !w || !pool_k || !pool_valid || !scores) return DSAI_ERR_NULLPTR;
   if (!aligned(q) || !aligned(pool_k)) return DSAI_ERR_INVALID_ARG;
   dsai::PooledScoresArgs a;

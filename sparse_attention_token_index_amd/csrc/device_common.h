@@ -16,6 +16,7 @@ typedef DSAI_LDS char lds_char;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -75,6 +76,18 @@ __device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t x) {
 __device__ __forceinline__ uint32_t wave_and(uint32_t x) {
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) x &= __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
   return x;
 }
 

@@ -22,8 +22,9 @@ struct ScoreTopkArgs {
 // Launch geometry of the fused score + select kernel.
 struct ScoreSelectPlan {
   int rows_per_block;  // 0: the request does not fit in LDS
-  int cap;             // candidate-store entries per row
-  int idx_bytes;       // 2 (Skv <= 65536) or 4
+  int cap;             // store entries per row
+  bool dense;          // one slot per visible key (index = slot)
+  int idx_bytes;       // filter store: 2 (Skv <= 65536) or 4
   size_t lds_bytes;
 };
 

@@ -102,9 +102,9 @@ hipError_t launch_kpool(const KpoolArgs& a, hipStream_t st) {
 // index_scores: [Q, P] scores of decode queries against pool keys, -inf for
 // invalid candidates (glm5next_dsa: "[Q, P] scores + candidate validity").
 // Grid (pool blocks, row blocks of 4); each block stages its pool keys in
-// 64-key LDS tiles shared by its 4 query rows (one per wavefront).
+// 32-key LDS tiles shared by its 4 query rows (one per wavefront).
 // ---------------------------------------------------------------------------
-constexpr int kPoolTilesPerBlock = 4;
+constexpr int kPoolTilesPerBlock = 8;
 
 template <int HP, int D>
 __global__ __launch_bounds__(256) void pooled_scores_kernel(
@@ -126,23 +126,24 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(
   int ntiles = (P - p0 + G::kTileKeys - 1) / G::kTileKeys;
   if (ntiles > kPoolTilesPerBlock) ntiles = kPoolTilesPerBlock;
   TileLoader<D, 256> ld;
-  ld.load(pool_k, D, p0, P);
+  ld.init(pool_k, (uint32_t)D, (uint32_t)((int64_t)P * D * 2));  // < 2^32 (checked on the host)
+  ld.load((uint32_t)p0);
   for (int it = 0; it < ntiles; ++it) {
     __syncthreads();
     ld.store(tile);
     __syncthreads();
-    if (it + 1 < ntiles) ld.load(pool_k, D, p0 + (it + 1) * G::kTileKeys, P);
+    if (it + 1 < ntiles) ld.load((uint32_t)(p0 + (it + 1) * G::kTileKeys));
     if (active) {
-      const float s = sc.score(tile);
-      const int p = p0 + it * G::kTileKeys + lane;
-      if (p < P) scores[(int64_t)row * P + p] = pool_valid[p] ? s : -__builtin_inff();
+      const float s = sc.score(tile);  // lanes l and l + 32 hold pool l % 32
+      const int p = p0 + it * G::kTileKeys + (lane & 31);
+      if (lane < 32 && p < P) scores[(int64_t)row * P + p] = pool_valid[p] ? s : -__builtin_inff();
     }
   }
 }
 
 template <int HP, int D>
 static hipError_t launch_scores_t(const PooledScoresArgs& a, hipStream_t st) {
-  const int per_block = kPoolTilesPerBlock * 64;
+  const int per_block = kPoolTilesPerBlock * TileGeom<D>::kTileKeys;
   const int64_t pool_blocks = (a.P + per_block - 1) / per_block;
   const int64_t blocks = pool_blocks * ((a.Q + 3) / 4);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -154,10 +155,9 @@ static hipError_t launch_scores_t(const PooledScoresArgs& a, hipStream_t st) {
 
 hipError_t launch_pooled_scores(const PooledScoresArgs& a, hipStream_t st) {
   if (a.Q <= 0 || a.P <= 0) return hipSuccess;
-  const int HP = a.H <= 16 ? 16 : (a.H <= 32 ? 32 : 64);
+  const int HP = a.H <= 32 ? 32 : 64;
 #define DSAI_CASE(hp, d) \
   if (HP == hp && a.D == d) return launch_scores_t<hp, d>(a, st);
-  DSAI_CASE(16, 32) DSAI_CASE(16, 64) DSAI_CASE(16, 128)
   DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
   DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)
 #undef DSAI_CASE
@@ -183,9 +183,10 @@ __global__ __launch_bounds__(1024) void topk_rows_kernel(const float* __restrict
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int row = blockIdx.x;
-  const size_t per_wave = (size_t)cap * 8 + 1024;
+  const size_t per_wave = (size_t)cap * 8 + kSelScratchBytes;
   lds_char* mine = smem + wave * per_wave;
-  const RowStore<uint32_t> rs{(lds_u32*)mine, (lds_u32*)mine + cap, (lds_u32*)mine + 2 * cap};
+  const RowStore<uint32_t> rs{(lds_u32*)mine, (lds_u32*)mine + cap, (lds_u32*)mine + 2 * cap,
+                              (lds_u32*)mine + 2 * cap + 256, 256u};
   lds_u32* merged = (lds_u32*)(smem + NW * per_wave);   // [NW * sel] keys, then indices
   lds_u32* counts = merged + 2 * NW * sel;              // [NW]
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(1024) void topk_rows_kernel(const float* __restrict
   }
   __syncthreads();
   if (wave == 0) {
-    const RowStore<uint32_t> all{merged, merged + NW * sel, rs.hist};
+    const RowStore<uint32_t> all{merged, merged + NW * sel, rs.hist, rs.side, rs.side_cap};
     wave_finish_row(all, uniform(total), sel, orow, osc);
   }
 }
@@ -241,7 +242,7 @@ TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit) {
   const int cap = ((sel + 4 * kWave) + kWave - 1) / kWave * kWave;
   for (int NW = 16; NW >= 1; NW /= 2) {
     if (NW > 1 && (int64_t)NW * kWave * 2 > P) continue;  // at least two loads per lane
-    const size_t lds = (size_t)NW * ((size_t)cap * 8 + 1024) +
+    const size_t lds = (size_t)NW * ((size_t)cap * 8 + kSelScratchBytes) +
                        (NW > 1 ? (size_t)NW * sel * 8 + 16 * 4 : 0);
     if (lds <= lds_limit) {
       pl.waves = NW;

@@ -1,21 +1,21 @@
-// Index scores of one query row against a 64-key tile staged in LDS, on the
-// gfx950 matrix cores (v_mfma_f32_16x16x32_bf16), fused with ReLU and the
+// Index scores of one query row against a 32-key tile staged in LDS, on the
+// gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), fused with ReLU and the
 // weighted reduction over heads.
 //
 // Score of key s for a query row (the lightning-indexer score; per-head
 // weights reduce over heads after a per-head ReLU):
 //     I[s] = sum_h w[h] * max(0, sum_d q[h, d] * k[s, d])
 //
-// Mapping: heads are the MFMA M dimension (M-tiles of 16 heads, heads past H
-// are zero), keys the N dimension (four 16-key N-blocks per tile) and the
-// head dim the K dimension (k-steps of 32).  The reduction index is permuted
-// consistently for both operands: lane (c = l % 16, g = l / 16) supplies the
-// 8 consecutive dims [32 j + 8 g, 32 j + 8 g + 8) at k-step j, so each operand
-// fragment is one 16-byte load.  The accumulator lane (c, g) holds key c of an
-// N-block for the 4 heads 4 g .. 4 g + 3 of each M-tile: ReLU, the head
-// weights and the sum over M-tiles run in registers, and a 3-shuffle
-// reduce-scatter over the four lane groups leaves lane l holding the full
-// score of key l of the tile.
+// Mapping: heads are the MFMA M dimension (M-tiles of 32 heads, heads past H
+// are zero), the tile's 32 keys the N dimension and the head dim the K
+// dimension (k-steps of 16).  The reduction index is permuted consistently
+// for both operands: lane (c = l % 32, g = l / 32) supplies dims
+// [g*D/2 + 8 j, g*D/2 + 8 j + 8) at k-step j, so every operand fragment is one
+// 16-byte load and a lane's fragments cover one contiguous half of the head
+// dim.  The accumulator lane (c, g) holds key c for 16 heads of each M-tile
+// (rows 8 (r/4) + 4 g + r%4): ReLU, the head weights and the sum over M-tiles
+// run in registers, and one shuffle adds the other half of the heads, leaving
+// lanes l and l + 32 both holding the full score of key l % 32.
 #pragma once
 
 #include "device_common.h"
@@ -23,43 +23,58 @@
 namespace dsai {
 
 // Byte stride of one staged key row in LDS: 16 bytes of padding put the 16
-// keys a ds_read_b128 gathers on distinct bank groups.
+// keys a half-wave's ds_read_b128 gathers on distinct bank groups.
 template <int D>
 struct TileGeom {
   static constexpr int kRowBytes = 2 * D + 16;
-  static constexpr int kTileKeys = 64;
+  static constexpr int kTileKeys = 32;
   static constexpr int kTileBytes = kTileKeys * kRowBytes;
   static constexpr int kChunksPerRow = D / 8;               // 16-byte chunks
   static constexpr int kChunks = kTileKeys * kChunksPerRow;
 };
 
-// Stages 64 consecutive key rows (bf16, `row_stride` elements apart) from
-// global memory into an LDS tile, through registers so the next tile's loads
-// overlap the current tile's math.  Rows at or past `rows_valid` read as zero.
+// Stages kTileKeys consecutive key rows (bf16, `row_stride` elements apart) from
+// device memory into an LDS tile, through registers so the next tile's loads
+// overlap the current tile's math.  Loads go through a buffer resource whose
+// range ends at the last valid key row: rows past it read as zero without a
+// branch, and each thread's byte offsets within a tile are loop-invariant
+// (the tile's row offset is a scalar).
 template <int D, int NTHREADS>
 struct TileLoader {
   using G = TileGeom<D>;
-  static_assert(G::kChunks % NTHREADS == 0, "tile chunks must divide over the block");
-  static constexpr int kPer = G::kChunks / NTHREADS;
+  static_assert(G::kChunks % NTHREADS == 0 || NTHREADS % G::kChunks == 0,
+                "tile chunks must divide over the block (or the block over the chunks)");
+  static constexpr int kPer = G::kChunks >= NTHREADS ? G::kChunks / NTHREADS : 1;
+  static constexpr bool kSpare = G::kChunks < NTHREADS;  // some threads load nothing
   u32x4 r[kPer];
+  uint32_t voff[kPer];
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t row_bytes;  // bytes between consecutive key rows
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t row_stride,
-                                       int64_t row0, int64_t rows_valid) {
+  // base: row 0 of the keys; valid_bytes: bytes from base through the end of
+  // the last valid row (< 2^32).
+  __device__ __forceinline__ void init(const uint16_t* base, uint32_t row_stride,
+                                       uint32_t valid_bytes) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)valid_bytes, 0x00020000);
+    row_bytes = row_stride * 2u;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int ch = (int)threadIdx.x + i * NTHREADS;
+      const int ch = kSpare ? (int)threadIdx.x % G::kChunks : (int)threadIdx.x + i * NTHREADS;
       const int row = ch / G::kChunksPerRow;
       const int part = ch % G::kChunksPerRow;
-      const int64_t s = row0 + row;
-      if (s < rows_valid) {
-        r[i] = *reinterpret_cast<const u32x4*>(base + s * row_stride + part * 8);
-      } else {
-        r[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      voff[i] = (uint32_t)row * row_bytes + (uint32_t)part * 16u;
     }
   }
 
+  __device__ __forceinline__ void load(uint32_t row0) {
+    const uint32_t soff = row0 * row_bytes;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0));
+  }
+
   __device__ __forceinline__ void store(lds_char* tile) const {
+    if (kSpare && (int)threadIdx.x >= G::kChunks) return;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int ch = (int)threadIdx.x + i * NTHREADS;
@@ -72,82 +87,61 @@ struct TileLoader {
 
 template <int HP, int D>
 struct TileScorer {
-  static_assert(HP % 16 == 0 && HP >= 16 && HP <= 64, "padded heads: 16, 32, 48 or 64");
-  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dim: 32, 64, 96 or 128");
-  static constexpr int MT = HP / 16;
-  static constexpr int KS = D / 32;
+  static_assert(HP == 32 || HP == 64, "padded heads: 32 or 64");
+  static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dim: 32, 48, ... 128");
+  static constexpr int MT = HP / 32;
+  static constexpr int KS = D / 16;
   using G = TileGeom<D>;
 
   bf16x8 qf[MT][KS];
-  float wv[MT][4];
+  float wv[MT][16];
 
   // qrow: [H, D] bf16 of this query row; wrow: [H] fp32.  Inactive rows and
   // heads past H load zeros (zero weight, zero query: no contribution).
   __device__ __forceinline__ void load_query(const uint16_t* __restrict__ qrow,
                                              const float* __restrict__ wrow, int H, bool active) {
     const int lane = lane_id();
-    const int c = lane & 15, g = lane >> 4;
+    const int c = lane & 31, g = lane >> 5;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int h = 16 * m + c;
+      const int h = 32 * m + c;
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         if (active && h < H) {
-          qf[m][j] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * D + 32 * j + 8 * g);
+          qf[m][j] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * D + g * (D / 2) + 8 * j);
         } else {
           qf[m][j] = bf16x8{};
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hw = 16 * m + 4 * g + i;
-        wv[m][i] = (active && hw < H) ? wrow[hw] : 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        const int hw = 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+        wv[m][r] = (active && hw < H) ? wrow[hw] : 0.0f;
       }
     }
   }
 
-  // Full score of key `lane` of the staged tile.
+  // Full score of key `lane % 32` of the staged tile (in lanes l and l + 32).
   __device__ __forceinline__ float score(const lds_char* tile) const {
     const int lane = lane_id();
-    const int c = lane & 15, g = lane >> 4;
-    floatx4 acc[4][MT];
+    const int c = lane & 31, g = lane >> 5;
+    floatx16 acc[MT];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[nb][m] = floatx4{0.f, 0.f, 0.f, 0.f};
-
+    for (int m = 0; m < MT; ++m) acc[m] = floatx16{};
+    const lds_char* rowp = tile + c * G::kRowBytes + g * D;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8 b = *reinterpret_cast<const DSAI_LDS bf16x8*>(
-            tile + (nb * 16 + c) * G::kRowBytes + (32 * j + 8 * g) * 2);
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-          acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[m][j], b, acc[nb][m], 0, 0, 0);
-      }
-    }
-
-    float p[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      float s = 0.f;
+      const bf16x8 b = *reinterpret_cast<const DSAI_LDS bf16x8*>(rowp + 16 * j);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(wv[m][i], fmaxf(acc[nb][m][i], 0.f), s);
-      p[nb] = s;
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[m][j], b, acc[m], 0, 0, 0);
     }
-
-    // Reduce-scatter over the lane groups g = 0..3: lane group g ends with the
-    // total of N-block g (key 16 g + c = lane).
-    const bool h1 = (g >> 1) & 1, h0 = g & 1;
-    const float keep0 = h1 ? p[2] : p[0], keep1 = h1 ? p[3] : p[1];
-    const float send0 = h1 ? p[0] : p[2], send1 = h1 ? p[1] : p[3];
-    const float q0 = keep0 + __shfl_xor(send0, 32);
-    const float q1 = keep1 + __shfl_xor(send1, 32);
-    const float keep = h0 ? q1 : q0, send = h0 ? q0 : q1;
-    return keep + __shfl_xor(send, 16);
+    float p = 0.f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p = fmaf(wv[m][r], fmaxf(acc[m][r], 0.f), p);
+    return p + __shfl_xor(p, 32);
   }
 };
 

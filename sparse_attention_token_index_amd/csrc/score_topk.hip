@@ -8,17 +8,21 @@
 // compress_ratio, topk; result [batch, seqlen, topk]); causal masking per the
 // module summary, with key s visible to query t iff s < floor((t+1)/ratio).
 //
-// One workgroup = 4 wavefronts; each wavefront owns one query row of a block
-// of R consecutive rows (same batch), so the rows of a block see nearly the
-// same keys.  The block streams its keys through LDS in 64-key tiles (loaded
-// once per block, shared by its R rows); each wavefront scores the tile on
-// the matrix cores (TileScorer) and appends the keys that beat its running
-// threshold to its LDS candidate store.  When the store fills, a radix select
-// cuts it to the top k and raises the threshold.  After the last tile the
-// row's top k is written in ascending index order; no score ever goes to
-// device memory.  (Score-descending order is produced by the row sort.)
-// Blocks are numbered heaviest (largest t) first so the causal imbalance is
-// absorbed by the dispatcher.
+// One workgroup = 4 wavefronts, two workgroups per CU; each wavefront owns one
+// query row of a block of up to 4 consecutive rows of one batch, so the rows
+// of a block see nearly the same keys.  The block streams its keys through
+// LDS in 32-key tiles (loaded once per block, shared by its rows); each wavefront
+// scores the tile on the matrix cores (TileScorer) and records the scores in
+// its LDS row store:
+//   dense   when every visible key fits: the order key of key s goes to slot s
+//           (no indices, no selection until the end);
+//   filter  otherwise: keys beating the row's running threshold are appended
+//           with their index; when the store fills, a radix select cuts it to
+//           the top k and raises the threshold.
+// After the last tile the row's top k is selected exactly and written in
+// ascending index order; no score goes to device memory.  (Score-descending
+// order is produced by the row sort.)  Blocks are numbered heaviest (largest
+// t) first so the causal imbalance is absorbed by the dispatcher.
 #include "internal.h"
 #include "score_tile.h"
 #include "topk_wave.h"
@@ -28,23 +32,29 @@ namespace dsai {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-template <int HP, int D, typename IdxT>
-__global__ __launch_bounds__(kThreads, 2) void score_select_kernel(
+template <int HP, int D, bool DENSE, typename IdxT>
+__global__ __launch_bounds__(kThreads) void score_select_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
-    int stage_bytes, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   extern __shared__ __align__(16) char smem_raw[];
   lds_char* smem = (lds_char*)smem_raw;
   using G = TileGeom<D>;
+  constexpr int kScratch = DENSE ? 1024 : kSelScratchBytes;
+  // Dense rows reuse the tile region for their side lists after the loop.
+  constexpr int kTileRegion =
+      (DENSE && G::kTileBytes < kWaves * 1024) ? kWaves * 1024 : G::kTileBytes;
 
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int row_bytes = cap * 4 + ((cap * (int)sizeof(IdxT) + 15) & ~15);
+  const int row_bytes = DENSE ? cap * 4 : cap * 4 + ((cap * (int)sizeof(IdxT) + 15) & ~15);
 
   lds_char* tile = smem;
-  lds_char* mine = smem + stage_bytes + R * 1024 + wave * row_bytes;
-  const RowStore<IdxT> rs{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4),
-                          (lds_u32*)(smem + stage_bytes) + wave * 256};
+  lds_u32* scratch = (lds_u32*)(smem + kTileRegion + wave * kScratch);
+  lds_char* mine = smem + kTileRegion + R * kScratch + wave * row_bytes;
+  // Dense rows get their side list in the tile region once the loop is done.
+  lds_u32* side = DENSE ? (lds_u32*)(smem + wave * 1024) : scratch + 256;
+  const RowStore<IdxT> rs{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4), scratch, side, 256u};
 
   const int nrow = row_end - row_begin;
   const int nrb = (nrow + R - 1) / R;
@@ -64,76 +74,105 @@ __global__ __launch_bounds__(kThreads, 2) void score_select_kernel(
 
   uint32_t count = 0u, tau = 0u;
   TileLoader<D, kThreads> ld;
-  const int64_t kstride = (int64_t)B * D;
-  const uint16_t* kb = k + (int64_t)b * D;
-  if (ntiles > 0) ld.load(kb, kstride, 0, Skv);
+  const int64_t kbytes = ((int64_t)Skv * B - b) * D * 2;  // < 2^32 (checked on the host)
+  ld.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
+  if (ntiles > 0) ld.load(0u);
 
   for (int it = 0; it < ntiles; ++it) {
     __syncthreads();
     ld.store(tile);
     __syncthreads();
-    if (it + 1 < ntiles) ld.load(kb, kstride, (int64_t)(it + 1) * G::kTileKeys, Skv);
+    if (it + 1 < ntiles) ld.load((uint32_t)(it + 1) * G::kTileKeys);
     if (active && it * G::kTileKeys < n_t) {
-      const float s = sc.score(tile);
-      const uint32_t key = (uint32_t)(it * G::kTileKeys + lane);
+      const float s = sc.score(tile);  // lanes l and l + 32 hold key l % 32
+      const uint32_t key = (uint32_t)(it * G::kTileKeys + (lane & 31));
       const uint32_t u = ord_key(s);
-      wave_append(rs, count, key < (uint32_t)n_t && u > tau, u, key);
-      if (count > (uint32_t)(cap - G::kTileKeys)) count = wave_keep_topk(rs, count, topk, &tau);
+      if constexpr (DENSE) {
+        if (lane < 32) rs.key[key] = u;
+      } else {
+        wave_append(rs, count, lane < 32 && key < (uint32_t)n_t && u > tau, u, key);
+        if (count > (uint32_t)(cap - G::kTileKeys)) count = wave_keep_topk(rs, count, topk, &tau);
+      }
     }
   }
+  if constexpr (DENSE) __syncthreads();  // the tile region now holds the side lists
   if (!active) return;
   const int64_t orow = ((int64_t)b * S + t) * topk;
-  wave_finish_row(rs, count, topk, out_idx + orow, out_score + orow);
+  if constexpr (DENSE) {
+    uint32_t v = 0u, eq = 0u;
+    wave_lds_sync();
+    if (n_t > topk) {
+      const uint2 sel = wave_radix_select(rs.key, rs.hist, rs.side, rs.side_cap, (uint32_t)n_t,
+                                          (uint32_t)topk);
+      v = sel.x;
+      eq = sel.y;
+    }
+    wave_emit_dense(rs.key, (uint32_t)n_t, v, eq, topk, out_idx + orow, out_score + orow);
+  } else {
+    wave_finish_row(rs, count, topk, out_idx + orow, out_score + orow);
+  }
 }
 
 namespace {
 
 int store_row_bytes(int cap, int idx_bytes) { return cap * 4 + ((cap * idx_bytes + 15) & ~15); }
 
-int stage_bytes_for(int D) { return 64 * (2 * D + 16); }
+int tile_bytes_for(int D) { return 32 * (2 * D + 16); }
 
-// Largest candidate-store capacity (a multiple of 64) for R rows in `budget`
-// bytes of LDS.
-int cap_for(int D, int R, int idx_bytes, size_t budget) {
-  const long fixed = stage_bytes_for(D) + R * 1024;
-  long per_row = ((long)budget - fixed) / R;
-  if (per_row <= 0) return 0;
-  int cap = (int)(per_row / (4 + idx_bytes)) & ~63;
-  while (cap > 0 && store_row_bytes(cap, idx_bytes) > per_row) cap -= 64;
-  return cap;
+bool plan_dense(int D, int64_t Skv, int64_t budget, ScoreSelectPlan* p) {
+  const int64_t tile = tile_bytes_for(D);
+  const int64_t region = tile > kWaves * 1024 ? tile : kWaves * 1024;
+  const int64_t cap = Skv > 0 ? ((Skv + 63) / 64) * 64 : 64;
+  const int64_t lds = region + kWaves * 1024 + (int64_t)kWaves * cap * 4;
+  if (lds > budget) return false;
+  p->rows_per_block = kWaves;
+  p->cap = (int)cap;
+  p->dense = true;
+  p->idx_bytes = 0;
+  p->lds_bytes = (size_t)lds;
+  return true;
+}
+
+bool plan_filter(int D, int topk, int64_t Skv, int64_t budget, int min_rows, ScoreSelectPlan* p) {
+  const int64_t tile = tile_bytes_for(D);
+  const int idx_bytes = Skv <= 65536 ? 2 : 4;
+  const int need = topk + 8 * 32;
+  for (int R = kWaves; R >= min_rows; --R) {
+    const int64_t per_row = (budget - tile - (int64_t)R * kSelScratchBytes) / R;
+    if (per_row <= 0) continue;
+    int cap = (int)(per_row / (4 + idx_bytes)) & ~63;
+    while (cap > 0 && store_row_bytes(cap, idx_bytes) > per_row) cap -= 64;
+    if (cap < need) continue;
+    p->rows_per_block = R;
+    p->cap = cap;
+    p->dense = false;
+    p->idx_bytes = idx_bytes;
+    p->lds_bytes = (size_t)(tile + (int64_t)R * kSelScratchBytes +
+                            (int64_t)R * store_row_bytes(cap, idx_bytes));
+    return true;
+  }
+  return false;
 }
 
 }  // namespace
 
-// Pick rows per block and store capacity: prefer 4 rows and two blocks per
-// CU (half the LDS each); the store must hold the top k plus room for at
-// least 4 tiles of new candidates.  It never needs more than every visible
-// key plus one tile.
+// Launch geometry, in order of preference: two 4-row blocks per CU with a
+// dense store (one slot per visible key), then with a filter store (the top
+// k plus at least 8 tiles of candidates); then one block per CU, dense, then
+// filter with as many rows as fit.
 ScoreSelectPlan plan_score_select(int D, int topk, int64_t Skv, size_t lds_limit) {
   ScoreSelectPlan p{};
-  const int idx_bytes = Skv <= 65536 ? 2 : 4;
-  const int need = topk + 4 * 64;
-  const int64_t useful = ((Skv + 63) / 64) * 64 + 64;
-  const size_t budgets[2] = {lds_limit / 2, lds_limit};
-  for (size_t budget : budgets) {
-    for (int R = kWaves; R >= 1; --R) {
-      int cap = cap_for(D, R, idx_bytes, budget);
-      if (cap < need) continue;
-      if (cap > useful) cap = (int)useful;
-      if (cap < need) cap = need;
-      p.rows_per_block = R;
-      p.cap = cap;
-      p.idx_bytes = idx_bytes;
-      p.lds_bytes = (size_t)stage_bytes_for(D) + R * 1024 + (size_t)R * store_row_bytes(cap, idx_bytes);
-      return p;
-    }
-  }
-  return p;  // rows_per_block == 0: does not fit
+  const int64_t half = (int64_t)lds_limit / 2, full = (int64_t)lds_limit;
+  if (plan_dense(D, Skv, half, &p)) return p;
+  if (plan_filter(D, topk, Skv, half, kWaves, &p)) return p;
+  if (plan_dense(D, Skv, full, &p)) return p;
+  if (plan_filter(D, topk, Skv, full, 1, &p)) return p;
+  return ScoreSelectPlan{};  // rows_per_block == 0: does not fit
 }
 
-template <int HP, int D, typename IdxT>
+template <int HP, int D, bool DENSE, typename IdxT>
 static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
-  auto kern = score_select_kernel<HP, D, IdxT>;
+  auto kern = score_select_kernel<HP, D, DENSE, IdxT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)p.lds_bytes);
   if (e != hipSuccess) return e;
@@ -144,7 +183,7 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
     const int64_t blocks = ((r1 - r0 + R - 1) / R) * a.B;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), p.lds_bytes, st, a.q, a.k,
                        a.w, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio, a.topk, (int)r0,
-                       (int)r1, R, p.cap, stage_bytes_for(D), a.out_idx, a.out_score);
+                       (int)r1, R, p.cap, a.out_idx, a.out_score);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -152,13 +191,17 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
   return hipSuccess;
 }
 
+template <int HP, int D>
+static hipError_t launch_hd(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
+  if (p.dense) return launch_t<HP, D, true, uint16_t>(a, p, st);
+  return p.idx_bytes == 2 ? launch_t<HP, D, false, uint16_t>(a, p, st)
+                          : launch_t<HP, D, false, uint32_t>(a, p, st);
+}
+
 hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
-  const int HP = a.H <= 16 ? 16 : (a.H <= 32 ? 32 : 64);
-#define DSAI_CASE(hp, d)                                                       \
-  if (HP == hp && a.D == d)                                                    \
-    return p.idx_bytes == 2 ? launch_t<hp, d, uint16_t>(a, p, st)              \
-                            : launch_t<hp, d, uint32_t>(a, p, st);
-  DSAI_CASE(16, 32) DSAI_CASE(16, 64) DSAI_CASE(16, 128)
+  const int HP = a.H <= 32 ? 32 : 64;
+#define DSAI_CASE(hp, d) \
+  if (HP == hp && a.D == d) return launch_hd<hp, d>(a, p, st);
   DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
   DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)
 #undef DSAI_CASE

@@ -9,11 +9,11 @@
 //
 //   wave_append        ballot + prefix count: appends the passing lanes in
 //                      lane order after the current entries.
-//   wave_radix_select  8-bit MSD radix select of the k-th largest key value v
-//                      (4 histogram passes over the store) and how many
-//                      entries equal to v belong to the top k.  Loads are
-//                      batched and the histogram atomics return nothing, so
-//                      the passes run at LDS throughput, not latency.
+//   wave_radix_select  radix select of the k-th largest key value v and how
+//                      many entries equal to v belong to the top k: a min/max
+//                      pass, a 256-bin pass over the key range, then 8-bit
+//                      passes inside the chosen bin.  Loads are batched and
+//                      the histogram atomics return nothing.
 //   wave_compact       stable in-place compaction to exactly the top k.
 //   wave_emit          stable selection of the top k written straight to the
 //                      output row (index order), then (-1, -inf) padding.
@@ -31,6 +31,8 @@ struct RowStore {
   lds_u32* key;                       // [cap] order keys
   DSAI_LDS IdxT* idx;                 // [cap] indices
   lds_u32* hist;                      // [256] radix-select histogram (wave-private)
+  lds_u32* side;                      // [side_cap] scratch keys for the select
+  uint32_t side_cap;
 };
 
 __device__ __forceinline__ uint32_t uniform(uint32_t x) {
@@ -49,19 +51,60 @@ __device__ __forceinline__ void wave_append(const RowStore<IdxT>& rs, uint32_t& 
   count = uniform(count + (uint32_t)__popcll(m));
 }
 
-// Keys per lane handled per batch of the histogram loop.
+// LDS bytes per wavefront for the select: a 256-bin histogram and a 256-key
+// side list.
+constexpr int kSelScratchBytes = 2048;
+
+// Keys per lane handled per batch of the store-scanning loops.
 constexpr int kSelBatch = 8;
 
-// k-th largest key value v among key[0, n), 1 <= k <= n (.x), and the number
-// of entries equal to v that belong to the top k (.y).
-__device__ __noinline__ uint2 wave_radix_select(lds_u32* key, lds_u32* hist, uint32_t n,
-                                                uint32_t k) {
+// Bin b (of 256) of the k-th largest key among `cnt` keys whose histogram
+// sits in hist[0..255] (lane L owns bins 4L..4L+3); .y = number of keys in
+// bins above b, so rank k falls at position k - .y inside bin b.
+__device__ __forceinline__ uint2 find_bin(lds_u32* hist, uint32_t rem) {
   const int lane = lane_id();
-  uint32_t prefix = 0u, rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = lane; i < 256; i += kWave) hist[i] = 0u;
-    wave_lds_sync();
-    const uint32_t hi_mask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
+  const u32x4 c = *reinterpret_cast<const DSAI_LDS u32x4*>(&hist[4 * lane]);
+  const uint32_t s = c.x + c.y + c.z + c.w;
+  const uint32_t a3 = wave_incl_suffix(s) - s;
+  const uint32_t a2 = a3 + c.w, a1 = a2 + c.z, a0 = a1 + c.y;
+  int found = -1;
+  uint32_t above = 0u;
+  if (a3 < rem && rem <= a3 + c.w) {
+    found = 3; above = a3;
+  } else if (a2 < rem && rem <= a2 + c.z) {
+    found = 2; above = a2;
+  } else if (a1 < rem && rem <= a1 + c.y) {
+    found = 1; above = a1;
+  } else if (a0 < rem && rem <= a0 + c.x) {
+    found = 0; above = a0;
+  }
+  const uint64_t fm = ballot(found >= 0);
+  const int src = (int)__ffsll((unsigned long long)fm) - 1;
+  const uint32_t bin = (uint32_t)__shfl(4 * lane + found, src);
+  const uint32_t ab = (uint32_t)__shfl((int)above, src);
+  return make_uint2(uniform(bin), uniform(ab));
+}
+
+__device__ __forceinline__ void clear_hist(lds_u32* hist) {
+  const int lane = lane_id();
+  *reinterpret_cast<DSAI_LDS u32x4*>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+  wave_lds_sync();
+}
+
+__device__ __forceinline__ void hist_add(lds_u32* hist, uint32_t bin) {
+  __hip_atomic_fetch_add(&hist[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// Radix select over a key range: finds the k-th largest of the keys in
+// `key[0, n)` that lie in [lo, lo + 2^bits) (`m` of them, k <= m), resolving
+// `bits` low bits 8 at a time with histograms of (u - lo) digits.
+__device__ __forceinline__ uint2 select_in_range(const lds_u32* key, uint32_t n, lds_u32* hist,
+                                                 uint32_t lo, int bits, uint32_t rem) {
+  const int lane = lane_id();
+  while (bits > 0) {
+    const int shift = bits > 8 ? bits - 8 : 0;
+    clear_hist(hist);
+    const uint32_t width = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
     for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
       uint32_t u[kSelBatch];
 #pragma unroll
@@ -72,37 +115,91 @@ __device__ __noinline__ uint2 wave_radix_select(lds_u32* key, lds_u32* hist, uin
 #pragma unroll
       for (int j = 0; j < kSelBatch; ++j) {
         const uint32_t i = base + j * kWave + lane;
-        if (i < n && (u[j] & hi_mask) == prefix)
-          __hip_atomic_fetch_add(&hist[(u[j] >> shift) & 255u], 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+        const uint32_t d = u[j] - lo;
+        if (i < n && u[j] >= lo && d <= width) hist_add(hist, d >> shift);
       }
     }
     wave_lds_sync();
-    // lane L owns bins 4L .. 4L+3; count entries in higher bins
-    const u32x4 c = *reinterpret_cast<const DSAI_LDS u32x4*>(&hist[4 * lane]);
-    const uint32_t s = c.x + c.y + c.z + c.w;
-    const uint32_t a3 = wave_incl_suffix(s) - s;
-    const uint32_t a2 = a3 + c.w, a1 = a2 + c.z, a0 = a1 + c.y;
-    int found = -1;
-    uint32_t above = 0u;
-    if (a3 < rem && rem <= a3 + c.w) {
-      found = 3; above = a3;
-    } else if (a2 < rem && rem <= a2 + c.z) {
-      found = 2; above = a2;
-    } else if (a1 < rem && rem <= a1 + c.y) {
-      found = 1; above = a1;
-    } else if (a0 < rem && rem <= a0 + c.x) {
-      found = 0; above = a0;
-    }
-    const uint64_t fm = ballot(found >= 0);
-    const int src = (int)__ffsll((unsigned long long)fm) - 1;
-    const uint32_t digit = (uint32_t)__shfl(4 * lane + found, src);
-    const uint32_t above_d = (uint32_t)__shfl((int)above, src);
-    prefix = uniform(prefix | (digit << shift));
-    rem = uniform(rem - above_d);
+    const uint2 fb = find_bin(hist, rem);
+    lo += fb.x << shift;
+    rem -= fb.y;
+    bits = shift;
     wave_lds_sync();
   }
-  return make_uint2(prefix, rem);
+  return make_uint2(lo, rem);
+}
+
+// k-th largest key value v among key[0, n), 1 <= k <= n (.x), and the number
+// of entries equal to v that belong to the top k (.y).
+//
+// Pass 1 bins the keys by (u - min) scaled so the key range spans 256 bins,
+// which spreads the histogram atomics over many addresses (raw high bytes of
+// similar scores would all hit the same few bins).  The chosen bin is then
+// resolved 8 bits at a time; when it holds few keys they are first copied to
+// a side list so later passes touch only them.
+__device__ __noinline__ uint2 wave_radix_select(lds_u32* key, lds_u32* hist, lds_u32* side,
+                                                uint32_t side_cap, uint32_t n, uint32_t k) {
+  const int lane = lane_id();
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
+    uint32_t u[kSelBatch];
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      u[j] = i < n ? key[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      if (i < n) {
+        mn = min(mn, u[j]);
+        mx = max(mx, u[j]);
+      }
+    }
+  }
+  mn = uniform(wave_min(mn));
+  mx = uniform(wave_max(mx));
+  const uint32_t range = mx - mn;
+  if (range == 0u) return make_uint2(mn, k);  // every key equal
+  const int rbits = 32 - __clz(range);        // range < 2^rbits
+  const int shift = rbits > 8 ? rbits - 8 : 0;
+  clear_hist(hist);
+  for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
+    uint32_t u[kSelBatch];
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      u[j] = i < n ? key[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      if (i < n) hist_add(hist, (u[j] - mn) >> shift);
+    }
+  }
+  wave_lds_sync();
+  const uint2 fb = find_bin(hist, k);
+  const uint32_t cnt_bin = uniform(hist[fb.x]);
+  const uint32_t lo = mn + (fb.x << shift);
+  uint32_t rem = k - fb.y;
+  wave_lds_sync();
+  if (shift == 0) return make_uint2(lo, rem);
+  const uint32_t width = (1u << shift) - 1u;
+  if (cnt_bin <= side_cap) {
+    // gather the bin's keys (order is irrelevant for the value search)
+    uint32_t nside = 0u;
+    for (uint32_t base = 0; base < n; base += kWave) {
+      const uint32_t i = base + lane;
+      const uint32_t u = i < n ? key[i] : 0u;
+      const bool in = i < n && u >= lo && (u - lo) <= width;
+      const uint64_t m = ballot(in);
+      if (in) side[nside + lanes_below(m)] = u;
+      nside = uniform(nside + (uint32_t)__popcll(m));
+    }
+    wave_lds_sync();
+    return select_in_range(side, nside, hist, lo, shift, rem);
+  }
+  return select_in_range(key, n, hist, lo, shift, rem);
 }
 
 // Keep, in store order, the entries with key > v and the first `take_eq`
@@ -149,7 +246,7 @@ __device__ __forceinline__ uint32_t wave_keep_topk(const RowStore<IdxT>& rs, uin
                                                    uint32_t k, uint32_t* tau) {
   if (count <= k) return count;
   wave_lds_sync();
-  const uint2 sel = wave_radix_select(rs.key, rs.hist, count, k);
+  const uint2 sel = wave_radix_select(rs.key, rs.hist, rs.side, rs.side_cap, count, k);
   *tau = sel.x;
   return wave_compact(rs, count, sel.x, sel.y);
 }
@@ -186,6 +283,46 @@ __device__ __noinline__ void wave_emit(RowStore<IdxT> rs, uint32_t n, uint32_t v
   }
 }
 
+// Dense store: key[i] is the order key of index i, for i < n.  Writes the top k
+// (entries with key > v and the first `take_eq` with key == v) in index
+// order, then (-1, -inf) padding up to `topk` slots.
+__device__ __noinline__ void wave_emit_dense(const lds_u32* key, uint32_t n, uint32_t v,
+                                             uint32_t take_eq, int topk,
+                                             int32_t* __restrict__ out_idx,
+                                             float* __restrict__ out_score) {
+  const int lane = lane_id();
+  uint32_t wpos = 0u, eq_seen = 0u;
+  constexpr int kB = 4;
+  for (uint32_t base = 0; base < n; base += kWave * kB) {
+    uint32_t u[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      u[j] = i < n ? key[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      const bool in = i < n;
+      const bool eq = in && (u[j] == v);
+      const uint64_t meq = ballot(eq);
+      const bool keep = (in && u[j] > v) || (eq && (eq_seen + lanes_below(meq)) < take_eq);
+      const uint64_t mk = ballot(keep);
+      if (keep) {
+        const uint32_t p = wpos + lanes_below(mk);
+        out_idx[p] = (int32_t)i;
+        out_score[p] = ord_to_float(u[j]);
+      }
+      wpos = uniform(wpos + (uint32_t)__popcll(mk));
+      eq_seen = uniform(eq_seen + (uint32_t)__popcll(meq));
+    }
+  }
+  for (uint32_t p = wpos + lane; p < (uint32_t)topk; p += kWave) {
+    out_idx[p] = -1;
+    out_score[p] = -__builtin_inff();
+  }
+}
+
 // The row's top k (index order) from a store holding `count` entries.
 template <typename IdxT>
 __device__ __forceinline__ void wave_finish_row(const RowStore<IdxT>& rs, uint32_t count, int topk,
@@ -194,7 +331,7 @@ __device__ __forceinline__ void wave_finish_row(const RowStore<IdxT>& rs, uint32
   uint32_t v = 0u, eq = 0u;
   if (count > (uint32_t)topk) {
     wave_lds_sync();
-    const uint2 sel = wave_radix_select(rs.key, rs.hist, count, (uint32_t)topk);
+    const uint2 sel = wave_radix_select(rs.key, rs.hist, rs.side, rs.side_cap, count, (uint32_t)topk);
     v = sel.x;
     eq = sel.y;
   }

@@ -76,6 +76,13 @@ MEDIUM = [
                    topk=300, w_var=1 / 16, seed=18),
     SY.IndexerCase("h64d128_k4096", B=1, S=4200, Skv=4200, H=64, D=128, compress_ratio=1,
                    topk=4096, w_var=1 / 64, seed=19),
+    # more keys than a dense row store holds: the filtering store with compactions
+    SY.IndexerCase("filter_h32d64_k64", B=1, S=5000, Skv=5000, H=32, D=64, compress_ratio=1,
+                   topk=64, w_var=1 / 32, seed=24),
+    SY.IndexerCase("filter_h64d128_k2048", B=1, S=6000, Skv=6000, H=64, D=128,
+                   compress_ratio=1, topk=2048, w_var=1 / 64, seed=25),
+    SY.IndexerCase("filter_b2_r2_k300", B=2, S=9000, Skv=4500, H=16, D=128, compress_ratio=2,
+                   topk=300, w_var=1 / 16, seed=26),
 ]
 
 
@@ -172,6 +179,18 @@ def test_empty_and_degenerate_shapes(dsai):
         m = min(10, t + 1)
         assert gidx[0, t, :m].tolist() == list(range(m)), t
         assert np.all(gsc[0, t, :m] == 0.0)
+
+
+def test_filter_store_wide_indices(dsai):
+    """Skv > 65536: the filtering store keeps 32-bit indices."""
+    case = SY.IndexerCase("wide_idx", B=1, S=70000, Skv=70000, H=4, D=32, compress_ratio=1,
+                          topk=16, w_var=1 / 4, seed=27)
+    log(f"[gpu] wide indices {case}")
+    inp = SY.indexer_inputs(case)
+    gidx, gsc = run_gpu(dsai, case, inp)
+    rows = [0, 15, 16, 65535, 65536, 65537, 69999] + list(range(1000, 70000, 7000))
+    _, _, full = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
+    compare(case, gidx, gsc, rows, full)
 
 
 def _sample_rows(case, extra=24, seed=0):
