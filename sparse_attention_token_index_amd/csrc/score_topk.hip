@@ -99,15 +99,8 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(
   if (!active) return;
   const int64_t orow = ((int64_t)b * S + t) * topk;
   if constexpr (DENSE) {
-    uint32_t v = 0u, eq = 0u;
-    wave_lds_sync();
-    if (n_t > topk) {
-      const uint2 sel = wave_radix_select(rs.key, rs.hist, rs.side, rs.side_cap, (uint32_t)n_t,
-                                          (uint32_t)topk);
-      v = sel.x;
-      eq = sel.y;
-    }
-    wave_emit_dense(rs.key, (uint32_t)n_t, v, eq, topk, out_idx + orow, out_score + orow);
+    dense_finish(rs.key, (uint32_t)n_t, (uint32_t)topk, rs.hist, rs.side, topk, out_idx + orow,
+                 out_score + orow);
   } else {
     wave_finish_row(rs, count, topk, out_idx + orow, out_score + orow);
   }
@@ -122,7 +115,7 @@ int tile_bytes_for(int D) { return 32 * (2 * D + 16); }
 bool plan_dense(int D, int64_t Skv, int64_t budget, ScoreSelectPlan* p) {
   const int64_t tile = tile_bytes_for(D);
   const int64_t region = tile > kWaves * 1024 ? tile : kWaves * 1024;
-  const int64_t cap = Skv > 0 ? ((Skv + 63) / 64) * 64 : 64;
+  const int64_t cap = Skv > 0 ? ((Skv + 255) / 256) * 256 : 256;  // whole 256-key groups
   const int64_t lds = region + kWaves * 1024 + (int64_t)kWaves * cap * 4;
   if (lds > budget) return false;
   p->rows_per_block = kWaves;

@@ -283,38 +283,119 @@ __device__ __noinline__ void wave_emit(RowStore<IdxT> rs, uint32_t n, uint32_t v
   }
 }
 
-// Dense store: key[i] is the order key of index i, for i < n.  Writes the top k
-// (entries with key > v and the first `take_eq` with key == v) in index
-// order, then (-1, -inf) padding up to `topk` slots.
-__device__ __noinline__ void wave_emit_dense(const lds_u32* key, uint32_t n, uint32_t v,
-                                             uint32_t take_eq, int topk,
+// ---------------------------------------------------------------------------
+// Dense rows: key[i] is the order key of index i for i < n, the store is a
+// multiple of 256 entries and 16-byte aligned.  Everything here is inlined so
+// the row size and k stay scalar (uniform loops, no divergent bookkeeping).
+// ---------------------------------------------------------------------------
+
+// k-th largest key v among key[0, n), k <= n (.x), and how many entries equal
+// to v belong to the top k (.y).  Pass 1: min/max; pass 2: 256-bin histogram
+// of (u - min) scaled to the key range; pass 3: the chosen bin's keys go to
+// the side list (up to 256), whose remaining bits are resolved in registers-
+// sized passes.  Reads are 16 bytes per lane.
+__device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, uint32_t k,
+                                              lds_u32* hist, lds_u32* side) {
+  const int lane = lane_id();
+  const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
+  const uint32_t ngroups = (n + 255u) >> 8;  // 256 keys per group, 4 per lane
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (uint32_t gi = 0; gi < ngroups; ++gi) {
+    const u32x4 u = k4[gi * 64u + lane];
+    const uint32_t i0 = gi * 256u + 4u * lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i0 + e < n) {
+        mn = min(mn, u[e]);
+        mx = max(mx, u[e]);
+      }
+    }
+  }
+  mn = uniform(wave_min(mn));
+  mx = uniform(wave_max(mx));
+  const uint32_t range = mx - mn;
+  if (range == 0u) return make_uint2(mn, k);
+  const int rbits = 32 - __clz(range);
+  const int shift = rbits > 8 ? rbits - 8 : 0;
+  clear_hist(hist);
+  for (uint32_t gi = 0; gi < ngroups; ++gi) {
+    const u32x4 u = k4[gi * 64u + lane];
+    const uint32_t i0 = gi * 256u + 4u * lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i0 + e < n) hist_add(hist, (u[e] - mn) >> shift);
+  }
+  wave_lds_sync();
+  const uint2 fb = find_bin(hist, k);
+  const uint32_t cnt_bin = uniform(hist[fb.x]);
+  const uint32_t lo = mn + (fb.x << shift);
+  const uint32_t rem = k - fb.y;
+  wave_lds_sync();
+  if (shift == 0) return make_uint2(lo, rem);
+  const uint32_t width = (1u << shift) - 1u;
+  if (cnt_bin > 256u) return select_in_range(key, n, hist, lo, shift, rem);
+  uint32_t ns = 0u;
+  for (uint32_t gi = 0; gi < ngroups; ++gi) {
+    const u32x4 u = k4[gi * 64u + lane];
+    const uint32_t i0 = gi * 256u + 4u * lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = (i0 + e < n) && u[e] >= lo && (u[e] - lo) <= width;
+      const uint64_t m = ballot(in);
+      if (m) {
+        if (in) side[ns + lanes_below(m)] = u[e];
+        ns = uniform(ns + (uint32_t)__popcll(m));
+      }
+    }
+  }
+  wave_lds_sync();
+  return select_in_range(side, ns, hist, lo, shift, rem);
+}
+
+// Write the dense row's top k in index order (entries > v, then the first
+// `take_eq` entries == v), then (-1, -inf) padding up to `topk` slots.  With
+// n <= k every visible key is written.
+__device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uint32_t k,
+                                             lds_u32* hist, lds_u32* side, int topk,
                                              int32_t* __restrict__ out_idx,
                                              float* __restrict__ out_score) {
   const int lane = lane_id();
-  uint32_t wpos = 0u, eq_seen = 0u;
-  constexpr int kB = 4;
-  for (uint32_t base = 0; base < n; base += kWave * kB) {
-    uint32_t u[kB];
-#pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      u[j] = i < n ? key[i] : 0u;
+  uint32_t wpos = n;
+  if (n <= k) {
+    for (uint32_t i = lane; i < n; i += kWave) {
+      out_idx[i] = (int32_t)i;
+      out_score[i] = ord_to_float(key[i]);
     }
+  } else {
+    wave_lds_sync();
+    const uint2 sel = dense_select(key, n, k, hist, side);
+    const uint32_t v = sel.x, take_eq = sel.y;
+    wpos = 0u;
+    uint32_t eq_seen = 0u;
+    for (uint32_t base = 0; base < n; base += kWave * 4) {
+      uint32_t u[4];
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      const bool in = i < n;
-      const bool eq = in && (u[j] == v);
-      const uint64_t meq = ballot(eq);
-      const bool keep = (in && u[j] > v) || (eq && (eq_seen + lanes_below(meq)) < take_eq);
-      const uint64_t mk = ballot(keep);
-      if (keep) {
-        const uint32_t p = wpos + lanes_below(mk);
-        out_idx[p] = (int32_t)i;
-        out_score[p] = ord_to_float(u[j]);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t i = base + j * kWave + lane;
+        u[j] = i < n ? key[i] : 0u;
       }
-      wpos = uniform(wpos + (uint32_t)__popcll(mk));
-      eq_seen = uniform(eq_seen + (uint32_t)__popcll(meq));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t i = base + j * kWave + lane;
+        bool keep = u[j] > v;  // u = 0 past n: never kept (real keys are never 0)
+        const uint64_t meq = ballot(i < n && u[j] == v);
+        if (meq) {
+          if (i < n && u[j] == v) keep = (eq_seen + lanes_below(meq)) < take_eq;
+          eq_seen = uniform(eq_seen + (uint32_t)__popcll(meq));
+        }
+        const uint64_t mk = ballot(keep);
+        if (keep) {
+          const uint32_t p = wpos + lanes_below(mk);
+          out_idx[p] = (int32_t)i;
+          out_score[p] = ord_to_float(u[j]);
+        }
+        wpos = uniform(wpos + (uint32_t)__popcll(mk));
+      }
     }
   }
   for (uint32_t p = wpos + lane; p < (uint32_t)topk; p += kWave) {
