@@ -191,6 +191,21 @@ int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,
                 void* stream);
 
+/* ---- row order ----------------------------------------------------------- */
+/* Reorder `rows` top-k rows of k (index, score) entries in place, row r at
+ * idx[r * k .. r * k + k) / score[r * k .. r * k + k): by score descending,
+ * the lower index first among equal scores, entries with a negative index
+ * last as (-1, -inf).  This is the step that turns a DSAI_ORDER_INDEX result
+ * of dsai_score_topk or dsai_topk_pools into the DSAI_ORDER_SCORE result
+ * (those calls run it themselves under DSAI_ORDER_SCORE); the real entries of
+ * each row must be listed in ascending index order, as DSAI_ORDER_INDEX
+ * writes them (rows in another order get the same entries in score order,
+ * equal scores in an unspecified order).  Scores are finite.
+ * rows >= 0 (< 2^31), 1 <= k <= DSAI_MAX_TOPK (DSAI_ERR_INVALID_ARG
+ * otherwise); nothing is launched when rows == 0 or k == 1. */
+int dsai_sort_rows(dsai_handle h, int32_t* idx, float* score, int64_t rows, int k,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,7 @@ EXPORTS = (
     "dsai_create", "dsai_destroy", "dsai_status_string", "dsai_last_hip_error",
     "dsai_score_topk", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
     "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
+    "dsai_sort_rows",
 )
 
 DSAI_OK = 0
@@ -82,6 +83,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_select_workspace_size": [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
         "dsai_select": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "dsai_expand": [vp, vp, i64, vp, vp],
+        "dsai_sort_rows": [vp, vp, vp, i64, c_int, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -306,3 +308,19 @@ class Indexer:
             st = self._lib.dsai_expand(self._h, _ptr(pool_ids), Q, _ptr(tokens), _stream(dev))
         self._check(st, "dsai_expand")
         return tokens
+
+    def sort_rows(self, idx, score):
+        """In place: each row of idx/score [..., k] (ascending-index top-k rows,
+        as written in DSAI_ORDER_INDEX order) reordered by score descending,
+        lower index first among equal scores, padding (-1, -inf) last."""
+        if idx.dim() < 1:
+            raise ValueError("idx: needs a last (row) dimension")
+        k = idx.shape[-1]
+        rows = idx.numel() // k if k else 0
+        dev = idx.device
+        _need(idx, "idx", torch.int32, tuple(idx.shape))
+        _need(score, "score", torch.float32, tuple(idx.shape), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_sort_rows(self._h, _ptr(idx), _ptr(score), rows, int(k), _stream(dev))
+        self._check(st, "dsai_sort_rows")
+        return idx, score

@@ -22,7 +22,10 @@ SOURCES = ["api.cpp", "score_topk.hip", "sort_rows.hip", "pooled.hip"]
 # so NaN-preserving canonicalization (an extra VALU op per ReLU) is dropped.
 HIP_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-fno-honor-nans", "-Wall", "-Wno-unused-function"]
+             "-fno-honor-nans", "-Wall", "-Wno-unused-function",
+             # matrix-core results in ordinary VGPRs: the epilogue reads them
+             # directly instead of copying each accumulator out of AGPRs
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -224,4 +224,14 @@ int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* toke
   return hip_status(h, dsai::launch_expand(a, static_cast<hipStream_t>(stream)));
 }
 
+int dsai_sort_rows(dsai_handle h, int32_t* idx, float* score, int64_t rows, int k, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (rows < 0 || rows > kI32 || k < 1 || k > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
+  if (rows == 0 || k == 1) return DSAI_OK;
+  if (!idx || !score) return DSAI_ERR_NULLPTR;
+  if (reinterpret_cast<uintptr_t>(idx) % 4 != 0 || reinterpret_cast<uintptr_t>(score) % 4 != 0)
+    return DSAI_ERR_INVALID_ARG;
+  return hip_status(h, dsai::launch_sort_rows(idx, score, rows, k, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -51,50 +51,67 @@ __device__ __forceinline__ float ord_to_float(uint32_t u) {
   return __uint_as_float(b);
 }
 
+// Cross-lane steps use DPP moves (no LDS round trip).  A row is 16 lanes.
+// Lanes whose DPP source lies outside their row read 0; rows outside
+// ROW_MASK read 0.  Every helper below must be called by all 64 lanes.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, true);
+}
+
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowShr1 = 0x111;      // row_shr:n = 0x110 + n
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row -> the next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 -> rows 2 and 3
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
 // Inclusive sum over lanes [0, lane].
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t y = __shfl_up(x, off);
-    if (l >= off) x += y;
-  }
+  x += dpp_mov<kDppRowShr1>(x);
+  x += dpp_mov<kDppRowShr1 + 1>(x);
+  x += dpp_mov<kDppRowShr1 + 3>(x);
+  x += dpp_mov<kDppRowShr1 + 7>(x);
+  x += dpp_mov<kDppRowBcast15, 0xA>(x);
+  x += dpp_mov<kDppRowBcast31, 0xC>(x);
   return x;
 }
 
 // Inclusive sum over lanes [lane, 63].
 __device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t y = __shfl_down(x, off);
-    if (l + off < kWave) x += y;
-  }
-  return x;
+  const uint32_t incl = wave_incl_scan(x);
+  return lane_value(incl, kWave - 1) - incl + x;
+}
+
+// Reduction over all lanes (the same value in every lane).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
+  x = op(x, dpp_mov<kDppQuadXor1>(x));
+  x = op(x, dpp_mov<kDppQuadXor2>(x));
+  x = op(x, dpp_mov<kDppRowHalfMirror>(x));
+  x = op(x, dpp_mov<kDppRowMirror>(x));
+  return op(op(lane_value(x, 0), lane_value(x, 16)), op(lane_value(x, 32), lane_value(x, 48)));
 }
 
 __device__ __forceinline__ uint32_t wave_and(uint32_t x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x &= __shfl_xor(x, off);
-  return x;
-}
-
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
-  return x;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
-  return x;
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return a & b; });
 }
 
 __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x |= __shfl_xor(x, off);
-  return x;
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return a | b; });
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -121,11 +121,13 @@ struct TileScorer {
     }
   }
 
-  // Full score of key `lane % 32` of the staged tile (in lanes l and l + 32).
-  __device__ __forceinline__ float score(const lds_char* tile) const {
+  // Products of the staged tile's 32 keys with the query heads, on the matrix
+  // cores: acc[m] holds M-tile m (lane (c, g): key c, 16 heads).  Only issues
+  // the LDS reads and MFMAs; reduce() consumes the result, so a caller can
+  // overlap one tile's reduction with the next tile's products.
+  __device__ __forceinline__ void mma(const lds_char* tile, floatx16 (&acc)[MT]) const {
     const int lane = lane_id();
     const int c = lane & 31, g = lane >> 5;
-    floatx16 acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = floatx16{};
     const lds_char* rowp = tile + c * G::kRowBytes + g * D;
@@ -136,12 +138,26 @@ struct TileScorer {
       for (int m = 0; m < MT; ++m)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[m][j], b, acc[m], 0, 0, 0);
     }
-    float p = 0.f;
+  }
+
+  // ReLU, head weights and the sum over heads of mma()'s products: the full
+  // score of key lane % 32, in lanes l and l + 32 (four partial sums keep the
+  // dependency chains short enough to interleave with matrix-core work).
+  __device__ __forceinline__ float reduce(const floatx16 (&acc)[MT]) const {
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p = fmaf(wv[m][r], fmaxf(acc[m][r], 0.f), p);
-    return p + __shfl_xor(p, 32);
+      for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[m][r], fmaxf(acc[m][r], 0.f), p[r & 3]);
+    const float s = (p[0] + p[1]) + (p[2] + p[3]);
+    return s + __shfl_xor(s, 32);
+  }
+
+  // Full score of key `lane % 32` of the staged tile (in lanes l and l + 32).
+  __device__ __forceinline__ float score(const lds_char* tile) const {
+    floatx16 acc[MT];
+    mma(tile, acc);
+    return reduce(acc);
   }
 };
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(
   constexpr int kTileRegion =
       (DENSE && G::kTileBytes < kWaves * 1024) ? kWaves * 1024 : G::kTileBytes;
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform
   const int lane = lane_id();
   const int row_bytes = DENSE ? cap * 4 : cap * 4 + ((cap * (int)sizeof(IdxT) + 15) & ~15);
 
@@ -78,22 +78,51 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(
   ld.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
   if (ntiles > 0) ld.load(0u);
 
-  for (int it = 0; it < ntiles; ++it) {
+  // Software pipeline: the products of tile `it` are issued before the
+  // reduction and recording of tile it - 1, so the vector ALU work of one tile
+  // overlaps the matrix-core work of the next.  The wave's tiles are a prefix
+  // [0, nt_w) of the block's; the accumulators alternate between two register
+  // sets (the loop body is unrolled twice so no copies are needed).
+  constexpr int MT = TileScorer<HP, D>::MT;
+  const int nt_w = (n_t + G::kTileKeys - 1) / G::kTileKeys;  // 0 when inactive
+  auto record = [&](int it_rec, const floatx16 (&a)[MT]) {
+    const float s = sc.reduce(a);  // lanes l and l + 32 hold key l % 32
+    const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
+    const uint32_t u = ord_key(s);
+    if constexpr (DENSE) {
+      if (lane < 32) rs.key[key] = u;
+    } else {
+      wave_append(rs, count, lane < 32 && key < (uint32_t)n_t && u > tau, u, key);
+      if (count > (uint32_t)(cap - G::kTileKeys)) count = wave_keep_topk(rs, count, topk, &tau);
+    }
+  };
+  auto stage = [&](int it) {
     __syncthreads();
     ld.store(tile);
     __syncthreads();
     if (it + 1 < ntiles) ld.load((uint32_t)(it + 1) * G::kTileKeys);
-    if (active && it * G::kTileKeys < n_t) {
-      const float s = sc.score(tile);  // lanes l and l + 32 hold key l % 32
-      const uint32_t key = (uint32_t)(it * G::kTileKeys + (lane & 31));
-      const uint32_t u = ord_key(s);
-      if constexpr (DENSE) {
-        if (lane < 32) rs.key[key] = u;
-      } else {
-        wave_append(rs, count, lane < 32 && key < (uint32_t)n_t && u > tau, u, key);
-        if (count > (uint32_t)(cap - G::kTileKeys)) count = wave_keep_topk(rs, count, topk, &tau);
-      }
+  };
+  auto step = [&](int it, floatx16 (&cur)[MT], const floatx16 (&old)[MT]) {
+    stage(it);
+    if (it < nt_w) {
+      sc.mma(tile, cur);
+      record(it - 1, old);
+    } else if (it == nt_w) {
+      record(it - 1, old);
     }
+  };
+  floatx16 acc0[MT], acc1[MT];
+  if (ntiles > 0) {
+    stage(0);
+    if (nt_w > 0) sc.mma(tile, acc0);
+  }
+  for (int it = 1; it < ntiles; it += 2) {
+    step(it, acc1, acc0);
+    if (it + 1 < ntiles) step(it + 1, acc0, acc1);
+  }
+  if (nt_w > 0 && nt_w == ntiles) {
+    if ((ntiles - 1) & 1) record(ntiles - 1, acc1);
+    else record(ntiles - 1, acc0);
   }
   if constexpr (DENSE) __syncthreads();  // the tile region now holds the side lists
   if (!active) return;

@@ -1,20 +1,26 @@
-// Stable in-place sort of top-k rows by score descending.
+// In-place sort of top-k rows by score descending, the lower index first among
+// equal scores.  Padding slots (index -1, score -inf) end up at the tail.
 //
-// Rows arrive in ascending index order (the selection kernels emit them that
-// way), so a stable sort on the score alone yields the order "score
-// descending, lower index first among equal scores".  Padding slots
-// (index -1, score -inf) stay at the tail.
+// One workgroup (256 threads) sorts one row of up to 256 * ITEMS entries.
 //
-// One workgroup (256 threads) sorts one row with a block-wide LSD radix sort
-// on the 32-bit order key (4-bit digits), the row held in registers in a
-// blocked arrangement (thread t owns slots [t*ITEMS, (t+1)*ITEMS)):
-//   count   each thread counts its items per digit in private LDS counters,
-//   scan    exclusive scan over (digit, thread) gives every item its rank,
-//   scatter items go to their rank in an LDS exchange buffer, then are
-//           read back blocked.
-// Digit positions on which every real key agrees are skipped.  The
-// workgroup's LDS footprint is small, so several rows are sorted per CU at
-// once and LDS latency is hidden by the other workgroups.
+// Bucket path (the common case).  The row's real entries are spread over
+// NB = 256 * ITEMS buckets by a monotone map of the score onto [0, NB)
+// (linear in the score between the row's maximum and minimum, so higher
+// scores land in lower buckets); a counting pass and a scan give every bucket
+// its output range, the entries are scattered into their bucket's range, and
+// each entry's final slot inside its bucket is its rank there under
+// (score descending, index ascending), counted by comparing it with the
+// bucket's other entries.  With about one entry per bucket this costs a few
+// LDS operations per entry instead of a pass per digit.
+//
+// Radix path (rows with a bucket of more than kBucketLimit entries: many
+// equal or nearly equal scores).  A stable block-wide LSD radix sort on the
+// 32-bit order key with 4-bit digits; digit positions on which every real key
+// agrees are skipped.  Stability gives the index order among equal scores
+// because rows arrive in ascending index order (the selection kernels write
+// them that way).
+#include <float.h>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -22,25 +28,48 @@ namespace dsai {
 
 constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / kWave;
+constexpr uint32_t kBucketLimit = 64;
+
+template <int ITEMS>
+struct SortLayout {
+  static constexpr int NB = kSortThreads * ITEMS;  // buckets (>= entries per row)
+  // bucket path, in words: start[NB + 1] | pad | cur[NB] | kv[NB] (key, index pairs)
+  static constexpr int kStart = 0, kCur = NB + 2, kKV = 2 * NB + 2;
+  static constexpr int kBucketWords = 4 * NB + 2;
+  // radix path: cnt[16][256] | xk[256 * (ITEMS + 1)] | xv[256 * (ITEMS + 1)]
+  static constexpr int kRadixWords = 16 * kSortThreads + 2 * kSortThreads * (ITEMS + 1);
+  static constexpr int kRed = kBucketWords > kRadixWords ? kBucketWords : kRadixWords;
+  static constexpr int kWords = kRed + 4 * kSortWaves;
+};
+
+// Monotone non-increasing map of a score onto [0, nb): every step (halving,
+// subtraction, scaling, clamping) is monotone under round-to-nearest, so a
+// higher score never lands in a higher bucket.  Halving keeps the difference
+// of any two finite scores finite.
+__device__ __forceinline__ uint32_t bucket_of(uint32_t key, float top_half, float scale,
+                                              uint32_t nb) {
+  // explicit roundings: both call sites must map a key to the same bucket
+  const float d = __fmul_rn(__fsub_rn(top_half, __fmul_rn(0.5f, ord_to_float(key))), scale);
+  const uint32_t b = (uint32_t)fminf(d, (float)(nb - 1u));  // d >= 0 for a real entry
+  return b < nb ? b : nb - 1u;
+}
 
 __device__ __forceinline__ uint32_t blocked_addr(uint32_t p, int items) {
   return p + p / (uint32_t)items;  // one pad word per thread block of items: odd stride
 }
 
+// Stable LSD radix sort of the row (reloaded in a blocked arrangement: thread
+// t owns slots [t * ITEMS, (t + 1) * ITEMS)).
 template <int ITEMS>
-__global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* __restrict__ idx,
-                                                                 float* __restrict__ score,
-                                                                 int topk) {
-  extern __shared__ __align__(16) uint32_t sort_smem[];
-  uint32_t* cnt = sort_smem;                                  // [digit][thread]
-  uint32_t* xk = cnt + 16 * kSortThreads;                      // exchange keys
-  int32_t* xv = (int32_t*)(xk + kSortThreads * (ITEMS + 1));   // exchange indices
-  uint32_t* red = (uint32_t*)(xv + kSortThreads * (ITEMS + 1));
-
+__device__ void radix_sort_row(int32_t* __restrict__ ri, float* __restrict__ rs, int topk,
+                               uint32_t* smem) {
+  using L = SortLayout<ITEMS>;
+  uint32_t* cnt = smem;                                        // [digit][thread]
+  uint32_t* xk = cnt + 16 * kSortThreads;                       // exchange keys
+  int32_t* xv = (int32_t*)(xk + kSortThreads * (ITEMS + 1));    // exchange indices
+  uint32_t* red = smem + L::kRed;
   const int t = threadIdx.x;
   const int lane = lane_id(), wave = t >> 6;
-  int32_t* ri = idx + (int64_t)blockIdx.x * topk;
-  float* rs = score + (int64_t)blockIdx.x * topk;
 
   uint32_t key[ITEMS];
   int32_t val[ITEMS];
@@ -58,6 +87,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* __rest
   }
   a = wave_and(a);
   o = wave_or(o);
+  __syncthreads();  // the bucket path's reads of `red` are done
   if (lane == 0) {
     red[wave] = a;
     red[kSortWaves + wave] = o;
@@ -69,7 +99,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* __rest
     ba &= red[w];
     bo |= red[kSortWaves + w];
   }
-  const uint32_t diff = ba ^ bo;  // 0 when the row has no real entry
+  const uint32_t diff = ba ^ bo;
 
   for (int shift = 0; shift < 32; shift += 4) {
     if (((diff >> shift) & 15u) == 0u) continue;
@@ -128,29 +158,241 @@ __global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* __rest
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int p = t * ITEMS + i;
-    if (p < topk && val[i] >= 0) {
-      ri[p] = val[i];
-      rs[p] = ord_to_float(~key[i]);
+    if (p < topk) {
+      ri[p] = val[i] >= 0 ? val[i] : -1;
+      rs[p] = val[i] >= 0 ? ord_to_float(~key[i]) : -__builtin_huge_valf();
     }
   }
 }
 
-static size_t sort_lds_bytes(int items) {
-  return 4 * ((size_t)16 * kSortThreads + 2 * (size_t)kSortThreads * (items + 1) + 2 * kSortWaves);
+// Bucket path for one row (falls back to the radix path when a bucket is too
+// full).  key/val: the row's entries in the striped arrangement (slot
+// i * 256 + t), val < 0 for padding.
+template <int ITEMS>
+__device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float* __restrict__ rs,
+                                                int topk, uint32_t* smem, uint32_t (&key)[ITEMS],
+                                                int32_t (&val)[ITEMS]) {
+  using L = SortLayout<ITEMS>;
+  constexpr uint32_t NB = (uint32_t)L::NB;
+  uint32_t* start = smem + L::kStart;  // counts, then each bucket's first slot
+  uint32_t* cur = smem + L::kCur;      // scatter cursors
+  uint2* kv = reinterpret_cast<uint2*>(smem + L::kKV);  // entries grouped by bucket
+  uint32_t* red = smem + L::kRed;
+  const int t = threadIdx.x;
+  const int lane = lane_id(), wave = t >> 6;
+
+  // Real entries, their key range.
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nreal = 0u;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    if (val[i] >= 0) {
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+    nreal += (uint32_t)__popcll(ballot(val[i] >= 0));
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  __syncthreads();  // the previous row's readers of `red` and `kv` are done
+  if (lane == 0) {
+    red[wave] = kmin;
+    red[kSortWaves + wave] = kmax;
+    red[2 * kSortWaves + wave] = nreal;
+  }
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) start[t * ITEMS + j] = 0u;
+  __syncthreads();
+  uint32_t nv = 0u;
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) {
+    kmin = min(kmin, red[w]);
+    kmax = max(kmax, red[kSortWaves + w]);
+    nv += red[2 * kSortWaves + w];
+  }
+  const float top_half = 0.5f * ord_to_float(kmax);
+  const float range = top_half - 0.5f * ord_to_float(kmin);
+  const float scale = (nv > 0u && range > 0.f) ? fminf((float)NB / range, FLT_MAX) : 0.f;
+
+  // Count entries per bucket.
+  uint32_t bkt[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    bkt[i] = bucket_of(key[i], top_half, scale, NB);
+    if (val[i] >= 0) atomicAdd(&start[bkt[i]], 1u);
+  }
+  __syncthreads();
+
+  // Exclusive scan of the counts (thread t owns buckets [t*ITEMS, (t+1)*ITEMS))
+  // and the largest bucket.
+  uint32_t c[ITEMS];
+  uint32_t run = 0u, big = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const uint32_t n = start[t * ITEMS + j];
+    c[j] = run;
+    run += n;
+    big = max(big, n);
+  }
+  const uint32_t incl = wave_incl_scan(run);
+  big = wave_max(big);
+  if (lane == kWave - 1) {
+    red[3 * kSortWaves + wave] = incl;
+    red[wave] = big;  // every thread read red[0..3] before the last barrier
+  }
+  __syncthreads();
+  uint32_t base = incl - run;
+  big = 0u;
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) {
+    if (w < wave) base += red[3 * kSortWaves + w];
+    big = max(big, red[w]);
+  }
+  if (big > kBucketLimit) {  // block-uniform
+    radix_sort_row<ITEMS>(ri, rs, topk, smem);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    start[t * ITEMS + j] = base + c[j];
+    cur[t * ITEMS + j] = base + c[j];
+  }
+  if (t == 0) start[NB] = nv;
+  __syncthreads();
+
+  // Scatter into the buckets' ranges (arbitrary order inside a bucket).
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    if (val[i] >= 0) {
+      const uint32_t slot = atomicAdd(&cur[bkt[i]], 1u);
+      kv[slot] = make_uint2(key[i], (uint32_t)val[i]);
+    }
+  }
+  __syncthreads();
+
+  // Rank of each entry inside its bucket: entries with a higher key, or the
+  // same key and a lower index, go first.  The comparison loops of the
+  // thread's entries run side by side so their LDS reads overlap.
+  uint32_t s0[ITEMS], cnt[ITEMS], rank[ITEMS];
+  uint32_t maxc = 0u;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t p = (uint32_t)(i * kSortThreads + t);
+    s0[i] = p;
+    cnt[i] = 0u;
+    rank[i] = 0u;
+    if (p < nv) {
+      const uint2 e = kv[p];
+      key[i] = e.x;
+      val[i] = (int32_t)e.y;
+      const uint32_t b = bucket_of(key[i], top_half, scale, NB);
+      const uint32_t lo = start[b], n = start[b + 1] - lo;
+      if (n > 1u) {
+        s0[i] = lo;
+        cnt[i] = n;
+      }
+    }
+    maxc = max(maxc, cnt[i]);
+  }
+  for (uint32_t j = 0; j < maxc; ++j) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      if (j < cnt[i]) {
+        const uint2 e = kv[s0[i] + j];
+        rank[i] += (e.x > key[i] || (e.x == key[i] && (int32_t)e.y < val[i])) ? 1u : 0u;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    if ((uint32_t)(i * kSortThreads + t) < nv)
+      kv[s0[i] + rank[i]] = make_uint2(key[i], (uint32_t)val[i]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = i * kSortThreads + t;
+    if (p < topk) {
+      const bool real = (uint32_t)p < nv;
+      const uint2 e = real ? kv[p] : make_uint2(0u, 0u);
+      ri[p] = real ? (int32_t)e.y : -1;
+      rs[p] = real ? ord_to_float(e.x) : -__builtin_huge_valf();
+    }
+  }
+}
+
+// Each workgroup sorts rows blockIdx.x, blockIdx.x + gridDim.x, ...; the next
+// row's entries are loaded while the current row is sorted.
+template <int ITEMS>
+__global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* __restrict__ idx,
+                                                                 float* __restrict__ score,
+                                                                 int topk, int rows) {
+  extern __shared__ __align__(16) uint32_t sort_smem[];
+  const int t = threadIdx.x;
+  uint32_t nk[ITEMS];
+  int32_t nval[ITEMS];
+  float nsc[ITEMS];
+  auto load = [&](int row) {
+    const int32_t* ri = idx + (int64_t)row * topk;
+    const float* rs = score + (int64_t)row * topk;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = i * kSortThreads + t;
+      nval[i] = p < topk ? ri[p] : -1;
+      nsc[i] = p < topk ? rs[p] : 0.f;
+    }
+  };
+  int row = blockIdx.x;
+  if (row < rows) load(row);
+  for (; row < rows; row += gridDim.x) {
+    uint32_t key[ITEMS];
+    int32_t val[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      val[i] = nval[i];
+      key[i] = val[i] >= 0 ? ord_key(nsc[i]) : 0u;
+    }
+    if (row + (int)gridDim.x < rows) load(row + gridDim.x);
+    bucket_sort_row<ITEMS>(idx + (int64_t)row * topk, score + (int64_t)row * topk, topk,
+                           sort_smem, key, val);
+  }
+}
+
+// Workgroups for `rows` rows: as many as are resident at once (LDS-bound:
+// 160 KB per CU on gfx950, at most 8 workgroups of 4 waves), each taking
+// every grid-th row, so a resident workgroup moves straight on to its next
+// row whose loads it has already issued.
+static unsigned sort_groups(int64_t rows, size_t lds) {
+  static int cus_cache[64];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < 64) cus = cus_cache[dev];
+  if (cus <= 0) {
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                       hipSuccess || cus <= 0)
+      cus = 256;
+    if (dev >= 0 && dev < 64) cus_cache[dev] = cus;
+  }
+  int64_t per_cu = (int64_t)(163840 / lds);
+  per_cu = per_cu < 1 ? 1 : per_cu > 8 ? 8 : per_cu;
+  const int64_t resident = (int64_t)cus * per_cu;
+  return (unsigned)(rows < resident ? rows : resident);
 }
 
 hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st) {
   if (rows <= 0 || topk <= 1) return hipSuccess;
   if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)rows);
 #define DSAI_ITEMS(n)                                                                          \
   if (topk <= kSortThreads * n) {                                                              \
-    const size_t lds = sort_lds_bytes(n);                                                      \
+    const size_t lds = 4 * (size_t)SortLayout<n>::kWords;                                      \
     hipError_t e = hipFuncSetAttribute((const void*)sort_rows_kernel<n>,                       \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
     if (e != hipSuccess) return e;                                                             \
-    hipLaunchKernelGGL(sort_rows_kernel<n>, grid, dim3(kSortThreads), lds, st, idx, score,     \
-                       topk);                                                                  \
+    hipLaunchKernelGGL(sort_rows_kernel<n>, dim3(sort_groups(rows, lds)), dim3(kSortThreads),   \
+                       lds, st, idx, score,                                                    \
+                       topk, (int)rows);                                                       \
     return hipGetLastError();                                                                  \
   }
   DSAI_ITEMS(1) DSAI_ITEMS(2) DSAI_ITEMS(4) DSAI_ITEMS(8) DSAI_ITEMS(16) DSAI_ITEMS(32)

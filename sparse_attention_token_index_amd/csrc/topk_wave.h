@@ -80,9 +80,7 @@ __device__ __forceinline__ uint2 find_bin(lds_u32* hist, uint32_t rem) {
   }
   const uint64_t fm = ballot(found >= 0);
   const int src = (int)__ffsll((unsigned long long)fm) - 1;
-  const uint32_t bin = (uint32_t)__shfl(4 * lane + found, src);
-  const uint32_t ab = (uint32_t)__shfl((int)above, src);
-  return make_uint2(uniform(bin), uniform(ab));
+  return make_uint2(lane_value((uint32_t)(4 * lane + found), src), lane_value(above, src));
 }
 
 __device__ __forceinline__ void clear_hist(lds_u32* hist) {

@@ -172,6 +172,22 @@ def test_pooled_argument_errors(lib):
     lib.dsai_destroy(h)
 
 
+def test_sort_rows_argument_errors(lib):
+    st, h = _create(lib)
+    assert st == OK
+    assert lib.dsai_sort_rows(h, FAKE, FAKE, -1, 8, None) == INVALID
+    assert lib.dsai_sort_rows(h, FAKE, FAKE, 2 ** 31, 8, None) == INVALID
+    assert lib.dsai_sort_rows(h, FAKE, FAKE, 4, 0, None) == INVALID
+    assert lib.dsai_sort_rows(h, FAKE, FAKE, 4, 8193, None) == INVALID
+    assert lib.dsai_sort_rows(h, FAKE, FAKE, 0, 8, None) == OK       # nothing to do
+    assert lib.dsai_sort_rows(h, FAKE, FAKE, 4, 1, None) == OK       # one entry per row
+    assert lib.dsai_sort_rows(h, None, FAKE, 4, 8, None) == NULLPTR
+    assert lib.dsai_sort_rows(h, FAKE, None, 4, 8, None) == NULLPTR
+    assert lib.dsai_sort_rows(h, ctypes.c_void_p(0x10002), FAKE, 4, 8, None) == INVALID
+    assert lib.dsai_sort_rows(None, FAKE, FAKE, 4, 8, None) == NULLPTR
+    lib.dsai_destroy(h)
+
+
 def test_binding_refuses_cpu_tensors(lib):
     import torch
     import sparse_attention_token_index_amd as dsai
