@@ -183,6 +183,7 @@ int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, in
   dsai::TopkPoolsArgs a;
   a.scores = scores; a.Q = Q; a.P = P; a.sel = select_k(h->cfg);
   a.pool_ids = pool_ids; a.pool_scores = pool_scores;
+  a.sort = h->cfg.order == DSAI_ORDER_SCORE;
   return hip_status(h, dsai::launch_topk_pools(a, plan, static_cast<hipStream_t>(stream)));
 }
 

@@ -56,6 +56,7 @@ struct TopkPoolsArgs {
   int sel;
   int32_t* pool_ids;    // [Q, sel]
   float* pool_scores;   // [Q, sel]
+  bool sort;            // score-descending rows (else ascending pool id)
 };
 
 struct ExpandArgs {

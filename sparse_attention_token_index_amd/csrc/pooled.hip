@@ -236,6 +236,213 @@ __global__ __launch_bounds__(1024) void topk_rows_kernel(const float* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// topk_pools for rows of at most 1024 * 32 pools: one 1024-thread workgroup
+// per row holds the row in registers (thread t owns pools [t*ITEMS,
+// (t+1)*ITEMS)) and finds the select_k-th largest key with a block-wide radix
+// select: a histogram of (key - lo) >> shift over 2048 bins (LDS atomics), a
+// suffix search for the bin holding rank k, and at most three such passes
+// (11 bits each) inside the chosen bin's range.  That gives the threshold key
+// T and how many entries equal to T to keep (the lowest pool ids).  Selected
+// entries are written in pool-id order after two block scans; for the
+// score order with select_k <= kRankSortMax, each selected entry's rank under
+// (score desc, pool id asc) is counted against the others in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kBlockSelThreads = 1024;
+constexpr int kBlockSelWaves = kBlockSelThreads / kWave;
+constexpr int kBlockSelBins = 2048;
+constexpr int kRankSortMax = 512;
+
+// Block-wide inclusive prefix sum of one value per thread; `red` holds
+// kBlockSelWaves words.  Returns (inclusive, total).
+__device__ __forceinline__ uint2 block_incl_scan(uint32_t x, uint32_t* red) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(x);
+  __syncthreads();  // earlier readers of `red` are done
+  if (lane == kWave - 1) red[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0u, total = 0u;
+#pragma unroll
+  for (int w = 0; w < kBlockSelWaves; ++w) {
+    const uint32_t c = red[w];
+    base += w < wave ? c : 0u;
+    total += c;
+  }
+  return make_uint2(base + incl, total);
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
+    const float* __restrict__ scores, int P, int sel, int score_order, int32_t* __restrict__ ids,
+    float* __restrict__ out_scores) {
+  __shared__ uint32_t hist[kBlockSelBins];
+  __shared__ uint32_t red[kBlockSelWaves];
+  __shared__ uint32_t found[2];
+  __shared__ uint2 staged[kRankSortMax];
+  const int t = threadIdx.x;
+  const float* srow = scores + (int64_t)blockIdx.x * P;
+  int32_t* orow = ids + (int64_t)blockIdx.x * sel;
+  float* osc = out_scores + (int64_t)blockIdx.x * sel;
+
+  // Load; -inf (an invalid pool) and slots past P never count.
+  uint32_t u[ITEMS];
+  uint32_t nloc = 0u, kmin = 0xFFFFFFFFu, kmax = 0u;
+  const int p0 = t * ITEMS;
+  if constexpr (ITEMS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; j += 4) {
+      float4 v;
+      if (p0 + j + 3 < P && (reinterpret_cast<uintptr_t>(srow) & 15u) == 0u) {
+        v = *reinterpret_cast<const float4*>(srow + p0 + j);
+      } else {
+        v.x = p0 + j < P ? srow[p0 + j] : -__builtin_inff();
+        v.y = p0 + j + 1 < P ? srow[p0 + j + 1] : -__builtin_inff();
+        v.z = p0 + j + 2 < P ? srow[p0 + j + 2] : -__builtin_inff();
+        v.w = p0 + j + 3 < P ? srow[p0 + j + 3] : -__builtin_inff();
+      }
+      u[j] = v.x == -__builtin_inff() ? 0u : ord_key(v.x);
+      u[j + 1] = v.y == -__builtin_inff() ? 0u : ord_key(v.y);
+      u[j + 2] = v.z == -__builtin_inff() ? 0u : ord_key(v.z);
+      u[j + 3] = v.w == -__builtin_inff() ? 0u : ord_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const float v = p0 + j < P ? srow[p0 + j] : -__builtin_inff();
+      u[j] = v == -__builtin_inff() ? 0u : ord_key(v);
+    }
+  }
+  // Key 0 is below every finite score's key (ord_key(-inf) = 0x007FFFFF), so
+  // it marks "not a candidate".
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    if (u[j] != 0u) {
+      ++nloc;
+      kmin = min(kmin, u[j]);
+      kmax = max(kmax, u[j]);
+    }
+  }
+  const uint32_t wmin = wave_min(kmin), wmax = wave_max(kmax);
+  const uint2 cnt = block_incl_scan(nloc, red);
+  const uint32_t nvalid = cnt.y;
+  __syncthreads();
+  if ((t & (kWave - 1)) == 0) {
+    red[t >> 6] = wmin;
+    hist[t >> 6] = wmax;  // hist is free until the first histogram pass
+  }
+  __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kBlockSelWaves; ++w) {
+    lo = min(lo, red[w]);
+    hi = max(hi, hist[w]);
+  }
+
+  // Threshold key T and the number of entries equal to T to keep.
+  uint32_t T = 0u, need_eq = 0u;
+  const uint32_t k = (uint32_t)sel;
+  if (nvalid > k) {
+    uint32_t span = hi - lo, rem = k;
+    while (true) {
+      if (span == 0u) {
+        T = lo;
+        need_eq = rem;
+        break;
+      }
+      const int bits = 32 - __builtin_clz(span);
+      const int shift = bits > 11 ? bits - 11 : 0;
+      __syncthreads();  // readers of hist / red / found from the last round are done
+      hist[2 * t] = 0u;
+      hist[2 * t + 1] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t d = u[j] - lo;
+        if (u[j] != 0u && u[j] >= lo && d <= span) atomicAdd(&hist[d >> shift], 1u);
+      }
+      __syncthreads();
+      // suffix sums: S(b) = entries in bins >= b; find b with S(b) >= rem > S(b + 1)
+      const uint32_t h0 = hist[2 * t], h1 = hist[2 * t + 1];
+      const uint2 sc = block_incl_scan(h0 + h1, red);
+      const uint32_t after = sc.y - sc.x;  // entries in bins above 2t + 1
+      if (h1 + after >= rem && after < rem) {
+        found[0] = (uint32_t)(2 * t + 1);
+        found[1] = after;
+      } else if (h0 + h1 + after >= rem && h1 + after < rem) {
+        found[0] = (uint32_t)(2 * t);
+        found[1] = h1 + after;
+      }
+      __syncthreads();
+      const uint32_t b = found[0];
+      rem -= found[1];
+      lo += b << shift;
+      if (shift == 0) {
+        T = lo;
+        need_eq = rem;
+        break;
+      }
+      const uint32_t width = (1u << shift) - 1u;
+      span = min(span - (b << shift), width);
+    }
+  }
+
+  // Selection flags in pool-id order: above T, or equal to T among the first
+  // need_eq equal entries.
+  uint32_t eq_loc = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) eq_loc += (nvalid > k && u[j] == T && u[j] != 0u) ? 1u : 0u;
+  const uint2 eqs = block_incl_scan(eq_loc, red);
+  uint32_t eq_rank = eqs.x - eq_loc;
+  uint32_t take = 0u;  // bit j: item j selected
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    bool s = u[j] != 0u;
+    if (nvalid > k) {
+      if (u[j] == T) {
+        s = eq_rank < need_eq;
+        ++eq_rank;
+      } else {
+        s = u[j] > T;
+      }
+    }
+    take |= (s ? 1u : 0u) << j;
+  }
+  const uint32_t nsel_loc = (uint32_t)__builtin_popcount(take);
+  const uint2 ss = block_incl_scan(nsel_loc, red);
+  const uint32_t nsel = ss.y;  // min(nvalid, sel)
+  uint32_t pos = ss.x - nsel_loc;
+  const bool rank_sort = score_order && sel <= kRankSortMax;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    if ((take >> j) & 1u) {
+      if (rank_sort) {
+        staged[pos] = make_uint2(u[j], (uint32_t)(p0 + j));
+      } else {
+        orow[pos] = p0 + j;
+        osc[pos] = ord_to_float(u[j]);
+      }
+      ++pos;
+    }
+  }
+  if (rank_sort) {
+    __syncthreads();
+    if ((uint32_t)t < nsel) {
+      const uint2 me = staged[t];
+      uint32_t r = 0u;
+      for (uint32_t i = 0; i < nsel; ++i) {
+        const uint2 o = staged[i];
+        r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+      }
+      orow[r] = (int32_t)me.y;
+      osc[r] = ord_to_float(me.x);
+    }
+  }
+  for (int i = (int)nsel + t; i < sel; i += kBlockSelThreads) {
+    orow[i] = -1;
+    osc[i] = -__builtin_inff();
+  }
+}
+
 // Waves per row and store capacity for select_k = sel within `lds_limit`.
 TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit) {
   TopkRowsPlan pl{};
@@ -256,13 +463,27 @@ TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit) {
 
 hipError_t launch_topk_pools(const TopkPoolsArgs& a, const TopkRowsPlan& pl, hipStream_t st) {
   if (a.Q <= 0) return hipSuccess;
+  if (a.P <= (int64_t)kBlockSelThreads * 32) {
+    const bool ranked = a.sort && a.sel <= kRankSortMax;
+#define DSAI_ITEMS(n)                                                                          \
+    if (a.P <= (int64_t)kBlockSelThreads * n) {                                                \
+      hipLaunchKernelGGL(block_select_kernel<n>, dim3((unsigned)a.Q), dim3(kBlockSelThreads), \
+                         0, st, a.scores, (int)a.P, a.sel, (int)a.sort, a.pool_ids,            \
+                         a.pool_scores);                                                       \
+    } else
+    DSAI_ITEMS(1) DSAI_ITEMS(2) DSAI_ITEMS(4) DSAI_ITEMS(8) DSAI_ITEMS(16) DSAI_ITEMS(32) {}
+#undef DSAI_ITEMS
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.sort || ranked) return e;
+    return launch_sort_rows(a.pool_ids, a.pool_scores, a.Q, a.sel, st);
+  }
   hipError_t e = hipFuncSetAttribute((const void*)topk_rows_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)a.Q), dim3(pl.waves * kWave), pl.lds_bytes,
                      st, a.scores, (int)a.P, a.sel, pl.cap, pl.waves, a.pool_ids, a.pool_scores);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.sort) return e;
   return launch_sort_rows(a.pool_ids, a.pool_scores, a.Q, a.sel, st);
 }
 

@@ -123,28 +123,48 @@ def test_index_scores_elementwise(dsai, case):
     assert np.all(np.abs(g[~inv] - o[~inv]) <= tol(o[~inv]))
 
 
-def test_topk_pools_exact_on_fp32_scores(dsai):
+@pytest.mark.parametrize("Q,P,KP,index_topk", [
+    (70, 16384, 4, 512),      # block select, ranked in LDS
+    (9, 16384, 4, 4096),      # block select, then the row sort (select_k > 512)
+    (6, 40000, 4, 512),       # more pools than one workgroup holds: streaming select
+    (12, 1000, 1, 64),        # one pool per thread
+    (5, 5001, 2, 64),         # rows not 16-byte aligned: scalar loads
+    (4, 3, 1, 2),             # tiny rows
+])
+@pytest.mark.parametrize("order", ["score", "index"])
+def test_topk_pools_exact_on_fp32_scores(dsai, Q, P, KP, index_topk, order):
     """topk_pools selects on the fp32 values it is given: with the oracle run on
-    the same fp32 values, ids, order and scores must match exactly."""
-    log("[gpu] topk_pools exact")
-    rng = np.random.default_rng(41)
-    Q, P, KP, index_topk = 70, 16384, 4, 512
+    the same fp32 values, ids, order and scores must match exactly (index
+    order: the oracle's selection sorted by pool id)."""
+    log(f"[gpu] topk_pools exact Q={Q} P={P} KP={KP} index_topk={index_topk} order={order}")
+    rng = np.random.default_rng(41 + P)
     s = rng.standard_normal((Q, P)).astype(np.float32)
     s[rng.random((Q, P)) < 0.08] = -np.inf                   # invalid candidates
-    s[5:15] = np.round(s[5:15] * 2).astype(np.float32)        # many exact ties
-    s[20, :] = 0.0                                            # one big tie
-    s[21, :] = -np.inf                                        # no valid pool
-    s[22, :] = -np.inf
-    s[22, [7, 99, 3000]] = [1.0, 2.0, 1.0]                   # fewer valid than select_k
-    s[23] = -np.abs(s[23])                                    # all negative
-    s[24, ::2] = -0.0                                         # signed zeros tie with +0
-    s[24, 1::2] = 0.0
-    ix = dsai.Indexer(heads=32, dim=128, kpool=KP, index_topk=index_topk)
+    if Q > 4:
+        s[1:3] = np.round(s[1:3] * 2).astype(np.float32)      # many exact ties
+        s[3, :] = 0.0                                         # one big tie
+        s[4, :] = -np.inf                                     # no valid pool
+    if Q > 8:
+        s[5, :] = -np.inf
+        s[5, [0, P // 2, P - 1]] = [1.0, 2.0, 1.0]            # fewer valid than select_k
+        s[6] = -np.abs(s[6])                                  # all negative
+        s[7, ::2] = -0.0                                      # signed zeros tie with +0
+        s[7, 1::2] = 0.0
+        s[8, :] = 3.0e38                                      # the largest finite scores
+        s[8, ::3] = -3.0e38
+    ix = dsai.Indexer(heads=32, dim=128, kpool=KP, index_topk=index_topk,
+                      order=dsai.DSAI_ORDER_SCORE if order == "score" else dsai.DSAI_ORDER_INDEX)
     ids, vals = ix.topk_pools(torch.from_numpy(s).cuda())
     torch.cuda.synchronize()
+    gids, gvals = ids.cpu().numpy(), vals.cpu().numpy().astype(np.float64)
     oids, ovals = oracle.topk_pools(s.astype(np.float64), index_topk // KP)
-    assert np.array_equal(ids.cpu().numpy(), oids)
-    assert np.array_equal(vals.cpu().numpy().astype(np.float64), ovals)
+    if order == "index":
+        for r in range(Q):
+            m = int((oids[r] >= 0).sum())
+            o = np.argsort(oids[r, :m], kind="stable")
+            oids[r, :m], ovals[r, :m] = oids[r, :m][o], ovals[r, :m][o]
+    assert np.array_equal(gids, oids), np.argwhere(gids != oids)[:8]
+    assert np.array_equal(gvals, ovals)
 
 
 @pytest.mark.parametrize("case", POOL_CASES, ids=[c.name for c in POOL_CASES])
