@@ -112,7 +112,7 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   hipError_t e = device_limits(h);
   if (e != hipSuccess) return hip_status(h, e);
   const dsai::ScoreSelectPlan plan =
-      dsai::plan_score_select(h->cfg.dim, topk, Skv, h->lds_limit);
+      dsai::plan_score_select(h->cfg.heads <= 32 ? 32 : 64, h->cfg.dim, topk, Skv, h->lds_limit);
   if (plan.rows_per_block < 1) return DSAI_ERR_UNSUPPORTED;
   dsai::ScoreTopkArgs a;
   a.q = static_cast<const uint16_t*>(index_q);

@@ -21,6 +21,8 @@ struct ScoreTopkArgs {
 
 // Launch geometry of the fused score + select kernel.
 struct ScoreSelectPlan {
+  int waves;           // wavefronts per workgroup
+  int rows_per_wave;   // query rows per wavefront
   int rows_per_block;  // 0: the request does not fit in LDS
   int cap;             // store entries per row
   bool dense;          // one slot per visible key (index = slot)
@@ -73,7 +75,7 @@ struct TopkRowsPlan {
   size_t lds_bytes;
 };
 
-ScoreSelectPlan plan_score_select(int D, int topk, int64_t Skv, size_t lds_limit);
+ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t lds_limit);
 TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit);
 
 hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st);

@@ -22,34 +22,42 @@
 
 namespace dsai {
 
-// Byte stride of one staged key row in LDS: 16 bytes of padding put the 16
-// keys a half-wave's ds_read_b128 gathers on distinct bank groups.
+// Layout of staged key rows in LDS.  D = 128: rows are packed (256 bytes)
+// and the 16-byte chunk x of row r is stored at chunk x ^ (r & 15), so the
+// 16 keys a quarter-wave's ds_read_b128 gathers (same chunk of consecutive
+// rows) land on distinct bank groups without padding.  Smaller D: rows are
+// padded by 16 bytes instead.
 template <int D>
 struct TileGeom {
-  static constexpr int kRowBytes = 2 * D + 16;
-  static constexpr int kTileKeys = 32;
+  static constexpr int kChunksPerRow = D / 8;  // 16-byte chunks
+  static constexpr bool kSwizzle = D == 128;
+  static constexpr int kRowBytes = kSwizzle ? 2 * D : 2 * D + 16;
+  static constexpr int kTileKeys = 32;  // keys per matrix-core tile
   static constexpr int kTileBytes = kTileKeys * kRowBytes;
-  static constexpr int kChunksPerRow = D / 8;               // 16-byte chunks
-  static constexpr int kChunks = kTileKeys * kChunksPerRow;
+  static __device__ __forceinline__ uint32_t chunk_offset(int row, int x) {
+    return (uint32_t)(row * kRowBytes + 16 * (kSwizzle ? (x ^ (row & 15)) : x));
+  }
 };
 
-// Stages kTileKeys consecutive key rows (bf16, `row_stride` elements apart) from
-// device memory into an LDS tile, through registers so the next tile's loads
-// overlap the current tile's math.  Loads go through a buffer resource whose
+// Stages KEYS consecutive key rows (bf16, `row_stride` elements apart) from
+// device memory into LDS, through registers so the next stage's loads
+// overlap the current stage's math.  Loads go through a buffer resource whose
 // range ends at the last valid key row: rows past it read as zero without a
-// branch, and each thread's byte offsets within a tile are loop-invariant
-// (the tile's row offset is a scalar).
-template <int D, int NTHREADS>
+// branch, and each thread's byte offsets within a stage are loop-invariant
+// (the stage's row offset is a scalar).
+template <int D, int NTHREADS, int KEYS = 32>
 struct TileLoader {
   using G = TileGeom<D>;
-  static_assert(G::kChunks % NTHREADS == 0 || NTHREADS % G::kChunks == 0,
-                "tile chunks must divide over the block (or the block over the chunks)");
-  static constexpr int kPer = G::kChunks >= NTHREADS ? G::kChunks / NTHREADS : 1;
-  static constexpr bool kSpare = G::kChunks < NTHREADS;  // some threads load nothing
+  static constexpr int kChunks = KEYS * G::kChunksPerRow;
+  static_assert(kChunks % NTHREADS == 0 || NTHREADS % kChunks == 0,
+                "stage chunks must divide over the block (or the block over the chunks)");
+  static constexpr int kPer = kChunks >= NTHREADS ? kChunks / NTHREADS : 1;
+  static constexpr bool kSpare = kChunks < NTHREADS;  // some threads load nothing
   u32x4 r[kPer];
   uint32_t voff[kPer];
+  uint32_t loff[kPer];
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t row_bytes;  // bytes between consecutive key rows
+  uint32_t row_bytes;  // bytes between consecutive key rows in device memory
 
   // base: row 0 of the keys; valid_bytes: bytes from base through the end of
   // the last valid row (< 2^32).
@@ -59,10 +67,11 @@ struct TileLoader {
     row_bytes = row_stride * 2u;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int ch = kSpare ? (int)threadIdx.x % G::kChunks : (int)threadIdx.x + i * NTHREADS;
+      const int ch = kSpare ? (int)threadIdx.x % kChunks : (int)threadIdx.x + i * NTHREADS;
       const int row = ch / G::kChunksPerRow;
       const int part = ch % G::kChunksPerRow;
       voff[i] = (uint32_t)row * row_bytes + (uint32_t)part * 16u;
+      loff[i] = G::chunk_offset(row, part);
     }
   }
 
@@ -73,33 +82,40 @@ struct TileLoader {
       r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0));
   }
 
-  __device__ __forceinline__ void store(lds_char* tile) const {
-    if (kSpare && (int)threadIdx.x >= G::kChunks) return;
+  __device__ __forceinline__ void store(lds_char* stage) const {
+    if (kSpare && (int)threadIdx.x >= kChunks) return;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int ch = (int)threadIdx.x + i * NTHREADS;
-      const int row = ch / G::kChunksPerRow;
-      const int part = ch % G::kChunksPerRow;
-      *reinterpret_cast<DSAI_LDS u32x4*>(tile + row * G::kRowBytes + part * 16) = r[i];
-    }
+    for (int i = 0; i < kPer; ++i) *reinterpret_cast<DSAI_LDS u32x4*>(stage + loff[i]) = r[i];
   }
 };
 
-template <int HP, int D>
+// NR query rows per wavefront share each key fragment read from LDS: every
+// k-step feeds NR * MT independent accumulators, enough for one wavefront to
+// keep the matrix core busy on its own.
+template <int HP, int D, int NR = 1>
 struct TileScorer {
   static_assert(HP == 32 || HP == 64, "padded heads: 32 or 64");
   static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dim: 32, 48, ... 128");
   static constexpr int MT = HP / 32;
   static constexpr int KS = D / 16;
   using G = TileGeom<D>;
+  using Acc = floatx16[NR][MT];
 
-  bf16x8 qf[MT][KS];
-  float wv[MT][16];
+  bf16x8 qf[NR][MT][KS];
+  float wv[NR][MT][16];
+  uint32_t boff[KS];  // LDS offset of this lane's key fragment at each k-step
 
-  // qrow: [H, D] bf16 of this query row; wrow: [H] fp32.  Inactive rows and
-  // heads past H load zeros (zero weight, zero query: no contribution).
-  __device__ __forceinline__ void load_query(const uint16_t* __restrict__ qrow,
-                                             const float* __restrict__ wrow, int H, bool active) {
+  __device__ __forceinline__ void init_offsets() {
+    const int lane = lane_id();
+    const int c = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) boff[j] = G::chunk_offset(c, g * KS + j);  // dims g*D/2 + 8j
+  }
+
+  // Row `rr` of the wavefront: qrow [H, D] bf16, wrow [H] fp32.  Inactive rows
+  // and heads past H load zeros (zero weight, zero query: no contribution).
+  __device__ __forceinline__ void load_row(int rr, const uint16_t* __restrict__ qrow,
+                                           const float* __restrict__ wrow, int H, bool active) {
     const int lane = lane_id();
     const int c = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -108,56 +124,78 @@ struct TileScorer {
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         if (active && h < H) {
-          qf[m][j] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * D + g * (D / 2) + 8 * j);
+          qf[rr][m][j] =
+              *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * D + g * (D / 2) + 8 * j);
         } else {
-          qf[m][j] = bf16x8{};
+          qf[rr][m][j] = bf16x8{};
         }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hw = 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-        wv[m][r] = (active && hw < H) ? wrow[hw] : 0.0f;
+        wv[rr][m][r] = (active && hw < H) ? wrow[hw] : 0.0f;
       }
     }
   }
 
-  // Products of the staged tile's 32 keys with the query heads, on the matrix
-  // cores: acc[m] holds M-tile m (lane (c, g): key c, 16 heads).  Only issues
-  // the LDS reads and MFMAs; reduce() consumes the result, so a caller can
-  // overlap one tile's reduction with the next tile's products.
-  __device__ __forceinline__ void mma(const lds_char* tile, floatx16 (&acc)[MT]) const {
-    const int lane = lane_id();
-    const int c = lane & 31, g = lane >> 5;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = floatx16{};
-    const lds_char* rowp = tile + c * G::kRowBytes + g * D;
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      const bf16x8 b = *reinterpret_cast<const DSAI_LDS bf16x8*>(rowp + 16 * j);
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[m][j], b, acc[m], 0, 0, 0);
-    }
+  // One-row form (NR == 1).
+  __device__ __forceinline__ void load_query(const uint16_t* __restrict__ qrow,
+                                             const float* __restrict__ wrow, int H, bool active) {
+    init_offsets();
+    load_row(0, qrow, wrow, H, active);
   }
 
-  // ReLU, head weights and the sum over heads of mma()'s products: the full
+  using Frag = bf16x8[KS];
+
+  // This lane's key fragments of a staged tile (LDS reads only), so a caller
+  // can fetch the next tile while the current one is on the matrix cores.
+  __device__ __forceinline__ void fetch(const lds_char* tile, Frag& bf) const {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) bf[j] = *reinterpret_cast<const DSAI_LDS bf16x8*>(tile + boff[j]);
+  }
+
+  // Products of a tile's 32 keys (fragments from fetch()) with the query
+  // heads, on the matrix cores: acc[rr][m] holds row rr's M-tile m (lane
+  // (c, g): key c, 16 heads).  reduce() consumes the result, so a caller can
+  // overlap one tile's reduction with the next tile's products.
+  __device__ __forceinline__ void mma(const Frag& bf, Acc& acc) const {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[rr][m] = floatx16{};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[rr][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rr][m][j], bf[j], acc[rr][m], 0, 0, 0);
+  }
+
+  __device__ __forceinline__ void mma(const lds_char* tile, Acc& acc) const {
+    Frag bf;
+    fetch(tile, bf);
+    mma(bf, acc);
+  }
+
+  // ReLU, head weights and the sum over heads of row rr's products: the full
   // score of key lane % 32, in lanes l and l + 32 (four partial sums keep the
   // dependency chains short enough to interleave with matrix-core work).
-  __device__ __forceinline__ float reduce(const floatx16 (&acc)[MT]) const {
+  __device__ __forceinline__ float reduce(const Acc& acc, int rr) const {
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[m][r], fmaxf(acc[m][r], 0.f), p[r & 3]);
+      for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[rr][m][r], fmaxf(acc[rr][m][r], 0.f), p[r & 3]);
     const float s = (p[0] + p[1]) + (p[2] + p[3]);
     return s + __shfl_xor(s, 32);
   }
 
   // Full score of key `lane % 32` of the staged tile (in lanes l and l + 32).
   __device__ __forceinline__ float score(const lds_char* tile) const {
-    floatx16 acc[MT];
+    Acc acc;
     mma(tile, acc);
-    return reduce(acc);
+    return reduce(acc, 0);
   }
 };
 

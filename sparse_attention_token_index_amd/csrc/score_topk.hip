@@ -8,12 +8,13 @@
 // compress_ratio, topk; result [batch, seqlen, topk]); causal masking per the
 // module summary, with key s visible to query t iff s < floor((t+1)/ratio).
 //
-// One workgroup = 4 wavefronts, two workgroups per CU; each wavefront owns one
-// query row of a block of up to 4 consecutive rows of one batch, so the rows
-// of a block see nearly the same keys.  The block streams its keys through
-// LDS in 32-key tiles (loaded once per block, shared by its rows); each wavefront
-// scores the tile on the matrix cores (TileScorer) and records the scores in
-// its LDS row store:
+// One workgroup = NW wavefronts (4 or 8); each wavefront owns one query row of
+// a block of up to NW consecutive rows of one batch, so the rows of a block
+// see nearly the same keys.  The block streams its keys through two LDS
+// buffers of 32-key tiles (loaded once per block, shared by its rows; the
+// next tile is written while the current one is read, one barrier per tile).
+// Each wavefront scores the tile on the matrix cores (TileScorer) and records
+// the scores in its LDS row store:
 //   dense   when every visible key fits: the order key of key s goes to slot s
 //           (no indices, no selection until the end);
 //   filter  otherwise: keys beating the row's running threshold are appended
@@ -29,109 +30,188 @@
 
 namespace dsai {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+// LDS bytes per wavefront of the dense store's final select (histogram and
+// side list); they live in the tile buffers once the key loop is done.
+constexpr int kDenseScratch = 2048;
 
-template <int HP, int D, bool DENSE, typename IdxT>
-__global__ __launch_bounds__(kThreads) void score_select_kernel(
+template <int D, int NW>
+struct ScoreLds {
+  static constexpr int kTileBytes = TileGeom<D>::kTileBytes;
+  static constexpr int kTiles = 2 * kTileBytes;  // double buffer
+  // dense: stage buffers (reused by the final select) | rows
+  static constexpr int kDenseRegion = kTiles > NW * kDenseScratch ? kTiles : NW * kDenseScratch;
+};
+
+template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
+__global__ __launch_bounds__(NW * 64) void score_select_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   extern __shared__ __align__(16) char smem_raw[];
   lds_char* smem = (lds_char*)smem_raw;
   using G = TileGeom<D>;
-  constexpr int kScratch = DENSE ? 1024 : kSelScratchBytes;
-  // Dense rows reuse the tile region for their side lists after the loop.
-  constexpr int kTileRegion =
-      (DENSE && G::kTileBytes < kWaves * 1024) ? kWaves * 1024 : G::kTileBytes;
+  using L = ScoreLds<D, NW>;
+  using Scorer = TileScorer<HP, D, NR>;
+  using Acc = typename Scorer::Acc;
+  constexpr int kThreads = NW * 64;
 
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform
   const int lane = lane_id();
   const int row_bytes = DENSE ? cap * 4 : cap * 4 + ((cap * (int)sizeof(IdxT) + 15) & ~15);
+  const int region = DENSE ? L::kDenseRegion : L::kTiles + NW * kSelScratchBytes;
 
-  lds_char* tile = smem;
-  lds_u32* scratch = (lds_u32*)(smem + kTileRegion + wave * kScratch);
-  lds_char* mine = smem + kTileRegion + R * kScratch + wave * row_bytes;
-  // Dense rows get their side list in the tile region once the loop is done.
-  lds_u32* side = DENSE ? (lds_u32*)(smem + wave * 1024) : scratch + 256;
-  const RowStore<IdxT> rs{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4), scratch, side, 256u};
+  lds_u32* scratch = DENSE ? (lds_u32*)(smem + wave * kDenseScratch)
+                           : (lds_u32*)(smem + L::kTiles + wave * kSelScratchBytes);
 
+  // Rows of the block: t0 .. t0 + R - 1; wavefront `wave` owns rows
+  // t0 + wave * NR + rr, rr < NR, each with its own LDS row store.
   const int nrow = row_end - row_begin;
   const int nrb = (nrow + R - 1) / R;
-  const int j = blockIdx.x / B;
-  const int b = blockIdx.x - j * B;
-  const int t0 = row_begin + (nrb - 1 - j) * R;
-  const int t = t0 + wave;
-  const bool active = (wave < R) && (t < row_end);
+  const int jb = blockIdx.x / B;
+  const int b = blockIdx.x - jb * B;
+  const int t0 = row_begin + (nrb - 1 - jb) * R;
   const int t_last = min(t0 + R, row_end) - 1;
   const int n_max = min(Skv, (t_last + 1) / ratio);
-  const int n_t = active ? min(Skv, (t + 1) / ratio) : 0;
   const int ntiles = (n_max + G::kTileKeys - 1) / G::kTileKeys;
 
-  TileScorer<HP, D> sc;
-  const int64_t row = (int64_t)(active ? t : 0) * B + b;
-  sc.load_query(q + row * H * D, w + row * H, H, active);
+  Scorer sc;
+  sc.init_offsets();
+  RowStore<IdxT> rs[NR];
+  int t[NR], n_t[NR];
+  bool active[NR];
+  int n_w = 0;  // keys of the wave's longest row
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    const int slot = wave * NR + rr;
+    t[rr] = t0 + slot;
+    active[rr] = slot < R && t[rr] < row_end;
+    n_t[rr] = active[rr] ? min(Skv, (t[rr] + 1) / ratio) : 0;
+    n_w = max(n_w, n_t[rr]);
+    lds_char* mine = smem + region + slot * row_bytes;
+    rs[rr] = RowStore<IdxT>{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4), scratch,
+                            scratch + 256, 256u};
+    const int64_t row = (int64_t)(active[rr] ? t[rr] : 0) * B + b;
+    sc.load_row(rr, q + row * H * D, w + row * H, H, active[rr]);
+  }
 
-  uint32_t count = 0u, tau = 0u;
+  uint32_t count[NR], tau[NR];
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) count[rr] = tau[rr] = 0u;
   TileLoader<D, kThreads> ld;
   const int64_t kbytes = ((int64_t)Skv * B - b) * D * 2;  // < 2^32 (checked on the host)
   ld.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
-  if (ntiles > 0) ld.load(0u);
 
-  // Software pipeline: the products of tile `it` are issued before the
-  // reduction and recording of tile it - 1, so the vector ALU work of one tile
-  // overlaps the matrix-core work of the next.  The wave's tiles are a prefix
-  // [0, nt_w) of the block's; the accumulators alternate between two register
-  // sets (the loop body is unrolled twice so no copies are needed).
-  constexpr int MT = TileScorer<HP, D>::MT;
-  const int nt_w = (n_t + G::kTileKeys - 1) / G::kTileKeys;  // 0 when inactive
-  auto record = [&](int it_rec, const floatx16 (&a)[MT]) {
-    const float s = sc.reduce(a);  // lanes l and l + 32 hold key l % 32
+  // Keys stream in 32-key tiles through two LDS buffers, one barrier per
+  // tile.  Iteration `it`: write tile it + 1 (loaded from device memory during
+  // the previous iteration) into buffer (it + 1) & 1 and start the loads of
+  // tile it + 2; barrier; run tile it's products on the matrix cores; reduce
+  // and record tile it - 1 (software pipeline: its vector ALU work overlaps
+  // tile it's matrix work).  Buffer (it + 1) & 1 was last read for tile
+  // it - 1, before the previous barrier.
+  using Frag = typename Scorer::Frag;
+  auto buf = [&](int it) { return smem + (it & 1) * L::kTileBytes; };
+  auto record = [&](int it_rec, const Acc& a) {
     const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
-    const uint32_t u = ord_key(s);
-    if constexpr (DENSE) {
-      if (lane < 32) rs.key[key] = u;
-    } else {
-      wave_append(rs, count, lane < 32 && key < (uint32_t)n_t && u > tau, u, key);
-      if (count > (uint32_t)(cap - G::kTileKeys)) count = wave_keep_topk(rs, count, topk, &tau);
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      const uint32_t u = ord_key(sc.reduce(a, rr));  // lanes l and l + 32 hold key l % 32
+      if constexpr (DENSE) {
+        rs[rr].key[key] = u;  // lanes l and l + 32 store the same value
+      } else {
+        wave_append(rs[rr], count[rr], lane < 32 && key < (uint32_t)n_t[rr] && u > tau[rr], u, key);
+        if (count[rr] > (uint32_t)(cap - G::kTileKeys))
+          count[rr] = wave_keep_topk(rs[rr], count[rr], topk, &tau[rr]);
+      }
     }
   };
-  auto stage = [&](int it) {
-    __syncthreads();
-    ld.store(tile);
-    __syncthreads();
-    if (it + 1 < ntiles) ld.load((uint32_t)(it + 1) * G::kTileKeys);
-  };
-  auto step = [&](int it, floatx16 (&cur)[MT], const floatx16 (&old)[MT]) {
-    stage(it);
-    if (it < nt_w) {
-      sc.mma(tile, cur);
-      record(it - 1, old);
-    } else if (it == nt_w) {
-      record(it - 1, old);
-    }
-  };
-  floatx16 acc0[MT], acc1[MT];
-  if (ntiles > 0) {
-    stage(0);
-    if (nt_w > 0) sc.mma(tile, acc0);
-  }
-  for (int it = 1; it < ntiles; it += 2) {
-    step(it, acc1, acc0);
-    if (it + 1 < ntiles) step(it + 1, acc0, acc1);
-  }
-  if (nt_w > 0 && nt_w == ntiles) {
-    if ((ntiles - 1) & 1) record(ntiles - 1, acc1);
-    else record(ntiles - 1, acc0);
-  }
-  if constexpr (DENSE) __syncthreads();  // the tile region now holds the side lists
-  if (!active) return;
-  const int64_t orow = ((int64_t)b * S + t) * topk;
+  Acc acc0, acc1;
   if constexpr (DENSE) {
-    dense_finish(rs.key, (uint32_t)n_t, (uint32_t)topk, rs.hist, rs.side, topk, out_idx + orow,
-                 out_score + orow);
+    // Every wavefront runs all of the block's tiles, so the steady-state
+    // iteration has no branch: rows shorter than the block's longest score a
+    // few keys past their n_t, whose slots are never read; stores and loads
+    // of tiles past the last one move unused data (rows past the key range
+    // read as zero).  Tile it + 1's fragments are fetched into registers right
+    // after the barrier and consumed one iteration later, so no MFMA waits
+    // on LDS.
+    Frag f0, f1;
+    auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old) {
+      ld.store(buf(it + 1));
+      ld.load((uint32_t)(it + 2) * G::kTileKeys);
+      __syncthreads();
+      sc.fetch(buf(it + 1), fnext);
+      sc.mma(fcur, cur);
+      record(it - 1, old);
+    };
+    if (ntiles > 0) {
+      ld.load(0u);
+      ld.store(buf(0));
+      ld.load((uint32_t)G::kTileKeys);
+      __syncthreads();
+      sc.fetch(buf(0), f0);
+      ld.store(buf(1));
+      ld.load((uint32_t)(2 * G::kTileKeys));
+      __syncthreads();
+      sc.fetch(buf(1), f1);
+      sc.mma(f0, acc0);
+      int it = 1;
+      if (ntiles > 1) {
+        step(1, f1, f0, acc1, acc0);
+        for (it = 2; it + 1 < ntiles; it += 2) {
+          step(it, f0, f1, acc0, acc1);
+          step(it + 1, f1, f0, acc1, acc0);
+        }
+        if (it < ntiles) step(it, f0, f1, acc0, acc1);
+      }
+      if ((ntiles - 1) & 1) record(ntiles - 1, acc1);
+      else record(ntiles - 1, acc0);
+    }
   } else {
-    wave_finish_row(rs, count, topk, out_idx + orow, out_score + orow);
+    // The wave's tiles are a prefix [0, nt_w) of the block's.
+    const int nt_w = (n_w + G::kTileKeys - 1) / G::kTileKeys;  // 0 when inactive
+    // Here tile it's products come first and tile it + 1 is written after
+    // them, so buffer (it + 1) & 1 (read for tile it - 1 before the previous
+    // barrier) is free.
+    auto step = [&](int it, Acc& cur, const Acc& old) {
+      if (it < nt_w) {
+        sc.mma(buf(it), cur);
+        record(it - 1, old);
+      } else if (it == nt_w) {
+        record(it - 1, old);
+      }
+      if (it + 1 < ntiles) ld.store(buf(it + 1));
+      if (it + 2 < ntiles) ld.load((uint32_t)(it + 2) * G::kTileKeys);
+      __syncthreads();
+    };
+    if (ntiles > 0) {
+      ld.load(0u);
+      ld.store(buf(0));
+      if (ntiles > 1) ld.load((uint32_t)G::kTileKeys);
+      __syncthreads();
+      if (nt_w > 0) sc.mma(buf(0), acc0);
+      if (1 < ntiles) ld.store(buf(1));
+      if (2 < ntiles) ld.load((uint32_t)(2 * G::kTileKeys));
+      __syncthreads();
+    }
+    for (int it = 1; it < ntiles; it += 2) {
+      step(it, acc1, acc0);
+      if (it + 1 < ntiles) step(it + 1, acc0, acc1);
+    }
+    if (nt_w > 0 && nt_w == ntiles) {
+      if ((ntiles - 1) & 1) record(ntiles - 1, acc1);
+      else record(ntiles - 1, acc0);
+    }
+  }
+
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    if (!active[rr]) continue;
+    const int64_t orow = ((int64_t)b * S + t[rr]) * topk;
+    if constexpr (DENSE) {
+      dense_finish(rs[rr].key, (uint32_t)n_t[rr], (uint32_t)topk, rs[rr].hist, rs[rr].side, topk,
+                   out_idx + orow, out_score + orow);
+    } else {
+      wave_finish_row(rs[rr], count[rr], topk, out_idx + orow, out_score + orow);
+    }
   }
 }
 
@@ -139,15 +219,17 @@ namespace {
 
 int store_row_bytes(int cap, int idx_bytes) { return cap * 4 + ((cap * idx_bytes + 15) & ~15); }
 
-int tile_bytes_for(int D) { return 32 * (2 * D + 16); }
+int tile_bytes_for(int D) { return 32 * (D == 128 ? 2 * D : 2 * D + 16); }
 
-bool plan_dense(int D, int64_t Skv, int64_t budget, ScoreSelectPlan* p) {
-  const int64_t tile = tile_bytes_for(D);
-  const int64_t region = tile > kWaves * 1024 ? tile : kWaves * 1024;
+bool plan_dense(int D, int NW, int NR, int64_t Skv, int64_t budget, ScoreSelectPlan* p) {
+  const int64_t tiles = 2 * (int64_t)tile_bytes_for(D);
+  const int64_t region = tiles > (int64_t)NW * kDenseScratch ? tiles : (int64_t)NW * kDenseScratch;
   const int64_t cap = Skv > 0 ? ((Skv + 255) / 256) * 256 : 256;  // whole 256-key groups
-  const int64_t lds = region + kWaves * 1024 + (int64_t)kWaves * cap * 4;
+  const int64_t lds = region + (int64_t)NW * NR * cap * 4;
   if (lds > budget) return false;
-  p->rows_per_block = kWaves;
+  p->waves = NW;
+  p->rows_per_wave = NR;
+  p->rows_per_block = NW * NR;
   p->cap = (int)cap;
   p->dense = true;
   p->idx_bytes = 0;
@@ -155,21 +237,24 @@ bool plan_dense(int D, int64_t Skv, int64_t budget, ScoreSelectPlan* p) {
   return true;
 }
 
-bool plan_filter(int D, int topk, int64_t Skv, int64_t budget, int min_rows, ScoreSelectPlan* p) {
-  const int64_t tile = tile_bytes_for(D);
+bool plan_filter(int D, int NW, int NR, int topk, int64_t Skv, int64_t budget, int min_rows,
+                 ScoreSelectPlan* p) {
+  const int64_t tiles = 2 * (int64_t)tile_bytes_for(D);
   const int idx_bytes = Skv <= 65536 ? 2 : 4;
   const int need = topk + 8 * 32;
-  for (int R = kWaves; R >= min_rows; --R) {
-    const int64_t per_row = (budget - tile - (int64_t)R * kSelScratchBytes) / R;
+  for (int R = NW * NR; R >= min_rows; --R) {
+    const int64_t per_row = (budget - tiles - (int64_t)NW * kSelScratchBytes) / R;
     if (per_row <= 0) continue;
     int cap = (int)(per_row / (4 + idx_bytes)) & ~63;
     while (cap > 0 && store_row_bytes(cap, idx_bytes) > per_row) cap -= 64;
     if (cap < need) continue;
+    p->waves = NW;
+    p->rows_per_wave = NR;
     p->rows_per_block = R;
     p->cap = cap;
     p->dense = false;
     p->idx_bytes = idx_bytes;
-    p->lds_bytes = (size_t)(tile + (int64_t)R * kSelScratchBytes +
+    p->lds_bytes = (size_t)(tiles + (int64_t)NW * kSelScratchBytes +
                             (int64_t)R * store_row_bytes(cap, idx_bytes));
     return true;
   }
@@ -178,23 +263,26 @@ bool plan_filter(int D, int topk, int64_t Skv, int64_t budget, int min_rows, Sco
 
 }  // namespace
 
-// Launch geometry, in order of preference: two 4-row blocks per CU with a
-// dense store (one slot per visible key), then with a filter store (the top
-// k plus at least 8 tiles of candidates); then one block per CU, dense, then
-// filter with as many rows as fit.
-ScoreSelectPlan plan_score_select(int D, int topk, int64_t Skv, size_t lds_limit) {
+// Launch geometry, in order of preference.  Heads padded to 64: four
+// wavefronts of two rows (four accumulator chains per wavefront keep the
+// matrix core busy with one wavefront per SIMD); 32: eight wavefronts of one
+// row.  One 8-row block per CU with a dense store (one slot per visible key),
+// else a filter store (the top k plus at least 8 tiles of candidates), then
+// fewer rows per block.
+ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t lds_limit) {
   ScoreSelectPlan p{};
-  const int64_t half = (int64_t)lds_limit / 2, full = (int64_t)lds_limit;
-  if (plan_dense(D, Skv, half, &p)) return p;
-  if (plan_filter(D, topk, Skv, half, kWaves, &p)) return p;
-  if (plan_dense(D, Skv, full, &p)) return p;
-  if (plan_filter(D, topk, Skv, full, 1, &p)) return p;
+  const int64_t full = (int64_t)lds_limit;
+  const int NW = 8, NR = 1;
+  (void)HP;
+  if (plan_dense(D, NW, NR, Skv, full, &p)) return p;
+  if (plan_filter(D, NW, NR, topk, Skv, full, NW * NR, &p)) return p;
+  if (plan_filter(D, NW, NR, topk, Skv, full, 1, &p)) return p;
   return ScoreSelectPlan{};  // rows_per_block == 0: does not fit
 }
 
-template <int HP, int D, bool DENSE, typename IdxT>
+template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
 static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
-  auto kern = score_select_kernel<HP, D, DENSE, IdxT>;
+  auto kern = score_select_kernel<HP, D, NW, NR, DENSE, IdxT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)p.lds_bytes);
   if (e != hipSuccess) return e;
@@ -203,7 +291,7 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
   for (int64_t r0 = 0; r0 < a.S; r0 += chunk) {
     const int64_t r1 = (r0 + chunk < a.S) ? r0 + chunk : a.S;
     const int64_t blocks = ((r1 - r0 + R - 1) / R) * a.B;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), p.lds_bytes, st, a.q, a.k,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), p.lds_bytes, st, a.q, a.k,
                        a.w, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio, a.topk, (int)r0,
                        (int)r1, R, p.cap, a.out_idx, a.out_score);
     e = hipGetLastError();
@@ -213,11 +301,16 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
   return hipSuccess;
 }
 
+template <int HP, int D, int NW, int NR>
+static hipError_t launch_w(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
+  if (p.dense) return launch_t<HP, D, NW, NR, true, uint16_t>(a, p, st);
+  return p.idx_bytes == 2 ? launch_t<HP, D, NW, NR, false, uint16_t>(a, p, st)
+                          : launch_t<HP, D, NW, NR, false, uint32_t>(a, p, st);
+}
+
 template <int HP, int D>
 static hipError_t launch_hd(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
-  if (p.dense) return launch_t<HP, D, true, uint16_t>(a, p, st);
-  return p.idx_bytes == 2 ? launch_t<HP, D, false, uint16_t>(a, p, st)
-                          : launch_t<HP, D, false, uint32_t>(a, p, st);
+  return launch_w<HP, D, 8, 1>(a, p, st);
 }
 
 hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
