@@ -103,13 +103,24 @@ struct TileScorer {
 
   bf16x8 qf[NR][MT][KS];
   float wv[NR][MT][16];
-  uint32_t boff[KS];  // LDS offset of this lane's key fragment at each k-step
+  uint32_t boff0;  // LDS offset of this lane's key fragment at k-step 0
 
   __device__ __forceinline__ void init_offsets() {
     const int lane = lane_id();
     const int c = lane & 31, g = lane >> 5;
-#pragma unroll
-    for (int j = 0; j < KS; ++j) boff[j] = G::chunk_offset(c, g * KS + j);  // dims g*D/2 + 8j
+    boff0 = G::chunk_offset(c, g * KS);  // dims g*D/2 + 8j at k-step j
+  }
+
+  // Offset at k-step j: chunk g*KS + j of row c.  Swizzled rows: KS = 8 and
+  // g*KS + j = 8g | j, so XOR-ing j into the chunk bits of the k-step-0
+  // offset applies the row's swizzle; padded rows: consecutive chunks.
+  __device__ __forceinline__ uint32_t frag_offset(int j) const {
+    if constexpr (G::kSwizzle) {
+      static_assert(KS == 8, "swizzled rows hold 16 chunks");
+      return boff0 ^ ((uint32_t)j << 4);
+    } else {
+      return boff0 + 16u * (uint32_t)j;
+    }
   }
 
   // Row `rr` of the wavefront: qrow [H, D] bf16, wrow [H] fp32.  Inactive rows
@@ -151,7 +162,7 @@ struct TileScorer {
   // can fetch the next tile while the current one is on the matrix cores.
   __device__ __forceinline__ void fetch(const lds_char* tile, Frag& bf) const {
 #pragma unroll
-    for (int j = 0; j < KS; ++j) bf[j] = *reinterpret_cast<const DSAI_LDS bf16x8*>(tile + boff[j]);
+    for (int j = 0; j < KS; ++j) bf[j] = *reinterpret_cast<const DSAI_LDS bf16x8*>(tile + frag_offset(j));
   }
 
   // Products of a tile's 32 keys (fragments from fetch()) with the query
@@ -182,14 +193,22 @@ struct TileScorer {
   // score of key lane % 32, in lanes l and l + 32 (four partial sums keep the
   // dependency chains short enough to interleave with matrix-core work).
   __device__ __forceinline__ float reduce(const Acc& acc, int rr) const {
+    return combine(reduce_half(acc, rr));
+  }
+
+  // The part of reduce() over this lane's 16 heads per M-tile (lanes l and
+  // l + 32 hold the two halves of key l % 32's heads) ...
+  __device__ __forceinline__ float reduce_half(const Acc& acc, int rr) const {
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[rr][m][r], fmaxf(acc[rr][m][r], 0.f), p[r & 3]);
-    const float s = (p[0] + p[1]) + (p[2] + p[3]);
-    return s + __shfl_xor(s, 32);
+    return (p[0] + p[1]) + (p[2] + p[3]);
   }
+
+  // ... and the cross-half sum that completes it.
+  static __device__ __forceinline__ float combine(float half) { return half + __shfl_xor(half, 32); }
 
   // Full score of key `lane % 32` of the staged tile (in lanes l and l + 32).
   __device__ __forceinline__ float score(const lds_char* tile) const {

@@ -42,8 +42,10 @@ struct ScoreLds {
   static constexpr int kDenseRegion = kTiles > NW * kDenseScratch ? kTiles : NW * kDenseScratch;
 };
 
+// Two wavefronts per SIMD (two 4-wave blocks or one 8-wave block per CU):
+// at most 256 registers per lane.
 template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
-__global__ __launch_bounds__(NW * 64) void score_select_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_select_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
@@ -94,9 +96,14 @@ __global__ __launch_bounds__(NW * 64) void score_select_kernel(
     sc.load_row(rr, q + row * H * D, w + row * H, H, active[rr]);
   }
 
-  uint32_t count[NR], tau[NR];
+  uint32_t count[NR], tau[NR];       // filter store: entries, running threshold
+  uint32_t kmin[NR], kmax[NR];       // dense store: this lane's extreme keys
 #pragma unroll
-  for (int rr = 0; rr < NR; ++rr) count[rr] = tau[rr] = 0u;
+  for (int rr = 0; rr < NR; ++rr) {
+    count[rr] = tau[rr] = 0u;
+    kmin[rr] = 0xFFFFFFFFu;
+    kmax[rr] = 0u;
+  }
   TileLoader<D, kThreads> ld;
   const int64_t kbytes = ((int64_t)Skv * B - b) * D * 2;  // < 2^32 (checked on the host)
   ld.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
@@ -117,6 +124,9 @@ __global__ __launch_bounds__(NW * 64) void score_select_kernel(
       const uint32_t u = ord_key(sc.reduce(a, rr));  // lanes l and l + 32 hold key l % 32
       if constexpr (DENSE) {
         rs[rr].key[key] = u;  // lanes l and l + 32 store the same value
+        const bool vis = key < (uint32_t)n_t[rr];
+        kmin[rr] = min(kmin[rr], vis ? u : 0xFFFFFFFFu);
+        kmax[rr] = max(kmax[rr], vis ? u : 0u);
       } else {
         wave_append(rs[rr], count[rr], lane < 32 && key < (uint32_t)n_t[rr] && u > tau[rr], u, key);
         if (count[rr] > (uint32_t)(cap - G::kTileKeys))
@@ -130,40 +140,67 @@ __global__ __launch_bounds__(NW * 64) void score_select_kernel(
     // iteration has no branch: rows shorter than the block's longest score a
     // few keys past their n_t, whose slots are never read; stores and loads
     // of tiles past the last one move unused data (rows past the key range
-    // read as zero).  Tile it + 1's fragments are fetched into registers right
-    // after the barrier and consumed one iteration later, so no MFMA waits
-    // on LDS.
+    // read as zero).  Iteration `it`, after the barrier that publishes tile
+    // it + 1:
+    //   fetch tile it + 1's fragments into registers (consumed next
+    //   iteration, so no MFMA waits on LDS);
+    //   finish tile it - 2 (cross-half sum, order key, store to the row);
+    //   write tile it + 2 (loaded during the previous iteration) into buffer
+    //   it & 1, whose last reader, the fetch of tile it, completed before
+    //   this barrier; start the loads of tile it + 3;
+    //   tile it's products on the matrix cores, interleaved with the head
+    //   reduction of tile it - 1.
+    // Every LDS access is issued early in its iteration, so the next
+    // barrier does not wait on a recent one.
     Frag f0, f1;
-    auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old) {
-      ld.store(buf(it + 1));
-      ld.load((uint32_t)(it + 2) * G::kTileKeys);
+    float part[NR];  // reduce_half of the tile awaiting finish()
+    auto finish = [&](int it_rec) {
+      const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) {
+        const uint32_t u = ord_key(Scorer::combine(part[rr]));
+        rs[rr].key[key] = u;  // lanes l and l + 32 store the same value
+        const bool vis = key < (uint32_t)n_t[rr];
+        kmin[rr] = min(kmin[rr], vis ? u : 0xFFFFFFFFu);
+        kmax[rr] = max(kmax[rr], vis ? u : 0u);
+      }
+    };
+    auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
+                    bool red) {
       __syncthreads();
       sc.fetch(buf(it + 1), fnext);
+      if (fin) finish(it - 2);
+      ld.store(buf(it + 2));
+      ld.load((uint32_t)(it + 3) * G::kTileKeys);
       sc.mma(fcur, cur);
-      record(it - 1, old);
+      if (red) {
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
+      }
     };
     if (ntiles > 0) {
       ld.load(0u);
       ld.store(buf(0));
       ld.load((uint32_t)G::kTileKeys);
-      __syncthreads();
-      sc.fetch(buf(0), f0);
       ld.store(buf(1));
       ld.load((uint32_t)(2 * G::kTileKeys));
       __syncthreads();
-      sc.fetch(buf(1), f1);
-      sc.mma(f0, acc0);
+      sc.fetch(buf(0), f0);
+      step(0, f0, f1, acc0, acc1, false, false);
       int it = 1;
       if (ntiles > 1) {
-        step(1, f1, f0, acc1, acc0);
+        step(1, f1, f0, acc1, acc0, false, true);
         for (it = 2; it + 1 < ntiles; it += 2) {
-          step(it, f0, f1, acc0, acc1);
-          step(it + 1, f1, f0, acc1, acc0);
+          step(it, f0, f1, acc0, acc1, true, true);
+          step(it + 1, f1, f0, acc1, acc0, true, true);
         }
-        if (it < ntiles) step(it, f0, f1, acc0, acc1);
+        if (it < ntiles) step(it, f0, f1, acc0, acc1, true, true);
+        finish(ntiles - 2);
       }
-      if ((ntiles - 1) & 1) record(ntiles - 1, acc1);
-      else record(ntiles - 1, acc0);
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+        part[rr] = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, rr);
+      finish(ntiles - 1);
     }
   } else {
     // The wave's tiles are a prefix [0, nt_w) of the block's.
@@ -207,8 +244,8 @@ __global__ __launch_bounds__(NW * 64) void score_select_kernel(
     if (!active[rr]) continue;
     const int64_t orow = ((int64_t)b * S + t[rr]) * topk;
     if constexpr (DENSE) {
-      dense_finish(rs[rr].key, (uint32_t)n_t[rr], (uint32_t)topk, rs[rr].hist, rs[rr].side, topk,
-                   out_idx + orow, out_score + orow);
+      dense_finish(rs[rr].key, (uint32_t)n_t[rr], (uint32_t)topk, kmin[rr], kmax[rr], rs[rr].hist,
+                   rs[rr].side, topk, out_idx + orow, out_score + orow);
     } else {
       wave_finish_row(rs[rr], count[rr], topk, out_idx + orow, out_score + orow);
     }
@@ -272,11 +309,13 @@ bool plan_filter(int D, int NW, int NR, int topk, int64_t Skv, int64_t budget, i
 ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t lds_limit) {
   ScoreSelectPlan p{};
   const int64_t full = (int64_t)lds_limit;
-  const int NW = 8, NR = 1;
+  const int64_t half = full / 2;
   (void)HP;
-  if (plan_dense(D, NW, NR, Skv, full, &p)) return p;
-  if (plan_filter(D, NW, NR, topk, Skv, full, NW * NR, &p)) return p;
-  if (plan_filter(D, NW, NR, topk, Skv, full, 1, &p)) return p;
+  if (plan_dense(D, 4, 1, Skv, half, &p)) return p;
+  if (plan_dense(D, 8, 1, Skv, full, &p)) return p;
+  if (plan_filter(D, 4, 1, topk, Skv, half, 4, &p)) return p;
+  if (plan_filter(D, 8, 1, topk, Skv, full, 8, &p)) return p;
+  if (plan_filter(D, 8, 1, topk, Skv, full, 1, &p)) return p;
   return ScoreSelectPlan{};  // rows_per_block == 0: does not fit
 }
 
@@ -310,7 +349,7 @@ static hipError_t launch_w(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
 
 template <int HP, int D>
 static hipError_t launch_hd(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
-  return launch_w<HP, D, 8, 1>(a, p, st);
+  return p.waves == 4 ? launch_w<HP, D, 4, 1>(a, p, st) : launch_w<HP, D, 8, 1>(a, p, st);
 }
 
 hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {

@@ -93,16 +93,19 @@ __device__ __forceinline__ void hist_add(lds_u32* hist, uint32_t bin) {
   __hip_atomic_fetch_add(&hist[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
+__device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b) {
+  return a > 0xFFFFFFFFu - b ? 0xFFFFFFFFu : a + b;
+}
+
 // Radix select over a key range: finds the k-th largest of the keys in
-// `key[0, n)` that lie in [lo, lo + 2^bits) (`m` of them, k <= m), resolving
-// `bits` low bits 8 at a time with histograms of (u - lo) digits.
+// `key[0, n)` that lie in [lo, hi] (hi - lo < 2^bits; `m` of them, k <= m),
+// resolving `bits` low bits 8 at a time with histograms of (u - lo) digits.
 __device__ __forceinline__ uint2 select_in_range(const lds_u32* key, uint32_t n, lds_u32* hist,
-                                                 uint32_t lo, int bits, uint32_t rem) {
+                                                 uint32_t lo, uint32_t hi, int bits, uint32_t rem) {
   const int lane = lane_id();
   while (bits > 0) {
     const int shift = bits > 8 ? bits - 8 : 0;
     clear_hist(hist);
-    const uint32_t width = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
     for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
       uint32_t u[kSelBatch];
 #pragma unroll
@@ -113,8 +116,7 @@ __device__ __forceinline__ uint2 select_in_range(const lds_u32* key, uint32_t n,
 #pragma unroll
       for (int j = 0; j < kSelBatch; ++j) {
         const uint32_t i = base + j * kWave + lane;
-        const uint32_t d = u[j] - lo;
-        if (i < n && u[j] >= lo && d <= width) hist_add(hist, d >> shift);
+        if (i < n && u[j] >= lo && u[j] <= hi) hist_add(hist, (u[j] - lo) >> shift);
       }
     }
     wave_lds_sync();
@@ -122,6 +124,7 @@ __device__ __forceinline__ uint2 select_in_range(const lds_u32* key, uint32_t n,
     lo += fb.x << shift;
     rem -= fb.y;
     bits = shift;
+    if (shift > 0 && hi - lo > (1u << shift) - 1u) hi = lo + ((1u << shift) - 1u);
     wave_lds_sync();
   }
   return make_uint2(lo, rem);
@@ -195,9 +198,9 @@ __device__ __noinline__ uint2 wave_radix_select(lds_u32* key, lds_u32* hist, lds
       nside = uniform(nside + (uint32_t)__popcll(m));
     }
     wave_lds_sync();
-    return select_in_range(side, nside, hist, lo, shift, rem);
+    return select_in_range(side, nside, hist, lo, sat_add(lo, width), shift, rem);
   }
-  return select_in_range(key, n, hist, lo, shift, rem);
+  return select_in_range(key, n, hist, lo, sat_add(lo, width), shift, rem);
 }
 
 // Keep, in store order, the entries with key > v and the first `take_eq`
@@ -287,74 +290,96 @@ __device__ __noinline__ void wave_emit(RowStore<IdxT> rs, uint32_t n, uint32_t v
 // the row size and k stay scalar (uniform loops, no divergent bookkeeping).
 // ---------------------------------------------------------------------------
 
-// k-th largest key v among key[0, n), k <= n (.x), and how many entries equal
-// to v belong to the top k (.y).  Pass 1: min/max; pass 2: 256-bin histogram
-// of (u - min) scaled to the key range; pass 3: the chosen bin's keys go to
-// the side list (up to 256), whose remaining bits are resolved in registers-
-// sized passes.  Reads are 16 bytes per lane.
+// Float-linear histogram bin (0..255) of an order key over the candidate key
+// range [a, b]: monotone non-decreasing in the key (halving, subtraction,
+// scaling and the clamp are each monotone under round-to-nearest), so the
+// bins partition [a, b] into consecutive key intervals.  Halving keeps the
+// difference of any two finite scores finite.
+struct FloatBins {
+  float base_h, scale;
+  __device__ __forceinline__ FloatBins(uint32_t a, uint32_t b) {
+    base_h = 0.5f * ord_to_float(a);
+    const float span = 0.5f * ord_to_float(b) - base_h;
+    scale = span > 0.f ? fminf(256.f / span, 3.4e38f) : 0.f;
+  }
+  __device__ __forceinline__ uint32_t operator()(uint32_t u) const {
+    const float d = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, ord_to_float(u)), base_h), scale);
+    const uint32_t bin = (uint32_t)fminf(fmaxf(d, 0.f), 255.f);
+    return bin < 255u ? bin : 255u;
+  }
+};
+
+// The k-th largest key among the dense row's n keys (key[0, n), slots up to
+// the next multiple of 256 readable) and how many keys equal to it belong to
+// the top k.  [kmin, kmax]: the smallest and largest key.  Histograms over
+// float-linear bins of the candidate range spread a row's scores evenly, so
+// the bin holding rank k usually has a few dozen keys: they are gathered into
+// the side list and the exact key is found among them.  A bin with more than
+// 256 keys narrows the range to that bin and repeats; after three levels the
+// exact radix select over the key range finishes the search.
 __device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, uint32_t k,
-                                              lds_u32* hist, lds_u32* side) {
+                                              uint32_t kmin, uint32_t kmax, lds_u32* hist,
+                                              lds_u32* side) {
   const int lane = lane_id();
   const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
   const uint32_t ngroups = (n + 255u) >> 8;  // 256 keys per group, 4 per lane
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (uint32_t gi = 0; gi < ngroups; ++gi) {
-    const u32x4 u = k4[gi * 64u + lane];
-    const uint32_t i0 = gi * 256u + 4u * lane;
+  uint32_t a = kmin, b = kmax, rem = k;
+  for (int level = 0; level < 3; ++level) {
+    if (a == b) return make_uint2(a, rem);
+    const FloatBins bins(a, b);
+    clear_hist(hist);
+    for (uint32_t gi = 0; gi < ngroups; ++gi) {
+      const u32x4 u = k4[gi * 64u + lane];
+      const uint32_t i0 = gi * 256u + 4u * lane;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (i0 + e < n) {
-        mn = min(mn, u[e]);
-        mx = max(mx, u[e]);
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < n && u[e] >= a && u[e] <= b) hist_add(hist, bins(u[e]));
+    }
+    wave_lds_sync();
+    const uint2 fb = find_bin(hist, rem);
+    const uint32_t cnt = uniform(hist[fb.x]);
+    rem -= fb.y;
+    wave_lds_sync();
+    // keys of the chosen bin: their range, and (if few) the side list
+    const bool gather = cnt <= 256u;
+    uint32_t ns = 0u, lo = 0xFFFFFFFFu, hi = 0u;
+    for (uint32_t gi = 0; gi < ngroups; ++gi) {
+      const u32x4 u = k4[gi * 64u + lane];
+      const uint32_t i0 = gi * 256u + 4u * lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = i0 + e < n && u[e] >= a && u[e] <= b && bins(u[e]) == fb.x;
+        if (in) {
+          lo = min(lo, u[e]);
+          hi = max(hi, u[e]);
+        }
+        if (gather) {
+          const uint64_t m = ballot(in);
+          if (in) side[ns + lanes_below(m)] = u[e];
+          ns += (uint32_t)__popcll(m);
+        }
       }
     }
-  }
-  mn = uniform(wave_min(mn));
-  mx = uniform(wave_max(mx));
-  const uint32_t range = mx - mn;
-  if (range == 0u) return make_uint2(mn, k);
-  const int rbits = 32 - __clz(range);
-  const int shift = rbits > 8 ? rbits - 8 : 0;
-  clear_hist(hist);
-  for (uint32_t gi = 0; gi < ngroups; ++gi) {
-    const u32x4 u = k4[gi * 64u + lane];
-    const uint32_t i0 = gi * 256u + 4u * lane;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i0 + e < n) hist_add(hist, (u[e] - mn) >> shift);
-  }
-  wave_lds_sync();
-  const uint2 fb = find_bin(hist, k);
-  const uint32_t cnt_bin = uniform(hist[fb.x]);
-  const uint32_t lo = mn + (fb.x << shift);
-  const uint32_t rem = k - fb.y;
-  wave_lds_sync();
-  if (shift == 0) return make_uint2(lo, rem);
-  const uint32_t width = (1u << shift) - 1u;
-  if (cnt_bin > 256u) return select_in_range(key, n, hist, lo, shift, rem);
-  uint32_t ns = 0u;
-  for (uint32_t gi = 0; gi < ngroups; ++gi) {
-    const u32x4 u = k4[gi * 64u + lane];
-    const uint32_t i0 = gi * 256u + 4u * lane;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool in = (i0 + e < n) && u[e] >= lo && (u[e] - lo) <= width;
-      const uint64_t m = ballot(in);
-      if (m) {
-        if (in) side[ns + lanes_below(m)] = u[e];
-        ns = uniform(ns + (uint32_t)__popcll(m));
-      }
+    a = wave_min(lo);
+    b = wave_max(hi);
+    if (gather) {
+      wave_lds_sync();
+      if (a == b) return make_uint2(a, rem);
+      return select_in_range(side, ns, hist, a, b, 32 - __clz(b - a), rem);
     }
   }
-  wave_lds_sync();
-  return select_in_range(side, ns, hist, lo, shift, rem);
+  if (a == b) return make_uint2(a, rem);
+  return select_in_range(key, n, hist, a, b, 32 - __clz(b - a), rem);
 }
 
 // Write the dense row's top k in index order (entries > v, then the first
 // `take_eq` entries == v), then (-1, -inf) padding up to `topk` slots.  With
-// n <= k every visible key is written.
+// n <= k every visible key is written.  kmin / kmax: this lane's smallest and
+// largest key (the wave's extremes are reduced here).  Each lane handles four
+// consecutive keys per group of 256; two wave scans place the kept ones.
 __device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uint32_t k,
-                                             lds_u32* hist, lds_u32* side, int topk,
+                                             uint32_t kmin, uint32_t kmax, lds_u32* hist,
+                                             lds_u32* side, int topk,
                                              int32_t* __restrict__ out_idx,
                                              float* __restrict__ out_score) {
   const int lane = lane_id();
@@ -366,34 +391,47 @@ __device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uin
     }
   } else {
     wave_lds_sync();
-    const uint2 sel = dense_select(key, n, k, hist, side);
+    const uint2 sel = dense_select(key, n, k, wave_min(kmin), wave_max(kmax), hist, side);
     const uint32_t v = sel.x, take_eq = sel.y;
+    const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
+    const uint32_t ngroups = (n + 255u) >> 8;
     wpos = 0u;
     uint32_t eq_seen = 0u;
-    for (uint32_t base = 0; base < n; base += kWave * 4) {
-      uint32_t u[4];
+    for (uint32_t gi = 0; gi < ngroups; ++gi) {
+      const u32x4 u = k4[gi * 64u + lane];
+      const uint32_t i0 = gi * 256u + 4u * lane;
+      uint32_t keep = 0u, eqm = 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t i = base + j * kWave + lane;
-        u[j] = i < n ? key[i] : 0u;
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = i0 + e < n;
+        keep |= (valid && u[e] > v) ? (1u << e) : 0u;
+        eqm |= (valid && u[e] == v) ? (1u << e) : 0u;
       }
+      if (ballot(eqm != 0u)) {  // equal keys: the first take_eq of them (index order) are kept
+        const uint32_t ne = (uint32_t)__builtin_popcount(eqm);
+        const uint32_t incl = wave_incl_scan(ne);
+        uint32_t r = eq_seen + incl - ne;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t i = base + j * kWave + lane;
-        bool keep = u[j] > v;  // u = 0 past n: never kept (real keys are never 0)
-        const uint64_t meq = ballot(i < n && u[j] == v);
-        if (meq) {
-          if (i < n && u[j] == v) keep = (eq_seen + lanes_below(meq)) < take_eq;
-          eq_seen = uniform(eq_seen + (uint32_t)__popcll(meq));
+        for (int e = 0; e < 4; ++e) {
+          if ((eqm >> e) & 1u) {
+            keep |= r < take_eq ? (1u << e) : 0u;
+            ++r;
+          }
         }
-        const uint64_t mk = ballot(keep);
-        if (keep) {
-          const uint32_t p = wpos + lanes_below(mk);
-          out_idx[p] = (int32_t)i;
-          out_score[p] = ord_to_float(u[j]);
-        }
-        wpos = uniform(wpos + (uint32_t)__popcll(mk));
+        eq_seen += lane_value(incl, kWave - 1);
       }
+      const uint32_t nk = (uint32_t)__builtin_popcount(keep);
+      const uint32_t kincl = wave_incl_scan(nk);
+      uint32_t p = wpos + kincl - nk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((keep >> e) & 1u) {
+          out_idx[p] = (int32_t)(i0 + e);
+          out_score[p] = ord_to_float(u[e]);
+          ++p;
+        }
+      }
+      wpos += lane_value(kincl, kWave - 1);
     }
   }
   for (uint32_t p = wpos + lane; p < (uint32_t)topk; p += kWave) {
