@@ -114,6 +114,18 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return wave_reduce(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
+__device__ __forceinline__ float wave_fmin(float x) {
+  return __uint_as_float(wave_reduce(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+
+__device__ __forceinline__ float wave_fmax(float x) {
+  return __uint_as_float(wave_reduce(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);

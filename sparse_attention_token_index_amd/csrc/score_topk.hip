@@ -97,12 +97,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   uint32_t count[NR], tau[NR];       // filter store: entries, running threshold
-  uint32_t kmin[NR], kmax[NR];       // dense store: this lane's extreme keys
+  float smin[NR], smax[NR];           // dense store: this lane's extreme scores
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
     count[rr] = tau[rr] = 0u;
-    kmin[rr] = 0xFFFFFFFFu;
-    kmax[rr] = 0u;
+    smin[rr] = __builtin_inff();
+    smax[rr] = -__builtin_inff();
   }
   TileLoader<D, kThreads> ld;
   const int64_t kbytes = ((int64_t)Skv * B - b) * D * 2;  // < 2^32 (checked on the host)
@@ -121,12 +121,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
-      const uint32_t u = ord_key(sc.reduce(a, rr));  // lanes l and l + 32 hold key l % 32
+      const float x = sc.reduce(a, rr) + 0.f;  // lanes l and l + 32 hold key l % 32 (-0 -> +0)
+      const uint32_t u = ord_key(x);
       if constexpr (DENSE) {
-        rs[rr].key[key] = u;  // lanes l and l + 32 store the same value
+        rs[rr].key[key] = __float_as_uint(x);  // lanes l and l + 32 store the same value
         const bool vis = key < (uint32_t)n_t[rr];
-        kmin[rr] = min(kmin[rr], vis ? u : 0xFFFFFFFFu);
-        kmax[rr] = max(kmax[rr], vis ? u : 0u);
+        smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
+        smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
       } else {
         wave_append(rs[rr], count[rr], lane < 32 && key < (uint32_t)n_t[rr] && u > tau[rr], u, key);
         if (count[rr] > (uint32_t)(cap - G::kTileKeys))
@@ -158,11 +159,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
 #pragma unroll
       for (int rr = 0; rr < NR; ++rr) {
-        const uint32_t u = ord_key(Scorer::combine(part[rr]));
-        rs[rr].key[key] = u;  // lanes l and l + 32 store the same value
+        const float x = Scorer::combine(part[rr]) + 0.f;  // -0 -> +0
+        rs[rr].key[key] = __float_as_uint(x);  // lanes l and l + 32 store the same value
         const bool vis = key < (uint32_t)n_t[rr];
-        kmin[rr] = min(kmin[rr], vis ? u : 0xFFFFFFFFu);
-        kmax[rr] = max(kmax[rr], vis ? u : 0u);
+        smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
+        smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
       }
     };
     auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (!active[rr]) continue;
     const int64_t orow = ((int64_t)b * S + t[rr]) * topk;
     if constexpr (DENSE) {
-      dense_finish(rs[rr].key, (uint32_t)n_t[rr], (uint32_t)topk, kmin[rr], kmax[rr], rs[rr].hist,
+      dense_finish(rs[rr].key, (uint32_t)n_t[rr], (uint32_t)topk, smin[rr], smax[rr], rs[rr].hist,
                    rs[rr].side, topk, out_idx + orow, out_score + orow);
     } else {
       wave_finish_row(rs[rr], count[rr], topk, out_idx + orow, out_score + orow);

@@ -100,6 +100,8 @@ __device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b) {
 // Radix select over a key range: finds the k-th largest of the keys in
 // `key[0, n)` that lie in [lo, hi] (hi - lo < 2^bits; `m` of them, k <= m),
 // resolving `bits` low bits 8 at a time with histograms of (u - lo) digits.
+// FLOAT_KEYS: key[] holds fp32 scores (bits), mapped to order keys on load.
+template <bool FLOAT_KEYS = false>
 __device__ __forceinline__ uint2 select_in_range(const lds_u32* key, uint32_t n, lds_u32* hist,
                                                  uint32_t lo, uint32_t hi, int bits, uint32_t rem) {
   const int lane = lane_id();
@@ -112,6 +114,7 @@ __device__ __forceinline__ uint2 select_in_range(const lds_u32* key, uint32_t n,
       for (int j = 0; j < kSelBatch; ++j) {
         const uint32_t i = base + j * kWave + lane;
         u[j] = i < n ? key[i] : 0u;
+        if constexpr (FLOAT_KEYS) u[j] = ord_key(__uint_as_float(u[j]));
       }
 #pragma unroll
       for (int j = 0; j < kSelBatch; ++j) {
@@ -290,95 +293,135 @@ __device__ __noinline__ void wave_emit(RowStore<IdxT> rs, uint32_t n, uint32_t v
 // the row size and k stay scalar (uniform loops, no divergent bookkeeping).
 // ---------------------------------------------------------------------------
 
-// Float-linear histogram bin (0..255) of an order key over the candidate key
-// range [a, b]: monotone non-decreasing in the key (halving, subtraction,
+// Float-linear histogram bin (0..255) of a score in the candidate range
+// [a, b]: monotone non-decreasing in the score (halving, subtraction,
 // scaling and the clamp are each monotone under round-to-nearest), so the
-// bins partition [a, b] into consecutive key intervals.  Halving keeps the
+// bins partition [a, b] into consecutive intervals.  Halving keeps the
 // difference of any two finite scores finite.
 struct FloatBins {
   float base_h, scale;
-  __device__ __forceinline__ FloatBins(uint32_t a, uint32_t b) {
-    base_h = 0.5f * ord_to_float(a);
-    const float span = 0.5f * ord_to_float(b) - base_h;
+  __device__ __forceinline__ FloatBins(float a, float b) {
+    base_h = 0.5f * a;
+    const float span = 0.5f * b - base_h;
     scale = span > 0.f ? fminf(256.f / span, 3.4e38f) : 0.f;
   }
-  __device__ __forceinline__ uint32_t operator()(uint32_t u) const {
-    const float d = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, ord_to_float(u)), base_h), scale);
-    const uint32_t bin = (uint32_t)fminf(fmaxf(d, 0.f), 255.f);
-    return bin < 255u ? bin : 255u;
+  __device__ __forceinline__ uint32_t operator()(float x) const {
+    const float d = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, x), base_h), scale);
+    return (uint32_t)fminf(fmaxf(d, 0.f), 255.f);
   }
 };
 
-// The k-th largest key among the dense row's n keys (key[0, n), slots up to
-// the next multiple of 256 readable) and how many keys equal to it belong to
-// the top k.  [kmin, kmax]: the smallest and largest key.  Histograms over
-// float-linear bins of the candidate range spread a row's scores evenly, so
-// the bin holding rank k usually has a few dozen keys: they are gathered into
-// the side list and the exact key is found among them.  A bin with more than
+// Dense row store: slot s holds the fp32 score of key s (-0 stored as +0,
+// so equal scores have equal bits).  Slots up to the next multiple of 256 are
+// readable.
+
+// Appends the lanes' flagged values (up to four per lane, bit e of `m`:
+// element e) to side[ns...] in (lane, element) order; returns the new count.
+__device__ __forceinline__ uint32_t wave_append4(lds_u32* side, uint32_t ns, uint32_t m,
+                                                 const uint32_t (&val)[4]) {
+  const uint32_t c = (uint32_t)__builtin_popcount(m);
+  const uint32_t incl = wave_incl_scan(c);
+  uint32_t p = ns + incl - c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if ((m >> e) & 1u) side[p++] = val[e];
+  }
+  return ns + lane_value(incl, kWave - 1);
+}
+
+// The k-th largest score among the dense row's n scores (as fp32 bits, .x)
+// and how many scores equal to it belong to the top k (.y).  [smin, smax]:
+// the row's smallest and largest score.  Histograms over float-linear bins
+// of the candidate range spread a row's scores evenly, so the bin holding
+// rank k usually has a few dozen keys: their order keys are gathered into
+// the side list and the exact one is found among them.  A bin with more than
 // 256 keys narrows the range to that bin and repeats; after three levels the
-// exact radix select over the key range finishes the search.
+// exact radix select over the whole row finishes the search.
 __device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, uint32_t k,
-                                              uint32_t kmin, uint32_t kmax, lds_u32* hist,
+                                              float smin, float smax, lds_u32* hist,
                                               lds_u32* side) {
   const int lane = lane_id();
   const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
   const uint32_t ngroups = (n + 255u) >> 8;  // 256 keys per group, 4 per lane
-  uint32_t a = kmin, b = kmax, rem = k;
+  float a = smin, b = smax;
+  uint32_t rem = k;
   for (int level = 0; level < 3; ++level) {
-    if (a == b) return make_uint2(a, rem);
+    if (!(a < b)) return make_uint2(__float_as_uint(a), rem);
     const FloatBins bins(a, b);
     clear_hist(hist);
     for (uint32_t gi = 0; gi < ngroups; ++gi) {
       const u32x4 u = k4[gi * 64u + lane];
       const uint32_t i0 = gi * 256u + 4u * lane;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (i0 + e < n && u[e] >= a && u[e] <= b) hist_add(hist, bins(u[e]));
+      for (int e = 0; e < 4; ++e) {
+        const float x = __uint_as_float(u[e]);
+        if (i0 + e < n && (level == 0 || (x >= a && x <= b))) hist_add(hist, bins(x));
+      }
     }
     wave_lds_sync();
     const uint2 fb = find_bin(hist, rem);
     const uint32_t cnt = uniform(hist[fb.x]);
     rem -= fb.y;
     wave_lds_sync();
-    // keys of the chosen bin: their range, and (if few) the side list
-    const bool gather = cnt <= 256u;
-    uint32_t ns = 0u, lo = 0xFFFFFFFFu, hi = 0u;
+    if (cnt <= 256u) {
+      // gather the bin's keys (as order keys) into the side list
+      uint32_t ns = 0u;
+      for (uint32_t gi = 0; gi < ngroups; ++gi) {
+        const u32x4 u = k4[gi * 64u + lane];
+        const uint32_t i0 = gi * 256u + 4u * lane;
+        uint32_t m = 0u, ok[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = __uint_as_float(u[e]);
+          const bool in = i0 + e < n && x >= a && x <= b && bins(x) == fb.x;
+          m |= in ? (1u << e) : 0u;
+          ok[e] = ord_key(x);
+        }
+        ns = wave_append4(side, ns, m, ok);
+      }
+      wave_lds_sync();
+      uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+      for (uint32_t i = lane; i < ns; i += kWave) {
+        lo = min(lo, side[i]);
+        hi = max(hi, side[i]);
+      }
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      uint2 r = make_uint2(lo, rem);
+      if (lo != hi) r = select_in_range(side, ns, hist, lo, hi, 32 - __clz(hi - lo), rem);
+      return make_uint2(__float_as_uint(ord_to_float(r.x)), r.y);
+    }
+    // narrow to the bin's score range
+    float lo = 3.4e38f, hi = -3.4e38f;
     for (uint32_t gi = 0; gi < ngroups; ++gi) {
       const u32x4 u = k4[gi * 64u + lane];
       const uint32_t i0 = gi * 256u + 4u * lane;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool in = i0 + e < n && u[e] >= a && u[e] <= b && bins(u[e]) == fb.x;
-        if (in) {
-          lo = min(lo, u[e]);
-          hi = max(hi, u[e]);
-        }
-        if (gather) {
-          const uint64_t m = ballot(in);
-          if (in) side[ns + lanes_below(m)] = u[e];
-          ns += (uint32_t)__popcll(m);
+        const float x = __uint_as_float(u[e]);
+        if (i0 + e < n && x >= a && x <= b && bins(x) == fb.x) {
+          lo = fminf(lo, x);
+          hi = fmaxf(hi, x);
         }
       }
     }
-    a = wave_min(lo);
-    b = wave_max(hi);
-    if (gather) {
-      wave_lds_sync();
-      if (a == b) return make_uint2(a, rem);
-      return select_in_range(side, ns, hist, a, b, 32 - __clz(b - a), rem);
-    }
+    a = wave_fmin(lo);
+    b = wave_fmax(hi);
   }
-  if (a == b) return make_uint2(a, rem);
-  return select_in_range(key, n, hist, a, b, 32 - __clz(b - a), rem);
+  if (!(a < b)) return make_uint2(__float_as_uint(a), rem);
+  const uint32_t oa = ord_key(a), ob = ord_key(b);
+  const uint2 r = select_in_range<true>(key, n, hist, oa, ob, 32 - __clz(ob - oa), rem);
+  return make_uint2(__float_as_uint(ord_to_float(r.x)), r.y);
 }
 
-// Write the dense row's top k in index order (entries > v, then the first
-// `take_eq` entries == v), then (-1, -inf) padding up to `topk` slots.  With
-// n <= k every visible key is written.  kmin / kmax: this lane's smallest and
-// largest key (the wave's extremes are reduced here).  Each lane handles four
-// consecutive keys per group of 256; two wave scans place the kept ones.
+// Write the dense row's top k in index order (scores > v, then the first
+// `take_eq` scores == v), then (-1, -inf) padding up to `topk` slots.  With
+// n <= k every visible key is written.  smin / smax: this lane's smallest
+// and largest score (the wave's extremes are reduced here).  Each lane
+// handles four consecutive keys per group of 256; two wave scans place the
+// kept ones.
 __device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uint32_t k,
-                                             uint32_t kmin, uint32_t kmax, lds_u32* hist,
+                                             float smin, float smax, lds_u32* hist,
                                              lds_u32* side, int topk,
                                              int32_t* __restrict__ out_idx,
                                              float* __restrict__ out_score) {
@@ -387,12 +430,13 @@ __device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uin
   if (n <= k) {
     for (uint32_t i = lane; i < n; i += kWave) {
       out_idx[i] = (int32_t)i;
-      out_score[i] = ord_to_float(key[i]);
+      out_score[i] = __uint_as_float(key[i]);
     }
   } else {
     wave_lds_sync();
-    const uint2 sel = dense_select(key, n, k, wave_min(kmin), wave_max(kmax), hist, side);
-    const uint32_t v = sel.x, take_eq = sel.y;
+    const uint2 sel = dense_select(key, n, k, wave_fmin(smin), wave_fmax(smax), hist, side);
+    const float v = __uint_as_float(sel.x);
+    const uint32_t take_eq = sel.y;
     const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
     const uint32_t ngroups = (n + 255u) >> 8;
     wpos = 0u;
@@ -404,8 +448,9 @@ __device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uin
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool valid = i0 + e < n;
-        keep |= (valid && u[e] > v) ? (1u << e) : 0u;
-        eqm |= (valid && u[e] == v) ? (1u << e) : 0u;
+        const float x = __uint_as_float(u[e]);
+        keep |= (valid && x > v) ? (1u << e) : 0u;
+        eqm |= (valid && x == v) ? (1u << e) : 0u;
       }
       if (ballot(eqm != 0u)) {  // equal keys: the first take_eq of them (index order) are kept
         const uint32_t ne = (uint32_t)__builtin_popcount(eqm);
@@ -427,7 +472,7 @@ __device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uin
       for (int e = 0; e < 4; ++e) {
         if ((keep >> e) & 1u) {
           out_idx[p] = (int32_t)(i0 + e);
-          out_score[p] = ord_to_float(u[e]);
+          out_score[p] = __uint_as_float(u[e]);
           ++p;
         }
       }
