@@ -279,6 +279,8 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
   __shared__ uint32_t red[kBlockSelWaves];
   __shared__ uint32_t found[2];
   __shared__ uint2 staged[kRankSortMax];
+  __shared__ uint32_t cand[kBlockSelThreads];
+  __shared__ uint32_t ncand;
   const int t = threadIdx.x;
   const float* srow = scores + (int64_t)blockIdx.x * P;
   int32_t* orow = ids + (int64_t)blockIdx.x * sel;
@@ -322,27 +324,115 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
       kmax = max(kmax, u[j]);
     }
   }
+  // Per-wave count / min / max, combined after one barrier.
+  const uint32_t wcnt = wave_reduce(nloc, [](uint32_t x, uint32_t y) { return x + y; });
   const uint32_t wmin = wave_min(kmin), wmax = wave_max(kmax);
-  const uint2 cnt = block_incl_scan(nloc, red);
-  const uint32_t nvalid = cnt.y;
-  __syncthreads();
   if ((t & (kWave - 1)) == 0) {
     red[t >> 6] = wmin;
-    hist[t >> 6] = wmax;  // hist is free until the first histogram pass
+    hist[t >> 6] = wmax;                    // hist is free until the first histogram pass
+    hist[kBlockSelWaves + (t >> 6)] = wcnt;
   }
   __syncthreads();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, nvalid = 0u;
 #pragma unroll
   for (int w = 0; w < kBlockSelWaves; ++w) {
     lo = min(lo, red[w]);
     hi = max(hi, hist[w]);
+    nvalid += hist[kBlockSelWaves + w];
   }
 
   // Threshold key T and the number of entries equal to T to keep.
   uint32_t T = 0u, need_eq = 0u;
   const uint32_t k = (uint32_t)sel;
-  if (nvalid > k) {
-    uint32_t span = hi - lo, rem = k;
+  bool resolved = false;
+  uint32_t span = hi - lo, rem = k;
+  if (nvalid > k && span != 0u) {
+    // First round on float-linear bins of [min, max] (monotone in the score),
+    // which spread a row's scores evenly: the bin holding rank k usually has
+    // a few keys, and the threshold is found among them by direct counting.
+    const float base_h = 0.5f * ord_to_float(lo);
+    const float fspan = 0.5f * ord_to_float(hi) - base_h;
+    const float scale = fspan > 0.f ? fminf((float)kBlockSelBins / fspan, 3.4e38f) : 0.f;
+    auto fbin = [&](uint32_t key) {
+      const float d = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, ord_to_float(key)), base_h), scale);
+      return (uint32_t)fminf(fmaxf(d, 0.f), (float)(kBlockSelBins - 1));
+    };
+    __syncthreads();
+    hist[2 * t] = 0u;
+    hist[2 * t + 1] = 0u;
+    if (t == 0) ncand = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (u[j] != 0u) atomicAdd(&hist[fbin(u[j])], 1u);
+    __syncthreads();
+    {
+      const uint32_t h0 = hist[2 * t], h1 = hist[2 * t + 1];
+      const uint2 sc = block_incl_scan(h0 + h1, red);
+      const uint32_t after = sc.y - sc.x;
+      if (h1 + after >= rem && after < rem) {
+        found[0] = (uint32_t)(2 * t + 1);
+        found[1] = after;
+      } else if (h0 + h1 + after >= rem && h1 + after < rem) {
+        found[0] = (uint32_t)(2 * t);
+        found[1] = h1 + after;
+      }
+    }
+    __syncthreads();
+    const uint32_t fb = found[0];
+    const uint32_t ncb = hist[fb];
+    rem -= found[1];
+    if (ncb <= (uint32_t)kBlockSelThreads) {
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j)
+        if (u[j] != 0u && fbin(u[j]) == fb) cand[atomicAdd(&ncand, 1u)] = u[j];
+      __syncthreads();
+      if ((uint32_t)t < ncb) {
+        const uint32_t me = cand[t];
+        uint32_t gt = 0u, eq = 0u;
+        for (uint32_t i = 0; i < ncb; ++i) {
+          const uint32_t o = cand[i];
+          gt += o > me ? 1u : 0u;
+          eq += o == me ? 1u : 0u;
+        }
+        if (gt < rem && rem <= gt + eq) {  // every thread holding the threshold key agrees
+          found[0] = me;
+          found[1] = rem - gt;
+        }
+      }
+      __syncthreads();
+      T = found[0];
+      need_eq = found[1];
+      resolved = true;
+    } else {
+      // many keys in one bin: continue with the radix rounds on its key range
+      uint32_t bl = 0xFFFFFFFFu, bh = 0u;
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        if (u[j] != 0u && fbin(u[j]) == fb) {
+          bl = min(bl, u[j]);
+          bh = max(bh, u[j]);
+        }
+      }
+      bl = wave_min(bl);
+      bh = wave_max(bh);
+      __syncthreads();
+      if ((t & (kWave - 1)) == 0) {
+        red[t >> 6] = bl;
+        hist[t >> 6] = bh;
+      }
+      __syncthreads();
+      lo = 0xFFFFFFFFu;
+      hi = 0u;
+#pragma unroll
+      for (int w = 0; w < kBlockSelWaves; ++w) {
+        lo = min(lo, red[w]);
+        hi = max(hi, hist[w]);
+      }
+      span = hi - lo;
+    }
+  }
+  if (nvalid > k && !resolved) {
     while (true) {
       if (span == 0u) {
         T = lo;
@@ -386,53 +476,58 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     }
   }
 
-  // Selection flags in pool-id order: above T, or equal to T among the first
-  // need_eq equal entries.
-  uint32_t eq_loc = 0u;
-#pragma unroll
-  for (int j = 0; j < ITEMS; ++j) eq_loc += (nvalid > k && u[j] == T && u[j] != 0u) ? 1u : 0u;
-  const uint2 eqs = block_incl_scan(eq_loc, red);
-  uint32_t eq_rank = eqs.x - eq_loc;
-  uint32_t take = 0u;  // bit j: item j selected
+  // Selection in pool-id order: keys above T, and the first need_eq keys
+  // equal to T.  One block scan of (equal count << 16 | above count) places
+  // every selected key: its slot = keys above T before it + min(keys equal
+  // to T before it, need_eq).  (Counts fit 16 bits: at most 32768 pools.)
+  const bool cut = nvalid > k;
+  uint32_t ab_loc = 0u, eq_loc = 0u;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    bool s = u[j] != 0u;
-    if (nvalid > k) {
-      if (u[j] == T) {
-        s = eq_rank < need_eq;
-        ++eq_rank;
-      } else {
-        s = u[j] > T;
-      }
-    }
-    take |= (s ? 1u : 0u) << j;
+    ab_loc += (u[j] != 0u && (!cut || u[j] > T)) ? 1u : 0u;
+    eq_loc += (cut && u[j] == T) ? 1u : 0u;
   }
-  const uint32_t nsel_loc = (uint32_t)__builtin_popcount(take);
-  const uint2 ss = block_incl_scan(nsel_loc, red);
-  const uint32_t nsel = ss.y;  // min(nvalid, sel)
-  uint32_t pos = ss.x - nsel_loc;
+  const uint2 ss = block_incl_scan((eq_loc << 16) | ab_loc, red);
+  const uint32_t ab_before = (ss.x - ((eq_loc << 16) | ab_loc)) & 0xFFFFu;
+  uint32_t eq_before = (ss.x - ((eq_loc << 16) | ab_loc)) >> 16;
+  const uint32_t nsel = (ss.y & 0xFFFFu) + min(ss.y >> 16, need_eq);  // min(nvalid, sel)
+  uint32_t nab = 0u;
   const bool rank_sort = score_order && sel <= kRankSortMax;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    if ((take >> j) & 1u) {
+    const bool above = u[j] != 0u && (!cut || u[j] > T);
+    const bool eq = cut && u[j] == T;
+    const bool s = above || (eq && eq_before < need_eq);
+    if (s) {
+      const uint32_t pos = ab_before + nab + min(eq_before, need_eq);
       if (rank_sort) {
         staged[pos] = make_uint2(u[j], (uint32_t)(p0 + j));
       } else {
         orow[pos] = p0 + j;
         osc[pos] = ord_to_float(u[j]);
       }
-      ++pos;
     }
+    nab += above ? 1u : 0u;
+    eq_before += eq ? 1u : 0u;
   }
   if (rank_sort) {
+    // rank of each staged entry: `tpe` consecutive threads split the
+    // comparisons against the others, then sum their counts
     __syncthreads();
-    if ((uint32_t)t < nsel) {
-      const uint2 me = staged[t];
-      uint32_t r = 0u;
-      for (uint32_t i = 0; i < nsel; ++i) {
+    int tpe = kBlockSelThreads / kRankSortMax;
+    while (tpe * 2 * (int)nsel <= kBlockSelThreads && tpe < kWave) tpe *= 2;
+    const uint32_t e = (uint32_t)(t / tpe), part = (uint32_t)(t % tpe);
+    uint32_t r = 0u;
+    uint2 me = make_uint2(0u, 0u);
+    if (e < nsel) {
+      me = staged[e];
+      for (uint32_t i = part; i < nsel; i += (uint32_t)tpe) {
         const uint2 o = staged[i];
         r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
       }
+    }
+    for (int off = 1; off < tpe; off <<= 1) r += (uint32_t)__shfl_xor((int)r, off);
+    if (e < nsel && part == 0u) {
       orow[r] = (int32_t)me.y;
       osc[r] = ord_to_float(me.x);
     }
