@@ -101,55 +101,95 @@ hipError_t launch_kpool(const KpoolArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // index_scores: [Q, P] scores of decode queries against pool keys, -inf for
 // invalid candidates (glm5next_dsa: "[Q, P] scores + candidate validity").
-// Grid (pool blocks, row blocks of 4); each block stages its pool keys in
-// 32-key LDS tiles shared by its 4 query rows (one per wavefront).
+// One workgroup = 8 wavefronts = 8 query rows against a range of
+// kPoolTilesPerBlock 32-pool tiles, so each staged tile serves 8 rows and
+// each row's query stays in registers across the range.  The key loop is the
+// fused indexer's: double-buffered LDS tiles, the next tile's fragments
+// fetched right after the barrier, the head reduction of tile it - 1
+// interleaved with tile it's products, and tile it - 2's scores stored.
 // ---------------------------------------------------------------------------
-constexpr int kPoolTilesPerBlock = 8;
+constexpr int kPoolTilesPerBlock = 16;
+constexpr int kPoolRows = 8;
 
 template <int HP, int D>
-__global__ __launch_bounds__(256) void pooled_scores_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ w,
-    const uint16_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_valid, int Q, int P,
-    int H, int pool_blocks, float* __restrict__ scores) {
+__global__ __launch_bounds__(kPoolRows * 64) __attribute__((amdgpu_waves_per_eu(2))) void
+pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                     const uint16_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_valid,
+                     int Q, int P, int H, int pool_blocks, float* __restrict__ scores) {
   using G = TileGeom<D>;
-  __shared__ __align__(16) char tile_raw[G::kTileBytes];
-  lds_char* tile = (lds_char*)tile_raw;
-  const int wave = threadIdx.x >> 6;
+  using Scorer = TileScorer<HP, D>;
+  using Acc = typename Scorer::Acc;
+  using Frag = typename Scorer::Frag;
+  constexpr int kPer = kPoolTilesPerBlock * G::kTileKeys;
+  __shared__ __align__(16) char tiles_raw[2 * G::kTileBytes];
+  __shared__ uint8_t valid_s[kPer];
+  lds_char* tiles = (lds_char*)tiles_raw;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = lane_id();
-  const int pb = blockIdx.x % pool_blocks;
-  const int row = (blockIdx.x / pool_blocks) * 4 + wave;
+  const int pb = blockIdx.x % pool_blocks;  // consecutive blocks share a pool range
+  const int row = (blockIdx.x / pool_blocks) * kPoolRows + wave;
   const bool active = row < Q;
-  TileScorer<HP, D> sc;
+  const int p0 = pb * kPer;
+  const int np = min(kPer, P - p0);
+  const int ntiles = (np + G::kTileKeys - 1) / G::kTileKeys;
+
+  Scorer sc;
   sc.load_query(q + (int64_t)(active ? row : 0) * H * D, w + (int64_t)(active ? row : 0) * H, H,
                 active);
-  const int p0 = pb * kPoolTilesPerBlock * G::kTileKeys;
-  int ntiles = (P - p0 + G::kTileKeys - 1) / G::kTileKeys;
-  if (ntiles > kPoolTilesPerBlock) ntiles = kPoolTilesPerBlock;
-  TileLoader<D, 256> ld;
-  ld.init(pool_k, (uint32_t)D, (uint32_t)((int64_t)P * D * 2));  // < 2^32 (checked on the host)
-  ld.load((uint32_t)p0);
-  for (int it = 0; it < ntiles; ++it) {
+  for (int i = threadIdx.x; i < kPer; i += kPoolRows * 64) valid_s[i] = i < np ? pool_valid[p0 + i] : 0;
+  TileLoader<D, kPoolRows * 64> ld;
+  ld.init(pool_k + (int64_t)p0 * D, (uint32_t)D, (uint32_t)((int64_t)np * D * 2));
+  float* srow = scores + (int64_t)row * P + p0;
+
+  auto buf = [&](int it) { return tiles + (it & 1) * G::kTileBytes; };
+  float part = 0.f;
+  auto finish = [&](int it_rec) {
+    const float s = Scorer::combine(part);
+    const int i = it_rec * G::kTileKeys + (lane & 31);
+    if (active && lane < 32 && i < np) srow[i] = valid_s[i] ? s : -__builtin_inff();
+  };
+  auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin, bool red) {
     __syncthreads();
-    ld.store(tile);
-    __syncthreads();
-    if (it + 1 < ntiles) ld.load((uint32_t)(p0 + (it + 1) * G::kTileKeys));
-    if (active) {
-      const float s = sc.score(tile);  // lanes l and l + 32 hold pool l % 32
-      const int p = p0 + it * G::kTileKeys + (lane & 31);
-      if (lane < 32 && p < P) scores[(int64_t)row * P + p] = pool_valid[p] ? s : -__builtin_inff();
+    sc.fetch(buf(it + 1), fnext);
+    if (fin) finish(it - 2);
+    ld.store(buf(it + 2));
+    ld.load((uint32_t)(it + 3) * G::kTileKeys);
+    sc.mma(fcur, cur);
+    if (red) part = sc.reduce_half(old, 0);
+  };
+  Acc acc0, acc1;
+  Frag f0, f1;
+  ld.load(0u);
+  ld.store(buf(0));
+  ld.load((uint32_t)G::kTileKeys);
+  ld.store(buf(1));
+  ld.load((uint32_t)(2 * G::kTileKeys));
+  __syncthreads();
+  sc.fetch(buf(0), f0);
+  step(0, f0, f1, acc0, acc1, false, false);
+  if (ntiles > 1) {
+    step(1, f1, f0, acc1, acc0, false, true);
+    int it = 2;
+    for (; it + 1 < ntiles; it += 2) {
+      step(it, f0, f1, acc0, acc1, true, true);
+      step(it + 1, f1, f0, acc1, acc0, true, true);
     }
+    if (it < ntiles) step(it, f0, f1, acc0, acc1, true, true);
+    finish(ntiles - 2);
   }
+  part = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, 0);
+  finish(ntiles - 1);
 }
 
 template <int HP, int D>
 static hipError_t launch_scores_t(const PooledScoresArgs& a, hipStream_t st) {
   const int per_block = kPoolTilesPerBlock * TileGeom<D>::kTileKeys;
   const int64_t pool_blocks = (a.P + per_block - 1) / per_block;
-  const int64_t blocks = pool_blocks * ((a.Q + 3) / 4);
+  const int64_t blocks = pool_blocks * ((a.Q + kPoolRows - 1) / kPoolRows);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((pooled_scores_kernel<HP, D>), dim3((unsigned)blocks), dim3(256), 0, st, a.q,
-                     a.w, a.pool_k, a.pool_valid, (int)a.Q, (int)a.P, a.H, (int)pool_blocks,
-                     a.scores);
+  hipLaunchKernelGGL((pooled_scores_kernel<HP, D>), dim3((unsigned)blocks), dim3(kPoolRows * 64),
+                     0, st, a.q, a.w, a.pool_k, a.pool_valid, (int)a.Q, (int)a.P, a.H,
+                     (int)pool_blocks, a.scores);
   return hipGetLastError();
 }
 
