@@ -203,6 +203,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         part[rr] = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, rr);
       finish(ntiles - 1);
     }
+    // The final select's scratch lies in the tile buffers, which the last
+    // iteration of a slower wavefront may still be writing (its store of the
+    // unused tile past the end).
+    __syncthreads();
   } else {
     // The wave's tiles are a prefix [0, nt_w) of the block's.
     const int nt_w = (n_w + G::kTileKeys - 1) / G::kTileKeys;  // 0 when inactive
