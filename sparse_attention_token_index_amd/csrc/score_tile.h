@@ -207,8 +207,16 @@ struct TileScorer {
     return (p[0] + p[1]) + (p[2] + p[3]);
   }
 
-  // ... and the cross-half sum that completes it.
-  static __device__ __forceinline__ float combine(float half) { return half + __shfl_xor(half, 32); }
+  // ... and the cross-half sum that completes it.  v_permlane32_swap trades
+  // the upper half-wave of one copy for the lower half-wave of the other, so
+  // r[0] + r[1] is (lane l % 32's half) + (lane l % 32 + 32's half) in every
+  // lane (same operand order in both halves: identical bits), with no LDS
+  // round trip.
+  static __device__ __forceinline__ float combine(float half) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(half), __float_as_uint(half),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
 
   // Full score of key `lane % 32` of the staged tile (in lanes l and l + 32).
   __device__ __forceinline__ float score(const lds_char* tile) const {

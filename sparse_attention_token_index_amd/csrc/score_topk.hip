@@ -169,6 +169,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
                     bool red) {
       __syncthreads();
+      // Scheduling fences: the compiler may not hoist the next iteration's
+      // products above this barrier or sink this one's below the next, which
+      // would put a reduction right behind the products it reads.
+      __builtin_amdgcn_sched_barrier(0);
       sc.fetch(buf(it + 1), fnext);
       if (fin) finish(it - 2);
       ld.store(buf(it + 2));
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
     if (ntiles > 0) {
       ld.load(0u);
