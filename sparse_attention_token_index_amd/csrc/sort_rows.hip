@@ -15,7 +15,7 @@
 //
 // Radix path (rows with a bucket of more than kBucketLimit entries: many
 // equal or nearly equal scores).  A stable block-wide LSD radix sort on the
-// 32-bit order key with 4-bit digits; digit positions on which every real key
+// 32-bit order key with 3-bit digits; digit positions on which every real key
 // agrees are skipped.  Stability gives the index order among equal scores
 // because rows arrive in ascending index order (the selection kernels write
 // them that way).
@@ -30,17 +30,53 @@ constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr uint32_t kBucketLimit = 64;
 
+// Radix path digits: 3 bits (11 passes at most, constant digits skipped).
+constexpr int kRadixBits = 3;
+constexpr int kRadixDigits = 1 << kRadixBits;
+
 template <int ITEMS>
 struct SortLayout {
   static constexpr int NB = kSortThreads * ITEMS;  // buckets (>= entries per row)
-  // bucket path, in words: start[NB + 1] | pad | cur[NB] | kv[NB] (key, index pairs)
-  static constexpr int kStart = 0, kCur = NB + 2, kKV = 2 * NB + 2;
-  static constexpr int kBucketWords = 4 * NB + 2;
-  // radix path: cnt[16][256] | xk[256 * (ITEMS + 1)] | xv[256 * (ITEMS + 1)]
-  static constexpr int kRadixWords = 16 * kSortThreads + 2 * kSortThreads * (ITEMS + 1);
+  // bucket path, in words: start[NB] (counts, then bucket starts, then bucket
+  // ends) | pad | kv[NB] (key, index pairs)
+  static constexpr int kStart = 0, kKV = NB + 4;
+  static constexpr int kBucketWords = 3 * NB + 4;
+  // radix path: cnt[digits][256] | xk[256 * (ITEMS + 1)] | xv[256 * (ITEMS + 1)]
+  static constexpr int kRadixWords =
+      kRadixDigits * kSortThreads + 2 * kSortThreads * (ITEMS + 1);
   static constexpr int kRed = kBucketWords > kRadixWords ? kBucketWords : kRadixWords;
   static constexpr int kWords = kRed + 4 * kSortWaves;
 };
+
+// Thread t's ITEMS consecutive words w[t*ITEMS ..]: 16-byte accesses when
+// ITEMS is a multiple of 4 (word-strided accesses would hit the same banks).
+template <int ITEMS>
+__device__ __forceinline__ void load_run(const uint32_t* w, uint32_t (&v)[ITEMS]) {
+  const int t = threadIdx.x;
+  if constexpr (ITEMS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; j += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&w[t * ITEMS + j]);
+      v[j] = q.x; v[j + 1] = q.y; v[j + 2] = q.z; v[j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) v[j] = w[t * ITEMS + j];
+  }
+}
+
+template <int ITEMS>
+__device__ __forceinline__ void store_run(uint32_t* w, const uint32_t (&v)[ITEMS]) {
+  const int t = threadIdx.x;
+  if constexpr (ITEMS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; j += 4)
+      *reinterpret_cast<uint4*>(&w[t * ITEMS + j]) = make_uint4(v[j], v[j + 1], v[j + 2], v[j + 3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) w[t * ITEMS + j] = v[j];
+  }
+}
 
 // Monotone non-increasing map of a score onto [0, nb): every step (halving,
 // subtraction, scaling, clamping) is monotone under round-to-nearest, so a
@@ -64,9 +100,9 @@ template <int ITEMS>
 __device__ void radix_sort_row(int32_t* __restrict__ ri, float* __restrict__ rs, int topk,
                                uint32_t* smem) {
   using L = SortLayout<ITEMS>;
-  uint32_t* cnt = smem;                                        // [digit][thread]
-  uint32_t* xk = cnt + 16 * kSortThreads;                       // exchange keys
-  int32_t* xv = (int32_t*)(xk + kSortThreads * (ITEMS + 1));    // exchange indices
+  uint32_t* cnt = smem;                                             // [digit][thread]
+  uint32_t* xk = cnt + kRadixDigits * kSortThreads;                  // exchange keys
+  int32_t* xv = (int32_t*)(xk + kSortThreads * (ITEMS + 1));         // exchange indices
   uint32_t* red = smem + L::kRed;
   const int t = threadIdx.x;
   const int lane = lane_id(), wave = t >> 6;
@@ -101,28 +137,30 @@ __device__ void radix_sort_row(int32_t* __restrict__ ri, float* __restrict__ rs,
   }
   const uint32_t diff = ba ^ bo;
 
-  for (int shift = 0; shift < 32; shift += 4) {
-    if (((diff >> shift) & 15u) == 0u) continue;
+  constexpr uint32_t kMask = (uint32_t)kRadixDigits - 1u;
+  for (int shift = 0; shift < 32; shift += kRadixBits) {
+    if (((diff >> shift) & kMask) == 0u) continue;
 #pragma unroll
-    for (int d = 0; d < 16; ++d) cnt[d * kSortThreads + t] = 0u;
+    for (int d = 0; d < kRadixDigits; ++d) cnt[d * kSortThreads + t] = 0u;
     uint32_t r[ITEMS];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      const uint32_t d = (key[i] >> shift) & 15u;
+      const uint32_t d = (key[i] >> shift) & kMask;
       r[i] = cnt[d * kSortThreads + t];
       cnt[d * kSortThreads + t] = r[i] + 1u;
     }
     __syncthreads();
-    // exclusive scan over f = d * 256 + thread; thread t owns f in [16t, 16t + 16)
-    uint32_t v[16];
+    // exclusive scan over f = d * 256 + thread; thread t owns f in
+    // [kRadixDigits * t, kRadixDigits * (t + 1))
+    uint32_t v[kRadixDigits];
 #pragma unroll
-    for (int x = 0; x < 16; x += 4) {
-      const uint4 q = *reinterpret_cast<const uint4*>(&cnt[16 * t + x]);
+    for (int x = 0; x < kRadixDigits; x += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&cnt[kRadixDigits * t + x]);
       v[x] = q.x; v[x + 1] = q.y; v[x + 2] = q.z; v[x + 3] = q.w;
     }
     uint32_t run = 0u;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
+    for (int x = 0; x < kRadixDigits; ++x) {
       const uint32_t c = v[x];
       v[x] = run;
       run += c;
@@ -135,13 +173,13 @@ __device__ void radix_sort_row(int32_t* __restrict__ ri, float* __restrict__ rs,
     for (int w = 0; w < kSortWaves; ++w)
       if (w < wave) base += red[w];
 #pragma unroll
-    for (int x = 0; x < 16; x += 4)
-      *reinterpret_cast<uint4*>(&cnt[16 * t + x]) =
+    for (int x = 0; x < kRadixDigits; x += 4)
+      *reinterpret_cast<uint4*>(&cnt[kRadixDigits * t + x]) =
           make_uint4(base + v[x], base + v[x + 1], base + v[x + 2], base + v[x + 3]);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      const uint32_t d = (key[i] >> shift) & 15u;
+      const uint32_t d = (key[i] >> shift) & kMask;
       const uint32_t dst = blocked_addr(cnt[d * kSortThreads + t] + r[i], ITEMS);
       xk[dst] = key[i];
       xv[dst] = val[i];
@@ -167,15 +205,16 @@ __device__ void radix_sort_row(int32_t* __restrict__ ri, float* __restrict__ rs,
 
 // Bucket path for one row (falls back to the radix path when a bucket is too
 // full).  key/val: the row's entries in the striped arrangement (slot
-// i * 256 + t), val < 0 for padding.
+// i * 256 + t), val < 0 for padding.  One array serves as the counts, then
+// each bucket's first slot (scatter cursors), then, after the scatter, each
+// bucket's end: bucket b spans [end[b-1], end[b]).
 template <int ITEMS>
 __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float* __restrict__ rs,
                                                 int topk, uint32_t* smem, uint32_t (&key)[ITEMS],
                                                 int32_t (&val)[ITEMS]) {
   using L = SortLayout<ITEMS>;
   constexpr uint32_t NB = (uint32_t)L::NB;
-  uint32_t* start = smem + L::kStart;  // counts, then each bucket's first slot
-  uint32_t* cur = smem + L::kCur;      // scatter cursors
+  uint32_t* start = smem + L::kStart;
   uint2* kv = reinterpret_cast<uint2*>(smem + L::kKV);  // entries grouped by bucket
   uint32_t* red = smem + L::kRed;
   const int t = threadIdx.x;
@@ -199,8 +238,12 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
     red[kSortWaves + wave] = kmax;
     red[2 * kSortWaves + wave] = nreal;
   }
+  {
+    uint32_t z[ITEMS];
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) start[t * ITEMS + j] = 0u;
+    for (int j = 0; j < ITEMS; ++j) z[j] = 0u;
+    store_run<ITEMS>(start, z);
+  }
   __syncthreads();
   uint32_t nv = 0u;
   kmin = 0xFFFFFFFFu;
@@ -227,10 +270,11 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
   // Exclusive scan of the counts (thread t owns buckets [t*ITEMS, (t+1)*ITEMS))
   // and the largest bucket.
   uint32_t c[ITEMS];
+  load_run<ITEMS>(start, c);
   uint32_t run = 0u, big = 0u;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    const uint32_t n = start[t * ITEMS + j];
+    const uint32_t n = c[j];
     c[j] = run;
     run += n;
     big = max(big, n);
@@ -254,18 +298,16 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
     return;
   }
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    start[t * ITEMS + j] = base + c[j];
-    cur[t * ITEMS + j] = base + c[j];
-  }
-  if (t == 0) start[NB] = nv;
+  for (int j = 0; j < ITEMS; ++j) c[j] += base;
+  store_run<ITEMS>(start, c);
   __syncthreads();
 
-  // Scatter into the buckets' ranges (arbitrary order inside a bucket).
+  // Scatter into the buckets' ranges (arbitrary order inside a bucket); the
+  // cursors end at each bucket's end.
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     if (val[i] >= 0) {
-      const uint32_t slot = atomicAdd(&cur[bkt[i]], 1u);
+      const uint32_t slot = atomicAdd(&start[bkt[i]], 1u);
       kv[slot] = make_uint2(key[i], (uint32_t)val[i]);
     }
   }
@@ -287,7 +329,7 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
       key[i] = e.x;
       val[i] = (int32_t)e.y;
       const uint32_t b = bucket_of(key[i], top_half, scale, NB);
-      const uint32_t lo = start[b], n = start[b + 1] - lo;
+      const uint32_t lo = b > 0u ? start[b - 1u] : 0u, n = start[b] - lo;
       if (n > 1u) {
         s0[i] = lo;
         cnt[i] = n;
@@ -360,11 +402,13 @@ __global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* __rest
   }
 }
 
-// Workgroups for `rows` rows: as many as are resident at once (LDS-bound:
-// 160 KB per CU on gfx950, at most 8 workgroups of 4 waves), each taking
-// every grid-th row, so a resident workgroup moves straight on to its next
-// row whose loads it has already issued.
-static unsigned sort_groups(int64_t rows, size_t lds) {
+// Workgroups for `rows` rows: as many as are resident at once (the runtime's
+// occupancy for this kernel, its registers and `lds` bytes of LDS), each
+// taking every grid-th row, so a resident workgroup moves straight on to its
+// next row whose loads it has already issued.  A grid larger than the
+// resident set would leave its last workgroups waiting for whole persistent
+// workgroups to finish.
+static unsigned sort_groups(const void* kern, int64_t rows, size_t lds) {
   static int cus_cache[64];
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
@@ -375,8 +419,30 @@ static unsigned sort_groups(int64_t rows, size_t lds) {
       cus = 256;
     if (dev >= 0 && dev < 64) cus_cache[dev] = cus;
   }
-  int64_t per_cu = (int64_t)(163840 / lds);
-  per_cu = per_cu < 1 ? 1 : per_cu > 8 ? 8 : per_cu;
+  // One cached answer per (kernel, device); each kernel instance always runs
+  // with the same LDS size.
+  static const void* kern_cache[64][6];
+  static int per_cu_cache[64][6];
+  int per_cu = 0, slot = -1;
+  if (dev >= 0 && dev < 64) {
+    for (int i = 0; i < 6 && slot < 0; ++i) {
+      if (kern_cache[dev][i] == kern) {
+        per_cu = per_cu_cache[dev][i];
+        slot = i;
+      } else if (kern_cache[dev][i] == nullptr) {
+        slot = i;
+      }
+    }
+  }
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kSortThreads, lds) !=
+            hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (slot >= 0) {
+      kern_cache[dev][slot] = kern;
+      per_cu_cache[dev][slot] = per_cu;
+    }
+  }
   const int64_t resident = (int64_t)cus * per_cu;
   return (unsigned)(rows < resident ? rows : resident);
 }
@@ -390,7 +456,9 @@ hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, 
     hipError_t e = hipFuncSetAttribute((const void*)sort_rows_kernel<n>,                       \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
     if (e != hipSuccess) return e;                                                             \
-    hipLaunchKernelGGL(sort_rows_kernel<n>, dim3(sort_groups(rows, lds)), dim3(kSortThreads),   \
+    hipLaunchKernelGGL(sort_rows_kernel<n>,                                                    \
+                       dim3(sort_groups((const void*)sort_rows_kernel<n>, rows, lds)),         \
+                       dim3(kSortThreads),                                                     \
                        lds, st, idx, score,                                                    \
                        topk, (int)rows);                                                       \
     return hipGetLastError();                                                                  \
