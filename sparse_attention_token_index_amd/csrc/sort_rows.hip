@@ -337,12 +337,17 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
     }
     maxc = max(maxc, cnt[i]);
   }
-  for (uint32_t j = 0; j < maxc; ++j) {
+  // Two bucket entries per step (one paired LDS read); the second may lie
+  // past the bucket (still inside the allocation) and is then ignored.
+  for (uint32_t j = 0; j < maxc; j += 2) {
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       if (j < cnt[i]) {
-        const uint2 e = kv[s0[i] + j];
-        rank[i] += (e.x > key[i] || (e.x == key[i] && (int32_t)e.y < val[i])) ? 1u : 0u;
+        const uint2 e0 = kv[s0[i] + j];
+        const uint2 e1 = kv[s0[i] + j + 1u];
+        rank[i] += (e0.x > key[i] || (e0.x == key[i] && (int32_t)e0.y < val[i])) ? 1u : 0u;
+        rank[i] += (j + 1u < cnt[i] &&
+                    (e1.x > key[i] || (e1.x == key[i] && (int32_t)e1.y < val[i]))) ? 1u : 0u;
       }
     }
   }
@@ -368,7 +373,7 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
 // Each workgroup sorts rows blockIdx.x, blockIdx.x + gridDim.x, ...; the next
 // row's entries are loaded while the current row is sorted.
 template <int ITEMS>
-__global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* __restrict__ idx,
+__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(ITEMS <= 8 ? 6 : 1))) void sort_rows_kernel(int32_t* __restrict__ idx,
                                                                  float* __restrict__ score,
                                                                  int topk, int rows) {
   extern __shared__ __align__(16) uint32_t sort_smem[];
