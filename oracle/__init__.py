@@ -17,6 +17,7 @@ from .indexer import (  # noqa: F401
     rank_desc,
     select_topk,
     score_topk,
+    scores_at_indices,
     round_to_bf16,
     pool_count,
     kpool_compress,

@@ -147,6 +147,45 @@ def score_topk(q: np.ndarray, k: np.ndarray, w: np.ndarray, compress_ratio: int,
     return idx, vals
 
 
+def _usable_keys(s: np.ndarray, n_t: int) -> np.ndarray:
+    """Supplied key indices that name a key the row may see: 0 <= s < n_t."""
+    return (s >= 0) & (s < n_t)
+
+
+def scores_at_indices(q: np.ndarray, k: np.ndarray, w: np.ndarray, compress_ratio: int,
+                      topk_indices: np.ndarray, rows=None):
+    """Index scores at supplied key indices (v4_lighting_indexer with its
+    optional topk_indices [batch, seqlen, topk] int32, and
+    pytorch_extract_topk_scores: the scores gathered at given indices along
+    the key axis).
+
+    q [R, B, H, D], k [Skv, B, D], w [R, B, H] as in score_topk (with `rows`
+    the query positions of q's R rows, else 0..R-1); topk_indices [B, R, n]
+    integers.  Entry s of row (b, t) is usable when 0 <= s < n_t, the row's
+    causal/compressed bound: the result there is (s, I[t, s]).  Any other
+    entry (-1 padding, a masked or an out-of-range key) gives (-1, -inf).
+    Entries keep the supplied order; duplicates are scored each time.
+    Returns (idx int32 [B, R, n], vals float64 [B, R, n]).
+    """
+    R, B = q.shape[0], q.shape[1]
+    Skv = k.shape[0]
+    positions = list(range(R)) if rows is None else [int(t) for t in rows]
+    assert len(positions) == R
+    sup = np.asarray(topk_indices)
+    n = sup.shape[2]
+    idx = np.full((B, R, n), -1, dtype=np.int32)
+    vals = np.full((B, R, n), NEG_INF, dtype=np.float64)
+    for b in range(B):
+        for i, t in enumerate(positions):
+            n_t = visible_keys(t, Skv, compress_ratio)
+            s = sup[b, i].astype(np.int64)
+            ok = _usable_keys(s, n_t)
+            if np.any(ok):
+                vals[b, i, ok] = head_scores(q[i, b], k[s[ok], b], w[i, b])
+                idx[b, i, ok] = s[ok]
+    return idx, vals
+
+
 # ---------------------------------------------------------------------------
 # Pooled decode selection (glm5next_dsa page)
 # ---------------------------------------------------------------------------

@@ -473,12 +473,62 @@ def test_pooled_matches_unpooled_when_kp1():
 
 
 # ---------------------------------------------------------------------------
+# Scores at supplied indices
+# ---------------------------------------------------------------------------
+
+def check_bruteforce_scores_at_indices(n_cases=30, seed=5):
+    """Exact rational scores at random supplied indices, including -1,
+    out-of-range, masked (s >= n_t) and repeated entries."""
+    rng = np.random.default_rng(seed)
+    F = lambda x: Fraction(float(x))
+    for c in range(n_cases):
+        S, Skv = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        B, H, D = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        r, n = int(rng.integers(1, 4)), int(rng.integers(1, 10))
+        q, k, w = _tiny_case(rng, S, Skv, B, H, D, discrete=(c % 3 != 2))
+        sup = rng.integers(-2, Skv + 3, size=(B, S, n))
+        idx, vals = oracle.scores_at_indices(q, k, w, r, sup)
+        for b in range(B):
+            for t in range(S):
+                for j in range(n):
+                    s = int(sup[b, t, j])
+                    if s < 0 or not _brute_visible(s, t, Skv, r):
+                        assert idx[b, t, j] == -1 and vals[b, t, j] == -math.inf, (c, b, t, j)
+                        continue
+                    tot = Fraction(0)
+                    for h in range(H):
+                        dot = sum((F(q[t, b, h, d]) * F(k[s, b, d]) for d in range(D)), Fraction(0))
+                        tot += F(w[t, b, h]) * max(dot, Fraction(0))
+                    assert idx[b, t, j] == s and Fraction(float(vals[b, t, j])) == tot, (c, b, t, j)
+
+
+def check_scores_at_own_topk():
+    """Fed the indices score_topk selected, the gather returns exactly the
+    scores score_topk reported, padding included."""
+    rng = np.random.default_rng(9)
+    q, k, w = _tiny_case(rng, 40, 30, 2, 3, 8, discrete=False)
+    for r, topk in ((1, 7), (3, 12), (2, 40)):
+        idx, vals = oracle.score_topk(q, k, w, r, topk)
+        gi, gv = oracle.scores_at_indices(q, k, w, r, idx)
+        assert np.array_equal(gi, idx) and np.array_equal(gv, vals)
+
+
+def test_bruteforce_scores_at_indices():
+    check_bruteforce_scores_at_indices()
+
+
+def test_scores_at_own_topk():
+    check_scores_at_own_topk()
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
 ALL_CHECKS = [check_golden_indexer, check_golden_kpool, check_golden_pooled,
               lambda: check_bruteforce_score_topk(12), check_round_to_bf16,
-              check_bruteforce_pooled, check_invariants, check_kpool_invariants, check_expand]
+              check_bruteforce_pooled, check_invariants, check_kpool_invariants, check_expand,
+              lambda: check_bruteforce_scores_at_indices(10), check_scores_at_own_topk]
 
 
 def _some_check_fails():
@@ -503,6 +553,8 @@ MUTANTS = {
     "ascending order": ("rank_desc",
                         lambda s: np.lexsort((np.arange(len(s)), np.asarray(s, dtype=np.float64)))),
     "keys reversed": ("_dot_products", lambda q, k: q @ k[::-1].T),
+    "gather admits s == n_t": ("_usable_keys", lambda s, n: (s >= 0) & (s <= n)),
+    "gather admits masked keys": ("_usable_keys", lambda s, n: s >= 0),
     "softmax over channels": ("_slot_softmax",
                               lambda lg: np.exp(lg - lg.max(axis=1, keepdims=True)) /
                               np.exp(lg - lg.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)),
