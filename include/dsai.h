@@ -124,10 +124,19 @@ int dsai_last_hip_error(dsai_handle h);
  * S, Skv, B >= 0 (S == 0 or B == 0: nothing is written or launched);
  * Skv < 2^31; compress_ratio >= 1; 1 <= topk <= DSAI_MAX_TOPK
  * (DSAI_ERR_INVALID_ARG otherwise); index_k must span < 4 GiB
- * (Skv * B * D * 2 bytes; DSAI_ERR_UNSUPPORTED otherwise).  topk_indices must be NULL: scoring at
- * caller-supplied indices returns DSAI_ERR_UNSUPPORTED.  Query rows are
+ * (Skv * B * D * 2 bytes; DSAI_ERR_UNSUPPORTED otherwise).  Query rows are
  * processed in launches of cfg.chunk_rows rows (all rows if 0); no scratch
- * memory is used. */
+ * memory is used.
+ *
+ * Scores at supplied indices (the page's optional topk_indices
+ * [batch, seqlen, topk] int32, and pytorch_extract_topk_scores): when
+ * topk_indices is not NULL no key is selected.  For each entry s of row
+ * (b, t), in the supplied order, out_idx/out_score receive (s, I) if
+ * 0 <= s < min(Skv, floor((t+1) / compress_ratio)), else (-1, -inf); I is
+ * bit-identical to the score the selection reports for that key.
+ * topk_indices is device memory, 16-byte aligned (DSAI_ERR_INVALID_ARG
+ * otherwise), and may be out_idx itself (in place); cfg.order does not
+ * apply; index_k has no 4 GiB limit on this form. */
 int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
                     const float* weights, int64_t S, int64_t Skv, int64_t B,
                     int compress_ratio, int topk, const int32_t* topk_indices,

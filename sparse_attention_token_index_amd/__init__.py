@@ -166,7 +166,12 @@ class Indexer:
                    out_idx: Optional[torch.Tensor] = None,
                    out_score: Optional[torch.Tensor] = None):
         """index_q [S,B,H,D] bf16, index_k [Skv,B,D] bf16, weights [S,B,H] fp32 ->
-        (idx [B,S,topk] int32, score [B,S,topk] fp32)."""
+        (idx [B,S,topk] int32, score [B,S,topk] fp32).
+
+        With topk_indices [B,S,topk] int32 the keys are not selected: each
+        supplied index s with 0 <= s < n_t gets its score, any other entry
+        (-1, -inf); entries keep the supplied order (out_idx may be
+        topk_indices itself)."""
         S, B = index_q.shape[0], index_q.shape[1]
         Skv = index_k.shape[0]
         H, D = self.cfg.heads, self.cfg.dim
@@ -174,6 +179,8 @@ class Indexer:
         _need(index_q, "index_q", torch.bfloat16, (S, B, H, D))
         _need(index_k, "index_k", torch.bfloat16, (Skv, B, D), dev)
         _need(weights, "weights", torch.float32, (S, B, H), dev)
+        if topk_indices is not None:
+            _need(topk_indices, "topk_indices", torch.int32, (B, S, topk), dev)
         if out_idx is None:
             out_idx = torch.empty((B, S, topk), dtype=torch.int32, device=dev)
         if out_score is None:

@@ -101,7 +101,25 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   if (S < 0 || Skv < 0 || B < 0 || compress_ratio < 1) return DSAI_ERR_INVALID_ARG;
   if (topk < 1 || topk > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
   if (S > kI32 || Skv > kI32 || B > kI32 || S * B > kI32) return DSAI_ERR_INVALID_ARG;
-  if (topk_indices) return DSAI_ERR_UNSUPPORTED;
+  if (topk_indices) {
+    // scores at the supplied indices: one [B, S, topk] entry per output slot
+    if (S == 0 || B == 0) return DSAI_OK;
+    if (!index_q || !weights || !out_idx || !out_score) return DSAI_ERR_NULLPTR;
+    if (Skv > 0 && !index_k) return DSAI_ERR_NULLPTR;
+    if (!aligned(index_q) || !aligned(index_k) || !aligned(out_idx) || !aligned(out_score) ||
+        !aligned(topk_indices))
+      return DSAI_ERR_INVALID_ARG;
+    dsai::ScoreAtArgs a;
+    a.q = static_cast<const uint16_t*>(index_q);
+    a.k = static_cast<const uint16_t*>(index_k);
+    a.w = weights;
+    a.S = S; a.Skv = Skv; a.B = B;
+    a.H = h->cfg.heads; a.D = h->cfg.dim; a.ratio = compress_ratio; a.n = topk;
+    a.chunk_rows = h->cfg.chunk_rows;
+    a.sup = topk_indices;
+    a.out_idx = out_idx; a.out_score = out_score;
+    return hip_status(h, dsai::launch_score_at(a, static_cast<hipStream_t>(stream)));
+  }
   // keys of one batch are addressed with 32-bit byte offsets
   if (Skv * B * h->cfg.dim * 2 > (int64_t)0xFFFFFFFF) return DSAI_ERR_UNSUPPORTED;
   if (S == 0 || B == 0) return DSAI_OK;

@@ -79,6 +79,20 @@ ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t l
 TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit);
 
 hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st);
+
+// Scores at supplied key indices (score_at.hip).
+struct ScoreAtArgs {
+  const uint16_t* q;   // [S, B, H, D] bf16
+  const uint16_t* k;   // [Skv, B, D] bf16
+  const float* w;      // [S, B, H]
+  int64_t S, Skv, B;
+  int H, D, ratio, n;  // n: supplied entries per row
+  int64_t chunk_rows;  // 0: all rows in one launch
+  const int32_t* sup;  // [B, S, n] supplied key indices (may alias out_idx)
+  int32_t* out_idx;    // [B, S, n]
+  float* out_score;    // [B, S, n]
+};
+hipError_t launch_score_at(const ScoreAtArgs& a, hipStream_t st);
 // Stable sort of `rows` rows of `topk` (idx, score) pairs, each in ascending
 // index order with -1 padding at the tail, into score-descending order.
 hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st);

@@ -117,7 +117,13 @@ def test_score_topk_argument_errors(lib):
     assert call(topk=0) == INVALID
     assert call(topk=8193) == INVALID
     assert call(S=2 ** 31) == INVALID
-    assert call(tki=FAKE) == UNSUPPORTED          # supplied indices: not built
+    # supplied indices: the same argument rules, plus an aligned index array
+    assert call(tki=FAKE, S=0) == OK
+    assert call(tki=FAKE, q=None) == NULLPTR
+    assert call(tki=FAKE, k=None) == NULLPTR
+    assert call(tki=FAKE, oi=None) == NULLPTR
+    assert call(tki=ctypes.c_void_p(0x10004)) == INVALID  # misaligned index array
+    assert call(tki=FAKE, topk=0) == INVALID
     assert call(S=0) == OK                        # empty: nothing launched
     assert call(B=0) == OK
     assert call(q=None) == NULLPTR
