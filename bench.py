@@ -11,6 +11,9 @@ resident in device memory:
   * the pooled decode selection over one 65536-token indexer cache
     (kpool_compress -> select (index_scores + topk_pools) -> expand;
     KP=4, 64 query rows, 32 heads, index_topk=512).
+Outside the step, the same top-k rows are rescored through the
+topk_indices form of dsai_score_topk (scores at supplied indices) and
+reported in `breakdown` (score_at_indices_*).
 `value` = prefill query tokens per second of the whole step (the pooled
 stages' time is counted against it as well).  HIP events on the stream the
 library launches on give per-stage times; the fused kernel's roofline is its
@@ -59,6 +62,14 @@ def visible_pairs(case) -> int:
 
 def indexer_flops(case) -> float:
     return 2.0 * case.H * case.D * visible_pairs(case)
+
+
+def selected_entries(case) -> int:
+    """Usable (row, key) entries of the top-k output: sum over rows of
+    min(topk, n_t) - the pairs the gather form scores when fed that output."""
+    t = np.arange(case.S, dtype=np.int64)
+    n = np.minimum(case.Skv, (t + 1) // case.compress_ratio)
+    return int(np.minimum(case.topk, n).sum()) * case.B
 
 
 def kpool_bytes(pc, P) -> int:
@@ -371,6 +382,23 @@ def main():
     avg = {s: float(np.mean(v)) for s, v in per.items()}
     med = {s: float(np.median(v)) for s, v in per.items()}
 
+    # scores at supplied indices (the topk_indices form; not part of the
+    # step): the step's own top-k rows rescored
+    at_ix = dsai.Indexer(heads=case.H, dim=case.D, chunk_rows=case.chunk_rows)
+    at_idx, at_sc = torch.empty_like(out_idx), torch.empty_like(out_sc)
+    for _ in range(2):
+        at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
+                         out_idx=at_idx, out_score=at_sc)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(args.steps):
+        at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
+                         out_idx=at_idx, out_score=at_sc)
+    a1.record()
+    torch.cuda.synchronize()
+    at_ms = a0.elapsed_time(a1) / args.steps
+    at_flops = 2.0 * case.H * case.D * selected_entries(case)
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -417,6 +445,8 @@ def main():
             "select_ms": avg["select"], "select_TFLOPs": select_flops(pc, P) / (avg["select"] * 1e-3) / 1e12,
             "expand_ms": avg["expand"], "expand_GBps": eb / (avg["expand"] * 1e-3) / 1e9,
             "expand_bytes": eb, "wall_s": wall,
+            "score_at_indices_ms": at_ms,
+            "score_at_indices_TFLOPs": at_flops / (at_ms * 1e-3) / 1e12,
         },
     }
     if not args.no_cpu_baseline:
