@@ -354,8 +354,12 @@ __device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, ui
       const uint32_t i0 = gi * 256u + 4u * lane;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        // branch-free: a slot past the row (any bits; bins() lands in
+        // [0, 255] for every input) adds 0
         const float x = __uint_as_float(u[e]);
-        if (i0 + e < n && (level == 0 || (x >= a && x <= b))) hist_add(hist, bins(x));
+        const bool in = i0 + e < n && (level == 0 || (x >= a && x <= b));
+        __hip_atomic_fetch_add(&hist[bins(x)], in ? 1u : 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WAVEFRONT);
       }
     }
     wave_lds_sync();
