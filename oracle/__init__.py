@@ -19,6 +19,7 @@ from .indexer import (  # noqa: F401
     score_topk,
     scores_at_indices,
     round_to_bf16,
+    k_norm,
     pool_count,
     kpool_compress,
     pooled_index_scores,

@@ -206,6 +206,40 @@ def round_to_bf16(x: np.ndarray):
     return r, bits
 
 
+def _row_moments(x: np.ndarray):
+    """Per-row mean and biased variance (divide by the row length) of [N, D]."""
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    return mu, var
+
+
+def _inv_std(var: np.ndarray, eps: float) -> np.ndarray:
+    """1 / sqrt(var + eps): eps inside the square root."""
+    return 1.0 / np.sqrt(var + eps)
+
+
+def k_norm(k_raw: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float):
+    """The indexer's k_norm, the producer of the cache's k_normed rows
+    (glm5next_dsa: "indexer.k_norm is a LayerNorm with a bias"; the BF16
+    LayerNorm-with-bias module of its Constants).  Per row n of [N, D]:
+
+      mu = mean_c x[n, c],  var = mean_c (x[n, c] - mu)^2   (biased)
+      y[n, c] = (x[n, c] - mu) / sqrt(var + eps) * gamma[c] + beta[c]
+
+    rounded to bf16 (nearest even).  k_raw [N, D] bf16 values, gamma / beta
+    [D] bf16 values (the checkpoint's dtype), eps > 0.  Returns dict with
+    k_normed_f64 [N, D] (before rounding), k_normed (bf16 values as fp64) and
+    k_normed_bits uint16.
+    """
+    x = np.asarray(k_raw, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    b = np.asarray(beta, dtype=np.float64)
+    mu, var = _row_moments(x)
+    y = (x - mu) * _inv_std(var, float(eps)) * g[None, :] + b[None, :]
+    rv, rb = round_to_bf16(y)
+    return {"k_normed_f64": y, "k_normed": rv, "k_normed_bits": rb}
+
+
 def _slot_softmax(logits: np.ndarray) -> np.ndarray:
     """Softmax over the pool-slot axis (axis 0) of [KP, D] logits, per channel,
     with the per-channel maximum subtracted first (exact shift invariance)."""

@@ -522,13 +522,69 @@ def test_scores_at_own_topk():
 
 
 # ---------------------------------------------------------------------------
+# k_norm (LayerNorm with a bias)
+# ---------------------------------------------------------------------------
+
+def check_k_norm_hand_example():
+    """x = [1, 2, 3, 4]: mean 2.5, biased variance (2.25+0.25+0.25+2.25)/4 =
+    1.25; with eps = 0.25 the divisor is sqrt(1.5), and d/sqrt(1.5) for
+    d = -1.5, -0.5, 0.5, 1.5 is -sqrt(1.5), -sqrt(1/6), sqrt(1/6), sqrt(1.5).
+    gamma = [2, 1, 1, 0.5], beta = [0, 1, -1, 0.25] give
+    [-2 sqrt(1.5), 1 - sqrt(1/6), sqrt(1/6) - 1, 0.5 sqrt(1.5) + 0.25]."""
+    r = oracle.k_norm(np.array([[1.0, 2.0, 3.0, 4.0]]), np.array([2.0, 1.0, 1.0, 0.5]),
+                      np.array([0.0, 1.0, -1.0, 0.25]), 0.25)
+    expect = [-2.449489742783178, 0.5917517095361369, -0.5917517095361369, 0.8623724356957945]
+    assert np.allclose(r["k_normed_f64"][0], expect, rtol=0, atol=1e-14), r["k_normed_f64"]
+    # bf16 of those: 8 significant bits
+    assert np.array_equal(r["k_normed"][0], [-2.453125, 0.58984375, -0.58984375, 0.86328125])
+
+
+def check_k_norm_properties():
+    rng = np.random.default_rng(17)
+    x = SY.bf16_bits_to_f32(SY.f32_to_bf16_bits(
+        (rng.standard_normal((50, 128)) * 3 + rng.standard_normal((50, 1)) * 5).astype(np.float32)))
+    x = x.astype(np.float64)
+    eps = 1e-5
+    plain = oracle.k_norm(x, np.ones(128), np.zeros(128), eps)["k_normed_f64"]
+    # zero mean; variance var / (var + eps)
+    var = x.var(axis=1)
+    assert np.all(np.abs(plain.mean(axis=1)) < 1e-12)
+    assert np.allclose(plain.var(axis=1), var / (var + eps), rtol=1e-12, atol=0)
+    # a constant shift of a row changes nothing; with eps = 0 neither does a
+    # positive scale
+    shifted = oracle.k_norm(x + 7.25, np.ones(128), np.zeros(128), eps)["k_normed_f64"]
+    assert np.allclose(shifted, plain, rtol=0, atol=1e-11)
+    a0 = oracle.k_norm(x, np.ones(128), np.zeros(128), 0.0)["k_normed_f64"]
+    a3 = oracle.k_norm(3.0 * x, np.ones(128), np.zeros(128), 0.0)["k_normed_f64"]
+    assert np.allclose(a0, a3, rtol=0, atol=1e-12)
+    # the library LayerNorm (fp64, biased variance, eps inside the root,
+    # elementwise affine) agrees before rounding
+    import torch
+    g = rng.standard_normal(128)
+    b = rng.standard_normal(128)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (128,), torch.from_numpy(g),
+                                         torch.from_numpy(b), eps).numpy()
+    got = oracle.k_norm(x, g, b, eps)["k_normed_f64"]
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_k_norm_hand_example():
+    check_k_norm_hand_example()
+
+
+def test_k_norm_properties():
+    check_k_norm_properties()
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
 ALL_CHECKS = [check_golden_indexer, check_golden_kpool, check_golden_pooled,
               lambda: check_bruteforce_score_topk(12), check_round_to_bf16,
               check_bruteforce_pooled, check_invariants, check_kpool_invariants, check_expand,
-              lambda: check_bruteforce_scores_at_indices(10), check_scores_at_own_topk]
+              lambda: check_bruteforce_scores_at_indices(10), check_scores_at_own_topk,
+              check_k_norm_hand_example, check_k_norm_properties]
 
 
 def _some_check_fails():
@@ -554,6 +610,11 @@ MUTANTS = {
                         lambda s: np.lexsort((np.arange(len(s)), np.asarray(s, dtype=np.float64)))),
     "keys reversed": ("_dot_products", lambda q, k: q @ k[::-1].T),
     "gather admits s == n_t": ("_usable_keys", lambda s, n: (s >= 0) & (s <= n)),
+    "layernorm unbiased variance": ("_row_moments", lambda x: (
+        x.mean(axis=1, keepdims=True), x.var(axis=1, ddof=1, keepdims=True))),
+    "layernorm eps outside the root": ("_inv_std", lambda var, eps: 1.0 / np.sqrt(var) + eps),
+    "layernorm without centring": ("_row_moments", lambda x: (
+        np.zeros((x.shape[0], 1)), x.var(axis=1, keepdims=True))),
     "gather admits masked keys": ("_usable_keys", lambda s, n: s >= 0),
     "softmax over channels": ("_slot_softmax",
                               lambda lg: np.exp(lg - lg.max(axis=1, keepdims=True)) /
