@@ -12,8 +12,9 @@ resident in device memory:
     (kpool_compress -> select (index_scores + topk_pools) -> expand;
     KP=4, 64 query rows, 32 heads, index_topk=512).
 Outside the step, the same top-k rows are rescored through the
-topk_indices form of dsai_score_topk (scores at supplied indices) and
-reported in `breakdown` (score_at_indices_*).
+topk_indices form of dsai_score_topk (scores at supplied indices), and the
+cache write's k_norm runs over the 65536 cache rows; both are reported in
+`breakdown` (score_at_indices_*, k_norm_*).
 `value` = prefill query tokens per second of the whole step (the pooled
 stages' time is counted against it as well).  HIP events on the stream the
 library launches on give per-stage times; the fused kernel's roofline is its
@@ -399,6 +400,21 @@ def main():
     at_ms = a0.elapsed_time(a1) / args.steps
     at_flops = 2.0 * case.H * case.D * selected_entries(case)
 
+    # the cache write's k_norm (LayerNorm with a bias) over the pooled
+    # workload's 65536 cache rows (not part of the step)
+    ln_g = torch.ones((pc.D,), dtype=torch.bfloat16, device=dev)
+    ln_b = torch.zeros((pc.D,), dtype=torch.bfloat16, device=dev)
+    ln_out = torch.empty_like(kn)
+    for _ in range(2):
+        pix.k_norm(kn, ln_g, ln_b, 1e-5, out=ln_out)
+    a0.record()
+    for _ in range(args.steps):
+        pix.k_norm(kn, ln_g, ln_b, 1e-5, out=ln_out)
+    a1.record()
+    torch.cuda.synchronize()
+    ln_ms = a0.elapsed_time(a1) / args.steps
+    ln_bytes = 2 * kn.numel() * 2 + 2 * pc.D * 2
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -447,6 +463,8 @@ def main():
             "expand_bytes": eb, "wall_s": wall,
             "score_at_indices_ms": at_ms,
             "score_at_indices_TFLOPs": at_flops / (at_ms * 1e-3) / 1e12,
+            "k_norm_ms": ln_ms, "k_norm_GBps": ln_bytes / (ln_ms * 1e-3) / 1e9,
+            "k_norm_bytes": ln_bytes,
         },
     }
     if not args.no_cpu_baseline:

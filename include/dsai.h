@@ -200,6 +200,21 @@ int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,
                 void* stream);
 
+/* ---- cache write: the indexer's k_norm ------------------------------------ */
+/* k_norm ("Module glm5next_dsa", "Checkpoint and kernel facts": indexer.k_norm
+ * is a LayerNorm with a bias; Constants: the BF16 LayerNorm module): the
+ * producer of the k_normed rows kpool_compress reads.  Per row n of N:
+ *   mean = sum_c x[n,c] / D,  var = sum_c (x[n,c] - mean)^2 / D   (biased)
+ *   k_normed[n,c] = bf16( (x[n,c] - mean) / sqrt(var + eps) * gamma[c] + beta[c] )
+ * computed in fp32, rounded to nearest even.
+ *   k_raw [N, D] bf16, gamma [D] bf16, beta [D] bf16, k_normed [N, D] bf16
+ *   written (e.g. the cache rows the new tokens occupy; it may be k_raw
+ *   itself).  D = cfg.dim.  All device memory, 16-byte aligned
+ *   (DSAI_ERR_INVALID_ARG otherwise).  N >= 0 (0: nothing launched);
+ *   eps > 0 and finite (DSAI_ERR_INVALID_ARG otherwise). */
+int dsai_k_norm(dsai_handle h, const void* k_raw, const void* gamma, const void* beta, float eps,
+                int64_t N, void* k_normed, void* stream);
+
 /* ---- row order ----------------------------------------------------------- */
 /* Reorder `rows` top-k rows of k (index, score) entries in place, row r at
  * idx[r * k .. r * k + k) / score[r * k .. r * k + k): by score descending,

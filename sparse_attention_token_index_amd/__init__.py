@@ -8,7 +8,8 @@ provides device memory and streams.  There is no CPU fallback: without the
 built library, or without tensors on a ROCm GPU, every call raises.
 
 Names follow the C entry points: ``score_topk`` (lightning-indexer score +
-causal/compressed mask + top-k), and the pooled decode pipeline
+causal/compressed mask + top-k, or scores at supplied indices), ``k_norm``
+(the cache write's LayerNorm), and the pooled decode pipeline
 ``kpool_compress`` -> ``index_scores`` -> ``topk_pools`` -> ``expand``
 (``select`` = ``index_scores`` + ``topk_pools``).
 """
@@ -30,7 +31,7 @@ EXPORTS = (
     "dsai_create", "dsai_destroy", "dsai_status_string", "dsai_last_hip_error",
     "dsai_score_topk", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
     "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
-    "dsai_sort_rows",
+    "dsai_sort_rows", "dsai_k_norm",
 )
 
 DSAI_OK = 0
@@ -84,6 +85,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_select": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "dsai_expand": [vp, vp, i64, vp, vp],
         "dsai_sort_rows": [vp, vp, vp, i64, c_int, vp],
+        "dsai_k_norm": [vp, vp, vp, vp, ctypes.c_float, i64, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -194,6 +196,25 @@ class Indexer:
                                            _stream(dev))
         self._check(st, "dsai_score_topk")
         return out_idx, out_score
+
+    # -- cache write ---------------------------------------------------------
+    def k_norm(self, k_raw: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+               eps: float = 1e-5, out: Optional[torch.Tensor] = None):
+        """k_raw [N,D] bf16, gamma/beta [D] bf16 -> k_normed [N,D] bf16 (LayerNorm with a
+        bias, fp32 inside); `out` may be k_raw itself."""
+        N, D = k_raw.shape[0], self.cfg.dim
+        dev = k_raw.device
+        _need(k_raw, "k_raw", torch.bfloat16, (N, D))
+        _need(gamma, "gamma", torch.bfloat16, (D,), dev)
+        _need(beta, "beta", torch.bfloat16, (D,), dev)
+        if out is None:
+            out = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+        _need(out, "out", torch.bfloat16, (N, D), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_k_norm(self._h, _ptr(k_raw), _ptr(gamma), _ptr(beta),
+                                       float(eps), N, _ptr(out), _stream(dev))
+        self._check(st, "dsai_k_norm")
+        return out
 
     # -- pooled decode pipeline ---------------------------------------------
     def pool_count(self, N: int) -> int:

@@ -4,6 +4,8 @@
 
 #include <new>
 
+#include <cmath>
+
 #include "internal.h"
 
 struct dsai_context {
@@ -241,6 +243,23 @@ int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* toke
   a.pool_ids = pool_ids; a.Q = Q; a.sel = select_k(h->cfg); a.KP = h->cfg.kpool;
   a.first_key = h->cfg.first_key; a.tokens = tokens;
   return hip_status(h, dsai::launch_expand(a, static_cast<hipStream_t>(stream)));
+}
+
+int dsai_k_norm(dsai_handle h, const void* k_raw, const void* gamma, const void* beta, float eps,
+                int64_t N, void* k_normed, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (N < 0 || !(eps > 0.0f) || !(eps < INFINITY)) return DSAI_ERR_INVALID_ARG;
+  if (N == 0) return DSAI_OK;
+  if (!k_raw || !gamma || !beta || !k_normed) return DSAI_ERR_NULLPTR;
+  if (!aligned(k_raw) || !aligned(gamma) || !aligned(beta) || !aligned(k_normed))
+    return DSAI_ERR_INVALID_ARG;
+  dsai::KNormArgs a;
+  a.x = static_cast<const uint16_t*>(k_raw);
+  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.beta = static_cast<const uint16_t*>(beta);
+  a.eps = eps; a.n = N; a.D = h->cfg.dim;
+  a.y = static_cast<uint16_t*>(k_normed);
+  return hip_status(h, dsai::launch_k_norm(a, static_cast<hipStream_t>(stream)));
 }
 
 int dsai_sort_rows(dsai_handle h, int32_t* idx, float* score, int64_t rows, int k, void* stream) {

@@ -93,6 +93,18 @@ struct ScoreAtArgs {
   float* out_score;    // [B, S, n]
 };
 hipError_t launch_score_at(const ScoreAtArgs& a, hipStream_t st);
+
+// k_norm: LayerNorm with a bias over rows of D channels (k_norm.hip).
+struct KNormArgs {
+  const uint16_t* x;      // [n, D] bf16
+  const uint16_t* gamma;  // [D] bf16
+  const uint16_t* beta;   // [D] bf16
+  float eps;
+  int64_t n;
+  int D;
+  uint16_t* y;            // [n, D] bf16
+};
+hipError_t launch_k_norm(const KNormArgs& a, hipStream_t st);
 // Stable sort of `rows` rows of `topk` (idx, score) pairs, each in ascending
 // index order with -1 padding at the tail, into score-descending order.
 hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st);

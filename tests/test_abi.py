@@ -136,6 +136,28 @@ def test_score_topk_argument_errors(lib):
     lib.dsai_destroy(h)
 
 
+def test_k_norm_argument_errors(lib):
+    st, h = _create(lib)
+    assert st == OK
+    f = lib.dsai_k_norm
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_float, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    call = lambda N=8, eps=1e-5, x=FAKE, g=FAKE, b=FAKE, y=FAKE: f(h, x, g, b, eps, N, y, None)
+    assert call(N=-1) == INVALID
+    assert call(eps=0.0) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(eps=float("inf")) == INVALID
+    assert call(N=0) == OK                       # nothing launched
+    assert call(x=None) == NULLPTR
+    assert call(g=None) == NULLPTR
+    assert call(b=None) == NULLPTR
+    assert call(y=None) == NULLPTR
+    assert call(y=ctypes.c_void_p(0x10008)) == INVALID  # misaligned
+    assert f(None, FAKE, FAKE, FAKE, 1e-5, 8, FAKE, None) == NULLPTR
+    lib.dsai_destroy(h)
+
+
 def test_pooled_argument_errors(lib):
     st, h = _create(lib, kpool=4, index_topk=512, first_key=3)
     assert st == OK
