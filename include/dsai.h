@@ -126,7 +126,12 @@ int dsai_last_hip_error(dsai_handle h);
  * (DSAI_ERR_INVALID_ARG otherwise); index_k must span < 4 GiB
  * (Skv * B * D * 2 bytes; DSAI_ERR_UNSUPPORTED otherwise).  Query rows are
  * processed in launches of cfg.chunk_rows rows (all rows if 0); no scratch
- * memory is used.
+ * memory is used.  With more than one chunk, consecutive chunks run on two
+ * streams the handle owns, forked from `stream` (after the work already on
+ * it) and joined back to it (work enqueued on `stream` later waits for every
+ * chunk), so that two chunks are in flight; the streams and their events
+ * are created at the first such call on a device and released by
+ * dsai_destroy.
  *
  * Scores at supplied indices (the page's optional topk_indices
  * [batch, seqlen, topk] int32, and pytorch_extract_topk_scores): when

@@ -13,6 +13,13 @@ struct dsai_context {
   int last_hip_error = 0;
   int device = -1;           // device the cached limits belong to
   size_t lds_limit = 0;      // max LDS bytes per workgroup on that device
+  // Two streams (default priority) on which consecutive row chunks run,
+  // forked from and joined back to the caller's stream, so that a chunk of
+  // too few rows to fill the GPU on its own overlaps the next one.
+  int side_device = -1;
+  hipStream_t side[2] = {nullptr, nullptr};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[2] = {nullptr, nullptr};
 };
 
 namespace {
@@ -60,6 +67,58 @@ hipError_t device_limits(dsai_context* h) {
 
 constexpr int64_t kI32 = 2147483647;
 
+void release_side(dsai_context* h) {
+  for (int i = 0; i < 2; ++i) {
+    if (h->join[i]) (void)hipEventDestroy(h->join[i]);
+    if (h->side[i]) (void)hipStreamDestroy(h->side[i]);
+    h->join[i] = nullptr;
+    h->side[i] = nullptr;
+  }
+  if (h->fork) (void)hipEventDestroy(h->fork);
+  h->fork = nullptr;
+  h->side_device = -1;
+}
+
+hipError_t ensure_side(dsai_context* h) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (h->side_device == dev) return hipSuccess;
+  release_side(h);
+  for (int i = 0; i < 2; ++i) {
+    if ((e = hipStreamCreateWithFlags(&h->side[i], hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&h->join[i], hipEventDisableTiming)) != hipSuccess) {
+      release_side(h);
+      return e;
+    }
+  }
+  if ((e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming)) != hipSuccess) {
+    release_side(h);
+    return e;
+  }
+  h->side_device = dev;
+  return hipSuccess;
+}
+
+// launch(sa, sb) on the two side streams, ordered after the work already on
+// `st` and before anything enqueued on `st` afterwards.  The join is
+// recorded even when the launch fails, so `st` never runs ahead of work
+// that did start.
+template <class F>
+hipError_t on_side_streams(dsai_context* h, hipStream_t st, F launch) {
+  hipError_t e = ensure_side(h);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(h->fork, st)) != hipSuccess) return e;
+  for (int i = 0; i < 2; ++i)
+    if ((e = hipStreamWaitEvent(h->side[i], h->fork, 0)) != hipSuccess) return e;
+  const hipError_t le = launch(h->side[0], h->side[1]);
+  for (int i = 0; i < 2; ++i) {
+    if ((e = hipEventRecord(h->join[i], h->side[i])) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(st, h->join[i], 0)) != hipSuccess) return e;
+  }
+  return le;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,6 +136,7 @@ int dsai_create(const dsai_config* cfg, dsai_handle* out) {
 }
 
 int dsai_destroy(dsai_handle h) {
+  if (h) release_side(h);
   delete h;
   return DSAI_OK;
 }
@@ -120,7 +180,12 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
     a.chunk_rows = h->cfg.chunk_rows;
     a.sup = topk_indices;
     a.out_idx = out_idx; a.out_score = out_score;
-    return hip_status(h, dsai::launch_score_at(a, static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.chunk_rows > 0 && S > a.chunk_rows)
+      return hip_status(h, on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
+                          return dsai::launch_score_at(a, s0, s1);
+                        }));
+    return hip_status(h, dsai::launch_score_at(a, st, nullptr));
   }
   // keys of one batch are addressed with 32-bit byte offsets
   if (Skv * B * h->cfg.dim * 2 > (int64_t)0xFFFFFFFF) return DSAI_ERR_UNSUPPORTED;
@@ -143,7 +208,17 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   a.chunk_rows = h->cfg.chunk_rows;
   a.sort = h->cfg.order == DSAI_ORDER_SCORE;
   a.out_idx = out_idx; a.out_score = out_score;
-  return hip_status(h, dsai::launch_score_topk(a, plan, static_cast<hipStream_t>(stream)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t le;
+  if (a.chunk_rows > 0 && S > a.chunk_rows)
+    le = on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
+      return dsai::launch_score_topk(a, plan, s0, s1);
+    });
+  else
+    le = dsai::launch_score_topk(a, plan, st, nullptr);
+  if (le != hipSuccess) return hip_status(h, le);
+  if (a.sort) le = dsai::launch_sort_rows(out_idx, out_score, B * S, topk, st);
+  return hip_status(h, le);
 }
 
 int dsai_pool_count(dsai_handle h, int64_t N, int64_t* P) {

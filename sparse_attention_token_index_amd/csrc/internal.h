@@ -78,7 +78,11 @@ struct TopkRowsPlan {
 ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t lds_limit);
 TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit);
 
-hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st);
+// Chunk launches (ScoreTopkArgs::chunk_rows) alternate between st and st2
+// when st2 is not null (two chunks in flight); the score-order pass is the
+// caller's (launch_sort_rows on the joined stream).
+hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,
+                             hipStream_t st2);
 
 // Scores at supplied key indices (score_at.hip).
 struct ScoreAtArgs {
@@ -92,7 +96,7 @@ struct ScoreAtArgs {
   int32_t* out_idx;    // [B, S, n]
   float* out_score;    // [B, S, n]
 };
-hipError_t launch_score_at(const ScoreAtArgs& a, hipStream_t st);
+hipError_t launch_score_at(const ScoreAtArgs& a, hipStream_t st, hipStream_t st2);
 
 // k_norm: LayerNorm with a bias over rows of D channels (k_norm.hip).
 struct KNormArgs {

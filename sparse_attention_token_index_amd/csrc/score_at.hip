@@ -83,14 +83,15 @@ score_at_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 template <int HP, int D>
-static hipError_t launch_at_t(const ScoreAtArgs& a, hipStream_t st) {
+static hipError_t launch_at_t(const ScoreAtArgs& a, hipStream_t st, hipStream_t st2) {
   const int64_t chunk = a.chunk_rows > 0 ? a.chunk_rows : a.S;
-  for (int64_t r0 = 0; r0 < a.S; r0 += chunk) {
+  int64_t ci = 0;
+  for (int64_t r0 = 0; r0 < a.S; r0 += chunk, ++ci) {
     const int64_t r1 = (r0 + chunk < a.S) ? r0 + chunk : a.S;
     const int64_t blocks = ((r1 - r0) * a.B + kAtWaves - 1) / kAtWaves;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL((score_at_kernel<HP, D>), dim3((unsigned)blocks), dim3(kAtWaves * 64), 0,
-                       st, a.q, a.k, a.w, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio, a.n,
+                       (st2 && (ci & 1)) ? st2 : st, a.q, a.k, a.w, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio, a.n,
                        (int)r0, (int)r1, a.sup, a.out_idx, a.out_score);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -98,11 +99,11 @@ static hipError_t launch_at_t(const ScoreAtArgs& a, hipStream_t st) {
   return hipSuccess;
 }
 
-hipError_t launch_score_at(const ScoreAtArgs& a, hipStream_t st) {
+hipError_t launch_score_at(const ScoreAtArgs& a, hipStream_t st, hipStream_t st2) {
   if (a.S <= 0 || a.B <= 0 || a.n <= 0) return hipSuccess;
   const int HP = a.H <= 32 ? 32 : 64;
 #define DSAI_CASE(hp, d) \
-  if (HP == hp && a.D == d) return launch_at_t<hp, d>(a, st);
+  if (HP == hp && a.D == d) return launch_at_t<hp, d>(a, st, st2);
   DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
   DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)
 #undef DSAI_CASE

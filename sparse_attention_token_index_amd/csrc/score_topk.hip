@@ -330,42 +330,47 @@ ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t l
 }
 
 template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
-static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
+static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,
+                           hipStream_t st2) {
   auto kern = score_select_kernel<HP, D, NW, NR, DENSE, IdxT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)p.lds_bytes);
   if (e != hipSuccess) return e;
   const int R = p.rows_per_block;
   const int64_t chunk = a.chunk_rows > 0 ? a.chunk_rows : a.S;
-  for (int64_t r0 = 0; r0 < a.S; r0 += chunk) {
+  int64_t ci = 0;
+  for (int64_t r0 = 0; r0 < a.S; r0 += chunk, ++ci) {
     const int64_t r1 = (r0 + chunk < a.S) ? r0 + chunk : a.S;
     const int64_t blocks = ((r1 - r0 + R - 1) / R) * a.B;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), p.lds_bytes, st, a.q, a.k,
-                       a.w, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio, a.topk, (int)r0,
-                       (int)r1, R, p.cap, a.out_idx, a.out_score);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), p.lds_bytes,
+                       (st2 && (ci & 1)) ? st2 : st, a.q, a.k, a.w, (int)a.S, (int)a.Skv,
+                       (int)a.B, a.H, a.ratio, a.topk, (int)r0, (int)r1, R, p.cap, a.out_idx,
+                       a.out_score);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.sort) return launch_sort_rows(a.out_idx, a.out_score, a.B * a.S, a.topk, st);
   return hipSuccess;
 }
 
 template <int HP, int D, int NW, int NR>
-static hipError_t launch_w(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
-  if (p.dense) return launch_t<HP, D, NW, NR, true, uint16_t>(a, p, st);
-  return p.idx_bytes == 2 ? launch_t<HP, D, NW, NR, false, uint16_t>(a, p, st)
-                          : launch_t<HP, D, NW, NR, false, uint32_t>(a, p, st);
+static hipError_t launch_w(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,
+                           hipStream_t st2) {
+  if (p.dense) return launch_t<HP, D, NW, NR, true, uint16_t>(a, p, st, st2);
+  return p.idx_bytes == 2 ? launch_t<HP, D, NW, NR, false, uint16_t>(a, p, st, st2)
+                          : launch_t<HP, D, NW, NR, false, uint32_t>(a, p, st, st2);
 }
 
 template <int HP, int D>
-static hipError_t launch_hd(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
-  return p.waves == 4 ? launch_w<HP, D, 4, 1>(a, p, st) : launch_w<HP, D, 8, 1>(a, p, st);
+static hipError_t launch_hd(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,
+                            hipStream_t st2) {
+  return p.waves == 4 ? launch_w<HP, D, 4, 1>(a, p, st, st2) : launch_w<HP, D, 8, 1>(a, p, st, st2);
 }
 
-hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st) {
+hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,
+                             hipStream_t st2) {
   const int HP = a.H <= 32 ? 32 : 64;
 #define DSAI_CASE(hp, d) \
-  if (HP == hp && a.D == d) return launch_hd<hp, d>(a, p, st);
+  if (HP == hp && a.D == d) return launch_hd<hp, d>(a, p, st, st2);
   DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
   DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)
 #undef DSAI_CASE
