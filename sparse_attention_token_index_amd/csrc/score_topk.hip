@@ -34,6 +34,9 @@ namespace dsai {
 // side list); they live in the tile buffers once the key loop is done.
 constexpr int kDenseScratch = 2048;
 
+// Static LDS of the filter-store kernels (cut_flag), rounded up.
+constexpr int64_t kStaticLds = 128;
+
 template <int D, int NW>
 struct ScoreLds {
   static constexpr int kTileBytes = TileGeom<D>::kTileBytes;
@@ -50,6 +53,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   extern __shared__ __align__(16) char smem_raw[];
+  __shared__ uint32_t cut_flag[2][8];  // filter store: per-wavefront cut requests
   lds_char* smem = (lds_char*)smem_raw;
   using G = TileGeom<D>;
   using L = ScoreLds<D, NW>;
@@ -109,144 +113,131 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   ld.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
 
   // Keys stream in 32-key tiles through two LDS buffers, one barrier per
-  // tile.  Iteration `it`: write tile it + 1 (loaded from device memory during
-  // the previous iteration) into buffer (it + 1) & 1 and start the loads of
-  // tile it + 2; barrier; run tile it's products on the matrix cores; reduce
-  // and record tile it - 1 (software pipeline: its vector ALU work overlaps
-  // tile it's matrix work).  Buffer (it + 1) & 1 was last read for tile
-  // it - 1, before the previous barrier.
+  // tile.  Every wavefront runs all of the block's tiles, so the
+  // steady-state iteration has no branch: rows shorter than the block's
+  // longest score a few keys past their n_t, which are never recorded;
+  // stores and loads of tiles past the last one move unused data (rows past
+  // the key range read as zero).  Iteration `it`, after the barrier that
+  // publishes tile it + 1:
+  //   fetch tile it + 1's fragments into registers (consumed next
+  //   iteration, so no MFMA waits on LDS);
+  //   record tile it - 2 (cross-half sum; dense: the score goes to its
+  //   slot; filter: appended if it beats the row's threshold, the store cut
+  //   to the top k when full);
+  //   write tile it + 2 (loaded during the previous iteration) into buffer
+  //   it & 1, whose last reader, the fetch of tile it, completed before
+  //   this barrier; start the loads of tile it + 3;
+  //   tile it's products on the matrix cores, interleaved with the head
+  //   reduction of tile it - 1.
+  // Every LDS access is issued early in its iteration, so the next barrier
+  // does not wait on a recent one.
   using Frag = typename Scorer::Frag;
   auto buf = [&](int it) { return smem + (it & 1) * L::kTileBytes; };
-  auto record = [&](int it_rec, const Acc& a) {
+  Acc acc0, acc1;
+  Frag f0, f1;
+  float part[NR];  // reduce_half of the tile awaiting finish()
+  auto finish = [&](int it_rec) {
     const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
-      const float x = sc.reduce(a, rr) + 0.f;  // lanes l and l + 32 hold key l % 32 (-0 -> +0)
-      const uint32_t u = ord_key(x);
+      const float x = Scorer::combine(part[rr]) + 0.f;  // -0 -> +0
+      const bool vis = key < (uint32_t)n_t[rr];
       if constexpr (DENSE) {
         rs[rr].key[key] = __float_as_uint(x);  // lanes l and l + 32 store the same value
-        const bool vis = key < (uint32_t)n_t[rr];
         smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
         smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
       } else {
-        wave_append(rs[rr], count[rr], lane < 32 && key < (uint32_t)n_t[rr] && u > tau[rr], u, key);
-        if (count[rr] > (uint32_t)(cap - G::kTileKeys))
+        const uint32_t u = ord_key(x);
+        wave_append(rs[rr], count[rr], lane < 32 && vis && u > tau[rr], u, key);
+        if (__builtin_expect(count[rr] > (uint32_t)(cap - G::kTileKeys), 0))  // rare: store full
           count[rr] = wave_keep_topk(rs[rr], count[rr], topk, &tau[rr]);
       }
     }
-  };
-  Acc acc0, acc1;
-  if constexpr (DENSE) {
-    // Every wavefront runs all of the block's tiles, so the steady-state
-    // iteration has no branch: rows shorter than the block's longest score a
-    // few keys past their n_t, whose slots are never read; stores and loads
-    // of tiles past the last one move unused data (rows past the key range
-    // read as zero).  Iteration `it`, after the barrier that publishes tile
-    // it + 1:
-    //   fetch tile it + 1's fragments into registers (consumed next
-    //   iteration, so no MFMA waits on LDS);
-    //   finish tile it - 2 (cross-half sum, order key, store to the row);
-    //   write tile it + 2 (loaded during the previous iteration) into buffer
-    //   it & 1, whose last reader, the fetch of tile it, completed before
-    //   this barrier; start the loads of tile it + 3;
-    //   tile it's products on the matrix cores, interleaved with the head
-    //   reduction of tile it - 1.
-    // Every LDS access is issued early in its iteration, so the next
-    // barrier does not wait on a recent one.
-    Frag f0, f1;
-    float part[NR];  // reduce_half of the tile awaiting finish()
-    auto finish = [&](int it_rec) {
-      const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
+    if constexpr (!DENSE) {
+      // Ask for a block-wide cut once a store could not take two more tiles
+      // (read by every wavefront after the next barrier).
+      bool need = false;
 #pragma unroll
-      for (int rr = 0; rr < NR; ++rr) {
-        const float x = Scorer::combine(part[rr]) + 0.f;  // -0 -> +0
-        rs[rr].key[key] = __float_as_uint(x);  // lanes l and l + 32 store the same value
-        const bool vis = key < (uint32_t)n_t[rr];
-        smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
-        smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
-      }
-    };
-    auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
-                    bool red) {
-      __syncthreads();
-      // Scheduling fences: the compiler may not hoist the next iteration's
-      // products above this barrier or sink this one's below the next, which
-      // would put a reduction right behind the products it reads.
-      __builtin_amdgcn_sched_barrier(0);
+      for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - 2 * G::kTileKeys);
+      if (lane == 0) cut_flag[it_rec & 1][wave] = need ? 1u : 0u;
+    }
+  };
+  // Filter store: cut every wavefront's rows to the top k together when any
+  // of them asked for it after the previous barrier, so the block's waves
+  // spend one cut's time at the next barrier rather than one after another.
+  // The flags alternate between two slots, so a wavefront's next request
+  // never overwrites one that another wavefront has yet to read.
+  auto cut_together = [&](int it_req) {
+    uint32_t any = 0u;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) any |= cut_flag[it_req & 1][w2];
+    if (any) {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+        if (count[rr] > (uint32_t)topk) count[rr] = wave_keep_topk(rs[rr], count[rr], topk, &tau[rr]);
+    }
+  };
+  auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
+                  bool red) {
+    __syncthreads();
+    // Scheduling fences: the compiler may not hoist the next iteration's
+    // products above this barrier or sink this one's below the next, which
+    // would put a reduction right behind the products it reads.
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DENSE) {
       sc.fetch(buf(it + 1), fnext);
       if (fin) finish(it - 2);
       ld.store(buf(it + 2));
       ld.load((uint32_t)(it + 3) * G::kTileKeys);
       sc.mma(fcur, cur);
-      if (red) {
-#pragma unroll
-        for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if (ntiles > 0) {
-      ld.load(0u);
-      ld.store(buf(0));
-      ld.load((uint32_t)G::kTileKeys);
-      ld.store(buf(1));
-      ld.load((uint32_t)(2 * G::kTileKeys));
-      __syncthreads();
-      sc.fetch(buf(0), f0);
-      step(0, f0, f1, acc0, acc1, false, false);
-      int it = 1;
-      if (ntiles > 1) {
-        step(1, f1, f0, acc1, acc0, false, true);
-        for (it = 2; it + 1 < ntiles; it += 2) {
-          step(it, f0, f1, acc0, acc1, true, true);
-          step(it + 1, f1, f0, acc1, acc0, true, true);
-        }
-        if (it < ntiles) step(it, f0, f1, acc0, acc1, true, true);
-        finish(ntiles - 2);
-      }
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-        part[rr] = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, rr);
-      finish(ntiles - 1);
+    } else {
+      // The filter store's cut is a call: one fragment buffer (fcur, refilled
+      // with tile it + 1 once tile it's products have read it) keeps the
+      // registers that must survive it within the budget.
+      if (it >= 3) cut_together(it - 3);  // requests of the previous iteration's finish
+      if (fin) finish(it - 2);
+      ld.store(buf(it + 2));
+      ld.load((uint32_t)(it + 3) * G::kTileKeys);
+      sc.mma(fcur, cur);
     }
+    if (red) {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
+    }
+    if constexpr (!DENSE) sc.fetch(buf(it + 1), fcur);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (ntiles > 0) {
+    ld.load(0u);
+    ld.store(buf(0));
+    ld.load((uint32_t)G::kTileKeys);
+    ld.store(buf(1));
+    ld.load((uint32_t)(2 * G::kTileKeys));
+    __syncthreads();
+    sc.fetch(buf(0), f0);
+    // dense: fragments alternate between f0 and f1; filter: f0 only
+    Frag& fb = DENSE ? f1 : f0;
+    step(0, f0, fb, acc0, acc1, false, false);
+    int it = 1;
+    if (ntiles > 1) {
+      step(1, fb, f0, acc1, acc0, false, true);
+      for (it = 2; it + 1 < ntiles; it += 2) {
+        step(it, f0, fb, acc0, acc1, true, true);
+        step(it + 1, fb, f0, acc1, acc0, true, true);
+      }
+      if (it < ntiles) step(it, f0, fb, acc0, acc1, true, true);
+      finish(ntiles - 2);
+    }
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+      part[rr] = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, rr);
+    finish(ntiles - 1);
+  }
+  if constexpr (DENSE) {
     // The final select's scratch lies in the tile buffers, which the last
     // iteration of a slower wavefront may still be writing (its store of the
     // unused tile past the end).
     __syncthreads();
-  } else {
-    // The wave's tiles are a prefix [0, nt_w) of the block's.
-    const int nt_w = (n_w + G::kTileKeys - 1) / G::kTileKeys;  // 0 when inactive
-    // Here tile it's products come first and tile it + 1 is written after
-    // them, so buffer (it + 1) & 1 (read for tile it - 1 before the previous
-    // barrier) is free.
-    auto step = [&](int it, Acc& cur, const Acc& old) {
-      if (it < nt_w) {
-        sc.mma(buf(it), cur);
-        record(it - 1, old);
-      } else if (it == nt_w) {
-        record(it - 1, old);
-      }
-      if (it + 1 < ntiles) ld.store(buf(it + 1));
-      if (it + 2 < ntiles) ld.load((uint32_t)(it + 2) * G::kTileKeys);
-      __syncthreads();
-    };
-    if (ntiles > 0) {
-      ld.load(0u);
-      ld.store(buf(0));
-      if (ntiles > 1) ld.load((uint32_t)G::kTileKeys);
-      __syncthreads();
-      if (nt_w > 0) sc.mma(buf(0), acc0);
-      if (1 < ntiles) ld.store(buf(1));
-      if (2 < ntiles) ld.load((uint32_t)(2 * G::kTileKeys));
-      __syncthreads();
-    }
-    for (int it = 1; it < ntiles; it += 2) {
-      step(it, acc1, acc0);
-      if (it + 1 < ntiles) step(it + 1, acc0, acc1);
-    }
-    if (nt_w > 0 && nt_w == ntiles) {
-      if ((ntiles - 1) & 1) record(ntiles - 1, acc1);
-      else record(ntiles - 1, acc0);
-    }
   }
 
 #pragma unroll
@@ -320,12 +311,14 @@ ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t l
   ScoreSelectPlan p{};
   const int64_t full = (int64_t)lds_limit;
   const int64_t half = full / 2;
+  // the filter kernels' static LDS (cut requests) comes out of their budget
+  const int64_t full_f = full - kStaticLds, half_f = half - kStaticLds;
   (void)HP;
   if (plan_dense(D, 4, 1, Skv, half, &p)) return p;
   if (plan_dense(D, 8, 1, Skv, full, &p)) return p;
-  if (plan_filter(D, 4, 1, topk, Skv, half, 4, &p)) return p;
-  if (plan_filter(D, 8, 1, topk, Skv, full, 8, &p)) return p;
-  if (plan_filter(D, 8, 1, topk, Skv, full, 1, &p)) return p;
+  if (plan_filter(D, 4, 1, topk, Skv, half_f, 4, &p)) return p;
+  if (plan_filter(D, 8, 1, topk, Skv, full_f, 8, &p)) return p;
+  if (plan_filter(D, 8, 1, topk, Skv, full_f, 1, &p)) return p;
   return ScoreSelectPlan{};  // rows_per_block == 0: does not fit
 }
 
