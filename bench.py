@@ -384,21 +384,23 @@ def main():
     med = {s: float(np.median(v)) for s, v in per.items()}
 
     # scores at supplied indices (the topk_indices form; not part of the
-    # step): the step's own top-k rows rescored
-    at_ix = dsai.Indexer(heads=case.H, dim=case.D, chunk_rows=case.chunk_rows)
-    at_idx, at_sc = torch.empty_like(out_idx), torch.empty_like(out_sc)
-    for _ in range(2):
-        at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
-                         out_idx=at_idx, out_score=at_sc)
+    # step): the step's own top-k rows rescored (prefill workload only)
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record()
-    for _ in range(args.steps):
-        at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
-                         out_idx=at_idx, out_score=at_sc)
-    a1.record()
-    torch.cuda.synchronize()
-    at_ms = a0.elapsed_time(a1) / args.steps
-    at_flops = 2.0 * case.H * case.D * selected_entries(case)
+    at_ms = at_flops = None
+    if case.name == "prefill":
+        at_ix = dsai.Indexer(heads=case.H, dim=case.D, chunk_rows=case.chunk_rows)
+        at_idx, at_sc = torch.empty_like(out_idx), torch.empty_like(out_sc)
+        for _ in range(2):
+            at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
+                             out_idx=at_idx, out_score=at_sc)
+        a0.record()
+        for _ in range(args.steps):
+            at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
+                             out_idx=at_idx, out_score=at_sc)
+        a1.record()
+        torch.cuda.synchronize()
+        at_ms = a0.elapsed_time(a1) / args.steps
+        at_flops = 2.0 * case.H * case.D * selected_entries(case)
 
     # the cache write's k_norm (LayerNorm with a bias) over the pooled
     # workload's 65536 cache rows (not part of the step)
@@ -462,7 +464,7 @@ def main():
             "expand_ms": avg["expand"], "expand_GBps": eb / (avg["expand"] * 1e-3) / 1e9,
             "expand_bytes": eb, "wall_s": wall,
             "score_at_indices_ms": at_ms,
-            "score_at_indices_TFLOPs": at_flops / (at_ms * 1e-3) / 1e12,
+            "score_at_indices_TFLOPs": (at_flops / (at_ms * 1e-3) / 1e12) if at_ms else None,
             "k_norm_ms": ln_ms, "k_norm_GBps": ln_bytes / (ln_ms * 1e-3) / 1e9,
             "k_norm_bytes": ln_bytes,
         },
