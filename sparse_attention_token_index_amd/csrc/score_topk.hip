@@ -316,8 +316,8 @@ ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t l
   (void)HP;
   if (plan_dense(D, 4, 1, Skv, half, &p)) return p;
   if (plan_dense(D, 8, 1, Skv, full, &p)) return p;
-  if (plan_filter(D, 4, 1, topk, Skv, half_f, 4, &p)) return p;
   if (plan_filter(D, 8, 1, topk, Skv, full_f, 8, &p)) return p;
+  if (plan_filter(D, 4, 1, topk, Skv, half_f, 4, &p)) return p;
   if (plan_filter(D, 8, 1, topk, Skv, full_f, 1, &p)) return p;
   return ScoreSelectPlan{};  // rows_per_block == 0: does not fit
 }
