@@ -15,11 +15,12 @@
 // next tile is written while the current one is read, one barrier per tile).
 // Each wavefront scores the tile on the matrix cores (TileScorer) and records
 // the scores in its LDS row store:
-//   dense   when every visible key fits: the order key of key s goes to slot s
-//           (no indices, no selection until the end);
+//   dense   when every visible key fits: the fp32 score of key s goes to slot
+//           s (no indices, no selection until the end);
 //   filter  otherwise: keys beating the row's running threshold are appended
-//           with their index; when the store fills, a radix select cuts it to
-//           the top k and raises the threshold.
+//           (order key and index); when a store fills, every wavefront of
+//           the block cuts its rows to the top k by a radix select together,
+//           which raises the thresholds.
 // After the last tile the row's top k is selected exactly and written in
 // ascending index order; no score goes to device memory.  (Score-descending
 // order is produced by the row sort.)  Blocks are numbered heaviest (largest
@@ -301,12 +302,12 @@ bool plan_filter(int D, int NW, int NR, int topk, int64_t Skv, int64_t budget, i
 
 }  // namespace
 
-// Launch geometry, in order of preference.  Heads padded to 64: four
-// wavefronts of two rows (four accumulator chains per wavefront keep the
-// matrix core busy with one wavefront per SIMD); 32: eight wavefronts of one
-// row.  One 8-row block per CU with a dense store (one slot per visible key),
-// else a filter store (the top k plus at least 8 tiles of candidates), then
-// fewer rows per block.
+// Launch geometry, in order of preference (one wavefront per row):
+// dense store (one slot per visible key) with four wavefronts and two blocks
+// per CU, then with eight wavefronts and one block per CU; filter store (the
+// top k plus at least 8 tiles of candidates) with eight wavefronts and one
+// block per CU (the larger stores need half the cuts), then four, then fewer
+// rows per block.
 ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t lds_limit) {
   ScoreSelectPlan p{};
   const int64_t full = (int64_t)lds_limit;
