@@ -231,6 +231,26 @@ def test_empty_and_degenerate_shapes(dsai):
         assert np.all(gsc[0, t, :m] == 0.0)
 
 
+@pytest.mark.parametrize("heads,dim", [(64, 128), (20, 64)])
+def test_filter_store_block_cuts(dsai, heads, dim):
+    """Rows longer than any dense store (Skv = 6000 keys at D = 128) with
+    topk = 2048: the filter store fills and every block cuts its rows
+    together several times.  Sampled rows keep parity with the oracle, and a
+    second launch gives the same bits (the cut requests pass between
+    wavefronts through LDS)."""
+    case = SY.IndexerCase(f"filter_cuts_h{heads}d{dim}", B=1, S=6000, Skv=6000, H=heads, D=dim,
+                          compress_ratio=1, topk=2048, w_var=1 / heads, seed=41)
+    log(f"[gpu] filter-store cuts {case.name}")
+    inp = SY.indexer_inputs(case)
+    first = run_gpu(dsai, case, inp)
+    again = run_gpu(dsai, case, inp)
+    assert np.array_equal(first[0], again[0])
+    assert np.array_equal(first[1].view(np.uint32), again[1].view(np.uint32))
+    rows = [0, 2047, 2048, 3001, 4799, 5998, 5999]
+    _, _, full = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
+    compare(case, first[0], first[1], rows, full)
+
+
 def test_filter_store_wide_indices(dsai):
     """Skv > 65536: the filtering store keeps 32-bit indices."""
     case = SY.IndexerCase("wide_idx", B=1, S=70000, Skv=70000, H=4, D=32, compress_ratio=1,
