@@ -18,6 +18,7 @@ from .indexer import (  # noqa: F401
     select_topk,
     score_topk,
     scores_at_indices,
+    indexer_backward,
     round_to_bf16,
     k_norm,
     pool_count,

@@ -39,6 +39,9 @@ Readings where the pages are silent (each also listed in the design notes):
   select_k = index_topk / KP pools per row, ties to the lower pool id.
 * expand: slot i*KP + j of a row holds first_key + p_i*KP + j for the i-th
   selected pool p_i, and -1 where the pool id is -1.
+* Backward (V4IndexerFunction.backward(grad_scores, grad_indices)): the
+  gradient of the returned scores only (indices are integers); ReLU's
+  derivative is taken as 0 at 0; unusable entries (score -inf) get none.
 """
 from __future__ import annotations
 
@@ -184,6 +187,109 @@ def scores_at_indices(q: np.ndarray, k: np.ndarray, w: np.ndarray, compress_rati
                 vals[b, i, ok] = head_scores(q[i, b], k[s[ok], b], w[i, b])
                 idx[b, i, ok] = s[ok]
     return idx, vals
+
+
+def _pair_dots(qp: np.ndarray, kp: np.ndarray) -> np.ndarray:
+    """Per entry p and head h: d[p, h] = q_p[h, :] . k_p[:] (qp [P, H, D], kp [P, D])."""
+    return np.einsum("phd,pd->ph", qp, kp)
+
+
+def _gate_coef(g: np.ndarray, wp: np.ndarray, on: np.ndarray) -> np.ndarray:
+    """dI/dd_h times the incoming gradient: g[p] * w[p, h] * gate[p, h]."""
+    return g[:, None] * wp * on
+
+
+def _relu_gate(d: np.ndarray) -> np.ndarray:
+    """Derivative of ReLU used by the backward: 1 where d > 0, else 0 (the
+    subgradient 0 at d == 0)."""
+    return (d > 0).astype(np.float64)
+
+
+def _usable_entries(sup: np.ndarray, positions, Skv: int, compress_ratio: int, keys=None):
+    """(b, i, j, s) of every usable entry of supplied indices sup [B, R, n]:
+    row i of the batch-b block holds query position positions[i], and entry
+    j names key s with 0 <= s < n_t (optionally also s in `keys`)."""
+    B, R, n = sup.shape
+    n_t = np.array([visible_keys(t, Skv, compress_ratio) for t in positions], dtype=np.int64)
+    s = sup.astype(np.int64)
+    ok = _usable_keys(s, n_t[None, :, None])
+    if keys is not None:
+        ok &= np.isin(s, np.asarray(list(keys), dtype=np.int64))
+    b, i, j = np.nonzero(ok)
+    return b, i, j, s[b, i, j]
+
+
+def indexer_backward(q: np.ndarray, k: np.ndarray, w: np.ndarray, compress_ratio: int,
+                     topk_indices: np.ndarray, grad_scores: np.ndarray, rows=None, keys=None,
+                     with_bounds=False, chunk=512):
+    """Gradients of the selected index scores (V4IndexerFunction.backward,
+    whose inputs are grad_scores [batch, seqlen, topk] and grad_indices; the
+    returned indices are integers and carry no gradient, so only grad_scores
+    flows back).
+
+    The forward value of usable entry j of row (b, t), key s = idx[b, t, j],
+    is I = sum_h w[t,b,h] * ReLU(d_h) with d_h = q[t,b,h,:] . k[s,b,:]; an
+    unusable entry (-1, masked or out of range) is the constant -inf and has
+    no gradient.  With g = grad_scores[b, t, j] each usable entry adds
+
+      grad_w[t,b,h]   += g * ReLU(d_h)
+      grad_q[t,b,h,:] += g * w[t,b,h] * [d_h > 0] * k[s,b,:]
+      grad_k[s,b,:]   += g * sum_h w[t,b,h] * [d_h > 0] * q[t,b,h,:]
+
+    Repeated entries add once each.  q [R, B, H, D], k [Skv, B, D], w [R, B, H],
+    topk_indices / grad_scores [B, R, n]; `rows` lists the query positions of
+    the R rows (else 0..R-1).  `keys` restricts the sums to entries naming
+    those keys: then only grad_k at those key rows is complete.  fp64 on the
+    given values.
+
+    Returns a dict with grad_q, grad_k, grad_w; with_bounds=True adds, per
+    element, the sum of absolute values of its terms (abs_q, abs_k: the
+    products above; abs_w: |g| * sum_d |q_d k_d|), the number of terms summed
+    into each key row (count_k), and band_q / band_k: the absolute terms whose
+    gate is undecided in fp32 arithmetic, |d_h| <= D * 2^-24 * sum_d |q_d k_d|.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    g_all = np.asarray(grad_scores, dtype=np.float64)
+    R, B, H, D = q.shape
+    Skv = k.shape[0]
+    positions = list(range(R)) if rows is None else [int(t) for t in rows]
+    assert len(positions) == R
+    b_e, i_e, j_e, s_e = _usable_entries(np.asarray(topk_indices), positions, Skv,
+                                         compress_ratio, keys)
+    out = {"grad_q": np.zeros((R, B, H, D)), "grad_k": np.zeros((Skv, B, D)),
+           "grad_w": np.zeros((R, B, H))}
+    if with_bounds:
+        for name, shape in (("abs_q", (R, B, H, D)), ("band_q", (R, B, H, D)),
+                            ("abs_k", (Skv, B, D)), ("band_k", (Skv, B, D)),
+                            ("abs_w", (R, B, H))):
+            out[name] = np.zeros(shape)
+        out["count_k"] = np.zeros((Skv, B), dtype=np.int64)
+    for c0 in range(0, b_e.shape[0], chunk):
+        b, i, s = b_e[c0:c0 + chunk], i_e[c0:c0 + chunk], s_e[c0:c0 + chunk]
+        g = g_all[b, i, j_e[c0:c0 + chunk]]                      # [P]
+        qp = q[i, b]                                             # [P, H, D]
+        kp = k[s, b]                                             # [P, D]
+        wp = w[i, b]                                             # [P, H]
+        d = _pair_dots(qp, kp)                                   # [P, H]
+        on = _relu_gate(d)
+        np.add.at(out["grad_w"], (i, b), g[:, None] * _relu(d))
+        coef = _gate_coef(g, wp, on)                             # [P, H]
+        np.add.at(out["grad_q"], (i, b), coef[:, :, None] * kp[:, None, :])
+        np.add.at(out["grad_k"], (s, b), np.einsum("ph,phd->pd", coef, qp))
+        if with_bounds:
+            mag = np.einsum("phd,pd->ph", np.abs(qp), np.abs(kp))  # sum_d |q_d k_d|
+            undecided = np.abs(d) <= D * 2.0 ** -24 * mag
+            acoef = np.abs(g[:, None] * wp)
+            np.add.at(out["abs_w"], (i, b), np.abs(g)[:, None] * mag)
+            np.add.at(out["abs_q"], (i, b), (acoef * on)[:, :, None] * np.abs(kp)[:, None, :])
+            np.add.at(out["band_q"], (i, b),
+                      (acoef * undecided)[:, :, None] * np.abs(kp)[:, None, :])
+            np.add.at(out["abs_k"], (s, b), np.einsum("ph,phd->pd", acoef * on, np.abs(qp)))
+            np.add.at(out["band_k"], (s, b), np.einsum("ph,phd->pd", acoef * undecided, np.abs(qp)))
+            np.add.at(out["count_k"], (s, b), 1)
+    return out
 
 
 # ---------------------------------------------------------------------------

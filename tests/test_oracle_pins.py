@@ -577,6 +577,162 @@ def test_k_norm_properties():
 
 
 # ---------------------------------------------------------------------------
+# Backward (gradients of the selected scores)
+# ---------------------------------------------------------------------------
+
+_G_SET = np.array([-2.0, -1.0, -0.5, 0.25, 0.5, 1.0, 1.5, 3.0])
+
+
+def _selected_sum(q, k, w, r, sup, g):
+    """sum over usable entries of g * (score at the entry), in fp64."""
+    idx, vals = oracle.scores_at_indices(q, k, w, r, sup)
+    ok = idx >= 0
+    return float(np.sum(g[ok] * vals[ok]))
+
+
+def _backward_case(rng, S, Skv, B, H, D, n):
+    """Short-mantissa inputs where no usable (entry, head) dot product is 0,
+    so the score is differentiable at the point (resampled until so)."""
+    while True:
+        q, k, w = _tiny_case(rng, S, Skv, B, H, D)
+        r = int(rng.integers(1, 3))
+        sup = rng.integers(-1, Skv + 1, size=(B, S, n))
+        sup[:, :, 0] = rng.integers(0, Skv, size=(B, S))   # repeated entries are likely too
+        g = rng.choice(_G_SET, (B, S, n))
+        d = np.einsum("tbhd,sbd->btsh", q, k)
+        zero = False
+        for b in range(B):
+            for t in range(S):
+                for s in sup[b, t]:
+                    if 0 <= s < oracle.visible_keys(t, Skv, r) and np.any(d[b, t, s] == 0):
+                        zero = True
+        if not zero:
+            return q, k, w, r, sup, g
+
+
+def check_backward_finite_differences(n_cases=6, seed=21):
+    """Every input coordinate's gradient equals the central difference of
+    the forward selected-score sum, exactly: the score is piecewise linear,
+    the step 2^-12 crosses no kink (dot products are multiples of 2^-6 and
+    move by at most 2^-11), and all fp64 steps are exact on these values."""
+    rng = np.random.default_rng(seed)
+    eps = 2.0 ** -12
+    for c in range(n_cases):
+        S, Skv, B, H, D, n = 5, 5, 2, int(rng.integers(1, 4)), int(rng.integers(2, 5)), 3
+        q, k, w, r, sup, g = _backward_case(rng, S, Skv, B, H, D, n)
+        got = oracle.indexer_backward(q, k, w, r, sup, g)
+        for name, arr in (("grad_q", q), ("grad_k", k), ("grad_w", w)):
+            fd = np.zeros(arr.shape)
+            for pos in np.ndindex(*arr.shape):
+                keep = arr[pos]
+                arr[pos] = keep + eps
+                hi = _selected_sum(q, k, w, r, sup, g)
+                arr[pos] = keep - eps
+                lo = _selected_sum(q, k, w, r, sup, g)
+                arr[pos] = keep
+                fd[pos] = (hi - lo) / (2 * eps)
+            assert np.array_equal(got[name], fd), (c, name, np.argwhere(got[name] != fd)[:4])
+
+
+def check_backward_euler(seed=22):
+    """The score is positively homogeneous of degree 1 in w, in a query row's
+    q and in each key, so by Euler's theorem sum(w * dL/dw) = sum(q * dL/dq)
+    = sum(k * dL/dk) = L for L = sum of g * score over usable entries."""
+    rng = np.random.default_rng(seed)
+    for discrete in (True, False):
+        q, k, w = _tiny_case(rng, 12, 10, 2, 3, 8, discrete=discrete)
+        sup = rng.integers(-1, 11, size=(2, 12, 6))
+        g = rng.standard_normal((2, 12, 6))
+        L = _selected_sum(q, k, w, 2, sup, g)
+        got = oracle.indexer_backward(q, k, w, 2, sup, g)
+        for name, arr in (("grad_w", w), ("grad_q", q), ("grad_k", k)):
+            assert math.isclose(float(np.sum(arr * got[name])), L, rel_tol=1e-12, abs_tol=1e-12), name
+
+
+def check_backward_dense_form(seed=23):
+    """Dense restatement with library matrix products: with G[t, s] the sum
+    of g over row t's usable entries naming s, and per head h D_h = Q_h K^T,
+    M_h = [D_h > 0]:  dQ_h = (w_h * G * M_h) K,  dK = sum_h (w_h * G * M_h)^T Q_h,
+    dw_h = rowsum(G * ReLU(D_h))."""
+    rng = np.random.default_rng(seed)
+    S, Skv, H, D, n, r = 14, 11, 3, 6, 5, 2
+    q, k, w = _tiny_case(rng, S, Skv, 1, H, D, discrete=False)
+    sup = rng.integers(-1, Skv + 1, size=(1, S, n))
+    g = rng.standard_normal((1, S, n))
+    Gm = np.zeros((S, Skv))
+    for t in range(S):
+        for j in range(n):
+            s = int(sup[0, t, j])
+            if 0 <= s < oracle.visible_keys(t, Skv, r):
+                Gm[t, s] += g[0, t, j]
+    Q, K, W = q[:, 0], k[:, 0], w[:, 0]
+    dK = np.zeros((Skv, D))
+    got = oracle.indexer_backward(q, k, w, r, sup, g)
+    for h in range(H):
+        Dh = Q[:, h] @ K.T
+        P = W[:, h:h + 1] * Gm * (Dh > 0)
+        assert np.allclose(got["grad_q"][:, 0, h], P @ K, rtol=1e-12, atol=1e-12), h
+        assert np.allclose(got["grad_w"][:, 0, h], (Gm * np.maximum(Dh, 0)).sum(axis=1),
+                           rtol=1e-12, atol=1e-12), h
+        dK += P.T @ Q[:, h]
+    assert np.allclose(got["grad_k"][:, 0], dK, rtol=1e-12, atol=1e-12)
+
+
+def check_backward_gate_at_zero():
+    """A head whose dot product is exactly 0 passes no gradient to q or k
+    (ReLU's derivative read as 0 there) and adds ReLU(0) = 0 to dL/dw."""
+    q = np.zeros((1, 1, 2, 2))
+    q[0, 0, 0] = [1.0, -1.0]          # head 0: q . k = 0
+    q[0, 0, 1] = [1.0, 1.0]           # head 1: q . k = 2
+    k = np.array([[[1.0, 1.0]]])
+    w = np.array([[[3.0, 0.5]]])
+    got = oracle.indexer_backward(q, k, w, 1, np.array([[[0]]]), np.array([[[2.0]]]))
+    assert np.array_equal(got["grad_q"][0, 0], [[0.0, 0.0], [1.0, 1.0]])
+    assert np.array_equal(got["grad_k"][0, 0], [1.0, 1.0])
+    assert np.array_equal(got["grad_w"][0, 0], [0.0, 4.0])
+
+
+def check_backward_bounds_consistent(seed=24):
+    """abs_* bound |grad_*| and count_k counts the usable entries per key."""
+    rng = np.random.default_rng(seed)
+    q, k, w = _tiny_case(rng, 9, 7, 2, 3, 5, discrete=False)
+    sup = rng.integers(-1, 8, size=(2, 9, 4))
+    g = rng.standard_normal((2, 9, 4))
+    got = oracle.indexer_backward(q, k, w, 1, sup, g, with_bounds=True)
+    for x in ("q", "k"):
+        assert np.all(np.abs(got["grad_" + x]) <= got["abs_" + x] * (1 + 1e-12))
+        assert np.all(got["band_" + x] >= 0)
+    assert np.all(np.abs(got["grad_w"]) <= got["abs_w"] * (1 + 1e-12))
+    cnt = np.zeros((7, 2), dtype=np.int64)
+    for b in range(2):
+        for t in range(9):
+            for s in sup[b, t]:
+                if 0 <= s < oracle.visible_keys(t, 7, 1):
+                    cnt[s, b] += 1
+    assert np.array_equal(got["count_k"], cnt)
+
+
+def test_backward_finite_differences():
+    check_backward_finite_differences()
+
+
+def test_backward_euler():
+    check_backward_euler()
+
+
+def test_backward_dense_form():
+    check_backward_dense_form()
+
+
+def test_backward_gate_at_zero():
+    check_backward_gate_at_zero()
+
+
+def test_backward_bounds_consistent():
+    check_backward_bounds_consistent()
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
@@ -584,7 +740,9 @@ ALL_CHECKS = [check_golden_indexer, check_golden_kpool, check_golden_pooled,
               lambda: check_bruteforce_score_topk(12), check_round_to_bf16,
               check_bruteforce_pooled, check_invariants, check_kpool_invariants, check_expand,
               lambda: check_bruteforce_scores_at_indices(10), check_scores_at_own_topk,
-              check_k_norm_hand_example, check_k_norm_properties]
+              check_k_norm_hand_example, check_k_norm_properties,
+              lambda: check_backward_finite_differences(2), check_backward_euler,
+              check_backward_dense_form, check_backward_gate_at_zero]
 
 
 def _some_check_fails():
@@ -622,6 +780,13 @@ MUTANTS = {
     "plain mean instead of softmax": ("_slot_softmax", lambda lg: np.full(lg.shape, 1.0 / lg.shape[0])),
     "partial trailing pool kept": ("pool_count", lambda N, fk, kp: max(0, -(-(N - fk) // kp))),
     "pooling ignores first_key": ("pool_count", lambda N, fk, kp: max(0, N // kp)),
+    "backward gate is 1 at 0": ("_relu_gate", lambda d: (d >= 0).astype(np.float64)),
+    "backward gate dropped": ("_relu_gate", lambda d: np.ones_like(d)),
+    "backward gate inverted": ("_relu_gate", lambda d: (d < 0).astype(np.float64)),
+    "backward ignores head weights": ("_gate_coef", lambda g, wp, on: g[:, None] * on),
+    "backward drops the incoming gradient": ("_gate_coef", lambda g, wp, on: wp * on),
+    "backward keys from the wrong batch": ("_pair_dots",
+                                           lambda qp, kp: np.einsum("phd,pd->ph", qp, kp[::-1])),
     "round toward zero": ("round_to_bf16", lambda x: (
         np.ldexp(np.trunc(np.ldexp(np.frexp(x)[0], 8)), np.frexp(x)[1] - 8),
         (np.ldexp(np.trunc(np.ldexp(np.frexp(x)[0], 8)), np.frexp(x)[1] - 8)
