@@ -147,6 +147,51 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
                     int compress_ratio, int topk, const int32_t* topk_indices,
                     int32_t* out_idx, float* out_score, void* stream);
 
+/* ---- backward: gradients of the selected scores ------------------------- */
+/* Workspace of dsai_indexer_backward: Skv * B * cfg.dim * 4 bytes (an fp32
+ * accumulator of grad_k).  Host-only. */
+int dsai_backward_workspace_size(dsai_handle h, int64_t Skv, int64_t B, size_t* bytes);
+
+/* The backward of the indexer's autograd function (NeMo AutoModel page
+ * "...deepseek_v4.kernels.tilelang_indexer", V4IndexerFunction.backward with
+ * grad_scores and grad_indices): the gradient of the returned scores with
+ * respect to index_q, index_k and weights.  The indices are integers and
+ * take no gradient.  Entry j of row (b, t), key s = topk_indices[b,t,j], is
+ * usable iff 0 <= s < min(Skv, floor((t+1) / compress_ratio)) (the forward
+ * gives any other entry the constant score -inf); with g =
+ * grad_scores[b,t,j] and d_h = sum_d index_q[t,b,h,d] * index_k[s,b,d], each
+ * usable entry adds
+ *   grad_weights[t,b,h] += g * max(0, d_h)
+ *   grad_q[t,b,h,:]     += g * weights[t,b,h] * (d_h > 0) * index_k[s,b,:]
+ *   grad_k[s,b,:]       += g * sum_h weights[t,b,h] * (d_h > 0) * index_q[t,b,h,:]
+ * (ReLU's derivative is 0 at 0; repeated entries add once each).
+ *
+ *   index_q [S,B,H,D] bf16, index_k [Skv,B,D] bf16, weights [S,B,H] fp32,
+ *   topk_indices [B,S,topk] int32 (e.g. dsai_score_topk's out_idx),
+ *   grad_scores [B,S,topk] fp32;
+ *   grad_q [S,B,H,D] bf16, grad_k [Skv,B,D] bf16, grad_weights [S,B,H] fp32
+ *   written, every element (zero where nothing contributes).
+ *
+ * Arithmetic: d_h in fp32 on the matrix cores (the forward's products); the
+ * gated weight g * weights * (d_h > 0) is rounded to bf16 as the operand of
+ * the two gradient products, which accumulate in fp32; grad_k sums over
+ * rows with fp32 atomic adds (order unspecified) into the workspace;
+ * grad_q and grad_k are rounded to bf16 (nearest even) once at the end.
+ *
+ * S, Skv, B >= 0 (< 2^31, also S*B and Skv*B); compress_ratio >= 1;
+ * 1 <= topk <= DSAI_MAX_TOPK (DSAI_ERR_INVALID_ARG otherwise).  B == 0 or
+ * S == Skv == 0: nothing is written or launched; S == 0 writes grad_k = 0.
+ * workspace: device memory of dsai_backward_workspace_size bytes, 256-byte
+ * aligned (DSAI_ERR_WORKSPACE otherwise), overwritten.  index_q, index_k,
+ * grad_q, grad_k 16-byte aligned; the other arrays 4-byte aligned
+ * (DSAI_ERR_INVALID_ARG otherwise).  All arrays are device memory. */
+int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_k,
+                          const float* weights, const int32_t* topk_indices,
+                          const float* grad_scores, int64_t S, int64_t Skv, int64_t B,
+                          int compress_ratio, int topk, void* grad_q, void* grad_k,
+                          float* grad_weights, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* ---- pooled decode pipeline ("Module glm5next_dsa") -------------------- */
 /* P = floor(max(0, N - first_key) / kpool): the number of pools of a cache
  * of N tokens (pooling starts at first_key; a trailing partial pool is not a

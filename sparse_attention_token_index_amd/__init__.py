@@ -8,7 +8,9 @@ provides device memory and streams.  There is no CPU fallback: without the
 built library, or without tensors on a ROCm GPU, every call raises.
 
 Names follow the C entry points: ``score_topk`` (lightning-indexer score +
-causal/compressed mask + top-k, or scores at supplied indices), ``k_norm``
+causal/compressed mask + top-k, or scores at supplied indices),
+``indexer_backward`` (gradients of the selected scores; ``IndexerFunction``
+is the autograd pairing of the two), ``k_norm``
 (the cache write's LayerNorm), and the pooled decode pipeline
 ``kpool_compress`` -> ``index_scores`` -> ``topk_pools`` -> ``expand``
 (``select`` = ``index_scores`` + ``topk_pools``).
@@ -21,7 +23,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["DsaiError", "Indexer", "load_library", "library_path", "EXPORTS"]
+__all__ = ["DsaiError", "Indexer", "IndexerFunction", "load_library", "library_path", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdsai.so")
@@ -31,7 +33,7 @@ EXPORTS = (
     "dsai_create", "dsai_destroy", "dsai_status_string", "dsai_last_hip_error",
     "dsai_score_topk", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
     "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
-    "dsai_sort_rows", "dsai_k_norm",
+    "dsai_sort_rows", "dsai_k_norm", "dsai_backward_workspace_size", "dsai_indexer_backward",
 )
 
 DSAI_OK = 0
@@ -86,6 +88,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_expand": [vp, vp, i64, vp, vp],
         "dsai_sort_rows": [vp, vp, vp, i64, c_int, vp],
         "dsai_k_norm": [vp, vp, vp, vp, ctypes.c_float, i64, vp, vp],
+        "dsai_backward_workspace_size": [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "dsai_indexer_backward": [vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, vp, vp,
+                                  vp, ctypes.c_size_t, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -196,6 +201,58 @@ class Indexer:
                                            _stream(dev))
         self._check(st, "dsai_score_topk")
         return out_idx, out_score
+
+    # -- backward ------------------------------------------------------------
+    def backward_workspace_size(self, Skv: int, B: int) -> int:
+        n = ctypes.c_size_t()
+        self._check(self._lib.dsai_backward_workspace_size(self._h, int(Skv), int(B), ctypes.byref(n)),
+                    "dsai_backward_workspace_size")
+        return n.value
+
+    def indexer_backward(self, index_q: torch.Tensor, index_k: torch.Tensor,
+                         weights: torch.Tensor, topk_indices: torch.Tensor,
+                         grad_scores: torch.Tensor, compress_ratio: int,
+                         workspace: Optional[torch.Tensor] = None,
+                         grad_q: Optional[torch.Tensor] = None,
+                         grad_k: Optional[torch.Tensor] = None,
+                         grad_weights: Optional[torch.Tensor] = None):
+        """Gradients of the scores at topk_indices [B,S,topk] int32 given their
+        incoming gradient grad_scores [B,S,topk] fp32 -> (grad_q [S,B,H,D] bf16,
+        grad_k [Skv,B,D] bf16, grad_weights [S,B,H] fp32).  Entries that are
+        -1, masked or out of range pass nothing back.  `workspace` (uint8,
+        backward_workspace_size(Skv, B) bytes) is allocated when not given."""
+        S, B = index_q.shape[0], index_q.shape[1]
+        Skv = index_k.shape[0]
+        H, D = self.cfg.heads, self.cfg.dim
+        dev = index_q.device
+        _need(index_q, "index_q", torch.bfloat16, (S, B, H, D))
+        _need(index_k, "index_k", torch.bfloat16, (Skv, B, D), dev)
+        _need(weights, "weights", torch.float32, (S, B, H), dev)
+        if topk_indices.dim() != 3:
+            raise ValueError("topk_indices: expected [B, S, topk]")
+        topk = topk_indices.shape[2]
+        _need(topk_indices, "topk_indices", torch.int32, (B, S, topk), dev)
+        _need(grad_scores, "grad_scores", torch.float32, (B, S, topk), dev)
+        need = self.backward_workspace_size(Skv, B)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        if grad_q is None:
+            grad_q = torch.empty((S, B, H, D), dtype=torch.bfloat16, device=dev)
+        if grad_k is None:
+            grad_k = torch.empty((Skv, B, D), dtype=torch.bfloat16, device=dev)
+        if grad_weights is None:
+            grad_weights = torch.empty((S, B, H), dtype=torch.float32, device=dev)
+        _need(grad_q, "grad_q", torch.bfloat16, (S, B, H, D), dev)
+        _need(grad_k, "grad_k", torch.bfloat16, (Skv, B, D), dev)
+        _need(grad_weights, "grad_weights", torch.float32, (S, B, H), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_indexer_backward(
+                self._h, _ptr(index_q), _ptr(index_k), _ptr(weights), _ptr(topk_indices),
+                _ptr(grad_scores), S, Skv, B, int(compress_ratio), int(topk), _ptr(grad_q),
+                _ptr(grad_k), _ptr(grad_weights), _ptr(workspace),
+                workspace.numel() * workspace.element_size(), _stream(dev))
+        self._check(st, "dsai_indexer_backward")
+        return grad_q, grad_k, grad_weights
 
     # -- cache write ---------------------------------------------------------
     def k_norm(self, k_raw: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
@@ -352,3 +409,34 @@ class Indexer:
             st = self._lib.dsai_sort_rows(self._h, _ptr(idx), _ptr(score), rows, int(k), _stream(dev))
         self._check(st, "dsai_sort_rows")
         return idx, score
+
+
+class IndexerFunction(torch.autograd.Function):
+    """Autograd pairing of score_topk and indexer_backward (the V4 indexer's
+    autograd function): apply(indexer, index_q, index_k, weights,
+    compress_ratio, topk, topk_indices=None) -> (scores, indices), both
+    [B,S,topk]; scores fp32 (-inf padding), indices int32 (-1 padding).
+    The indices take no gradient; the scores pass theirs to index_q,
+    index_k and weights."""
+
+    @staticmethod
+    def forward(ctx, indexer: Indexer, index_q, index_k, weights, compress_ratio: int, topk: int,
+                topk_indices=None):
+        idx, score = indexer.score_topk(index_q.detach(), index_k.detach(), weights.detach(),
+                                        compress_ratio, topk, topk_indices=topk_indices)
+        ctx.indexer = indexer
+        ctx.compress_ratio = int(compress_ratio)
+        ctx.save_for_backward(index_q, index_k, weights, idx)
+        ctx.mark_non_differentiable(idx)
+        return score, idx
+
+    @staticmethod
+    def backward(ctx, grad_scores, grad_indices):
+        index_q, index_k, weights, idx = ctx.saved_tensors
+        if grad_scores is None:
+            return None, None, None, None, None, None, None
+        gq, gk, gw = ctx.indexer.indexer_backward(index_q.detach(), index_k.detach(),
+                                                  weights.detach(), idx,
+                                                  grad_scores.float().contiguous(),
+                                                  ctx.compress_ratio)
+        return None, gq, gk, gw, None, None, None

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsai.so")
 
-SOURCES = ["api.cpp", "score_topk.hip", "score_at.hip", "sort_rows.hip", "pooled.hip", "k_norm.hip"]
+SOURCES = ["api.cpp", "score_topk.hip", "score_at.hip", "sort_rows.hip", "pooled.hip", "k_norm.hip",
+           "indexer_bwd.hip"]
 
 # Packed-fp32 VALU forms are kept out of the device code: plain fp32 ops only.
 # No value the kernels handle is ever NaN (finite inputs; -inf only as padding),

@@ -221,6 +221,54 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   return hip_status(h, le);
 }
 
+int dsai_backward_workspace_size(dsai_handle h, int64_t Skv, int64_t B, size_t* bytes) {
+  if (!h || !bytes) return DSAI_ERR_NULLPTR;
+  if (Skv < 0 || B < 0) return DSAI_ERR_INVALID_ARG;
+  *bytes = (size_t)Skv * (size_t)B * (size_t)h->cfg.dim * sizeof(float);
+  return DSAI_OK;
+}
+
+int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_k,
+                          const float* weights, const int32_t* topk_indices,
+                          const float* grad_scores, int64_t S, int64_t Skv, int64_t B,
+                          int compress_ratio, int topk, void* grad_q, void* grad_k,
+                          float* grad_weights, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (S < 0 || Skv < 0 || B < 0 || compress_ratio < 1) return DSAI_ERR_INVALID_ARG;
+  if (topk < 1 || topk > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
+  if (S > kI32 || Skv > kI32 || B > kI32 || S * B > kI32 || Skv * B > kI32)
+    return DSAI_ERR_INVALID_ARG;
+  if (B == 0 || (S == 0 && Skv == 0)) return DSAI_OK;
+  size_t need = 0;
+  dsai_backward_workspace_size(h, Skv, B, &need);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return DSAI_ERR_WORKSPACE;
+  if (Skv > 0 && (!index_k || !grad_k)) return DSAI_ERR_NULLPTR;
+  if (S > 0 && (!index_q || !weights || !topk_indices || !grad_scores || !grad_q || !grad_weights))
+    return DSAI_ERR_NULLPTR;
+  if (!aligned(index_q) || !aligned(index_k) || !aligned(grad_q) || !aligned(grad_k) ||
+      reinterpret_cast<uintptr_t>(topk_indices) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(grad_scores) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(weights) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(grad_weights) % 4 != 0)
+    return DSAI_ERR_INVALID_ARG;
+  dsai::BackwardArgs a;
+  a.q = static_cast<const uint16_t*>(index_q);
+  a.k = static_cast<const uint16_t*>(index_k);
+  a.w = weights;
+  a.sup = topk_indices;
+  a.grad = grad_scores;
+  a.S = S; a.Skv = Skv; a.B = B;
+  a.H = h->cfg.heads; a.D = h->cfg.dim; a.ratio = compress_ratio; a.n = topk;
+  a.grad_q = static_cast<uint16_t*>(grad_q);
+  a.grad_k = static_cast<uint16_t*>(grad_k);
+  a.grad_w = grad_weights;
+  a.acc_k = static_cast<float*>(workspace);
+  return hip_status(h, dsai::launch_indexer_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 int dsai_pool_count(dsai_handle h, int64_t N, int64_t* P) {
   if (!h || !P) return DSAI_ERR_NULLPTR;
   if (N < 0) return DSAI_ERR_INVALID_ARG;

@@ -109,6 +109,22 @@ struct KNormArgs {
   uint16_t* y;            // [n, D] bf16
 };
 hipError_t launch_k_norm(const KNormArgs& a, hipStream_t st);
+// Gradients of the selected scores (indexer_bwd.hip).  acc_k is an fp32
+// [Skv, B, D] accumulator the launch clears and then converts into grad_k.
+struct BackwardArgs {
+  const uint16_t* q;    // [S, B, H, D] bf16
+  const uint16_t* k;    // [Skv, B, D] bf16
+  const float* w;       // [S, B, H]
+  const int32_t* sup;   // [B, S, n] key indices
+  const float* grad;    // [B, S, n] incoming gradient of the scores
+  int64_t S, Skv, B;
+  int H, D, ratio, n;
+  uint16_t* grad_q;     // [S, B, H, D] bf16
+  uint16_t* grad_k;     // [Skv, B, D] bf16
+  float* grad_w;        // [S, B, H]
+  float* acc_k;         // [Skv, B, D] fp32 workspace
+};
+hipError_t launch_indexer_backward(const BackwardArgs& a, hipStream_t st);
 // Stable sort of `rows` rows of `topk` (idx, score) pairs, each in ascending
 // index order with -1 padding at the tail, into score-descending order.
 hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st);

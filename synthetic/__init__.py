@@ -31,6 +31,7 @@ BLOCK = 1024  # leading-dimension rows per random stream block
 TID_Q, TID_K, TID_W, TID_HEAVY = 1, 2, 3, 4
 TID_KNORM, TID_GATE, TID_VALID, TID_APE, TID_PQ, TID_PW = 5, 6, 7, 8, 9, 10
 TID_INT_Q, TID_INT_K, TID_INT_W = 11, 12, 13
+TID_KEYS, TID_GRAD = 14, 15
 
 
 def _stream(seed: int, tid: int, block: int) -> np.random.Generator:
@@ -232,3 +233,42 @@ def random_pool_ids(seed: int, Q: int, select_k: int, P: int, missing_frac: floa
     ids = g.integers(0, max(P, 1), (Q, select_k)).astype(np.int32)
     ids[g.random((Q, select_k)) < missing_frac] = -1
     return ids
+
+
+# ---------------------------------------------------------------------------
+# Backward inputs: key lists and incoming gradients of their scores
+# ---------------------------------------------------------------------------
+
+def key_lists(seed: int, B: int, R: int, n: int, Skv: int, bound=None) -> np.ndarray:
+    """[B, R, n] int32: row r of batch b lists min(n, m) distinct keys drawn
+    uniformly from [0, m) in random order, then -1, where m = bound[r]
+    (default Skv).  A stand-in for a selection's index rows."""
+    out = np.full((B, R, n), -1, dtype=np.int32)
+    for b in range(B):
+        g = _stream(seed, TID_KEYS, b)
+        for r in range(R):
+            m = Skv if bound is None else int(bound[r])
+            if m <= 0:
+                continue
+            c = min(n, m)
+            out[b, r, :c] = g.permutation(m)[:c]
+    return out
+
+
+def noisy_key_lists(seed: int, B: int, R: int, n: int, Skv: int) -> np.ndarray:
+    """[B, R, n] int32 entries uniform in [-2, Skv + 3): padding, out-of-range
+    and (for any row bound) masked entries, and repeats."""
+    return _rows_blocked(seed, TID_KEYS, B, (R, n),
+                         lambda g, k: g.integers(-2, Skv + 3, k).astype(np.int32))
+
+
+def score_grads(seed: int, B: int, R: int, n: int, integer: bool = False) -> np.ndarray:
+    """[B, R, n] fp32 incoming gradients of selected scores: N(0, 1), or
+    (integer=True) drawn from {+-1/4, +-1/2, +-1, +-2} so products with
+    power-of-two weights stay exact."""
+    if integer:
+        choices = np.array([0.25, -0.25, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], dtype=np.float32)
+        draw = lambda g, k: choices[g.integers(0, len(choices), k)]
+    else:
+        draw = _normal(1.0)
+    return _rows_blocked(seed, TID_GRAD, B, (R, n), draw)

@@ -158,6 +158,44 @@ def test_k_norm_argument_errors(lib):
     lib.dsai_destroy(h)
 
 
+def test_backward_argument_errors(lib):
+    """Every check of dsai_indexer_backward returns before any HIP call."""
+    st, h = _create(lib, heads=64, dim=128)
+    assert st == OK
+    n = ctypes.c_size_t()
+    assert lib.dsai_backward_workspace_size(h, 4096, 2, ctypes.byref(n)) == OK
+    assert n.value == 4096 * 2 * 128 * 4
+    assert lib.dsai_backward_workspace_size(h, -1, 2, ctypes.byref(n)) == INVALID
+    assert lib.dsai_backward_workspace_size(h, 4, 2, None) == NULLPTR
+    ws_ok = 4096 * 2 * 128 * 4
+    WS = ctypes.c_void_p(0x100000)  # 256-byte aligned, never dereferenced
+
+    def call(S=8, Skv=4096, B=2, r=1, topk=4, q=FAKE, k=FAKE, w=FAKE, idx=FAKE, g=FAKE,
+             gq=FAKE, gk=FAKE, gw=FAKE, ws=WS, ws_bytes=ws_ok, handle=h):
+        return lib.dsai_indexer_backward(handle, q, k, w, idx, g, S, Skv, B, r, topk, gq, gk, gw,
+                                         ws, ws_bytes, None)
+
+    assert call(handle=None) == NULLPTR
+    for kw in ({"S": -1}, {"Skv": -1}, {"B": -1}, {"r": 0}, {"topk": 0}, {"topk": 8193},
+               {"S": 1 << 31}, {"S": 1 << 20, "B": 1 << 12}, {"Skv": 1 << 20, "B": 1 << 12}):
+        assert call(**kw) == INVALID, kw
+    assert call(B=0) == OK                  # nothing to write
+    assert call(S=0, Skv=0) == OK
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=ws_ok - 1) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100080)) == WORKSPACE   # not 256-byte aligned
+    for name in ("q", "k", "w", "idx", "g", "gq", "gk", "gw"):
+        assert call(**{name: None}) == NULLPTR, name
+    for name in ("q", "k", "gq", "gk"):
+        assert call(**{name: ctypes.c_void_p(0x10008)}) == INVALID, name
+    for name in ("w", "idx", "g", "gw"):
+        assert call(**{name: ctypes.c_void_p(0x10002)}) == INVALID, name
+    # S == 0 needs only the key side; Skv == 0 only the query side
+    assert call(S=0, q=None, w=None, idx=None, g=None, gq=None, gw=None, k=None) == NULLPTR
+    assert call(Skv=0, ws=None, ws_bytes=0, k=None, gk=None, q=None) == NULLPTR
+    lib.dsai_destroy(h)
+
+
 def test_pooled_argument_errors(lib):
     st, h = _create(lib, kpool=4, index_topk=512, first_key=3)
     assert st == OK
