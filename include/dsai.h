@@ -177,6 +177,9 @@ int dsai_backward_workspace_size(dsai_handle h, int64_t Skv, int64_t B, size_t* 
  * the two gradient products, which accumulate in fp32; grad_k sums over
  * rows with fp32 atomic adds (order unspecified) into the workspace;
  * grad_q and grad_k are rounded to bf16 (nearest even) once at the end.
+ * With S and Skv both positive, the key gradients and the per-row
+ * gradients run concurrently on the two streams the handle owns (see
+ * dsai_score_topk), forked from `stream` and joined back to it.
  *
  * S, Skv, B >= 0 (< 2^31, also S*B and Skv*B); compress_ratio >= 1;
  * 1 <= topk <= DSAI_MAX_TOPK (DSAI_ERR_INVALID_ARG otherwise).  B == 0 or

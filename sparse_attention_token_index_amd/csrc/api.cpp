@@ -266,7 +266,13 @@ int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_
   a.grad_k = static_cast<uint16_t*>(grad_k);
   a.grad_w = grad_weights;
   a.acc_k = static_cast<float*>(workspace);
-  return hip_status(h, dsai::launch_indexer_backward(a, static_cast<hipStream_t>(stream)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (S == 0 || Skv == 0) return hip_status(h, dsai::launch_indexer_backward(a, st, st));
+  // the atomic-bound key scatter and the matrix-core-bound per-row
+  // gradients overlap on the handle's two streams
+  return hip_status(h, on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
+                      return dsai::launch_indexer_backward(a, s0, s1);
+                    }));
 }
 
 int dsai_pool_count(dsai_handle h, int64_t N, int64_t* P) {

@@ -291,51 +291,45 @@ unsigned stream_blocks(int64_t n4) {
 }
 
 template <int HP, int D>
-hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
+hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t st_keys, hipStream_t st_rows) {
   const int64_t rows = a.S * a.B;
+  const int64_t n4 = a.Skv * a.B * a.D / 4;  // D is a multiple of 32
+  const int64_t kb = (rows + kBwdWaves - 1) / kBwdWaves;
+  const int64_t qb = (rows * (HP / 32) + kBwdWaves - 1) / kBwdWaves;
+  if (kb > 0x7FFFFFFF || qb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipError_t e;
   if (rows > 0) {
-    const int64_t kb = (rows + kBwdWaves - 1) / kBwdWaves;
-    const int64_t qb = (rows * (HP / 32) + kBwdWaves - 1) / kBwdWaves;
-    if (kb > 0x7FFFFFFF || qb > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_queries_kernel<HP, D>), dim3((unsigned)qb), dim3(kBwdWaves * 64), 0, st,
-                       a.q, a.k, a.w, a.sup, a.grad, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio,
-                       a.n, a.grad_q, a.grad_w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.Skv > 0) {
-      hipLaunchKernelGGL((bwd_keys_kernel<HP, D>), dim3((unsigned)kb), dim3(kBwdWaves * 64), 0, st,
-                         a.q, a.k, a.w, a.sup, a.grad, (int)a.S, (int)a.Skv, (int)a.B, a.H, a.ratio,
-                         a.n, a.acc_k);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    hipLaunchKernelGGL((bwd_queries_kernel<HP, D>), dim3((unsigned)qb), dim3(kBwdWaves * 64), 0,
+                       st_rows, a.q, a.k, a.w, a.sup, a.grad, (int)a.S, (int)a.Skv, (int)a.B, a.H,
+                       a.ratio, a.n, a.grad_q, a.grad_w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return hipSuccess;
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(stream_blocks(n4)), dim3(256), 0, st_keys,
+                     reinterpret_cast<float4*>(a.acc_k), n4);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_keys_kernel<HP, D>), dim3((unsigned)kb), dim3(kBwdWaves * 64), 0,
+                       st_keys, a.q, a.k, a.w, a.sup, a.grad, (int)a.S, (int)a.Skv, (int)a.B, a.H,
+                       a.ratio, a.n, a.acc_k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(stream_blocks(n4)), dim3(256), 0, st_keys,
+                     reinterpret_cast<const float4*>(a.acc_k), reinterpret_cast<uint2*>(a.grad_k),
+                     n4);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_indexer_backward(const BackwardArgs& a, hipStream_t st) {
-  const int64_t n4 = a.Skv * a.B * a.D / 4;  // D is a multiple of 32
-  if (n4 > 0) {
-    hipLaunchKernelGGL(zero_f32_kernel, dim3(stream_blocks(n4)), dim3(256), 0, st,
-                       reinterpret_cast<float4*>(a.acc_k), n4);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+hipError_t launch_indexer_backward(const BackwardArgs& a, hipStream_t st_keys, hipStream_t st_rows) {
   const int HP = a.H <= 32 ? 32 : 64;
-  hipError_t e = hipErrorInvalidValue;
 #define DSAI_CASE(hp, d) \
-  if (HP == hp && a.D == d) e = launch_bwd_t<hp, d>(a, st);
+  if (HP == hp && a.D == d) return launch_bwd_t<hp, d>(a, st_keys, st_rows);
   DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
   DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)
 #undef DSAI_CASE
-  if (e != hipSuccess) return e;
-  if (n4 > 0) {
-    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(stream_blocks(n4)), dim3(256), 0, st,
-                       reinterpret_cast<const float4*>(a.acc_k), reinterpret_cast<uint2*>(a.grad_k), n4);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dsai

@@ -111,6 +111,9 @@ struct KNormArgs {
 hipError_t launch_k_norm(const KNormArgs& a, hipStream_t st);
 // Gradients of the selected scores (indexer_bwd.hip).  acc_k is an fp32
 // [Skv, B, D] accumulator the launch clears and then converts into grad_k.
+// The key gradients (clear, scatter, convert) go to st_keys and the
+// per-row gradients (grad_q, grad_w) to st_rows; they share no output, so
+// the two may run concurrently (st_rows may be st_keys).
 struct BackwardArgs {
   const uint16_t* q;    // [S, B, H, D] bf16
   const uint16_t* k;    // [Skv, B, D] bf16
@@ -124,7 +127,7 @@ struct BackwardArgs {
   float* grad_w;        // [S, B, H]
   float* acc_k;         // [Skv, B, D] fp32 workspace
 };
-hipError_t launch_indexer_backward(const BackwardArgs& a, hipStream_t st);
+hipError_t launch_indexer_backward(const BackwardArgs& a, hipStream_t st_keys, hipStream_t st_rows);
 // Stable sort of `rows` rows of `topk` (idx, score) pairs, each in ascending
 // index order with -1 padding at the tail, into score-descending order.
 hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st);
