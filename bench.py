@@ -412,7 +412,8 @@ def main():
     if case.name == "prefill":
         bw_ix = dsai.Indexer(heads=case.H, dim=case.D)
         bw_g = torch.from_numpy(SY.score_grads(case.seed, case.B, case.S, case.topk)).to(dev)
-        bw_ws = torch.empty(bw_ix.backward_workspace_size(case.Skv, case.B), dtype=torch.uint8,
+        bw_ws = torch.empty(bw_ix.backward_workspace_size(case.S, case.Skv, case.B, case.topk,
+                                                          case.compress_ratio), dtype=torch.uint8,
                             device=dev)
         bw_out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w))
         for _ in range(2):

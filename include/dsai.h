@@ -148,9 +148,14 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
                     int32_t* out_idx, float* out_score, void* stream);
 
 /* ---- backward: gradients of the selected scores ------------------------- */
-/* Workspace of dsai_indexer_backward: Skv * B * cfg.dim * 4 bytes (an fp32
- * accumulator of grad_k).  Host-only. */
-int dsai_backward_workspace_size(dsai_handle h, int64_t Skv, int64_t B, size_t* bytes);
+/* Workspace bytes of dsai_indexer_backward for these sizes (the same
+ * arguments as the call): an fp32 [Skv, B, cfg.dim] accumulator of grad_k
+ * plus, when the entries are grouped by key block (Skv <= 262144 and
+ * B <= 65535), (B * S) * (ceil(Skv / 256) + 1) int32 bucket bounds and
+ * B * S * topk 8-byte bucketed entries.  Host-only; DSAI_ERR_INVALID_ARG for
+ * the sizes dsai_indexer_backward refuses. */
+int dsai_backward_workspace_size(dsai_handle h, int64_t S, int64_t Skv, int64_t B, int topk,
+                                 int compress_ratio, size_t* bytes);
 
 /* The backward of the indexer's autograd function (NeMo AutoModel page
  * "...deepseek_v4.kernels.tilelang_indexer", V4IndexerFunction.backward with
@@ -174,9 +179,11 @@ int dsai_backward_workspace_size(dsai_handle h, int64_t Skv, int64_t B, size_t* 
  *
  * Arithmetic: d_h in fp32 on the matrix cores (the forward's products); the
  * gated weight g * weights * (d_h > 0) is rounded to bf16 as the operand of
- * the two gradient products, which accumulate in fp32; grad_k sums over
- * rows with fp32 atomic adds (order unspecified) into the workspace;
- * grad_q and grad_k are rounded to bf16 (nearest even) once at the end.
+ * the two gradient products, which accumulate in fp32; grad_k's sum over
+ * query rows is accumulated in fp32 in the workspace (per key block and row
+ * chunk, then added with fp32 atomics: the order of those additions is
+ * unspecified); grad_q and grad_k are rounded to bf16 (nearest even) once
+ * at the end.
  * With S and Skv both positive, the key gradients and the per-row
  * gradients run concurrently on the two streams the handle owns (see
  * dsai_score_topk), forked from `stream` and joined back to it.
@@ -184,8 +191,8 @@ int dsai_backward_workspace_size(dsai_handle h, int64_t Skv, int64_t B, size_t* 
  * S, Skv, B >= 0 (< 2^31, also S*B and Skv*B); compress_ratio >= 1;
  * 1 <= topk <= DSAI_MAX_TOPK (DSAI_ERR_INVALID_ARG otherwise).  B == 0 or
  * S == Skv == 0: nothing is written or launched; S == 0 writes grad_k = 0.
- * workspace: device memory of dsai_backward_workspace_size bytes, 256-byte
- * aligned (DSAI_ERR_WORKSPACE otherwise), overwritten.  index_q, index_k,
+ * workspace: device memory of dsai_backward_workspace_size bytes (same
+ * sizes), 256-byte aligned (DSAI_ERR_WORKSPACE otherwise), overwritten.  index_q, index_k,
  * grad_q, grad_k 16-byte aligned; the other arrays 4-byte aligned
  * (DSAI_ERR_INVALID_ARG otherwise).  All arrays are device memory. */
 int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_k,

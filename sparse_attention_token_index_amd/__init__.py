@@ -88,7 +88,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_expand": [vp, vp, i64, vp, vp],
         "dsai_sort_rows": [vp, vp, vp, i64, c_int, vp],
         "dsai_k_norm": [vp, vp, vp, vp, ctypes.c_float, i64, vp, vp],
-        "dsai_backward_workspace_size": [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "dsai_backward_workspace_size": [vp, i64, i64, i64, c_int, c_int,
+                                         ctypes.POINTER(ctypes.c_size_t)],
         "dsai_indexer_backward": [vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, vp, vp,
                                   vp, ctypes.c_size_t, vp],
     }
@@ -203,9 +204,12 @@ class Indexer:
         return out_idx, out_score
 
     # -- backward ------------------------------------------------------------
-    def backward_workspace_size(self, Skv: int, B: int) -> int:
+    def backward_workspace_size(self, S: int, Skv: int, B: int, topk: int,
+                                compress_ratio: int) -> int:
         n = ctypes.c_size_t()
-        self._check(self._lib.dsai_backward_workspace_size(self._h, int(Skv), int(B), ctypes.byref(n)),
+        self._check(self._lib.dsai_backward_workspace_size(self._h, int(S), int(Skv), int(B),
+                                                           int(topk), int(compress_ratio),
+                                                           ctypes.byref(n)),
                     "dsai_backward_workspace_size")
         return n.value
 
@@ -220,7 +224,8 @@ class Indexer:
         incoming gradient grad_scores [B,S,topk] fp32 -> (grad_q [S,B,H,D] bf16,
         grad_k [Skv,B,D] bf16, grad_weights [S,B,H] fp32).  Entries that are
         -1, masked or out of range pass nothing back.  `workspace` (uint8,
-        backward_workspace_size(Skv, B) bytes) is allocated when not given."""
+        backward_workspace_size(S, Skv, B, topk, compress_ratio) bytes) is
+        allocated when not given."""
         S, B = index_q.shape[0], index_q.shape[1]
         Skv = index_k.shape[0]
         H, D = self.cfg.heads, self.cfg.dim
@@ -233,7 +238,7 @@ class Indexer:
         topk = topk_indices.shape[2]
         _need(topk_indices, "topk_indices", torch.int32, (B, S, topk), dev)
         _need(grad_scores, "grad_scores", torch.float32, (B, S, topk), dev)
-        need = self.backward_workspace_size(Skv, B)
+        need = self.backward_workspace_size(S, Skv, B, topk, compress_ratio)
         if workspace is None:
             workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
         if grad_q is None:

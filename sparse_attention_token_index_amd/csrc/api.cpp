@@ -221,10 +221,14 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   return hip_status(h, le);
 }
 
-int dsai_backward_workspace_size(dsai_handle h, int64_t Skv, int64_t B, size_t* bytes) {
+int dsai_backward_workspace_size(dsai_handle h, int64_t S, int64_t Skv, int64_t B, int topk,
+                                 int compress_ratio, size_t* bytes) {
   if (!h || !bytes) return DSAI_ERR_NULLPTR;
-  if (Skv < 0 || B < 0) return DSAI_ERR_INVALID_ARG;
-  *bytes = (size_t)Skv * (size_t)B * (size_t)h->cfg.dim * sizeof(float);
+  if (S < 0 || Skv < 0 || B < 0 || topk < 1 || topk > DSAI_MAX_TOPK || compress_ratio < 1)
+    return DSAI_ERR_INVALID_ARG;
+  if (S > kI32 || Skv > kI32 || B > kI32 || S * B > kI32 || Skv * B > kI32)
+    return DSAI_ERR_INVALID_ARG;
+  *bytes = dsai::plan_backward(S, Skv, B, h->cfg.dim, topk, compress_ratio).bytes;
   return DSAI_OK;
 }
 
@@ -240,10 +244,9 @@ int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_
   if (S > kI32 || Skv > kI32 || B > kI32 || S * B > kI32 || Skv * B > kI32)
     return DSAI_ERR_INVALID_ARG;
   if (B == 0 || (S == 0 && Skv == 0)) return DSAI_OK;
-  size_t need = 0;
-  dsai_backward_workspace_size(h, Skv, B, &need);
-  if (need > 0 && (!workspace || workspace_bytes < need ||
-                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+  const dsai::BackwardPlan plan = dsai::plan_backward(S, Skv, B, h->cfg.dim, topk, compress_ratio);
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes ||
+                         reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
     return DSAI_ERR_WORKSPACE;
   if (Skv > 0 && (!index_k || !grad_k)) return DSAI_ERR_NULLPTR;
   if (S > 0 && (!index_q || !weights || !topk_indices || !grad_scores || !grad_q || !grad_weights))
@@ -265,13 +268,13 @@ int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_
   a.grad_q = static_cast<uint16_t*>(grad_q);
   a.grad_k = static_cast<uint16_t*>(grad_k);
   a.grad_w = grad_weights;
-  a.acc_k = static_cast<float*>(workspace);
+  a.ws = workspace;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (S == 0 || Skv == 0) return hip_status(h, dsai::launch_indexer_backward(a, st, st));
-  // the atomic-bound key scatter and the matrix-core-bound per-row
-  // gradients overlap on the handle's two streams
+  if (S == 0 || Skv == 0) return hip_status(h, dsai::launch_indexer_backward(a, plan, st, st));
+  // the key gradients and the matrix-core-bound per-row gradients overlap on
+  // the handle's two streams
   return hip_status(h, on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
-                      return dsai::launch_indexer_backward(a, s0, s1);
+                      return dsai::launch_indexer_backward(a, plan, s0, s1);
                     }));
 }
 

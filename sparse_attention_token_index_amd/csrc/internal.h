@@ -111,9 +111,21 @@ struct KNormArgs {
 hipError_t launch_k_norm(const KNormArgs& a, hipStream_t st);
 // Gradients of the selected scores (indexer_bwd.hip).  acc_k is an fp32
 // [Skv, B, D] accumulator the launch clears and then converts into grad_k.
-// The key gradients (clear, scatter, convert) go to st_keys and the
-// per-row gradients (grad_q, grad_w) to st_rows; they share no output, so
-// the two may run concurrently (st_rows may be st_keys).
+// The key gradients (clear, grouping, products, convert) go to st_keys and
+// the per-row gradients (grad_q, grad_w) to st_rows; they share no output,
+// so the two may run concurrently (st_rows may be st_keys).
+#define DSAI_BWD_MAX_KEY_BLOCKS 1024
+struct BackwardPlan {
+  bool grouped;        // key-block kernels (else a per-entry atomic scatter)
+  int nbk;             // key blocks of 256 keys
+  int chunk_rows;      // query rows per key-block workgroup
+  int nchunks;
+  size_t bounds_off;   // workspace layout (bytes)
+  size_t ent_off;
+  size_t bytes;        // total workspace
+};
+BackwardPlan plan_backward(int64_t S, int64_t Skv, int64_t B, int D, int n, int ratio);
+
 struct BackwardArgs {
   const uint16_t* q;    // [S, B, H, D] bf16
   const uint16_t* k;    // [Skv, B, D] bf16
@@ -125,9 +137,10 @@ struct BackwardArgs {
   uint16_t* grad_q;     // [S, B, H, D] bf16
   uint16_t* grad_k;     // [Skv, B, D] bf16
   float* grad_w;        // [S, B, H]
-  float* acc_k;         // [Skv, B, D] fp32 workspace
+  void* ws;             // workspace of plan.bytes (acc_k at offset 0)
 };
-hipError_t launch_indexer_backward(const BackwardArgs& a, hipStream_t st_keys, hipStream_t st_rows);
+hipError_t launch_indexer_backward(const BackwardArgs& a, const BackwardPlan& p, hipStream_t st_keys,
+                                   hipStream_t st_rows);
 // Stable sort of `rows` rows of `topk` (idx, score) pairs, each in ascending
 // index order with -1 padding at the tail, into score-descending order.
 hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st);

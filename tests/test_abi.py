@@ -163,11 +163,19 @@ def test_backward_argument_errors(lib):
     st, h = _create(lib, heads=64, dim=128)
     assert st == OK
     n = ctypes.c_size_t()
-    assert lib.dsai_backward_workspace_size(h, 4096, 2, ctypes.byref(n)) == OK
-    assert n.value == 4096 * 2 * 128 * 4
-    assert lib.dsai_backward_workspace_size(h, -1, 2, ctypes.byref(n)) == INVALID
-    assert lib.dsai_backward_workspace_size(h, 4, 2, None) == NULLPTR
-    ws_ok = 4096 * 2 * 128 * 4
+    # grouped plan: accumulator + bucket bounds (16 key blocks + 1 per row) + entries
+    assert lib.dsai_backward_workspace_size(h, 8, 4096, 2, 4, 1, ctypes.byref(n)) == OK
+    acc = 4096 * 2 * 128 * 4
+    bounds = -(-(2 * 8 * 17 * 4) // 256) * 256     # B*S rows x (16 blocks + 1), 256-aligned
+    assert n.value == acc + bounds + 2 * 8 * 4 * 8
+    ws_ok = n.value
+    # past 1024 key blocks: the accumulator only (per-entry atomic scatter)
+    assert lib.dsai_backward_workspace_size(h, 8, 300000, 1, 4, 1, ctypes.byref(n)) == OK
+    assert n.value == 300000 * 128 * 4
+    for args in ((-1, 4096, 2, 4, 1), (8, -1, 2, 4, 1), (8, 4096, -1, 4, 1), (8, 4096, 2, 0, 1),
+                 (8, 4096, 2, 8193, 1), (8, 4096, 2, 4, 0)):
+        assert lib.dsai_backward_workspace_size(h, *args, ctypes.byref(n)) == INVALID, args
+    assert lib.dsai_backward_workspace_size(h, 8, 4, 2, 4, 1, None) == NULLPTR
     WS = ctypes.c_void_p(0x100000)  # 256-byte aligned, never dereferenced
 
     def call(S=8, Skv=4096, B=2, r=1, topk=4, q=FAKE, k=FAKE, w=FAKE, idx=FAKE, g=FAKE,

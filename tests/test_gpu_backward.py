@@ -59,8 +59,8 @@ def run_backward(dsai, case, inp, sup, grad, ws_fill=None):
     ix = dsai.Indexer(heads=case.H, dim=case.D)
     q, k = to_gpu_bf16(inp["q_bits"]), to_gpu_bf16(inp["k_bits"])
     w = torch.from_numpy(inp["w"]).cuda()
-    ws = torch.empty(max(ix.backward_workspace_size(case.Skv, case.B), 1), dtype=torch.uint8,
-                     device="cuda")
+    need = ix.backward_workspace_size(case.S, case.Skv, case.B, case.topk, case.compress_ratio)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     if ws_fill is not None:
         ws.fill_(ws_fill)  # stale contents the call must clear
     gq, gk, gw = ix.indexer_backward(q, k, w, torch.from_numpy(sup).cuda(),
@@ -192,6 +192,24 @@ def test_full_size_sampled(dsai, name):
                      refk["band_k"][keys], refk["count_k"][keys][:, :, None])
 
 
+def test_more_than_1024_key_blocks(dsai):
+    """Skv = 300000 (over 1024 blocks of 256 keys): the per-entry atomic
+    scatter instead of the key-block grouping; same bound."""
+    case = SY.IndexerCase("bwd_wide_keys", B=1, S=96, Skv=300000, H=20, D=64, compress_ratio=1,
+                          topk=40, w_var=1 / 20, seed=65)
+    log(f"[gpu] backward {case.name}")
+    inp = SY.indexer_inputs(case)
+    sup = SY.noisy_key_lists(case.seed, case.B, case.S, case.topk, 120)   # keys near the rows
+    grad = SY.score_grads(case.seed, case.B, case.S, case.topk)
+    gq, gk, gw = run_backward(dsai, case, inp, sup, grad, ws_fill=0x55)
+    ref = oracle_backward(case, inp, sup, grad, with_bounds=True)
+    check_bf16_bound("grad_q", gq, ref["grad_q"], ref["abs_q"], ref["band_q"], case.topk)
+    check_bf16_bound("grad_k", gk, ref["grad_k"], ref["abs_k"], ref["band_k"],
+                     ref["count_k"][:, :, None])
+    check_w_bound(gw, ref["grad_w"], ref["abs_w"], case.topk, case.D)
+    assert np.count_nonzero(ref["grad_k"]) > 0
+
+
 def test_edge_sizes(dsai):
     """S == 0 (grad_k all zero), Skv == 0 (grad_q / grad_weights zero), rows
     with no visible key, topk == 1, and no usable entry at all."""
@@ -260,7 +278,8 @@ def test_repeat_calls_and_stale_workspace(dsai):
     ix = dsai.Indexer(heads=case.H, dim=case.D)
     q, k = to_gpu_bf16(inp["q_bits"]), to_gpu_bf16(inp["k_bits"])
     w = torch.from_numpy(inp["w"]).cuda()
-    ws = torch.empty(ix.backward_workspace_size(case.Skv, case.B), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ix.backward_workspace_size(case.S, case.Skv, case.B, case.topk, case.compress_ratio),
+                     dtype=torch.uint8, device="cuda")
     tsup, tg = torch.from_numpy(sup).cuda(), torch.from_numpy(grad).cuda()
     a = [t.clone() for t in ix.indexer_backward(q, k, w, tsup, tg, case.compress_ratio, workspace=ws)]
     b = ix.indexer_backward(q, k, w, tsup, tg, case.compress_ratio, workspace=ws)
