@@ -192,6 +192,29 @@ def test_full_size_sampled(dsai, name):
                      refk["band_k"][keys], refk["count_k"][keys][:, :, None])
 
 
+def test_many_repeated_keys_in_one_block(dsai):
+    """2048 entries per row drawn from 40 keys: far more entries per key
+    block than threads per workgroup, each key repeated ~50 times (their
+    gradients add).  Integer data: grad_q and grad_weights are exact; the
+    key gradients sum a key's repeated gradients before the product with
+    the head weights, and that sum times w need not fit bf16, so grad_k is
+    held to the bound."""
+    case = SY.IndexerCase("bwd_repeats", B=2, S=48, Skv=300, H=64, D=128, compress_ratio=1,
+                          topk=2048, w_var=1 / 64, seed=66, integer=True)
+    log(f"[gpu] backward {case.name}")
+    inp = SY.indexer_inputs(case)
+    sup = SY.noisy_key_lists(case.seed, case.B, case.S, case.topk, 38)   # entries in [-2, 41)
+    grad = SY.score_grads(case.seed, case.B, case.S, case.topk, integer=True)
+    gq, gk, gw = run_backward(dsai, case, inp, sup, grad, ws_fill=0x33)
+    ref = oracle_backward(case, inp, sup, grad, with_bounds=True)
+    _, rq = oracle.round_to_bf16(ref["grad_q"])
+    assert np.array_equal(zero_normalised(gq), zero_normalised(rq)), np.argwhere(gq != rq)[:5]
+    assert np.array_equal(gw.astype(np.float64), ref["grad_w"])
+    check_bf16_bound("grad_k", gk, ref["grad_k"], ref["abs_k"], ref["band_k"],
+                     ref["count_k"][:, :, None])
+    assert np.count_nonzero(ref["grad_k"][:41]) > 0
+
+
 def test_more_than_1024_key_blocks(dsai):
     """Skv = 300000 (over 1024 blocks of 256 keys): the per-entry atomic
     scatter instead of the key-block grouping; same bound."""
@@ -260,6 +283,19 @@ def test_autograd_function(dsai):
     fin = torch.isfinite(scores)
     (torch.where(fin, scores, torch.zeros_like(scores)) * g).sum().backward()
     gq, gk, gw = ix.indexer_backward(q.detach(), k.detach(), w.detach(), idx,
+                                     torch.where(fin, g, torch.zeros_like(g)), case.compress_ratio)
+    torch.cuda.synchronize()
+    assert torch.equal(q.grad.view(torch.int16), gq.view(torch.int16))
+    assert torch.equal(k.grad.view(torch.int16), gk.view(torch.int16))
+    assert torch.equal(w.grad, gw)
+    # with supplied indices (padding, masked and repeated keys among them)
+    sup = torch.from_numpy(SY.noisy_key_lists(case.seed, case.B, case.S, case.topk, case.Skv)).cuda()
+    for t in (q, k, w):
+        t.grad = None
+    scores, idx = dsai.IndexerFunction.apply(ix, q, k, w, case.compress_ratio, case.topk, sup)
+    fin = torch.isfinite(scores)
+    (torch.where(fin, scores, torch.zeros_like(scores)) * g).sum().backward()
+    gq, gk, gw = ix.indexer_backward(q.detach(), k.detach(), w.detach(), sup,
                                      torch.where(fin, g, torch.zeros_like(g)), case.compress_ratio)
     torch.cuda.synchronize()
     assert torch.equal(q.grad.view(torch.int16), gq.view(torch.int16))
