@@ -179,7 +179,8 @@ int dsai_backward_workspace_size(dsai_handle h, int64_t S, int64_t Skv, int64_t 
  *
  * Arithmetic: d_h in fp32 on the matrix cores (the forward's products); the
  * gated weight g * weights * (d_h > 0) is rounded to bf16 as the operand of
- * the two gradient products, which accumulate in fp32; grad_k's sum over
+ * the two gradient products, which accumulate in fp32 (for grad_k, the g of
+ * a key listed more than once in a row are summed first); grad_k's sum over
  * query rows is accumulated in fp32 in the workspace (per key block and row
  * chunk, then added with fp32 atomics: the order of those additions is
  * unspecified); grad_q and grad_k are rounded to bf16 (nearest even) once
