@@ -647,6 +647,22 @@ BackwardPlan plan_backward(int64_t S, int64_t Skv, int64_t B, int D, int n, int 
   const int64_t nbk = (Skv + kKeyBlock - 1) / kKeyBlock;
   p.grouped = S > 0 && Skv > 0 && B > 0 && B <= 65535 && nbk <= kMaxKeyBlocks;
   if (!p.grouped) return p;
+  // The grouped form costs about one 32-key product unit per (row, 32 visible
+  // keys), the scatter about D atomic adds per entry; measured on MI355X, a
+  // unit costs as much as 5-6 entries.  With rows listing min(n, n_t) keys,
+  // group when the entries outnumber the units 8 to 1 (a quarter of the
+  // visible keys selected or more).
+  int64_t units = 0, entries = 0;
+  const int64_t vmax = Skv < S / ratio ? Skv : S / ratio;  // largest n_t
+  for (int64_t v = 1; v <= vmax; ++v) {  // rows with n_t = v: t in [v r - 1, (v + 1) r - 1)
+    const int64_t lo = v * ratio - 1;
+    const int64_t hi = v == Skv ? S : ((v + 1) * ratio - 1 < S ? (v + 1) * ratio - 1 : S);
+    if (hi <= lo) continue;
+    units += (hi - lo) * ((v + 31) / 32);
+    entries += (hi - lo) * (v < n ? v : n);
+  }
+  p.grouped = entries >= 8 * units;
+  if (!p.grouped) return p;
   p.nbk = (int)nbk;
   // Rows that see some key of each block, summed, are the grouped kernel's
   // work.  The chunk is the smallest that leaves at most kBusyBlocks busy

@@ -163,11 +163,13 @@ def test_backward_argument_errors(lib):
     st, h = _create(lib, heads=64, dim=128)
     assert st == OK
     n = ctypes.c_size_t()
-    # grouped plan: accumulator + bucket bounds (16 key blocks + 1 per row) + entries
+    # dense selection (half the visible keys): grouped by key block, so the
+    # accumulator + bucket bounds (2 blocks + 1 per row) + bucketed entries
+    assert lib.dsai_backward_workspace_size(h, 512, 512, 2, 256, 1, ctypes.byref(n)) == OK
+    assert n.value == 512 * 2 * 128 * 4 + 2 * 512 * 3 * 4 + 2 * 512 * 256 * 8
+    # sparse selection (4 of up to 4096 keys): per-entry scatter, accumulator only
     assert lib.dsai_backward_workspace_size(h, 8, 4096, 2, 4, 1, ctypes.byref(n)) == OK
-    acc = 4096 * 2 * 128 * 4
-    bounds = -(-(2 * 8 * 17 * 4) // 256) * 256     # B*S rows x (16 blocks + 1), 256-aligned
-    assert n.value == acc + bounds + 2 * 8 * 4 * 8
+    assert n.value == 4096 * 2 * 128 * 4
     ws_ok = n.value
     # past 1024 key blocks: the accumulator only (per-entry atomic scatter)
     assert lib.dsai_backward_workspace_size(h, 8, 300000, 1, 4, 1, ctypes.byref(n)) == OK

@@ -168,12 +168,22 @@ def test_gaussian_inputs_within_bound(dsai, case):
         assert rel < 2.0 ** -7, (name, rel)
 
 
-@pytest.mark.parametrize("name", ["prefill", "c4"])
+FULL_CASES = {
+    "prefill": SY.CASES["prefill"],   # key-block grouping
+    "c4": SY.CASES["c4"],             # sparse selection: per-entry scatter
+    # 16384 rows over 4096 keys, half selected: key-block workgroups of
+    # several hundred rows (more than one window of bucket bounds)
+    "dense_16k": SY.IndexerCase("dense_16k", B=1, S=16384, Skv=4096, H=64, D=128,
+                                compress_ratio=1, topk=2048, w_var=1 / 64, seed=67),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FULL_CASES))
 def test_full_size_sampled(dsai, name):
     """The benchmark's shapes: every row's grad_q / grad_weights computed on
     the GPU, the oracle on sampled rows; grad_k on sampled keys (the oracle
     sums every row's entries that name them)."""
-    case = SY.CASES[name]
+    case = FULL_CASES[name]
     log(f"[gpu] backward full size {name}")
     inp = SY.indexer_inputs(case)
     sup = SY.key_lists(case.seed + 7, case.B, case.S, case.topk, case.Skv, causal_bound(case))
