@@ -15,7 +15,8 @@ Outside the step, the same top-k rows are rescored through the
 topk_indices form of dsai_score_topk (scores at supplied indices), and the
 cache write's k_norm runs over the 65536 cache rows, and the backward
 (gradients of the selected scores, with seeded incoming gradients) runs at
-the step's top-k rows; all three are reported in `breakdown`
+the step's top-k rows of whichever indexer workload is chosen; all three are
+reported in `breakdown`
 (score_at_indices_*, k_norm_*, backward_*: 6*H*D flops per selected entry,
 and the D fp32 key-gradient adds per entry per second).
 `value` = prefill query tokens per second of the whole step (the pooled
@@ -406,28 +407,25 @@ def main():
         at_flops = 2.0 * case.H * case.D * selected_entries(case)
 
     # the backward (gradients of the selected scores) at the step's own top-k
-    # rows, with seeded incoming gradients (prefill workload only; not part
-    # of the step)
-    bw_ms = bw_entries = None
-    if case.name == "prefill":
-        bw_ix = dsai.Indexer(heads=case.H, dim=case.D)
-        bw_g = torch.from_numpy(SY.score_grads(case.seed, case.B, case.S, case.topk)).to(dev)
-        bw_ws = torch.empty(bw_ix.backward_workspace_size(case.S, case.Skv, case.B, case.topk,
-                                                          case.compress_ratio), dtype=torch.uint8,
-                            device=dev)
-        bw_out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w))
-        for _ in range(2):
-            bw_ix.indexer_backward(q, k, w, out_idx, bw_g, case.compress_ratio, workspace=bw_ws,
-                                   grad_q=bw_out[0], grad_k=bw_out[1], grad_weights=bw_out[2])
-        a0.record()
-        for _ in range(args.steps):
-            bw_ix.indexer_backward(q, k, w, out_idx, bw_g, case.compress_ratio, workspace=bw_ws,
-                                   grad_q=bw_out[0], grad_k=bw_out[1], grad_weights=bw_out[2])
-        a1.record()
-        torch.cuda.synchronize()
-        bw_ms = a0.elapsed_time(a1) / args.steps
-        bw_entries = selected_entries(case)
-        del bw_ws, bw_out
+    # rows, with seeded incoming gradients (not part of the step)
+    bw_ix = dsai.Indexer(heads=case.H, dim=case.D)
+    bw_g = torch.from_numpy(SY.score_grads(case.seed, case.B, case.S, case.topk)).to(dev)
+    bw_ws = torch.empty(bw_ix.backward_workspace_size(case.S, case.Skv, case.B, case.topk,
+                                                      case.compress_ratio), dtype=torch.uint8,
+                        device=dev)
+    bw_out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w))
+    for _ in range(2):
+        bw_ix.indexer_backward(q, k, w, out_idx, bw_g, case.compress_ratio, workspace=bw_ws,
+                               grad_q=bw_out[0], grad_k=bw_out[1], grad_weights=bw_out[2])
+    a0.record()
+    for _ in range(args.steps):
+        bw_ix.indexer_backward(q, k, w, out_idx, bw_g, case.compress_ratio, workspace=bw_ws,
+                               grad_q=bw_out[0], grad_k=bw_out[1], grad_weights=bw_out[2])
+    a1.record()
+    torch.cuda.synchronize()
+    bw_ms = a0.elapsed_time(a1) / args.steps
+    bw_entries = selected_entries(case)
+    del bw_ws, bw_out
 
     # the cache write's k_norm (LayerNorm with a bias) over the pooled
     # workload's 65536 cache rows (not part of the step)
@@ -495,10 +493,8 @@ def main():
             "k_norm_ms": ln_ms, "k_norm_GBps": ln_bytes / (ln_ms * 1e-3) / 1e9,
             "k_norm_bytes": ln_bytes,
             "backward_ms": bw_ms,
-            "backward_TFLOPs": (6.0 * case.H * case.D * bw_entries / (bw_ms * 1e-3) / 1e12)
-            if bw_ms else None,
-            "backward_key_adds_G_per_s": (case.D * bw_entries / (bw_ms * 1e-3) / 1e9)
-            if bw_ms else None,
+            "backward_TFLOPs": 6.0 * case.H * case.D * bw_entries / (bw_ms * 1e-3) / 1e12,
+            "backward_key_adds_G_per_s": case.D * bw_entries / (bw_ms * 1e-3) / 1e9,
         },
     }
     if not args.no_cpu_baseline:
