@@ -51,22 +51,43 @@ struct TrPitch {
   static constexpr int kBytes = D == 32 ? 64 : (D == 64 ? 192 : 320);
 };
 
-// B fragment of a 32x32x16 product whose K index runs over rows of a
-// row-major bf16 LDS matrix and whose N index runs over its columns: lane
-// (n = l % 32, g = l / 32) receives, as elements e = 0..7, rows
-// row0 + 8 (e / 4) + 4 g + e % 4 of column col0 + n.  ds_read_b64_tr_b16 gives
-// lane i of each 16-lane group column c0 + i of four rows: the row its lanes
-// 4j .. 4j + 3 point at is the group's j-th row (lane 4j + q names columns
-// c0 + 4q .. c0 + 4q + 3 of it).
-template <int PITCH>
-__device__ __forceinline__ bf16x8 tr_frag(const lds_char* m, int row0, int col0) {
-  const int lane = lane_id();
-  const int s = lane & 15, nh = (lane >> 4) & 1, g = lane >> 5;
-  const lds_char* p = m + (row0 + 4 * g + (s >> 2)) * PITCH + 2 * (col0 + 16 * nh + 4 * (s & 3));
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSAI_LDS s16x4*)p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSAI_LDS s16x4*)(p + 8 * PITCH));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
+// LDS image of a row-major bf16 matrix [rows][D] (a query row's heads, or a
+// tile of key rows) read two ways: 16-byte row pieces (lane = row) and
+// ds_read_b64_tr_b16 (lane = column: the B operand of dK = G^T Q or of
+// grad_q = G K).  D = 128: rows
+// packed (256 bytes), 16-byte chunk x of row r stored at chunk x ^ f(r) with
+// f(r) = 4 (r & 3) + ((r >> 2) & 3): the 16 consecutive rows of a row-piece
+// read, and the 4 rows x 4 chunks of a half-wave's transposed read, land on
+// 16 distinct bank groups.  Smaller D: rows padded to the transposed reads'
+// pitch instead.
+template <int D>
+struct QStage {
+  static constexpr bool kSwizzle = D == 128;
+  static constexpr int kPitch = kSwizzle ? 2 * D : TrPitch<D>::kBytes;
+  static __device__ __forceinline__ uint32_t offset(int row, int byte_in_row) {
+    if constexpr (kSwizzle) {
+      const int f = 4 * (row & 3) + ((row >> 2) & 3);
+      return (uint32_t)(row * kPitch + ((((byte_in_row >> 4) ^ f) << 4) | (byte_in_row & 15)));
+    } else {
+      return (uint32_t)(row * kPitch + byte_in_row);
+    }
+  }
+  // B fragment of a 32x32x16 product whose K index runs over the image's
+  // rows and whose N index over its columns: lane (n = l % 32, g = l / 32)
+  // receives, as elements e = 0..7, rows row0 + 8 (e / 4) + 4 g + e % 4 of
+  // column col0 + n.  ds_read_b64_tr_b16 gives lane i of each 16-lane group
+  // column c0 + i of four rows: the row its lanes 4j .. 4j + 3 point at is
+  // the group's j-th row (lane 4j + q names columns c0 + 4q .. c0 + 4q + 3).
+  static __device__ __forceinline__ bf16x8 tr(const lds_char* m, int row0, int col0) {
+    const int lane = lane_id();
+    const int s = lane & 15, nh = (lane >> 4) & 1, g = lane >> 5;
+    const int row = row0 + 4 * g + (s >> 2);
+    const int byte = 2 * (col0 + 16 * nh + 4 * (s & 3));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSAI_LDS s16x4*)(m + offset(row, byte)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSAI_LDS s16x4*)(m + offset(row + 8, byte)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
 
 // Entry j0 + (lane % 32) of a row of supplied indices: its key (-1 when not
 // usable), incoming gradient (0 when not usable) and that key's fragments
@@ -102,8 +123,8 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
   using Scorer = TileScorer<HP, D>;
   using Acc = typename Scorer::Acc;
   constexpr int MT = HP / 32, NB = D / 32;
-  constexpr int PITCH = TrPitch<D>::kBytes;
-  constexpr int kStage = HP * PITCH;
+  using QS = QStage<D>;
+  constexpr int kStage = HP * QS::kPitch;
   __shared__ __align__(16) char smem_raw[kBwdWaves][kStage + 128];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = lane_id();
@@ -126,7 +147,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
     const int h = ch / (D / 8), part = ch % (D / 8);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (h < H) v = *reinterpret_cast<const u32x4*>(q + (qrow * H + h) * D + part * 8);
-    *reinterpret_cast<DSAI_LDS u32x4*>(qs + h * PITCH + part * 16) = v;
+    *reinterpret_cast<DSAI_LDS u32x4*>(qs + QS::offset(h, part * 16)) = v;
   }
 
   const int64_t orow = ((int64_t)b * S + t) * n;
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
         for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int p = 0; p < 2; ++p)
-            dk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[m][p], tr_frag<PITCH>(qs, 32 * m + 16 * p, 32 * nb),
+            dk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[m][p], QS::tr(qs, 32 * m + 16 * p, 32 * nb),
                                                          dk, 0, 0, 0);
         float* dst = gk + (int64_t)b * D + 32 * nb + c;
 #pragma unroll
@@ -182,9 +203,9 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_queries_kernel(
     const int32_t* __restrict__ sup, const float* __restrict__ grad, int S, int Skv, int B, int H,
     int ratio, int n, uint16_t* __restrict__ gq, float* __restrict__ gw) {
   using Scorer = TileScorer<HP, D>;
+  using QS = QStage<D>;
   constexpr int MT = HP / 32, KS = D / 16, NB = D / 32;
-  constexpr int PITCH = TrPitch<D>::kBytes;
-  constexpr int kTile = 32 * PITCH;
+  constexpr int kTile = 32 * QS::kPitch;
   __shared__ __align__(16) char smem_raw[kBwdWaves][kTile + 128];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = lane_id();
@@ -228,7 +249,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_queries_kernel(
       wave_lds_sync();  // the last tile's transposed reads and slot reads are done
 #pragma unroll
       for (int x = 0; x < KS; ++x)
-        *reinterpret_cast<DSAI_LDS bf16x8*>(kt + c * PITCH + 2 * (g * (D / 2) + 8 * x)) = cur.f[x];
+        *reinterpret_cast<DSAI_LDS bf16x8*>(kt + QS::offset(c, 2 * (g * (D / 2) + 8 * x))) = cur.f[x];
       if (g == 0) slot_g[c] = cur.g;
       wave_lds_sync();
       float gs[16];
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_queries_kernel(
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
-          acc_q[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[p], tr_frag<PITCH>(kt, 16 * p, 32 * nb),
+          acc_q[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[p], QS::tr(kt, 16 * p, 32 * nb),
                                                               acc_q[nb], 0, 0, 0);
     }
     cur = nxt;
@@ -285,38 +306,6 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_queries_kernel(
 constexpr int kKeyBlock = 256;
 constexpr int kKeysPerWave = 32;
 constexpr int kBlockWaves = kKeyBlock / kKeysPerWave;
-
-// LDS image of one query row q_t [HP heads][D] bf16 for the key-block
-// kernel, read two ways: 16-byte row pieces (lane = head: the A operand of d)
-// and ds_read_b64_tr_b16 (lane = dim: the B operand of dK).  D = 128: rows
-// packed (256 bytes), 16-byte chunk x of row r stored at chunk x ^ f(r) with
-// f(r) = 4 (r & 3) + ((r >> 2) & 3): the 16 consecutive rows of a row-piece
-// read, and the 4 rows x 4 chunks of a half-wave's transposed read, land on
-// 16 distinct bank groups.  Smaller D: rows padded to the transposed reads'
-// pitch instead.
-template <int D>
-struct QStage {
-  static constexpr bool kSwizzle = D == 128;
-  static constexpr int kPitch = kSwizzle ? 2 * D : TrPitch<D>::kBytes;
-  static __device__ __forceinline__ uint32_t offset(int row, int byte_in_row) {
-    if constexpr (kSwizzle) {
-      const int f = 4 * (row & 3) + ((row >> 2) & 3);
-      return (uint32_t)(row * kPitch + ((((byte_in_row >> 4) ^ f) << 4) | (byte_in_row & 15)));
-    } else {
-      return (uint32_t)(row * kPitch + byte_in_row);
-    }
-  }
-  // B fragment of dK = G^T Q (tr_frag's contract) from this image
-  static __device__ __forceinline__ bf16x8 tr(const lds_char* m, int row0, int col0) {
-    const int lane = lane_id();
-    const int s = lane & 15, nh = (lane >> 4) & 1, g = lane >> 5;
-    const int row = row0 + 4 * g + (s >> 2);
-    const int byte = 2 * (col0 + 16 * nh + 4 * (s & 3));
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSAI_LDS s16x4*)(m + offset(row, byte)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSAI_LDS s16x4*)(m + offset(row + 8, byte)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  }
-};
 
 // Per query row (b-major, as the index array): usable entries bucketed by
 // key block.  bounds[row][i] = first bucketed entry of block i (relative to
