@@ -325,10 +325,18 @@ __global__ __launch_bounds__(4 * 64) void bwd_bucket_kernel(
   for (int i = lane; i < nbk; i += kWave) h[i] = 0u;
   wave_lds_sync();
   const int64_t off = r * n;
-  for (int j = lane; j < n; j += kWave) {
-    const int s = sup[off + j];
-    if (s >= 0 && s < n_t)
-      __hip_atomic_fetch_add(&h[s / kKeyBlock], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // The row's entries go 8 per lane at a time, their loads issued together
+  // (clamped to the row's last entry and masked), so a long row does not
+  // wait on one load latency per 64 entries.
+  constexpr int U = 8;
+  for (int j0 = 0; j0 < n; j0 += U * kWave) {
+    int sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) sv[u] = sup[off + min(j0 + u * kWave + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j0 + u * kWave + lane < n && sv[u] >= 0 && sv[u] < n_t)
+        __hip_atomic_fetch_add(&h[sv[u] / kKeyBlock], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   wave_lds_sync();
   // exclusive scan of the bins; each lane takes a contiguous range of them
@@ -347,12 +355,22 @@ __global__ __launch_bounds__(4 * 64) void bwd_bucket_kernel(
   }
   if (lane == kWave - 1) bo[nbk] = (int32_t)incl;
   wave_lds_sync();
-  for (int j = lane; j < n; j += kWave) {
-    const int s = sup[off + j];
-    if (s >= 0 && s < n_t) {
-      const uint32_t pos = __hip_atomic_fetch_add(&h[s / kKeyBlock], 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
-      ent[off + pos] = int2{s, __float_as_int(grad[off + j])};
+  for (int j0 = 0; j0 < n; j0 += U * kWave) {
+    int sv[U];
+    float gv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = off + min(j0 + u * kWave + lane, n - 1);
+      sv[u] = sup[j];
+      gv[u] = grad[j];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u * kWave + lane < n && sv[u] >= 0 && sv[u] < n_t) {
+        const uint32_t pos = __hip_atomic_fetch_add(&h[sv[u] / kKeyBlock], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+        ent[off + pos] = int2{sv[u], __float_as_int(gv[u])};
+      }
     }
   }
 }
