@@ -18,7 +18,9 @@ cache write's k_norm runs over the 65536 cache rows, and the backward
 the step's top-k rows of whichever indexer workload is chosen; all three are
 reported in `breakdown`
 (score_at_indices_*, k_norm_*, backward_*: 6*H*D flops per selected entry,
-and the D fp32 key-gradient adds per entry per second).
+and the D fp32 key-gradient adds per entry per second).  The pooled decode
+stages are also captured once in a HIP graph and replayed
+(pooled_decode_graph_ms).
 `value` = prefill query tokens per second of the whole step (the pooled
 stages' time is counted against it as well).  HIP events on the stream the
 library launches on give per-stage times; the fused kernel's roofline is its
@@ -427,6 +429,33 @@ def main():
     bw_entries = selected_entries(case)
     del bw_ws, bw_out
 
+    # the pooled decode stages (kpool_compress -> select -> expand) captured
+    # once in a HIP graph and replayed: the decode step's latency without
+    # per-call launch work (not part of the step)
+    def pooled():
+        pix.kpool_compress(kn, gate, valid, ape, pool_k=pool_k, pool_tok=pool_tok, pool_valid=pool_valid)
+        pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids, pool_scores=pscores)
+        pix.expand(pids, tokens=toks)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pooled()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pooled()
+    graph.replay()
+    torch.cuda.synchronize()
+    a0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    a1.record()
+    torch.cuda.synchronize()
+    pooled_graph_ms = a0.elapsed_time(a1) / args.steps
+    del graph
+
     # the cache write's k_norm (LayerNorm with a bias) over the pooled
     # workload's 65536 cache rows (not part of the step)
     ln_g = torch.ones((pc.D,), dtype=torch.bfloat16, device=dev)
@@ -492,6 +521,7 @@ def main():
             "score_at_indices_TFLOPs": (at_flops / (at_ms * 1e-3) / 1e12) if at_ms else None,
             "k_norm_ms": ln_ms, "k_norm_GBps": ln_bytes / (ln_ms * 1e-3) / 1e9,
             "k_norm_bytes": ln_bytes,
+            "pooled_decode_graph_ms": pooled_graph_ms,
             "backward_ms": bw_ms,
             "backward_TFLOPs": 6.0 * case.H * case.D * bw_entries / (bw_ms * 1e-3) / 1e12,
             "backward_key_adds_G_per_s": case.D * bw_entries / (bw_ms * 1e-3) / 1e9,
