@@ -89,31 +89,74 @@ struct QStage {
   }
 };
 
-// Entry j0 + (lane % 32) of a row of supplied indices: its key (-1 when not
+// Entries j0 .. j0 + 31 of a row of supplied indices as loaded (lane c and
+// c + 32: entry j0 + c): key and incoming gradient.  The loads are clamped to
+// the row's last entry and never skipped, so a loop that prefetches with
+// them issues the same loads on every path and the compiler's wait counts
+// stay exact; usability is decided when the tile is taken.
+struct EntryIdx {
+  int sv;
+  float gv;
+  bool in;  // j0 + c < n
+
+  __device__ __forceinline__ void load(const int32_t* __restrict__ sup, const float* __restrict__ grad,
+                                       int64_t orow, int n, int j0) {
+    const int j = j0 + (lane_id() & 31);
+    in = j < n;
+    const int64_t e = orow + min(j, n - 1);
+    sv = sup[e];
+    gv = grad[e];
+  }
+};
+
+// One 32-entry tile of a row: lane (c, g) holds entry c's key (-1 when not
 // usable), incoming gradient (0 when not usable) and that key's fragments
-// for the forward's tile layout (lane (c, g): dims g*D/2 + 8x, x < D/16).
-// An unusable entry reads key 0 (n_t > 0, so it exists) and is discarded.
+// for the forward's tile layout (dims g*D/2 + 8x, x < D/16).  An unusable
+// entry reads key 0 (n_t > 0, so it exists) and is discarded.
 template <int D>
 struct EntryTile {
   int s;
   float g;
   bf16x8 f[D / 16];
 
-  __device__ __forceinline__ void fetch(const int32_t* __restrict__ sup, const float* __restrict__ grad,
-                                        const uint16_t* __restrict__ k, int64_t orow, int n, int j0,
-                                        int n_t, int B, int b) {
-    const int lane = lane_id();
-    const int c = lane & 31, g2 = lane >> 5;
-    const int j = j0 + c;
-    const int sv = j < n ? sup[orow + j] : -1;
-    const bool ok = sv >= 0 && sv < n_t;
-    s = ok ? sv : -1;
-    g = ok ? grad[orow + j] : 0.f;
-    const uint16_t* src = k + ((int64_t)(ok ? sv : 0) * B + b) * D + g2 * (D / 2);
+  __device__ __forceinline__ void take(const EntryIdx& e, const uint16_t* __restrict__ k, int n_t,
+                                       int B, int b) {
+    const bool ok = e.in && e.sv >= 0 && e.sv < n_t;
+    s = ok ? e.sv : -1;
+    g = ok ? e.gv : 0.f;
+    const uint16_t* src = k + ((int64_t)(ok ? e.sv : 0) * B + b) * D + (lane_id() >> 5) * (D / 2);
 #pragma unroll
     for (int x = 0; x < D / 16; ++x) f[x] = *reinterpret_cast<const bf16x8*>(src + 8 * x);
   }
 };
+
+// Software pipeline over a row's ngroups >= 1 tiles of 32 entries: while
+// tile i is worked on by body(tile), the key rows of tile i + 1 and the
+// indices of tile i + 2 are in flight.  Past the row's end the prefetches
+// repeat its last tile, so every step issues the same loads, and the wait
+// before a step covers only loads issued one step earlier.  Two register
+// sets alternate, so no tile is copied.
+template <int D, class Body>
+__device__ __forceinline__ void for_each_entry_tile(const int32_t* __restrict__ sup,
+                                                    const float* __restrict__ grad,
+                                                    const uint16_t* __restrict__ k, int64_t orow,
+                                                    int n, int n_t, int B, int b, int ngroups,
+                                                    Body&& body) {
+  EntryTile<D> ta, tb;
+  EntryIdx ahead;
+  ahead.load(sup, grad, orow, n, 0);
+  ta.take(ahead, k, n_t, B, b);
+  ahead.load(sup, grad, orow, n, min(1, ngroups - 1) * 32);
+  auto step = [&](EntryTile<D>& cur, EntryTile<D>& nxt, int it) {
+    nxt.take(ahead, k, n_t, B, b);
+    ahead.load(sup, grad, orow, n, min(it + 2, ngroups - 1) * 32);
+    body(cur);
+  };
+  for (int it = 0; it < ngroups; it += 2) {
+    step(ta, tb, it);
+    if (it + 1 < ngroups) step(tb, ta, it + 1);
+  }
+}
 
 template <int HP, int D>
 __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
@@ -152,10 +195,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
 
   const int64_t orow = ((int64_t)b * S + t) * n;
   const int ngroups = (n + 31) / 32;
-  EntryTile<D> cur, nxt;
-  cur.fetch(sup, grad, k, orow, n, 0, n_t, B, b);
-  for (int it = 0; it < ngroups; ++it) {
-    if (it + 1 < ngroups) nxt.fetch(sup, grad, k, orow, n, (it + 1) * 32, n_t, B, b);
+  for_each_entry_tile<D>(sup, grad, k, orow, n, n_t, B, b, ngroups, [&](const EntryTile<D>& cur) {
     if (ballot(cur.s >= 0) != 0) {  // wave-uniform: some entry of the tile is usable
       Acc acc;
       sc.mma(cur.f, acc);  // lane (c, g): key c, heads 32m + 8(r/4) + 4g + r%4
@@ -193,8 +233,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
           if (key[rr] >= 0) unsafeAtomicAdd(dst + (int64_t)key[rr] * B * D, dk[rr]);
       }
     }
-    cur = nxt;
-  }
+  });
 }
 
 template <int HP, int D>
@@ -237,44 +276,40 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_queries_kernel(
   float acc_w = 0.f;
 
   const int64_t orow = ((int64_t)b * S + t) * n;
-  const int ngroups = n_t > 0 ? (n + 31) / 32 : 0;  // n_t == 0: no entry is usable
-  EntryTile<D> cur, nxt;
-  if (ngroups > 0) cur.fetch(sup, grad, k, orow, n, 0, n_t, B, b);
-  for (int it = 0; it < ngroups; ++it) {
-    if (it + 1 < ngroups) nxt.fetch(sup, grad, k, orow, n, (it + 1) * 32, n_t, B, b);
-    if (ballot(cur.s >= 0) != 0) {  // wave-uniform
-      floatx16 dt = {};  // lane (c, g): head h, key slots 8(r/4) + 4g + r%4
+  if (n_t > 0)  // else no entry is usable
+    for_each_entry_tile<D>(sup, grad, k, orow, n, n_t, B, b, (n + 31) / 32, [&](const EntryTile<D>& cur) {
+      if (ballot(cur.s >= 0) != 0) {  // wave-uniform
+        floatx16 dt = {};  // lane (c, g): head h, key slots 8(r/4) + 4g + r%4
 #pragma unroll
-      for (int x = 0; x < KS; ++x) dt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.f[x], qf[x], dt, 0, 0, 0);
-      wave_lds_sync();  // the last tile's transposed reads and slot reads are done
+        for (int x = 0; x < KS; ++x) dt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.f[x], qf[x], dt, 0, 0, 0);
+        wave_lds_sync();  // the last tile's transposed reads and slot reads are done
 #pragma unroll
-      for (int x = 0; x < KS; ++x)
-        *reinterpret_cast<DSAI_LDS bf16x8*>(kt + QS::offset(c, 2 * (g * (D / 2) + 8 * x))) = cur.f[x];
-      if (g == 0) slot_g[c] = cur.g;
-      wave_lds_sync();
-      float gs[16];
+        for (int x = 0; x < KS; ++x)
+          *reinterpret_cast<DSAI_LDS bf16x8*>(kt + QS::offset(c, 2 * (g * (D / 2) + 8 * x))) = cur.f[x];
+        if (g == 0) slot_g[c] = cur.g;
+        wave_lds_sync();
+        float gs[16];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const floatx4 v = *reinterpret_cast<const DSAI_LDS floatx4*>(slot_g + 8 * rb + 4 * g);
-        gs[4 * rb + 0] = v.x; gs[4 * rb + 1] = v.y; gs[4 * rb + 2] = v.z; gs[4 * rb + 3] = v.w;
+        for (int rb = 0; rb < 4; ++rb) {
+          const floatx4 v = *reinterpret_cast<const DSAI_LDS floatx4*>(slot_g + 8 * rb + 4 * g);
+          gs[4 * rb + 0] = v.x; gs[4 * rb + 1] = v.y; gs[4 * rb + 2] = v.z; gs[4 * rb + 3] = v.w;
+        }
+        // A operand of grad_q = G K at K-step p: lane (c, g) element e is key
+        // slot 16p + 8(e/4) + 4g + e%4 of head h, i.e. register 8p + e.
+        bf16x8 ga[2];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          acc_w = fmaf(gs[rr], fmaxf(dt[rr], 0.f), acc_w);
+          ga[rr >> 3][rr & 7] = (__bf16)(dt[rr] > 0.f ? gs[rr] * wh : 0.f);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+            acc_q[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[p], QS::tr(kt, 16 * p, 32 * nb),
+                                                                acc_q[nb], 0, 0, 0);
       }
-      // A operand of grad_q = G K at K-step p: lane (c, g) element e is key
-      // slot 16p + 8(e/4) + 4g + e%4 of head h, i.e. register 8p + e.
-      bf16x8 ga[2];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        acc_w = fmaf(gs[rr], fmaxf(dt[rr], 0.f), acc_w);
-        ga[rr >> 3][rr & 7] = (__bf16)(dt[rr] > 0.f ? gs[rr] * wh : 0.f);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          acc_q[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[p], QS::tr(kt, 16 * p, 32 * nb),
-                                                              acc_q[nb], 0, 0, 0);
-    }
-    cur = nxt;
-  }
+    });
 
   // grad_w: lanes c and c + 32 hold the two halves of head h's key slots
   const float tot_w = Scorer::combine(acc_w);

@@ -106,7 +106,10 @@ hipError_t launch_kpool(const KpoolArgs& a, hipStream_t st) {
 // each row's query stays in registers across the range.  The key loop is the
 // fused indexer's: double-buffered LDS tiles, the next tile's fragments
 // fetched right after the barrier, the head reduction of tile it - 1
-// interleaved with tile it's products, and tile it - 2's scores stored.
+// interleaved with tile it's products, and tile it - 2's scores stored.  With
+// one workgroup per CU and little math per tile, the loop is bound by load
+// latency, so two register stages (even and odd tiles) keep each tile's load
+// in flight for two steps before it is staged.
 // ---------------------------------------------------------------------------
 constexpr int kPoolTilesPerBlock = 16;
 constexpr int kPoolRows = 8;
@@ -137,8 +140,9 @@ pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   sc.load_query(q + (int64_t)(active ? row : 0) * H * D, w + (int64_t)(active ? row : 0) * H, H,
                 active);
   for (int i = threadIdx.x; i < kPer; i += kPoolRows * 64) valid_s[i] = i < np ? pool_valid[p0 + i] : 0;
-  TileLoader<D, kPoolRows * 64> ld;
-  ld.init(pool_k + (int64_t)p0 * D, (uint32_t)D, (uint32_t)((int64_t)np * D * 2));
+  TileLoader<D, kPoolRows * 64> lda, ldb;  // even and odd tiles
+  lda.init(pool_k + (int64_t)p0 * D, (uint32_t)D, (uint32_t)((int64_t)np * D * 2));
+  ldb.init(pool_k + (int64_t)p0 * D, (uint32_t)D, (uint32_t)((int64_t)np * D * 2));
   float* srow = scores + (int64_t)row * P + p0;
 
   auto buf = [&](int it) { return tiles + (it & 1) * G::kTileBytes; };
@@ -148,33 +152,36 @@ pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
     const int i = it_rec * G::kTileKeys + (lane & 31);
     if (active && lane < 32 && i < np) srow[i] = valid_s[i] ? s : -__builtin_inff();
   };
-  auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin, bool red) {
+  // ld holds tile it + 2 (loaded two steps earlier), then takes tile it + 4
+  auto step = [&](int it, TileLoader<D, kPoolRows * 64>& ld, Frag& fcur, Frag& fnext, Acc& cur,
+                  const Acc& old, bool fin, bool red) {
     __syncthreads();
     sc.fetch(buf(it + 1), fnext);
     if (fin) finish(it - 2);
     ld.store(buf(it + 2));
-    ld.load((uint32_t)(it + 3) * G::kTileKeys);
+    ld.load((uint32_t)(it + 4) * G::kTileKeys);
     sc.mma(fcur, cur);
     if (red) part = sc.reduce_half(old, 0);
   };
   Acc acc0, acc1;
   Frag f0, f1;
-  ld.load(0u);
-  ld.store(buf(0));
-  ld.load((uint32_t)G::kTileKeys);
-  ld.store(buf(1));
-  ld.load((uint32_t)(2 * G::kTileKeys));
+  lda.load(0u);
+  ldb.load((uint32_t)G::kTileKeys);
+  lda.store(buf(0));
+  lda.load((uint32_t)(2 * G::kTileKeys));
+  ldb.store(buf(1));
+  ldb.load((uint32_t)(3 * G::kTileKeys));
   __syncthreads();
   sc.fetch(buf(0), f0);
-  step(0, f0, f1, acc0, acc1, false, false);
+  step(0, lda, f0, f1, acc0, acc1, false, false);
   if (ntiles > 1) {
-    step(1, f1, f0, acc1, acc0, false, true);
+    step(1, ldb, f1, f0, acc1, acc0, false, true);
     int it = 2;
     for (; it + 1 < ntiles; it += 2) {
-      step(it, f0, f1, acc0, acc1, true, true);
-      step(it + 1, f1, f0, acc1, acc0, true, true);
+      step(it, lda, f0, f1, acc0, acc1, true, true);
+      step(it + 1, ldb, f1, f0, acc1, acc0, true, true);
     }
-    if (it < ntiles) step(it, f0, f1, acc0, acc1, true, true);
+    if (it < ntiles) step(it, lda, f0, f1, acc0, acc1, true, true);
     finish(ntiles - 2);
   }
   part = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, 0);
