@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+from parity import log
+
 pytestmark = pytest.mark.gpu
 
 
@@ -99,3 +101,33 @@ def test_sort_rows_is_idempotent_and_k1_is_a_noop(ix):
     ix.sort_rows(one_i, one_s)
     torch.cuda.synchronize()
     assert one_i.cpu().tolist() == [[5], [-1]]
+
+
+@pytest.mark.parametrize("k,rows", [(64, 40001), (512, 20001)])
+def test_sort_many_rows(ix, k, rows):
+    """More rows than 8 per resident workgroup slot, so each workgroup sorts
+    two rows (the second's loads in flight during the first's sort), with an
+    odd row count (the last workgroup has one row).  Tied scores, partly
+    padded rows and fully padded rows; checked against one host lexsort."""
+    log(f"[gpu] sort many rows k={k} rows={rows}")
+    rng = np.random.default_rng(31 + k)
+    idx = (np.cumsum(rng.integers(1, 5, size=(rows, k)), axis=1) - 1).astype(np.int32)
+    sc = (np.round(rng.standard_normal((rows, k)) * 8.0) / 8.0).astype(np.float32) + np.float32(0)
+    n = np.full(rows, k)
+    short = rng.random(rows) < 0.3
+    n[short] = rng.integers(0, k, size=int(short.sum()))
+    pad = np.arange(k)[None, :] >= n[:, None]
+    idx[pad] = -1
+    sc[pad] = -np.inf
+    gi, gs = torch.from_numpy(idx).cuda(), torch.from_numpy(sc).cuda()
+    ix.sort_rows(gi, gs)
+    torch.cuda.synchronize()
+    r = np.repeat(np.arange(rows), k)
+    order = np.lexsort((idx.ravel(), -sc.ravel().astype(np.float64), r))
+    ei, es = idx.ravel()[order].reshape(rows, k), sc.ravel()[order].reshape(rows, k)
+    got_i, got_s = gi.cpu().numpy(), gs.cpu().numpy()
+    bad = np.flatnonzero(~(got_i == ei).all(axis=1))
+    assert bad.size == 0, f"rows {bad[:5]} differ in indices"
+    z = np.float32(0)
+    assert np.array_equal(np.where(got_s == 0, z, got_s).view(np.uint32),
+                          np.where(es == 0, z, es).view(np.uint32))
