@@ -32,6 +32,19 @@
 
 namespace dsai {
 
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Elements e, e + 1 of a bf16 operand: the gated weights a (where d0 > 0)
+// and b (where d1 > 0), else 0, rounded to nearest even in one paired
+// conversion.
+__device__ __forceinline__ void set_gate_pair(bf16x8& v, int e, float d0, float a, float d1,
+                                              float b) {
+  const bf16x2 p = __builtin_convertvector((floatx2){d0 > 0.f ? a : 0.f, d1 > 0.f ? b : 0.f}, bf16x2);
+  v[e] = p[0];
+  v[e + 1] = p[1];
+}
+
 namespace {
 
 constexpr int kBwdWaves = 4;
@@ -205,9 +218,9 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          ga[m][rr >> 3][rr & 7] =
-              (__bf16)(acc[0][m][rr] > 0.f ? cur.g * sc.wv[0][m][rr] : 0.f);
+        for (int rr = 0; rr < 16; rr += 2)
+          set_gate_pair(ga[m][rr >> 3], rr & 7, acc[0][m][rr], cur.g * sc.wv[0][m][rr],
+                        acc[0][m][rr + 1], cur.g * sc.wv[0][m][rr + 1]);
       wave_lds_sync();  // the query stage (first tile) and the last tile's slot reads
       if (g == 0) slot_key[c] = cur.s;
       wave_lds_sync();
@@ -298,9 +311,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_queries_kernel(
         // slot 16p + 8(e/4) + 4g + e%4 of head h, i.e. register 8p + e.
         bf16x8 ga[2];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
+        for (int rr = 0; rr < 16; rr += 2) {
           acc_w = fmaf(gs[rr], fmaxf(dt[rr], 0.f), acc_w);
-          ga[rr >> 3][rr & 7] = (__bf16)(dt[rr] > 0.f ? gs[rr] * wh : 0.f);
+          acc_w = fmaf(gs[rr + 1], fmaxf(dt[rr + 1], 0.f), acc_w);
+          set_gate_pair(ga[rr >> 3], rr & 7, dt[rr], gs[rr] * wh, dt[rr + 1], gs[rr + 1] * wh);
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -572,9 +586,10 @@ __global__ __launch_bounds__(kBlockWaves * 64) void bwd_keyblock_kernel(
 #pragma unroll
             for (int tt = 0; tt < KT; ++tt)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
+              for (int i = 0; i < 4; i += 2) {
                 const int rr = 4 * rb + i;
-                ga[tt][m][rr >> 3][rr & 7] = (__bf16)(acc[tt][m][rr] > 0.f ? gv[tt] * w4[i] : 0.f);
+                set_gate_pair(ga[tt][m][rr >> 3], rr & 7, acc[tt][m][rr], gv[tt] * w4[i],
+                              acc[tt][m][rr + 1], gv[tt] * w4[i + 1]);
               }
           }
 #pragma unroll
