@@ -15,10 +15,12 @@ Outside the step, the same top-k rows are rescored through the
 topk_indices form of dsai_score_topk (scores at supplied indices), and the
 cache write's k_norm runs over the 65536 cache rows, and the backward
 (gradients of the selected scores, with seeded incoming gradients) runs at
-the step's top-k rows of whichever indexer workload is chosen; all three are
-reported in `breakdown`
+the step's top-k rows of whichever indexer workload is chosen, and the
+prefill rows and keys run as 4 packed sequences of 1024 (dsai_score_topk_packed,
+score order); all four are reported in `breakdown`
 (score_at_indices_*, k_norm_*, backward_*: 6*H*D flops per selected entry,
-and the D fp32 key-gradient adds per entry per second).  The pooled decode
+and the D fp32 key-gradient adds per entry per second; packed_4x1024_*:
+2*H*D flops per visible pair of the four sequences).  The pooled decode
 stages are also captured once in a HIP graph and replayed
 (pooled_decode_graph_ms).
 `value` = prefill query tokens per second of the whole step (the pooled
@@ -408,6 +410,30 @@ def main():
         at_ms = a0.elapsed_time(a1) / args.steps
         at_flops = 2.0 * case.H * case.D * selected_entries(case)
 
+    # packed sequences (not part of the step): the prefill rows and keys cut
+    # into 4 sequences of S/4, each causal on its own keys (prefill only)
+    pk_ms = pk_flops = None
+    if case.name == "prefill":
+        nseq = 4
+        cu = np.arange(nseq + 1, dtype=np.int64) * (case.S // nseq)
+        pk_ix = dsai.Indexer(heads=case.H, dim=case.D)
+        pq_, pk_, pw_ = q[:, 0], k[:, 0], w[:, 0]
+        pk_i = torch.empty((case.S, case.topk), dtype=torch.int32, device=dev)
+        pk_s = torch.empty((case.S, case.topk), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            pk_ix.score_topk_packed(pq_, pk_, pw_, cu, cu, case.compress_ratio, case.topk,
+                                    out_idx=pk_i, out_score=pk_s)
+        a0.record()
+        for _ in range(args.steps):
+            pk_ix.score_topk_packed(pq_, pk_, pw_, cu, cu, case.compress_ratio, case.topk,
+                                    out_idx=pk_i, out_score=pk_s)
+        a1.record()
+        torch.cuda.synchronize()
+        pk_ms = a0.elapsed_time(a1) / args.steps
+        t = np.arange(case.S // nseq, dtype=np.int64)
+        pk_flops = 2.0 * case.H * case.D * nseq * float(
+            np.minimum(case.S // nseq, (t + 1) // case.compress_ratio).sum())
+
     # the backward (gradients of the selected scores) at the step's own top-k
     # rows, with seeded incoming gradients (not part of the step)
     bw_ix = dsai.Indexer(heads=case.H, dim=case.D)
@@ -522,6 +548,8 @@ def main():
             "k_norm_ms": ln_ms, "k_norm_GBps": ln_bytes / (ln_ms * 1e-3) / 1e9,
             "k_norm_bytes": ln_bytes,
             "pooled_decode_graph_ms": pooled_graph_ms,
+            "packed_4x1024_ms": pk_ms,
+            "packed_4x1024_TFLOPs": (pk_flops / (pk_ms * 1e-3) / 1e12) if pk_ms else None,
             "backward_ms": bw_ms,
             "backward_TFLOPs": 6.0 * case.H * case.D * bw_entries / (bw_ms * 1e-3) / 1e12,
             "backward_key_adds_G_per_s": case.D * bw_entries / (bw_ms * 1e-3) / 1e9,

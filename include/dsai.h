@@ -147,6 +147,46 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
                     int compress_ratio, int topk, const int32_t* topk_indices,
                     int32_t* out_idx, float* out_score, void* stream);
 
+/* Packed sequences ("packed-sequence dispatch" among the local modifications
+ * listed on the NeMo AutoModel page
+ * "nemo_automodel.components.models.deepseek_v4.kernels"; the
+ * tilelang_indexer page offers a per-sample interface).  The page gives no layout
+ * for it; this call takes the plain reading that a packed batch is a set of
+ * independent samples laid end to end, each the B = 1 problem of
+ * dsai_score_topk:
+ *
+ *   index_q  [Tq, H, D]   bf16   rows of all sequences, concatenated
+ *   index_k  [Tk, D]      bf16
+ *   weights  [Tq, H]      fp32
+ *   cu_seqlens_q, cu_seqlens_k: HOST arrays of nseq + 1 int64 offsets,
+ *            0 = cu[0] <= cu[1] <= ... <= cu[nseq] = Tq (resp. Tk)
+ *   topk_indices NULL, or [Tq, topk] int32 (scores at supplied indices)
+ *   out_idx  [Tq, topk]   int32  written
+ *   out_score[Tq, topk]   fp32   written
+ *
+ * Sequence i owns query rows cu_seqlens_q[i] .. cu_seqlens_q[i+1] - 1 and
+ * keys cu_seqlens_k[i] .. cu_seqlens_k[i+1] - 1.  Its row at local position t
+ * (0 at the sequence's first row) sees its local keys s < min(len_k,
+ * floor((t+1) / compress_ratio)); indices, in and out, are local to the
+ * sequence (what dsai_score_topk returns for that sequence alone), with the
+ * same scores, ordering (cfg.order), ties and padding.  A sequence with no
+ * keys gets padding rows.
+ *
+ * topk % 4 == 0 (every sequence's output then starts 16-byte aligned), nseq
+ * >= 0, offsets as above, Tq and Tk < 2^31, compress_ratio >= 1
+ * (DSAI_ERR_INVALID_ARG otherwise); a sequence whose keys span 4 GiB or
+ * more, or a topk the selection cannot hold, gives DSAI_ERR_UNSUPPORTED;
+ * every refusal comes before the first launch.  One launch per non-empty
+ * sequence (one per cfg.chunk_rows rows of it, in order, if chunked);
+ * consecutive sequences alternate between the handle's two streams, forked
+ * from `stream` and joined back to it as for chunked dsai_score_topk calls;
+ * then, in score order, one row sort over all Tq rows on `stream`. */
+int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index_k,
+                           const float* weights, int64_t nseq, const int64_t* cu_seqlens_q,
+                           const int64_t* cu_seqlens_k, int compress_ratio, int topk,
+                           const int32_t* topk_indices, int32_t* out_idx, float* out_score,
+                           void* stream);
+
 /* ---- backward: gradients of the selected scores ------------------------- */
 /* Workspace bytes of dsai_indexer_backward for these sizes (the same
  * arguments as the call): an fp32 [Skv, B, cfg.dim] accumulator of grad_k

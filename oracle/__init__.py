@@ -17,6 +17,7 @@ from .indexer import (  # noqa: F401
     rank_desc,
     select_topk,
     score_topk,
+    score_topk_packed,
     scores_at_indices,
     indexer_backward,
     round_to_bf16,

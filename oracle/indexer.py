@@ -42,6 +42,11 @@ Readings where the pages are silent (each also listed in the design notes):
 * Backward (V4IndexerFunction.backward(grad_scores, grad_indices)): the
   gradient of the returned scores only (indices are integers); ReLU's
   derivative is taken as 0 at 0; unusable entries (score -inf) get none.
+* Packed sequences ("packed-sequence dispatch" among the local modifications
+  on the "nemo_automodel.components.models.deepseek_v4.kernels" page, which
+  gives it no layout): independent samples laid end to end, each the
+  one-sample problem on its own rows and keys (positions and key indices
+  local to the sample), split by cumulative offsets cu_q / cu_k.
 """
 from __future__ import annotations
 
@@ -147,6 +152,35 @@ def score_topk(q: np.ndarray, k: np.ndarray, w: np.ndarray, compress_ratio: int,
                 full.append(s)
     if row_values:
         return idx, vals, full
+    return idx, vals
+
+
+def _sequence_spans(cu_q, cu_k):
+    """(first row, end row, first key, end key) of each packed sequence."""
+    return [(int(cu_q[i]), int(cu_q[i + 1]), int(cu_k[i]), int(cu_k[i + 1]))
+            for i in range(len(cu_q) - 1)]
+
+
+def score_topk_packed(q: np.ndarray, k: np.ndarray, w: np.ndarray, cu_q, cu_k,
+                      compress_ratio: int, topk: int, topk_indices=None):
+    """Packed sequences: q [Tq, H, D], k [Tk, D], w [Tq, H], and nseq + 1
+    cumulative offsets cu_q, cu_k.  Sequence i is the one-sample problem
+    (B = 1) on rows cu_q[i]:cu_q[i+1] and keys cu_k[i]:cu_k[i+1], answered by
+    score_topk (or scores_at_indices with that sequence's rows of
+    topk_indices [Tq, topk], indices local to the sequence); the rows are
+    concatenated.  Returns (idx int32 [Tq, topk], vals float64 [Tq, topk])."""
+    Tq = q.shape[0]
+    idx = np.empty((Tq, topk), dtype=np.int32)
+    vals = np.empty((Tq, topk), dtype=np.float64)
+    for q0, q1, k0, k1 in _sequence_spans(cu_q, cu_k):
+        if q1 == q0:
+            continue
+        qs, ks, ws = q[q0:q1, None], k[k0:k1, None], w[q0:q1, None]
+        if topk_indices is None:
+            oi, ov = score_topk(qs, ks, ws, compress_ratio, topk)
+        else:
+            oi, ov = scores_at_indices(qs, ks, ws, compress_ratio, topk_indices[None, q0:q1])
+        idx[q0:q1], vals[q0:q1] = oi[0], ov[0]
     return idx, vals
 
 

@@ -21,6 +21,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 __all__ = ["DsaiError", "Indexer", "IndexerFunction", "load_library", "library_path", "EXPORTS"]
@@ -31,7 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "libdsai.so")
 # Every symbol include/dsai.h declares.
 EXPORTS = (
     "dsai_create", "dsai_destroy", "dsai_status_string", "dsai_last_hip_error",
-    "dsai_score_topk", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
+    "dsai_score_topk", "dsai_score_topk_packed", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
     "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
     "dsai_sort_rows", "dsai_k_norm", "dsai_backward_workspace_size", "dsai_indexer_backward",
 )
@@ -79,6 +80,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_status_string": [c_int],
         "dsai_last_hip_error": [vp],
         "dsai_score_topk": [vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, vp, vp, vp],
+        "dsai_score_topk_packed": [vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp, vp, vp],
         "dsai_pool_count": [vp, i64, ctypes.POINTER(i64)],
         "dsai_kpool_compress": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp],
         "dsai_index_scores": [vp, vp, vp, vp, vp, i64, i64, vp, vp],
@@ -201,6 +203,47 @@ class Indexer:
                                            _ptr(topk_indices), _ptr(out_idx), _ptr(out_score),
                                            _stream(dev))
         self._check(st, "dsai_score_topk")
+        return out_idx, out_score
+
+    def score_topk_packed(self, index_q: torch.Tensor, index_k: torch.Tensor,
+                          weights: torch.Tensor, cu_seqlens_q, cu_seqlens_k,
+                          compress_ratio: int, topk: int, topk_indices=None,
+                          out_idx: Optional[torch.Tensor] = None,
+                          out_score: Optional[torch.Tensor] = None):
+        """Packed sequences: index_q [Tq,H,D] bf16, index_k [Tk,D] bf16,
+        weights [Tq,H] fp32, cu_seqlens_q / cu_seqlens_k nseq + 1 offsets
+        (a sequence of ints or a CPU tensor; they are read on the host) ->
+        (idx [Tq,topk] int32, score [Tq,topk] fp32).  Each sequence is the
+        one-sample problem on its own rows and keys; indices are local to it.
+        topk must be a multiple of 4."""
+        cq = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
+        ck = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int64))
+        if cq.ndim != 1 or ck.shape != cq.shape or cq.size < 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k: equal-length 1-D offset lists")
+        nseq = cq.size - 1
+        Tq, Tk = index_q.shape[0], index_k.shape[0]
+        H, D = self.cfg.heads, self.cfg.dim
+        dev = index_q.device
+        _need(index_q, "index_q", torch.bfloat16, (Tq, H, D))
+        _need(index_k, "index_k", torch.bfloat16, (Tk, D), dev)
+        _need(weights, "weights", torch.float32, (Tq, H), dev)
+        if int(cq[-1]) != Tq or int(ck[-1]) != Tk:
+            raise ValueError("the last offsets must equal the row counts of index_q and index_k")
+        if topk_indices is not None:
+            _need(topk_indices, "topk_indices", torch.int32, (Tq, topk), dev)
+        if out_idx is None:
+            out_idx = torch.empty((Tq, topk), dtype=torch.int32, device=dev)
+        if out_score is None:
+            out_score = torch.empty((Tq, topk), dtype=torch.float32, device=dev)
+        _need(out_idx, "out_idx", torch.int32, (Tq, topk), dev)
+        _need(out_score, "out_score", torch.float32, (Tq, topk), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_score_topk_packed(
+                self._h, _ptr(index_q), _ptr(index_k), _ptr(weights), nseq,
+                cq.ctypes.data_as(ctypes.c_void_p), ck.ctypes.data_as(ctypes.c_void_p),
+                int(compress_ratio), int(topk), _ptr(topk_indices), _ptr(out_idx),
+                _ptr(out_score), _stream(dev))
+        self._check(st, "dsai_score_topk_packed")
         return out_idx, out_score
 
     # -- backward ------------------------------------------------------------

@@ -155,10 +155,11 @@ const char* dsai_status_string(int status) {
 
 int dsai_last_hip_error(dsai_handle h) { return h ? h->last_hip_error : 0; }
 
-int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, const float* weights,
-                    int64_t S, int64_t Skv, int64_t B, int compress_ratio, int topk,
-                    const int32_t* topk_indices, int32_t* out_idx, float* out_score,
-                    void* stream) {
+// One per-sample problem (the body of dsai_score_topk); `sort`: score order.
+static int score_topk_one(dsai_handle h, const void* index_q, const void* index_k,
+                          const float* weights, int64_t S, int64_t Skv, int64_t B,
+                          int compress_ratio, int topk, const int32_t* topk_indices,
+                          int32_t* out_idx, float* out_score, void* stream, bool sort) {
   if (!h) return DSAI_ERR_NULLPTR;
   if (S < 0 || Skv < 0 || B < 0 || compress_ratio < 1) return DSAI_ERR_INVALID_ARG;
   if (topk < 1 || topk > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
@@ -206,7 +207,7 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
   a.S = S; a.Skv = Skv; a.B = B;
   a.H = h->cfg.heads; a.D = h->cfg.dim; a.ratio = compress_ratio; a.topk = topk;
   a.chunk_rows = h->cfg.chunk_rows;
-  a.sort = h->cfg.order == DSAI_ORDER_SCORE;
+  a.sort = sort;
   a.out_idx = out_idx; a.out_score = out_score;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t le;
@@ -218,6 +219,97 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, con
     le = dsai::launch_score_topk(a, plan, st, nullptr);
   if (le != hipSuccess) return hip_status(h, le);
   if (a.sort) le = dsai::launch_sort_rows(out_idx, out_score, B * S, topk, st);
+  return hip_status(h, le);
+}
+
+int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k, const float* weights,
+                    int64_t S, int64_t Skv, int64_t B, int compress_ratio, int topk,
+                    const int32_t* topk_indices, int32_t* out_idx, float* out_score,
+                    void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  return score_topk_one(h, index_q, index_k, weights, S, Skv, B, compress_ratio, topk,
+                        topk_indices, out_idx, out_score, stream,
+                        h->cfg.order == DSAI_ORDER_SCORE);
+}
+
+int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index_k,
+                           const float* weights, int64_t nseq, const int64_t* cu_seqlens_q,
+                           const int64_t* cu_seqlens_k, int compress_ratio, int topk,
+                           const int32_t* topk_indices, int32_t* out_idx, float* out_score,
+                           void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (nseq < 0 || compress_ratio < 1 || topk < 1 || topk > DSAI_MAX_TOPK || topk % 4 != 0)
+    return DSAI_ERR_INVALID_ARG;
+  if (nseq == 0) return DSAI_OK;
+  if (!cu_seqlens_q || !cu_seqlens_k) return DSAI_ERR_NULLPTR;
+  if (cu_seqlens_q[0] != 0 || cu_seqlens_k[0] != 0) return DSAI_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < nseq; ++i)
+    if (cu_seqlens_q[i + 1] < cu_seqlens_q[i] || cu_seqlens_k[i + 1] < cu_seqlens_k[i])
+      return DSAI_ERR_INVALID_ARG;
+  const int64_t Tq = cu_seqlens_q[nseq];
+  if (Tq > kI32 || cu_seqlens_k[nseq] > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Tq == 0) return DSAI_OK;
+  if (!index_q || !weights || !out_idx || !out_score) return DSAI_ERR_NULLPTR;
+  if (cu_seqlens_k[nseq] > 0 && !index_k) return DSAI_ERR_NULLPTR;
+  const int64_t H = h->cfg.heads, D = h->cfg.dim;
+  const bool sort = h->cfg.order == DSAI_ORDER_SCORE && !topk_indices;
+  if (!topk_indices) {  // every refusal before the first launch
+    hipError_t e = device_limits(h);
+    if (e != hipSuccess) return hip_status(h, e);
+    for (int64_t i = 0; i < nseq; ++i) {
+      const int64_t Skv = cu_seqlens_k[i + 1] - cu_seqlens_k[i];
+      if (cu_seqlens_q[i + 1] == cu_seqlens_q[i]) continue;
+      if (Skv * D * 2 > (int64_t)0xFFFFFFFF) return DSAI_ERR_UNSUPPORTED;
+      if (dsai::plan_score_select(H <= 32 ? 32 : 64, (int)D, topk, Skv, h->lds_limit)
+              .rows_per_block < 1)
+        return DSAI_ERR_UNSUPPORTED;
+    }
+  }
+  if (!aligned(index_q) || !aligned(index_k) || !aligned(out_idx) || !aligned(out_score) ||
+      !aligned(topk_indices))
+    return DSAI_ERR_INVALID_ARG;
+  // Sequence i is the one-sample problem on its own rows and keys (topk % 4
+  // == 0 keeps each sequence's output rows 16-byte aligned).  Consecutive
+  // non-empty sequences alternate between the handle's two streams, so two
+  // are in flight; a sequence longer than cfg.chunk_rows runs its chunks in
+  // order on its stream.
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t le = on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
+    int64_t j = 0;
+    for (int64_t i = 0; i < nseq; ++i) {
+      const int64_t q0 = cu_seqlens_q[i], k0 = cu_seqlens_k[i];
+      const int64_t S = cu_seqlens_q[i + 1] - q0, Skv = cu_seqlens_k[i + 1] - k0;
+      if (S == 0) continue;
+      const hipStream_t sj = (j++ & 1) ? s1 : s0;
+      const uint16_t* q = static_cast<const uint16_t*>(index_q) + q0 * H * D;
+      const uint16_t* k = Skv > 0 ? static_cast<const uint16_t*>(index_k) + k0 * D : nullptr;
+      hipError_t e;
+      if (topk_indices) {
+        dsai::ScoreAtArgs a;
+        a.q = q; a.k = k; a.w = weights + q0 * H;
+        a.S = S; a.Skv = Skv; a.B = 1;
+        a.H = (int)H; a.D = (int)D; a.ratio = compress_ratio; a.n = topk;
+        a.chunk_rows = h->cfg.chunk_rows;
+        a.sup = topk_indices + q0 * topk;
+        a.out_idx = out_idx + q0 * topk; a.out_score = out_score + q0 * topk;
+        e = dsai::launch_score_at(a, sj, nullptr);
+      } else {
+        const dsai::ScoreSelectPlan plan =
+            dsai::plan_score_select(H <= 32 ? 32 : 64, (int)D, topk, Skv, h->lds_limit);
+        dsai::ScoreTopkArgs a;
+        a.q = q; a.k = k; a.w = weights + q0 * H;
+        a.S = S; a.Skv = Skv; a.B = 1;
+        a.H = (int)H; a.D = (int)D; a.ratio = compress_ratio; a.topk = topk;
+        a.chunk_rows = h->cfg.chunk_rows;
+        a.sort = false;
+        a.out_idx = out_idx + q0 * topk; a.out_score = out_score + q0 * topk;
+        e = dsai::launch_score_topk(a, plan, sj, nullptr);
+      }
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
+  if (le == hipSuccess && sort) le = dsai::launch_sort_rows(out_idx, out_score, Tq, topk, st);
   return hip_status(h, le);
 }
 

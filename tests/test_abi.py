@@ -136,6 +136,38 @@ def test_score_topk_argument_errors(lib):
     lib.dsai_destroy(h)
 
 
+def test_score_topk_packed_argument_errors(lib):
+    st, h = _create(lib)
+    assert st == OK
+    offs = lambda *v: (ctypes.c_int64 * len(v))(*v)
+
+    def call(n=2, cq=None, ck=None, r=1, topk=4, tki=None, q=FAKE, k=FAKE, w=FAKE, oi=FAKE,
+             os_=FAKE):
+        cq = offs(0, 3, 8) if cq is None else cq
+        ck = offs(0, 5, 9) if ck is None else ck
+        return lib.dsai_score_topk_packed(h, q, k, w, n, cq, ck, r, topk, tki, oi, os_, None)
+    assert call(n=-1) == INVALID
+    assert call(r=0) == INVALID
+    assert call(topk=0) == INVALID
+    assert call(topk=6) == INVALID                          # not a multiple of 4
+    assert call(topk=8196) == INVALID
+    assert call(n=0) == OK                                  # no sequence: nothing launched
+    assert lib.dsai_score_topk_packed(h, FAKE, FAKE, FAKE, 2, None, offs(0, 5, 9), 1, 4, None,
+                                      FAKE, FAKE, None) == NULLPTR
+    assert call(cq=offs(1, 3, 8)) == INVALID                # offsets start at 0
+    assert call(ck=offs(0, 5, 4)) == INVALID                # and never decrease
+    assert call(cq=offs(0, 0, 2 ** 31)) == INVALID
+    assert call(cq=offs(0, 0, 0)) == OK                     # every sequence empty
+    assert call(q=None) == NULLPTR
+    assert call(w=None) == NULLPTR
+    assert call(oi=None) == NULLPTR
+    assert call(os_=None) == NULLPTR
+    assert call(k=None) == NULLPTR                          # keys present, pointer missing
+    assert lib.dsai_score_topk_packed(None, FAKE, FAKE, FAKE, 2, offs(0, 3, 8), offs(0, 5, 9),
+                                      1, 4, None, FAKE, FAKE, None) == NULLPTR
+    lib.dsai_destroy(h)
+
+
 def test_k_norm_argument_errors(lib):
     st, h = _create(lib)
     assert st == OK

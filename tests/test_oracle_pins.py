@@ -182,6 +182,55 @@ def test_bruteforce_score_topk():
     check_bruteforce_score_topk()
 
 
+def _tiny_offsets(rng, n, total_max):
+    lens = rng.integers(0, total_max + 1, size=n)
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+def check_bruteforce_packed(n_cases=12, seed=11):
+    """Packed sequences against one global brute force: every packed row t of
+    sequence i (local position t - cu_q[i]) scores the global keys
+    cu_k[i] .. cu_k[i] + min(len_k, floor((t_local + 1) / r)) - 1 exactly,
+    ranks them by (score desc, global key asc) and reports them minus
+    cu_k[i]; no per-sequence sub-problem is formed.  Also the supplied-index
+    form at the rows' own selection."""
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        nseq = int(rng.integers(1, 4))
+        cu_q, cu_k = _tiny_offsets(rng, nseq, 5), _tiny_offsets(rng, nseq, 6)
+        Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+        H, D, r = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 3))
+        topk = int(rng.integers(1, 6))
+        q = rng.choice(_QK_SET, (Tq, H, D)).astype(np.float64)
+        k = rng.choice(_QK_SET, (max(Tk, 1), D)).astype(np.float64)[:Tk]
+        w = rng.choice(_W_SET, (Tq, H)).astype(np.float64)
+        idx, vals = oracle.score_topk_packed(q, k, w, cu_q, cu_k, r, topk)
+        for i in range(nseq):
+            for t in range(int(cu_q[i]), int(cu_q[i + 1])):
+                tl = t - int(cu_q[i])
+                n = min(int(cu_k[i + 1] - cu_k[i]), (tl + 1) // r)
+                keys = list(range(int(cu_k[i]), int(cu_k[i]) + n))
+                ex = []
+                for g in keys:
+                    tot = Fraction(0)
+                    for h in range(H):
+                        d = sum(Fraction(float(q[t, h, e])) * Fraction(float(k[g, e])) for e in range(D))
+                        tot += Fraction(float(w[t, h])) * max(d, Fraction(0))
+                    ex.append((-tot, g))
+                ex.sort()
+                want = [g - int(cu_k[i]) for _, g in ex[:topk]] + [-1] * max(0, topk - len(ex))
+                assert list(idx[t]) == want, (c, i, t, list(idx[t]), want)
+                for j, (negv, _) in enumerate(ex[:topk]):
+                    assert Fraction(float(vals[t, j])) == -negv
+                assert all(v == -math.inf for v in vals[t, len(ex):])
+        sidx, svals = oracle.score_topk_packed(q, k, w, cu_q, cu_k, r, topk, topk_indices=idx)
+        assert np.array_equal(sidx, idx) and np.array_equal(svals, vals), c
+
+
+def test_bruteforce_packed():
+    check_bruteforce_packed()
+
+
 def _brute_bf16(x: Fraction) -> Fraction:
     """Nearest bf16 value to an exact rational, ties to the even significand."""
     if x == 0:
@@ -742,7 +791,8 @@ ALL_CHECKS = [check_golden_indexer, check_golden_kpool, check_golden_pooled,
               lambda: check_bruteforce_scores_at_indices(10), check_scores_at_own_topk,
               check_k_norm_hand_example, check_k_norm_properties,
               lambda: check_backward_finite_differences(2), check_backward_euler,
-              check_backward_dense_form, check_backward_gate_at_zero]
+              check_backward_dense_form, check_backward_gate_at_zero,
+              lambda: check_bruteforce_packed(6)]
 
 
 def _some_check_fails():
@@ -787,6 +837,10 @@ MUTANTS = {
     "backward drops the incoming gradient": ("_gate_coef", lambda g, wp, on: wp * on),
     "backward keys from the wrong batch": ("_pair_dots",
                                            lambda qp, kp: np.einsum("phd,pd->ph", qp, kp[::-1])),
+    "packed keys from the batch start": ("_sequence_spans", lambda cq, ck: [
+        (int(cq[i]), int(cq[i + 1]), 0, int(ck[i + 1] - ck[i])) for i in range(len(cq) - 1)]),
+    "packed rows see the keys before them": ("_sequence_spans", lambda cq, ck: [
+        (int(cq[i]), int(cq[i + 1]), 0, int(ck[i + 1])) for i in range(len(cq) - 1)]),
     "round toward zero": ("round_to_bf16", lambda x: (
         np.ldexp(np.trunc(np.ldexp(np.frexp(x)[0], 8)), np.frexp(x)[1] - 8),
         (np.ldexp(np.trunc(np.ldexp(np.frexp(x)[0], 8)), np.frexp(x)[1] - 8)
