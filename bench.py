@@ -36,7 +36,7 @@ Profiling helpers (see the summaries under profiles/):
   --pmc-summary F W OUT   turn two rocprofv3 --pmc CSV directories (F with
                           FETCH_SIZE, W with WRITE_SIZE) into the traffic
                           summary OUT that later runs report as `traffic`
-  --stats-summary CSV OUT CMD   text table of a rocprofv3 kernel_stats.csv
+  --stats-summary CSV OUT CMD   text table of a rocprofv3 kernel_trace.csv
 """
 from __future__ import annotations
 
@@ -155,6 +155,11 @@ def pmc_summary(fetch_dir, write_dir, out):
     is_copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
     is_score = lambda n: SCORE_KERNEL in n
     names = sorted({r["Kernel_Name"] for r in fr if is_score(r["Kernel_Name"])})
+    # the prefill launch: the fused kernel's dispatches with the largest grid
+    # (the packed sequences' launches of the same kernel are smaller)
+    grid = max(int(r["Grid_Size"]) for r in fr + wr if is_score(r["Kernel_Name"]))
+    fr = [r for r in fr if not is_score(r["Kernel_Name"]) or int(r["Grid_Size"]) == grid]
+    wr = [r for r in wr if not is_score(r["Kernel_Name"]) or int(r["Grid_Size"]) == grid]
     f_k, w_k = _per_dispatch(fr, "FETCH_SIZE", is_score), _per_dispatch(wr, "WRITE_SIZE", is_score)
     f_c, w_c = _per_dispatch(fr, "FETCH_SIZE", is_copy), _per_dispatch(wr, "WRITE_SIZE", is_copy)
     if not (f_k and w_k and f_c and w_c):
@@ -175,6 +180,7 @@ def pmc_summary(fetch_dir, write_dir, out):
         "#   python3 bench.py --pmc-summary <F> <W> profiles/score_select_prefill_traffic.txt",
         f"kernel: {names[0] if names else SCORE_KERNEL}",
         f"source_sha1: {kernel_sources_sha1()}",
+        f"grid_threads: {grid}",
         f"dispatches: fetch {len(f_k)}, write {len(w_k)}",
         f"fetch_kib_per_dispatch: {np.mean(f_k):.1f}",
         f"write_kib_per_dispatch: {np.mean(w_k):.1f}",
@@ -193,16 +199,24 @@ def pmc_summary(fetch_dir, write_dir, out):
 
 
 def stats_summary(csv_path, out, command):
-    """Short text table of a rocprofv3 --kernel-trace --stats kernel summary."""
-    rows = list(csv.DictReader(open(csv_path)))
-    lines = ["# rocprofv3 kernel-trace statistics", f"# command: {command}",
-             f"# {'kernel':<72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
-    for r in rows:
-        name = r["Name"].strip('"')
-        name = name if len(name) <= 72 else name[:69] + "..."
-        lines.append(f"  {name:<72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
-                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
-                     f"{float(r['Percentage']):6.2f}")
+    """Short text table of a rocprofv3 --kernel-trace run (its
+    kernel_trace.csv), one line per kernel and grid size, so launches of one
+    kernel at different sizes (the prefill launch and the packed sequences'
+    launches of the fused kernel) are listed apart."""
+    groups = {}
+    for r in csv.DictReader(open(csv_path)):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((r["Kernel_Name"].strip('"'), grid), []).append(dur)
+    total = sum(sum(v) for v in groups.values())
+    lines = ["# rocprofv3 kernel-trace statistics per kernel and grid size (threads)",
+             f"# command: {command}",
+             f"# {'kernel':<64s} {'grid':>8s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
+             f"{'max_us':>9s} {'pct':>6s}"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        name = name if len(name) <= 64 else name[:61] + "..."
+        lines.append(f"  {name:<64s} {grid:8d} {len(v):6d} {np.mean(v):9.2f} {min(v):9.2f} "
+                     f"{max(v):9.2f} {100 * sum(v) / total:6.2f}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -283,7 +297,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
-    ap.add_argument("--stats-summary", nargs=3, metavar=("KERNEL_STATS_CSV", "OUT", "COMMAND"))
+    ap.add_argument("--stats-summary", nargs=3, metavar=("KERNEL_TRACE_CSV", "OUT", "COMMAND"))
     args = ap.parse_args()
 
     if args.pmc_summary:
