@@ -27,6 +27,7 @@
 // queries kernel: one wavefront per (query row, 32-head group); d transposed
 //   (lane = head, registers = keys) by swapping the operands, so G is the A
 //   operand of grad_q = G K and the ReLU'd products sum into grad_w per lane.
+#include "entry_tiles.h"
 #include "internal.h"
 #include "score_tile.h"
 
@@ -102,75 +103,6 @@ struct QStage {
   }
 };
 
-// Entries j0 .. j0 + 31 of a row of supplied indices as loaded (lane c and
-// c + 32: entry j0 + c): key and incoming gradient.  The loads are clamped to
-// the row's last entry and never skipped, so a loop that prefetches with
-// them issues the same loads on every path and the compiler's wait counts
-// stay exact; usability is decided when the tile is taken.
-struct EntryIdx {
-  int sv;
-  float gv;
-  bool in;  // j0 + c < n
-
-  __device__ __forceinline__ void load(const int32_t* __restrict__ sup, const float* __restrict__ grad,
-                                       int64_t orow, int n, int j0) {
-    const int j = j0 + (lane_id() & 31);
-    in = j < n;
-    const int64_t e = orow + min(j, n - 1);
-    sv = sup[e];
-    gv = grad[e];
-  }
-};
-
-// One 32-entry tile of a row: lane (c, g) holds entry c's key (-1 when not
-// usable), incoming gradient (0 when not usable) and that key's fragments
-// for the forward's tile layout (dims g*D/2 + 8x, x < D/16).  An unusable
-// entry reads key 0 (n_t > 0, so it exists) and is discarded.
-template <int D>
-struct EntryTile {
-  int s;
-  float g;
-  bf16x8 f[D / 16];
-
-  __device__ __forceinline__ void take(const EntryIdx& e, const uint16_t* __restrict__ k, int n_t,
-                                       int B, int b) {
-    const bool ok = e.in && e.sv >= 0 && e.sv < n_t;
-    s = ok ? e.sv : -1;
-    g = ok ? e.gv : 0.f;
-    const uint16_t* src = k + ((int64_t)(ok ? e.sv : 0) * B + b) * D + (lane_id() >> 5) * (D / 2);
-#pragma unroll
-    for (int x = 0; x < D / 16; ++x) f[x] = *reinterpret_cast<const bf16x8*>(src + 8 * x);
-  }
-};
-
-// Software pipeline over a row's ngroups >= 1 tiles of 32 entries: while
-// tile i is worked on by body(tile), the key rows of tile i + 1 and the
-// indices of tile i + 2 are in flight.  Past the row's end the prefetches
-// repeat its last tile, so every step issues the same loads, and the wait
-// before a step covers only loads issued one step earlier.  Two register
-// sets alternate, so no tile is copied.
-template <int D, class Body>
-__device__ __forceinline__ void for_each_entry_tile(const int32_t* __restrict__ sup,
-                                                    const float* __restrict__ grad,
-                                                    const uint16_t* __restrict__ k, int64_t orow,
-                                                    int n, int n_t, int B, int b, int ngroups,
-                                                    Body&& body) {
-  EntryTile<D> ta, tb;
-  EntryIdx ahead;
-  ahead.load(sup, grad, orow, n, 0);
-  ta.take(ahead, k, n_t, B, b);
-  ahead.load(sup, grad, orow, n, min(1, ngroups - 1) * 32);
-  auto step = [&](EntryTile<D>& cur, EntryTile<D>& nxt, int it) {
-    nxt.take(ahead, k, n_t, B, b);
-    ahead.load(sup, grad, orow, n, min(it + 2, ngroups - 1) * 32);
-    body(cur);
-  };
-  for (int it = 0; it < ngroups; it += 2) {
-    step(ta, tb, it);
-    if (it + 1 < ngroups) step(tb, ta, it + 1);
-  }
-}
-
 template <int HP, int D>
 __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
@@ -208,7 +140,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_keys_kernel(
 
   const int64_t orow = ((int64_t)b * S + t) * n;
   const int ngroups = (n + 31) / 32;
-  for_each_entry_tile<D>(sup, grad, k, orow, n, n_t, B, b, ngroups, [&](const EntryTile<D>& cur) {
+  for_each_entry_tile<D, true>(sup, grad, k, orow, n, n_t, B, b, ngroups, [&](const EntryTile<D, true>& cur, int) {
     if (ballot(cur.s >= 0) != 0) {  // wave-uniform: some entry of the tile is usable
       Acc acc;
       sc.mma(cur.f, acc);  // lane (c, g): key c, heads 32m + 8(r/4) + 4g + r%4
@@ -290,7 +222,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_queries_kernel(
 
   const int64_t orow = ((int64_t)b * S + t) * n;
   if (n_t > 0)  // else no entry is usable
-    for_each_entry_tile<D>(sup, grad, k, orow, n, n_t, B, b, (n + 31) / 32, [&](const EntryTile<D>& cur) {
+    for_each_entry_tile<D, true>(sup, grad, k, orow, n, n_t, B, b, (n + 31) / 32, [&](const EntryTile<D, true>& cur, int) {
       if (ballot(cur.s >= 0) != 0) {  // wave-uniform
         floatx16 dt = {};  // lane (c, g): head h, key slots 8(r/4) + 4g + r%4
 #pragma unroll

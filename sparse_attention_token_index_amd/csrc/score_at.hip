@@ -7,12 +7,14 @@
 // no LDS and no barrier.  The supplied indices are consumed 32 at a time:
 // lane (c, g) loads key idx[c]'s dims g*D/2 .. g*D/2 + D/2 - 1 straight into
 // the B fragments of the fused indexer's tile scorer (128 contiguous bytes
-// per lane at D = 128), the next group's indices and fragments are loaded
-// while the current group is on the matrix cores, and the score arithmetic
+// per lane at D = 128); the key rows of the next group and the indices of
+// the one after are in flight while the current group is on the matrix
+// cores (entry_tiles.h), and the score arithmetic
 // (products, ReLU, head weights, cross-half sum) is the fused kernel's, so a
 // key's score is bit-identical to the one the selection reports.  An entry
 // outside [0, n_t) (padding -1, a masked or an out-of-range key) yields
 // (-1, -inf); entries keep the supplied order.
+#include "entry_tiles.h"
 #include "internal.h"
 #include "score_tile.h"
 
@@ -45,41 +47,24 @@ score_at_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int64_t orow = ((int64_t)b * S + t) * n;
   const int c = lane & 31, g = lane >> 5;
 
-  // Entry j0 + c of the row and its key's fragments (key 0, visible whenever
-  // n_t > 0, stands in for an unusable entry; its products are discarded).
-  auto fetch = [&](int j0, int& s, Frag& bf) {
-    const int j = j0 + c;
-    s = j < n ? sup[orow + j] : -1;
-    if (n_t > 0) {  // wave-uniform; with no visible key nothing is read
-      const int key = (s >= 0 && s < n_t) ? s : 0;
-      const uint16_t* src = k + ((int64_t)key * B + b) * D + g * (D / 2);
-#pragma unroll
-      for (int x = 0; x < KS; ++x) bf[x] = *reinterpret_cast<const bf16x8*>(src + 8 * x);
-    } else {
-#pragma unroll
-      for (int x = 0; x < KS; ++x) bf[x] = bf16x8{};
+  if (n_t <= 0) {  // no visible key: every entry is (-1, -inf); nothing is read
+    for (int j = lane; j < n; j += kWave) {
+      out_idx[orow + j] = -1;
+      out_score[orow + j] = -__builtin_inff();
     }
-  };
-  const int ngroups = (n + 31) / 32;
-  int s0 = -1, s1 = -1;
-  Frag f0, f1;
+    return;
+  }
   Acc acc;
-  if (ngroups > 0) fetch(0, s0, f0);
-  for (int it = 0; it < ngroups; ++it) {
-    // the current group is in (s0, f0); load the next into (s1, f1)
-    if (it + 1 < ngroups) fetch((it + 1) * 32, s1, f1);
-    sc.mma(f0, acc);
+  for_each_entry_tile<D, false>(sup, nullptr, k, orow, n, n_t, B, b, (n + 31) / 32,
+                                [&](const EntryTile<D, false>& cur, int it) {
+    sc.mma(cur.f, acc);
     const float x = sc.reduce(acc, 0) + 0.f;  // -0 -> +0
     const int j = it * 32 + c;
     if (g == 0 && j < n) {
-      const bool ok = s0 >= 0 && s0 < n_t;
-      out_idx[orow + j] = ok ? s0 : -1;
-      out_score[orow + j] = ok ? x : -__builtin_inff();
+      out_idx[orow + j] = cur.s;
+      out_score[orow + j] = cur.s >= 0 ? x : -__builtin_inff();
     }
-    s0 = s1;
-#pragma unroll
-    for (int x2 = 0; x2 < KS; ++x2) f0[x2] = f1[x2];
-  }
+  });
 }
 
 template <int HP, int D>
