@@ -15,6 +15,8 @@ struct ScoreTopkArgs {
   int H, D, ratio, topk;
   int64_t chunk_rows;  // 0: all rows in one launch
   bool sort;           // score-descending rows (else ascending index order)
+  const int32_t* sup = nullptr;  // [B, S, topk] supplied indices (dense plan only;
+                                 // may alias out_idx): their scores, no selection
   int32_t* out_idx;    // [B, S, topk]
   float* out_score;    // [B, S, topk]
 };

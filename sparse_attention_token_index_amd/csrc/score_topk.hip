@@ -22,7 +22,9 @@
 //           the block cuts its rows to the top k by a radix select together,
 //           which raises the thresholds.
 // After the last tile the row's top k is selected exactly and written in
-// ascending index order; no score goes to device memory.  (Score-descending
+// ascending index order; no score goes to device memory.  With supplied
+// indices (dense store only) the row's entries are read from its store
+// instead of selected.  (Score-descending
 // order is produced by the row sort.)  Blocks are numbered heaviest (largest
 // t) first so the causal imbalance is absorbed by the dispatcher.
 #include "internal.h"
@@ -52,7 +54,7 @@ template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_select_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup) {
   extern __shared__ __align__(16) char smem_raw[];
   __shared__ uint32_t cut_flag[2][8];  // filter store: per-wavefront cut requests
   lds_char* smem = (lds_char*)smem_raw;
@@ -246,8 +248,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (!active[rr]) continue;
     const int64_t orow = ((int64_t)b * S + t[rr]) * topk;
     if constexpr (DENSE) {
-      dense_finish(rs[rr].key, (uint32_t)n_t[rr], (uint32_t)topk, smin[rr], smax[rr], rs[rr].hist,
-                   rs[rr].side, topk, out_idx + orow, out_score + orow);
+      if (sup) {  // scores at supplied indices: the row's scores gathered from its store
+        for (int j = lane; j < topk; j += kWave) {
+          const int sj = sup[orow + j];
+          const bool ok = sj >= 0 && sj < n_t[rr];
+          out_idx[orow + j] = ok ? sj : -1;
+          const float x = __uint_as_float(rs[rr].key[ok ? sj : 0]);
+          out_score[orow + j] = ok ? x : -__builtin_inff();
+        }
+      } else {
+        dense_finish(rs[rr].key, (uint32_t)n_t[rr], (uint32_t)topk, smin[rr], smax[rr],
+                     rs[rr].hist, rs[rr].side, topk, out_idx + orow, out_score + orow);
+      }
     } else {
       wave_finish_row(rs[rr], count[rr], topk, out_idx + orow, out_score + orow);
     }
@@ -339,7 +351,7 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), p.lds_bytes,
                        (st2 && (ci & 1)) ? st2 : st, a.q, a.k, a.w, (int)a.S, (int)a.Skv,
                        (int)a.B, a.H, a.ratio, a.topk, (int)r0, (int)r1, R, p.cap, a.out_idx,
-                       a.out_score);
+                       a.out_score, DENSE ? a.sup : nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
