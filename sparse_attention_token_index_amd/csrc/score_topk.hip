@@ -48,10 +48,10 @@ struct ScoreLds {
   static constexpr int kDenseRegion = kTiles > NW * kDenseScratch ? kTiles : NW * kDenseScratch;
 };
 
-// Two wavefronts per SIMD (two 4-wave blocks or one 8-wave block per CU):
-// at most 256 registers per lane.
+// The body of the two kernels below: sup == nullptr selects, else the
+// supplied entries are read from the dense store.
 template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_select_kernel(
+__device__ __forceinline__ void score_select_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup) {
@@ -266,6 +266,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// Two wavefronts per SIMD (two 4-wave blocks or one 8-wave block per CU):
+// at most 256 registers per lane.
+template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_select_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
+    int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  score_select_body<HP, D, NW, NR, DENSE, IdxT>(q, k, w, S, Skv, B, H, ratio, topk, row_begin,
+                                                row_end, R, cap, out_idx, out_score, nullptr);
+}
+
+// Scores at supplied indices through the dense store (its own kernel, so
+// profiles keep it apart from the selection).  sup may alias out_idx.
+template <int HP, int D, int NW, int NR>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_at_dense_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
+    int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
+    int32_t* out_idx, float* __restrict__ out_score, const int32_t* sup) {
+  score_select_body<HP, D, NW, NR, true, uint16_t>(q, k, w, S, Skv, B, H, ratio, topk, row_begin,
+                                                   row_end, R, cap, out_idx, out_score, sup);
+}
+
 namespace {
 
 int store_row_bytes(int cap, int idx_bytes) { return cap * 4 + ((cap * idx_bytes + 15) & ~15); }
@@ -338,8 +360,10 @@ ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t l
 template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
 static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,
                            hipStream_t st2) {
-  auto kern = score_select_kernel<HP, D, NW, NR, DENSE, IdxT>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+  const bool at = DENSE && a.sup;  // scores at supplied indices
+  const void* kern = at ? (const void*)score_at_dense_kernel<HP, D, NW, NR>
+                        : (const void*)score_select_kernel<HP, D, NW, NR, DENSE, IdxT>;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)p.lds_bytes);
   if (e != hipSuccess) return e;
   const int R = p.rows_per_block;
@@ -348,10 +372,17 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
   for (int64_t r0 = 0; r0 < a.S; r0 += chunk, ++ci) {
     const int64_t r1 = (r0 + chunk < a.S) ? r0 + chunk : a.S;
     const int64_t blocks = ((r1 - r0 + R - 1) / R) * a.B;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), p.lds_bytes,
-                       (st2 && (ci & 1)) ? st2 : st, a.q, a.k, a.w, (int)a.S, (int)a.Skv,
-                       (int)a.B, a.H, a.ratio, a.topk, (int)r0, (int)r1, R, p.cap, a.out_idx,
-                       a.out_score, DENSE ? a.sup : nullptr);
+    const hipStream_t sc = (st2 && (ci & 1)) ? st2 : st;
+    if (at)
+      hipLaunchKernelGGL((score_at_dense_kernel<HP, D, NW, NR>), dim3((unsigned)blocks),
+                         dim3(NW * 64), p.lds_bytes, sc, a.q, a.k, a.w, (int)a.S, (int)a.Skv,
+                         (int)a.B, a.H, a.ratio, a.topk, (int)r0, (int)r1, R, p.cap, a.out_idx,
+                         a.out_score, a.sup);
+    else
+      hipLaunchKernelGGL((score_select_kernel<HP, D, NW, NR, DENSE, IdxT>), dim3((unsigned)blocks),
+                         dim3(NW * 64), p.lds_bytes, sc, a.q, a.k, a.w, (int)a.S, (int)a.Skv,
+                         (int)a.B, a.H, a.ratio, a.topk, (int)r0, (int)r1, R, p.cap, a.out_idx,
+                         a.out_score);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
