@@ -243,6 +243,33 @@ int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_
                           float* grad_weights, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Packed sequences for the backward (the reading of dsai_score_topk_packed:
+ * samples laid end to end, each the B = 1 problem on its own rows and keys,
+ * key indices local to the sequence):
+ *   index_q, grad_q [Tq, H, D] bf16; weights, grad_weights [Tq, H] fp32;
+ *   topk_indices [Tq, topk] int32, grad_scores [Tq, topk] fp32;
+ *   index_k, grad_k [Tk, D] bf16; cu_seqlens_q / cu_seqlens_k: HOST arrays
+ *   of nseq + 1 int64 offsets as for dsai_score_topk_packed.
+ * Sequence i's rows and keys get exactly what dsai_indexer_backward gives
+ * the sequence alone (a sequence with no rows gets zero grad_k on its keys,
+ * one with no keys zero grad_q / grad_weights).  One dsai_indexer_backward
+ * per sequence, in order on `stream`, all sharing `workspace`, which must
+ * hold dsai_backward_packed_workspace_size bytes (the largest sequence's
+ * need; 256-byte aligned).  Offsets as for dsai_score_topk_packed, topk and
+ * compress_ratio as for dsai_indexer_backward (DSAI_ERR_INVALID_ARG or
+ * DSAI_ERR_NULLPTR otherwise); every refusal comes before the first
+ * launch. */
+int dsai_backward_packed_workspace_size(dsai_handle h, int64_t nseq, const int64_t* cu_seqlens_q,
+                                        const int64_t* cu_seqlens_k, int topk,
+                                        int compress_ratio, size_t* bytes);
+int dsai_indexer_backward_packed(dsai_handle h, const void* index_q, const void* index_k,
+                                 const float* weights, const int32_t* topk_indices,
+                                 const float* grad_scores, int64_t nseq,
+                                 const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                                 int compress_ratio, int topk, void* grad_q, void* grad_k,
+                                 float* grad_weights, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* ---- pooled decode pipeline ("Module glm5next_dsa") -------------------- */
 /* P = floor(max(0, N - first_key) / kpool): the number of pools of a cache
  * of N tokens (pooling starts at first_key; a trailing partial pool is not a

@@ -20,6 +20,7 @@ from .indexer import (  # noqa: F401
     score_topk_packed,
     scores_at_indices,
     indexer_backward,
+    indexer_backward_packed,
     round_to_bf16,
     k_norm,
     pool_count,

@@ -184,6 +184,31 @@ def score_topk_packed(q: np.ndarray, k: np.ndarray, w: np.ndarray, cu_q, cu_k,
     return idx, vals
 
 
+def indexer_backward_packed(q: np.ndarray, k: np.ndarray, w: np.ndarray, cu_q, cu_k,
+                            compress_ratio: int, topk_indices: np.ndarray,
+                            grad_scores: np.ndarray):
+    """Gradients of the selected scores for packed sequences (the reading of
+    score_topk_packed): q [Tq, H, D], k [Tk, D], w [Tq, H], topk_indices /
+    grad_scores [Tq, n] with key indices local to each sequence.  Sequence
+    i's slices get indexer_backward of the one-sample problem on its rows
+    and keys; keys of a sequence with no rows get zero.  Returns a dict with
+    grad_q [Tq, H, D], grad_k [Tk, D], grad_w [Tq, H]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    out = {"grad_q": np.zeros(q.shape), "grad_k": np.zeros(k.shape), "grad_w": np.zeros(w.shape)}
+    for q0, q1, k0, k1 in _sequence_spans(cu_q, cu_k):
+        if q1 == q0 or k1 == k0:
+            continue
+        r = indexer_backward(q[q0:q1, None], k[k0:k1, None], w[q0:q1, None], compress_ratio,
+                             np.asarray(topk_indices)[None, q0:q1],
+                             np.asarray(grad_scores, dtype=np.float64)[None, q0:q1])
+        out["grad_q"][q0:q1] = r["grad_q"][:, 0]
+        out["grad_k"][k0:k1] = r["grad_k"][:, 0]
+        out["grad_w"][q0:q1] = r["grad_w"][:, 0]
+    return out
+
+
 def _usable_keys(s: np.ndarray, n_t: int) -> np.ndarray:
     """Supplied key indices that name a key the row may see: 0 <= s < n_t."""
     return (s >= 0) & (s < n_t)

@@ -32,7 +32,8 @@ _LIB_PATH = os.path.join(_HERE, "libdsai.so")
 # Every symbol include/dsai.h declares.
 EXPORTS = (
     "dsai_create", "dsai_destroy", "dsai_status_string", "dsai_last_hip_error",
-    "dsai_score_topk", "dsai_score_topk_packed", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
+    "dsai_score_topk", "dsai_score_topk_packed", "dsai_backward_packed_workspace_size",
+    "dsai_indexer_backward_packed", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
     "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
     "dsai_sort_rows", "dsai_k_norm", "dsai_backward_workspace_size", "dsai_indexer_backward",
 )
@@ -81,6 +82,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_last_hip_error": [vp],
         "dsai_score_topk": [vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, vp, vp, vp],
         "dsai_score_topk_packed": [vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp, vp, vp],
+        "dsai_backward_packed_workspace_size": [vp, i64, vp, vp, c_int, c_int, vp],
+        "dsai_indexer_backward_packed": [vp, vp, vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp,
+                                         vp, vp, ctypes.c_size_t, vp],
         "dsai_pool_count": [vp, i64, ctypes.POINTER(i64)],
         "dsai_kpool_compress": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp],
         "dsai_index_scores": [vp, vp, vp, vp, vp, i64, i64, vp, vp],
@@ -106,6 +110,19 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _offsets(cu_q, cu_k):
+    """Host int64 copies of packed-sequence offsets and the sequence count."""
+    cq = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int64))
+    ck = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int64))
+    if cq.ndim != 1 or ck.shape != cq.shape or cq.size < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k: equal-length 1-D offset lists")
+    return cq, ck, cq.size - 1
+
+
+def _host(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
 
 
 def _stream(dev: torch.device):
@@ -216,11 +233,7 @@ class Indexer:
         (idx [Tq,topk] int32, score [Tq,topk] fp32).  Each sequence is the
         one-sample problem on its own rows and keys; indices are local to it.
         topk must be a multiple of 4."""
-        cq = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
-        ck = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int64))
-        if cq.ndim != 1 or ck.shape != cq.shape or cq.size < 1:
-            raise ValueError("cu_seqlens_q and cu_seqlens_k: equal-length 1-D offset lists")
-        nseq = cq.size - 1
+        cq, ck, nseq = _offsets(cu_seqlens_q, cu_seqlens_k)
         Tq, Tk = index_q.shape[0], index_k.shape[0]
         H, D = self.cfg.heads, self.cfg.dim
         dev = index_q.device
@@ -240,7 +253,7 @@ class Indexer:
         with torch.cuda.device(dev):
             st = self._lib.dsai_score_topk_packed(
                 self._h, _ptr(index_q), _ptr(index_k), _ptr(weights), nseq,
-                cq.ctypes.data_as(ctypes.c_void_p), ck.ctypes.data_as(ctypes.c_void_p),
+                _host(cq), _host(ck),
                 int(compress_ratio), int(topk), _ptr(topk_indices), _ptr(out_idx),
                 _ptr(out_score), _stream(dev))
         self._check(st, "dsai_score_topk_packed")
@@ -300,6 +313,61 @@ class Indexer:
                 _ptr(grad_k), _ptr(grad_weights), _ptr(workspace),
                 workspace.numel() * workspace.element_size(), _stream(dev))
         self._check(st, "dsai_indexer_backward")
+        return grad_q, grad_k, grad_weights
+
+    def backward_packed_workspace_size(self, cu_seqlens_q, cu_seqlens_k, topk: int,
+                                       compress_ratio: int) -> int:
+        cq, ck, nseq = _offsets(cu_seqlens_q, cu_seqlens_k)
+        n = ctypes.c_size_t()
+        self._check(self._lib.dsai_backward_packed_workspace_size(
+            self._h, nseq, _host(cq), _host(ck), int(topk), int(compress_ratio), ctypes.byref(n)),
+            "dsai_backward_packed_workspace_size")
+        return n.value
+
+    def indexer_backward_packed(self, index_q: torch.Tensor, index_k: torch.Tensor,
+                                weights: torch.Tensor, topk_indices: torch.Tensor,
+                                grad_scores: torch.Tensor, cu_seqlens_q, cu_seqlens_k,
+                                compress_ratio: int, workspace: Optional[torch.Tensor] = None,
+                                grad_q: Optional[torch.Tensor] = None,
+                                grad_k: Optional[torch.Tensor] = None,
+                                grad_weights: Optional[torch.Tensor] = None):
+        """Packed sequences: index_q [Tq,H,D], index_k [Tk,D], weights [Tq,H],
+        topk_indices / grad_scores [Tq,topk] (indices local to each sequence)
+        -> (grad_q [Tq,H,D] bf16, grad_k [Tk,D] bf16, grad_weights [Tq,H]
+        fp32); each sequence gets its one-sample gradients."""
+        cq, ck, nseq = _offsets(cu_seqlens_q, cu_seqlens_k)
+        Tq, Tk = index_q.shape[0], index_k.shape[0]
+        H, D = self.cfg.heads, self.cfg.dim
+        dev = index_q.device
+        _need(index_q, "index_q", torch.bfloat16, (Tq, H, D))
+        _need(index_k, "index_k", torch.bfloat16, (Tk, D), dev)
+        _need(weights, "weights", torch.float32, (Tq, H), dev)
+        if int(cq[-1]) != Tq or int(ck[-1]) != Tk:
+            raise ValueError("the last offsets must equal the row counts of index_q and index_k")
+        if topk_indices.dim() != 2:
+            raise ValueError("topk_indices: expected [Tq, topk]")
+        topk = topk_indices.shape[1]
+        _need(topk_indices, "topk_indices", torch.int32, (Tq, topk), dev)
+        _need(grad_scores, "grad_scores", torch.float32, (Tq, topk), dev)
+        need = self.backward_packed_workspace_size(cq, ck, topk, compress_ratio)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        if grad_q is None:
+            grad_q = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=dev)
+        if grad_k is None:
+            grad_k = torch.empty((Tk, D), dtype=torch.bfloat16, device=dev)
+        if grad_weights is None:
+            grad_weights = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+        _need(grad_q, "grad_q", torch.bfloat16, (Tq, H, D), dev)
+        _need(grad_k, "grad_k", torch.bfloat16, (Tk, D), dev)
+        _need(grad_weights, "grad_weights", torch.float32, (Tq, H), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_indexer_backward_packed(
+                self._h, _ptr(index_q), _ptr(index_k), _ptr(weights), _ptr(topk_indices),
+                _ptr(grad_scores), nseq, _host(cq), _host(ck), int(compress_ratio), int(topk),
+                _ptr(grad_q), _ptr(grad_k), _ptr(grad_weights), _ptr(workspace),
+                workspace.numel() * workspace.element_size(), _stream(dev))
+        self._check(st, "dsai_indexer_backward_packed")
         return grad_q, grad_k, grad_weights
 
     # -- cache write ---------------------------------------------------------

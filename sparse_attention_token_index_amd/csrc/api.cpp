@@ -119,6 +119,23 @@ hipError_t on_side_streams(dsai_context* h, hipStream_t st, F launch) {
   return le;
 }
 
+// Packed-sequence offsets: nseq + 1 host int64 values per side, starting at
+// 0 and never decreasing, totals below 2^31.  The totals go to *Tq, *Tk.
+int check_offsets(int64_t nseq, const int64_t* cu_q, const int64_t* cu_k, int64_t* Tq,
+                  int64_t* Tk) {
+  if (nseq < 0) return DSAI_ERR_INVALID_ARG;
+  *Tq = *Tk = 0;
+  if (nseq == 0) return DSAI_OK;
+  if (!cu_q || !cu_k) return DSAI_ERR_NULLPTR;
+  if (cu_q[0] != 0 || cu_k[0] != 0) return DSAI_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < nseq; ++i)
+    if (cu_q[i + 1] < cu_q[i] || cu_k[i + 1] < cu_k[i]) return DSAI_ERR_INVALID_ARG;
+  if (cu_q[nseq] > kI32 || cu_k[nseq] > kI32) return DSAI_ERR_INVALID_ARG;
+  *Tq = cu_q[nseq];
+  *Tk = cu_k[nseq];
+  return DSAI_OK;
+}
+
 // Visible (query, key) pairs of one batch: sum over t < S of
 // min(Skv, floor((t + 1) / r)), in closed form.
 int64_t visible_pairs(int64_t S, int64_t Skv, int64_t r) {
@@ -279,17 +296,11 @@ int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index
   if (!h) return DSAI_ERR_NULLPTR;
   if (nseq < 0 || compress_ratio < 1 || topk < 1 || topk > DSAI_MAX_TOPK || topk % 4 != 0)
     return DSAI_ERR_INVALID_ARG;
-  if (nseq == 0) return DSAI_OK;
-  if (!cu_seqlens_q || !cu_seqlens_k) return DSAI_ERR_NULLPTR;
-  if (cu_seqlens_q[0] != 0 || cu_seqlens_k[0] != 0) return DSAI_ERR_INVALID_ARG;
-  for (int64_t i = 0; i < nseq; ++i)
-    if (cu_seqlens_q[i + 1] < cu_seqlens_q[i] || cu_seqlens_k[i + 1] < cu_seqlens_k[i])
-      return DSAI_ERR_INVALID_ARG;
-  const int64_t Tq = cu_seqlens_q[nseq];
-  if (Tq > kI32 || cu_seqlens_k[nseq] > kI32) return DSAI_ERR_INVALID_ARG;
-  if (Tq == 0) return DSAI_OK;
+  int64_t Tq = 0, Tk = 0;
+  const int so = check_offsets(nseq, cu_seqlens_q, cu_seqlens_k, &Tq, &Tk);
+  if (so != DSAI_OK || Tq == 0) return so;
   if (!index_q || !weights || !out_idx || !out_score) return DSAI_ERR_NULLPTR;
-  if (cu_seqlens_k[nseq] > 0 && !index_k) return DSAI_ERR_NULLPTR;
+  if (Tk > 0 && !index_k) return DSAI_ERR_NULLPTR;
   const int64_t H = h->cfg.heads, D = h->cfg.dim;
   const bool sort = h->cfg.order == DSAI_ORDER_SCORE && !topk_indices;
   if (!topk_indices) {  // every refusal before the first launch
@@ -407,6 +418,76 @@ int dsai_indexer_backward(dsai_handle h, const void* index_q, const void* index_
   return hip_status(h, on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
                       return dsai::launch_indexer_backward(a, plan, s0, s1);
                     }));
+}
+
+int dsai_backward_packed_workspace_size(dsai_handle h, int64_t nseq, const int64_t* cu_seqlens_q,
+                                        const int64_t* cu_seqlens_k, int topk,
+                                        int compress_ratio, size_t* bytes) {
+  if (!h || !bytes) return DSAI_ERR_NULLPTR;
+  if (topk < 1 || topk > DSAI_MAX_TOPK || compress_ratio < 1) return DSAI_ERR_INVALID_ARG;
+  int64_t Tq = 0, Tk = 0;
+  const int so = check_offsets(nseq, cu_seqlens_q, cu_seqlens_k, &Tq, &Tk);
+  if (so != DSAI_OK) return so;
+  size_t most = 0;
+  for (int64_t i = 0; i < nseq; ++i) {
+    const size_t b = dsai::plan_backward(cu_seqlens_q[i + 1] - cu_seqlens_q[i],
+                                         cu_seqlens_k[i + 1] - cu_seqlens_k[i], 1, h->cfg.dim,
+                                         topk, compress_ratio).bytes;
+    most = b > most ? b : most;
+  }
+  *bytes = most;
+  return DSAI_OK;
+}
+
+int dsai_indexer_backward_packed(dsai_handle h, const void* index_q, const void* index_k,
+                                 const float* weights, const int32_t* topk_indices,
+                                 const float* grad_scores, int64_t nseq,
+                                 const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                                 int compress_ratio, int topk, void* grad_q, void* grad_k,
+                                 float* grad_weights, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (compress_ratio < 1 || topk < 1 || topk > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
+  int64_t Tq = 0, Tk = 0;
+  int st = check_offsets(nseq, cu_seqlens_q, cu_seqlens_k, &Tq, &Tk);
+  if (st != DSAI_OK || (Tq == 0 && Tk == 0)) return st;
+  // every refusal before the first launch: the workspace must hold the
+  // largest sequence's plan, and the base pointers pass the per-sample checks
+  // (each sequence's slices are offsets of whole rows from them)
+  size_t need = 0;
+  st = dsai_backward_packed_workspace_size(h, nseq, cu_seqlens_q, cu_seqlens_k, topk,
+                                           compress_ratio, &need);
+  if (st != DSAI_OK) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return DSAI_ERR_WORKSPACE;
+  if (Tk > 0 && (!index_k || !grad_k)) return DSAI_ERR_NULLPTR;
+  if (Tq > 0 && (!index_q || !weights || !topk_indices || !grad_scores || !grad_q || !grad_weights))
+    return DSAI_ERR_NULLPTR;
+  if (!aligned(index_q) || !aligned(index_k) || !aligned(grad_q) || !aligned(grad_k) ||
+      reinterpret_cast<uintptr_t>(topk_indices) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(grad_scores) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(weights) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(grad_weights) % 4 != 0)
+    return DSAI_ERR_INVALID_ARG;
+  const int64_t H = h->cfg.heads, D = h->cfg.dim;
+  // One per-sample backward per sequence, in order on `stream` (they share
+  // the workspace); a sequence with no rows still zeroes its keys' grad_k.
+  for (int64_t i = 0; i < nseq; ++i) {
+    const int64_t q0 = cu_seqlens_q[i], k0 = cu_seqlens_k[i];
+    const int64_t S = cu_seqlens_q[i + 1] - q0, Skv = cu_seqlens_k[i + 1] - k0;
+    if (S == 0 && Skv == 0) continue;
+    st = dsai_indexer_backward(
+        h, S > 0 ? static_cast<const uint16_t*>(index_q) + q0 * H * D : nullptr,
+        Skv > 0 ? static_cast<const uint16_t*>(index_k) + k0 * D : nullptr,
+        S > 0 ? weights + q0 * H : nullptr, S > 0 ? topk_indices + q0 * topk : nullptr,
+        S > 0 ? grad_scores + q0 * topk : nullptr, S, Skv, 1, compress_ratio, topk,
+        S > 0 ? static_cast<uint16_t*>(grad_q) + q0 * H * D : nullptr,
+        Skv > 0 ? static_cast<uint16_t*>(grad_k) + k0 * D : nullptr,
+        S > 0 ? grad_weights + q0 * H : nullptr, workspace, workspace_bytes, stream);
+    if (st != DSAI_OK) return st;
+  }
+  return DSAI_OK;
 }
 
 int dsai_pool_count(dsai_handle h, int64_t N, int64_t* P) {

@@ -168,6 +168,43 @@ def test_score_topk_packed_argument_errors(lib):
     lib.dsai_destroy(h)
 
 
+def test_backward_packed_argument_errors(lib):
+    st, h = _create(lib)
+    assert st == OK
+    offs = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    cq, ck = offs(0, 40, 100), offs(0, 64, 300)
+    need = ctypes.c_size_t()
+    assert lib.dsai_backward_packed_workspace_size(h, 2, cq, ck, 8, 1, ctypes.byref(need)) == OK
+    single = [ctypes.c_size_t(), ctypes.c_size_t()]
+    assert lib.dsai_backward_workspace_size(h, 40, 64, 1, 8, 1, ctypes.byref(single[0])) == OK
+    assert lib.dsai_backward_workspace_size(h, 60, 236, 1, 8, 1, ctypes.byref(single[1])) == OK
+    assert need.value == max(s.value for s in single)       # the largest sequence's need
+    assert lib.dsai_backward_packed_workspace_size(h, 2, cq, ck, 0, 1, ctypes.byref(need)) == INVALID
+    assert lib.dsai_backward_packed_workspace_size(h, 2, None, ck, 8, 1, ctypes.byref(need)) == NULLPTR
+    ws_ok = need.value
+
+    def call(n=2, cq=cq, ck=ck, r=1, topk=8, ws=FAKE, wsb=None, q=FAKE, k=FAKE, w=FAKE, sup=FAKE,
+             g=FAKE, gq=FAKE, gk=FAKE, gw=FAKE):
+        return lib.dsai_indexer_backward_packed(h, q, k, w, sup, g, n, cq, ck, r, topk, gq, gk, gw,
+                                                ws, ws_ok if wsb is None else wsb, None)
+    assert call(r=0) == INVALID
+    assert call(topk=0) == INVALID
+    assert call(n=-1) == INVALID
+    assert call(cq=offs(0, 50, 40)) == INVALID
+    assert call(cq=None) == NULLPTR
+    assert call(n=0) == OK
+    assert call(cq=offs(0, 0, 0), ck=offs(0, 0, 0)) == OK   # nothing to do
+    assert call(wsb=ws_ok - 1) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE    # not 256-byte aligned
+    assert call(ws=None) == WORKSPACE
+    assert call(k=None) == NULLPTR
+    assert call(gk=None) == NULLPTR
+    assert call(sup=None) == NULLPTR
+    assert call(gq=None) == NULLPTR
+    assert call(q=ctypes.c_void_p(0x10002)) == INVALID
+    lib.dsai_destroy(h)
+
+
 def test_k_norm_argument_errors(lib):
     st, h = _create(lib)
     assert st == OK

@@ -87,3 +87,54 @@ def test_packed_matches_oracle(dsai, name, cu_q, cu_k, H, D, r, topk, integer, c
         torch.cuda.synchronize()
         assert np.array_equal(si.cpu().numpy()[0], gi[q0:q1]), (name, i)
         assert np.array_equal(ss.cpu().numpy()[0].view(np.uint32), gs[q0:q1].view(np.uint32))
+
+
+def test_packed_backward_exact(dsai):
+    """dsai_indexer_backward_packed on integer inputs (every GPU step exact):
+    bit-identical to the fp64 packed oracle rounded to bf16, and to one
+    dsai_indexer_backward call per sequence.  A sequence with rows but no
+    keys, one with keys but no rows, ragged lengths, the compressed mask."""
+    log("[gpu] packed backward")
+    H, D, r, n = 4, 32, 2, 12
+    cu_q = np.array([0, 90, 90, 150, 400], np.int64)
+    cu_k = np.array([0, 45, 70, 70, 195], np.int64)
+    qb, kb, w = packed_inputs("bwd_packed", cu_q, cu_k, H, D, r, n, True, seed=41)
+    sup = np.full((int(cu_q[-1]), n), -1, np.int32)
+    for i in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = (int(x) for x in (cu_q[i], cu_q[i + 1], cu_k[i], cu_k[i + 1]))
+        if q1 > q0 and k1 > k0:
+            bound = [oracle.visible_keys(t, k1 - k0, r) for t in range(q1 - q0)]
+            sup[q0:q1] = SY.key_lists(41 + i, 1, q1 - q0, n, k1 - k0, bound)[0]
+    g = SY.score_grads(41, 1, int(cu_q[-1]), n, integer=True)[0]
+    ix = dsai.Indexer(heads=H, dim=D)
+    tq, tk, tw = bf16(qb), bf16(kb), torch.from_numpy(w).cuda()
+    tsup, tg = torch.from_numpy(sup).cuda(), torch.from_numpy(g).cuda()
+    gq, gk, gw = ix.indexer_backward_packed(tq, tk, tw, tsup, tg, cu_q, cu_k, r)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_backward_packed(SY.bf16_bits_to_f32(qb).astype(np.float64),
+                                         SY.bf16_bits_to_f32(kb).astype(np.float64),
+                                         w.astype(np.float64), cu_q, cu_k, r, sup,
+                                         g.astype(np.float64))
+
+    def bits(t):
+        b = t.cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        b[b == 0x8000] = 0
+        return b
+
+    for got, exact in ((gq, ref["grad_q"]), (gk, ref["grad_k"])):
+        want = oracle.round_to_bf16(exact)[1].copy()
+        want[want == 0x8000] = 0
+        assert np.array_equal(bits(got), want)
+    assert np.array_equal(gw.cpu().numpy().astype(np.float64), ref["grad_w"])
+    assert np.any(ref["grad_k"] != 0) and np.any(ref["grad_q"] != 0)
+
+    for i in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = (int(x) for x in (cu_q[i], cu_q[i + 1], cu_k[i], cu_k[i + 1]))
+        if q1 == q0 and k1 == k0:
+            continue
+        sq, sk, sw = ix.indexer_backward(tq[q0:q1, None], tk[k0:k1, None], tw[q0:q1, None],
+                                         tsup[None, q0:q1], tg[None, q0:q1], r)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(sq)[:, 0], bits(gq)[q0:q1]), i
+        assert np.array_equal(bits(sk)[:, 0], bits(gk)[k0:k1]), i
+        assert np.array_equal(sw.cpu().numpy()[:, 0], gw.cpu().numpy()[q0:q1]), i

@@ -231,6 +231,57 @@ def test_bruteforce_packed():
     check_bruteforce_packed()
 
 
+def check_backward_packed_finite_differences(n_cases=3, seed=12):
+    """Packed backward: every input coordinate's gradient equals the central
+    difference of L = sum of g * score over the usable supplied entries,
+    with the scores from the packed forward (its supplied-index form), so
+    the sequence slicing of the backward is checked against the forward's.
+    Dyadic inputs with no zero product on a usable entry: exact."""
+    rng = np.random.default_rng(seed)
+    eps = 2.0 ** -12
+    for c in range(n_cases):
+        while True:
+            nseq = 3
+            cu_q, cu_k = _tiny_offsets(rng, nseq, 3), _tiny_offsets(rng, nseq, 4)
+            Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+            H, D, r, n = int(rng.integers(1, 3)), int(rng.integers(2, 4)), 1, 3
+            q = rng.choice(_QK_SET, (Tq, H, D)).astype(np.float64)
+            k = rng.choice(_QK_SET, (Tk, D)).astype(np.float64)
+            w = rng.choice(_W_SET, (Tq, H)).astype(np.float64)
+            sup = rng.integers(-1, 5, size=(Tq, n)).astype(np.int32)
+            g = rng.choice(_G_SET, (Tq, n)).astype(np.float64)
+            zero = False
+            for i in range(nseq):
+                for t in range(int(cu_q[i]), int(cu_q[i + 1])):
+                    nt = min(int(cu_k[i + 1] - cu_k[i]), t - int(cu_q[i]) + 1)
+                    for s in sup[t]:
+                        if 0 <= s < nt and np.any(q[t] @ k[int(cu_k[i]) + s] == 0):
+                            zero = True
+            if Tq > 0 and Tk > 0 and not zero:
+                break
+
+        def loss():
+            _, v = oracle.score_topk_packed(q, k, w, cu_q, cu_k, r, n, topk_indices=sup)
+            ok = np.isfinite(v)
+            return float(np.sum(np.where(ok, v, 0.0) * g))
+        got = oracle.indexer_backward_packed(q, k, w, cu_q, cu_k, r, sup, g)
+        for name, arr in (("grad_q", q), ("grad_k", k), ("grad_w", w)):
+            fd = np.zeros(arr.shape)
+            for pos in np.ndindex(*arr.shape):
+                keep = arr[pos]
+                arr[pos] = keep + eps
+                hi = loss()
+                arr[pos] = keep - eps
+                lo = loss()
+                arr[pos] = keep
+                fd[pos] = (hi - lo) / (2 * eps)
+            assert np.array_equal(got[name], fd), (c, name, np.argwhere(got[name] != fd)[:4])
+
+
+def test_backward_packed_finite_differences():
+    check_backward_packed_finite_differences()
+
+
 def _brute_bf16(x: Fraction) -> Fraction:
     """Nearest bf16 value to an exact rational, ties to the even significand."""
     if x == 0:
@@ -792,7 +843,7 @@ ALL_CHECKS = [check_golden_indexer, check_golden_kpool, check_golden_pooled,
               check_k_norm_hand_example, check_k_norm_properties,
               lambda: check_backward_finite_differences(2), check_backward_euler,
               check_backward_dense_form, check_backward_gate_at_zero,
-              lambda: check_bruteforce_packed(6)]
+              lambda: check_bruteforce_packed(6), lambda: check_backward_packed_finite_differences(1)]
 
 
 def _some_check_fails():
