@@ -301,6 +301,9 @@ int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index
   if (so != DSAI_OK || Tq == 0) return so;
   if (!index_q || !weights || !out_idx || !out_score) return DSAI_ERR_NULLPTR;
   if (Tk > 0 && !index_k) return DSAI_ERR_NULLPTR;
+  if (!aligned(index_q) || !aligned(index_k) || !aligned(out_idx) || !aligned(out_score) ||
+      !aligned(topk_indices))
+    return DSAI_ERR_INVALID_ARG;
   const int64_t H = h->cfg.heads, D = h->cfg.dim;
   const bool sort = h->cfg.order == DSAI_ORDER_SCORE && !topk_indices;
   if (!topk_indices) {  // every refusal before the first launch
@@ -315,9 +318,6 @@ int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index
         return DSAI_ERR_UNSUPPORTED;
     }
   }
-  if (!aligned(index_q) || !aligned(index_k) || !aligned(out_idx) || !aligned(out_score) ||
-      !aligned(topk_indices))
-    return DSAI_ERR_INVALID_ARG;
   // Sequence i is the one-sample problem on its own rows and keys (topk % 4
   // == 0 keeps each sequence's output rows 16-byte aligned).  Consecutive
   // non-empty sequences alternate between the handle's two streams, so two

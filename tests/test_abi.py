@@ -163,6 +163,8 @@ def test_score_topk_packed_argument_errors(lib):
     assert call(oi=None) == NULLPTR
     assert call(os_=None) == NULLPTR
     assert call(k=None) == NULLPTR                          # keys present, pointer missing
+    assert call(q=ctypes.c_void_p(0x10002)) == INVALID      # misaligned, refused before any HIP call
+    assert call(oi=ctypes.c_void_p(0x10004)) == INVALID
     assert lib.dsai_score_topk_packed(None, FAKE, FAKE, FAKE, 2, offs(0, 3, 8), offs(0, 5, 9),
                                       1, 4, None, FAKE, FAKE, None) == NULLPTR
     lib.dsai_destroy(h)
