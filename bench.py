@@ -9,7 +9,8 @@ resident in device memory:
     same work and result as dsai_score_topk under DSAI_ORDER_SCORE, timed
     as two launches so the fused kernel has a duration of its own;
   * the pooled decode selection over one 65536-token indexer cache
-    (kpool_compress -> select (index_scores + topk_pools) -> expand;
+    (kpool_compress -> select with expand: index_scores + topk_pools, whose
+    kernel also writes the expanded token ids (dsai_select_expand);
     KP=4, 64 query rows, 32 heads, index_topk=512).
 Outside the step, the same top-k rows are rescored through the
 topk_indices form of dsai_score_topk (scores at supplied indices), and the
@@ -351,7 +352,7 @@ def main():
     pscores = torch.empty((pc.Q, sel), dtype=torch.float32, device=dev)
     toks = torch.empty((pc.Q, pc.index_topk), dtype=torch.int32, device=dev)
 
-    stages = ["score_topk", "sort_rows", "kpool_compress", "select", "expand"]
+    stages = ["score_topk", "sort_rows", "kpool_compress", "select_expand"]
 
     def step(ev=None):
         e = ev or {}
@@ -368,12 +369,10 @@ def main():
         mark("kpool_compress", 0)
         pix.kpool_compress(kn, gate, valid, ape, pool_k=pool_k, pool_tok=pool_tok, pool_valid=pool_valid)
         mark("kpool_compress", 1)
-        mark("select", 0)
-        pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids, pool_scores=pscores)
-        mark("select", 1)
-        mark("expand", 0)
-        pix.expand(pids, tokens=toks)
-        mark("expand", 1)
+        mark("select_expand", 0)   # index_scores + topk_pools + expand_selection
+        pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids, pool_scores=pscores,
+                   tokens=toks, expand=True)
+        mark("select_expand", 1)
 
     for _ in range(args.warmup):
         step()
@@ -469,13 +468,13 @@ def main():
     bw_entries = selected_entries(case)
     del bw_ws, bw_out
 
-    # the pooled decode stages (kpool_compress -> select -> expand) captured
+    # the pooled decode stages (kpool_compress -> select with expand) captured
     # once in a HIP graph and replayed: the decode step's latency without
     # per-call launch work (not part of the step)
     def pooled():
         pix.kpool_compress(kn, gate, valid, ape, pool_k=pool_k, pool_tok=pool_tok, pool_valid=pool_valid)
-        pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids, pool_scores=pscores)
-        pix.expand(pids, tokens=toks)
+        pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids, pool_scores=pscores,
+                   tokens=toks, expand=True)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -554,8 +553,8 @@ def main():
             "sort_rows_ms": avg["sort_rows"], "sort_rows_GBps": sb / (avg["sort_rows"] * 1e-3) / 1e9,
             "kpool_ms": avg["kpool_compress"], "kpool_GBps": kb / (avg["kpool_compress"] * 1e-3) / 1e9,
             "kpool_bytes": kb,
-            "select_ms": avg["select"], "select_TFLOPs": select_flops(pc, P) / (avg["select"] * 1e-3) / 1e12,
-            "expand_ms": avg["expand"], "expand_GBps": eb / (avg["expand"] * 1e-3) / 1e9,
+            "select_expand_ms": avg["select_expand"],
+            "select_expand_TFLOPs": select_flops(pc, P) / (avg["select_expand"] * 1e-3) / 1e12,
             "expand_bytes": eb, "wall_s": wall,
             "score_at_indices_ms": at_ms,
             "score_at_indices_TFLOPs": (at_flops / (at_ms * 1e-3) / 1e12) if at_ms else None,

@@ -328,6 +328,18 @@ int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,
                 void* stream);
 
+/* dsai_select followed by dsai_expand of its pool ids, in one call: the same
+ * pool_ids, pool_scores and tokens [Q, index_topk] int32 (16-byte aligned,
+ * DSAI_ERR_INVALID_ARG otherwise), with the same workspace.  Where the
+ * selection's rows are final when its kernel ends (P <= 32768, and in score
+ * order select_k <= 512), that kernel writes the token ids too, with no
+ * separate expand launch (the "Shape of the pipeline" of "Module glm5next_dsa"
+ * runs topk_pools then expand_selection; their outputs are unchanged). */
+int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                       const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
+                       float* pool_scores, int32_t* tokens, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* ---- cache write: the indexer's k_norm ------------------------------------ */
 /* k_norm ("Module glm5next_dsa", "Checkpoint and kernel facts": indexer.k_norm
  * is a LayerNorm with a bias; Constants: the BF16 LayerNorm module): the

@@ -33,7 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "libdsai.so")
 EXPORTS = (
     "dsai_create", "dsai_destroy", "dsai_status_string", "dsai_last_hip_error",
     "dsai_score_topk", "dsai_score_topk_packed", "dsai_backward_packed_workspace_size",
-    "dsai_indexer_backward_packed", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
+    "dsai_indexer_backward_packed", "dsai_select_expand", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
     "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
     "dsai_sort_rows", "dsai_k_norm", "dsai_backward_workspace_size", "dsai_indexer_backward",
 )
@@ -83,6 +83,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_score_topk": [vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, vp, vp, vp],
         "dsai_score_topk_packed": [vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp, vp, vp],
         "dsai_backward_packed_workspace_size": [vp, i64, vp, vp, c_int, c_int, vp],
+        "dsai_select_expand": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "dsai_indexer_backward_packed": [vp, vp, vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp,
                                          vp, vp, ctypes.c_size_t, vp],
         "dsai_pool_count": [vp, i64, ctypes.POINTER(i64)],
@@ -468,8 +469,12 @@ class Indexer:
                     "dsai_select_workspace_size")
         return n.value
 
-    def select(self, q, w, pool_k, pool_valid, workspace=None, pool_ids=None, pool_scores=None):
-        """index_scores + topk_pools with the [Q,P] scores in `workspace` (uint8 tensor)."""
+    def select(self, q, w, pool_k, pool_valid, workspace=None, pool_ids=None, pool_scores=None,
+               tokens=None, expand=False):
+        """index_scores + topk_pools with the [Q,P] scores in `workspace` (uint8
+        tensor) -> (pool_ids, pool_scores); with expand=True also the token ids
+        [Q, select_k*kpool] (dsai_select_expand) -> (pool_ids, pool_scores,
+        tokens)."""
         Q, P = q.shape[0], pool_k.shape[0]
         H, D = self.cfg.heads, self.cfg.dim
         dev = q.device
@@ -489,6 +494,17 @@ class Indexer:
             pool_scores = torch.empty((Q, K), dtype=torch.float32, device=dev)
         _need(pool_ids, "pool_ids", torch.int32, (Q, K), dev)
         _need(pool_scores, "pool_scores", torch.float32, (Q, K), dev)
+        if expand:
+            if tokens is None:
+                tokens = torch.empty((Q, K * self.cfg.kpool), dtype=torch.int32, device=dev)
+            _need(tokens, "tokens", torch.int32, (Q, K * self.cfg.kpool), dev)
+            with torch.cuda.device(dev):
+                st = self._lib.dsai_select_expand(
+                    self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid), Q, P,
+                    _ptr(pool_ids), _ptr(pool_scores), _ptr(tokens), _ptr(workspace),
+                    workspace.numel() * workspace.element_size(), _stream(dev))
+            self._check(st, "dsai_select_expand")
+            return pool_ids, pool_scores, tokens
         with torch.cuda.device(dev):
             st = self._lib.dsai_select(self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid),
                                        Q, P, _ptr(pool_ids), _ptr(pool_scores), _ptr(workspace),

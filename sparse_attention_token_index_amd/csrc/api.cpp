@@ -534,12 +534,9 @@ int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* 
   return hip_status(h, dsai::launch_pooled_scores(a, static_cast<hipStream_t>(stream)));
 }
 
-int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, int32_t* pool_ids,
-                    float* pool_scores, void* stream) {
-  if (!h) return DSAI_ERR_NULLPTR;
-  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
-  if (Q == 0) return DSAI_OK;
-  if (!pool_ids || !pool_scores || (P > 0 && !scores)) return DSAI_ERR_NULLPTR;
+// topk_pools, and with `tokens` the rows expanded to token ids as well.
+static int topk_pools_impl(dsai_handle h, const float* scores, int64_t Q, int64_t P,
+                           int32_t* pool_ids, float* pool_scores, int32_t* tokens, void* stream) {
   hipError_t e = device_limits(h);
   if (e != hipSuccess) return hip_status(h, e);
   const dsai::TopkRowsPlan plan = dsai::plan_topk_rows(select_k(h->cfg), P, h->lds_limit);
@@ -548,7 +545,17 @@ int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, in
   a.scores = scores; a.Q = Q; a.P = P; a.sel = select_k(h->cfg);
   a.pool_ids = pool_ids; a.pool_scores = pool_scores;
   a.sort = h->cfg.order == DSAI_ORDER_SCORE;
+  a.tokens = tokens; a.KP = h->cfg.kpool; a.first_key = h->cfg.first_key;
   return hip_status(h, dsai::launch_topk_pools(a, plan, static_cast<hipStream_t>(stream)));
+}
+
+int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, int32_t* pool_ids,
+                    float* pool_scores, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Q == 0) return DSAI_OK;
+  if (!pool_ids || !pool_scores || (P > 0 && !scores)) return DSAI_ERR_NULLPTR;
+  return topk_pools_impl(h, scores, Q, P, pool_ids, pool_scores, nullptr, stream);
 }
 
 int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* bytes) {
@@ -574,6 +581,27 @@ int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k
   if (st != DSAI_OK) return st;
   return dsai_topk_pools(h, static_cast<const float*>(workspace), Q, P, pool_ids, pool_scores,
                          stream);
+}
+
+int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                       const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
+                       float* pool_scores, int32_t* tokens, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Q == 0) return DSAI_OK;
+  if (!tokens || !pool_ids || !pool_scores) return DSAI_ERR_NULLPTR;
+  if (!aligned(tokens)) return DSAI_ERR_INVALID_ARG;
+  size_t need = 0;
+  dsai_select_workspace_size(h, Q, P, &need);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return DSAI_ERR_WORKSPACE;
+  int st = dsai_index_scores(h, q, w, pool_k, pool_valid, Q, P, static_cast<float*>(workspace),
+                             stream);
+  if (st != DSAI_OK) return st;
+  return topk_pools_impl(h, static_cast<const float*>(workspace), Q, P, pool_ids, pool_scores,
+                         tokens, stream);
 }
 
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,

@@ -61,6 +61,8 @@ struct TopkPoolsArgs {
   int32_t* pool_ids;    // [Q, sel]
   float* pool_scores;   // [Q, sel]
   bool sort;            // score-descending rows (else ascending pool id)
+  int32_t* tokens = nullptr;  // optional [Q, sel * KP]: the rows expanded to token ids
+  int KP = 1, first_key = 0;
 };
 
 struct ExpandArgs {

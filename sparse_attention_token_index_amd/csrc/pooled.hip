@@ -321,7 +321,7 @@ __device__ __forceinline__ uint2 block_incl_scan(uint32_t x, uint32_t* red) {
 template <int ITEMS>
 __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     const float* __restrict__ scores, int P, int sel, int score_order, int32_t* __restrict__ ids,
-    float* __restrict__ out_scores) {
+    float* __restrict__ out_scores, int32_t* __restrict__ tokens, int KP, int first_key) {
   __shared__ uint32_t hist[kBlockSelBins];
   __shared__ uint32_t red[kBlockSelWaves];
   __shared__ uint32_t found[2];
@@ -332,6 +332,15 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
   const float* srow = scores + (int64_t)blockIdx.x * P;
   int32_t* orow = ids + (int64_t)blockIdx.x * sel;
   float* osc = out_scores + (int64_t)blockIdx.x * sel;
+  // entry i of the row is pool `id` (-1: none); with `tokens`, its KP token
+  // slots are written too (expand_selection fused into the selection)
+  int32_t* trow = tokens ? tokens + (int64_t)blockIdx.x * sel * KP : nullptr;
+  auto put = [&](uint32_t i, int32_t id, float v) {
+    orow[i] = id;
+    osc[i] = v;
+    if (trow)
+      for (int j = 0; j < KP; ++j) trow[(int64_t)i * KP + j] = id >= 0 ? first_key + id * KP + j : -1;
+  };
 
   // Load; -inf (an invalid pool) and slots past P never count.
   uint32_t u[ITEMS];
@@ -550,8 +559,7 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
       if (rank_sort) {
         staged[pos] = make_uint2(u[j], (uint32_t)(p0 + j));
       } else {
-        orow[pos] = p0 + j;
-        osc[pos] = ord_to_float(u[j]);
+        put(pos, p0 + j, ord_to_float(u[j]));
       }
     }
     nab += above ? 1u : 0u;
@@ -575,14 +583,10 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     }
     for (int off = 1; off < tpe; off <<= 1) r += (uint32_t)__shfl_xor((int)r, off);
     if (e < nsel && part == 0u) {
-      orow[r] = (int32_t)me.y;
-      osc[r] = ord_to_float(me.x);
+      put(r, (int32_t)me.y, ord_to_float(me.x));
     }
   }
-  for (int i = (int)nsel + t; i < sel; i += kBlockSelThreads) {
-    orow[i] = -1;
-    osc[i] = -__builtin_inff();
-  }
+  for (int i = (int)nsel + t; i < sel; i += kBlockSelThreads) put((uint32_t)i, -1, -__builtin_inff());
 }
 
 // Waves per row and store capacity for select_k = sel within `lds_limit`.
@@ -607,17 +611,25 @@ hipError_t launch_topk_pools(const TopkPoolsArgs& a, const TopkRowsPlan& pl, hip
   if (a.Q <= 0) return hipSuccess;
   if (a.P <= (int64_t)kBlockSelThreads * 32) {
     const bool ranked = a.sort && a.sel <= kRankSortMax;
+    // the rows are final when the kernel ends (no row sort follows): then
+    // it writes the token ids as well
+    int32_t* tok = (a.tokens && (!a.sort || ranked)) ? a.tokens : nullptr;
 #define DSAI_ITEMS(n)                                                                          \
     if (a.P <= (int64_t)kBlockSelThreads * n) {                                                \
       hipLaunchKernelGGL(block_select_kernel<n>, dim3((unsigned)a.Q), dim3(kBlockSelThreads), \
                          0, st, a.scores, (int)a.P, a.sel, (int)a.sort, a.pool_ids,            \
-                         a.pool_scores);                                                       \
+                         a.pool_scores, tok, a.KP, a.first_key);                               \
     } else
     DSAI_ITEMS(1) DSAI_ITEMS(2) DSAI_ITEMS(4) DSAI_ITEMS(8) DSAI_ITEMS(16) DSAI_ITEMS(32) {}
 #undef DSAI_ITEMS
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !a.sort || ranked) return e;
-    return launch_sort_rows(a.pool_ids, a.pool_scores, a.Q, a.sel, st);
+    if (e == hipSuccess && a.sort && !ranked)
+      e = launch_sort_rows(a.pool_ids, a.pool_scores, a.Q, a.sel, st);
+    if (e != hipSuccess || !a.tokens || tok) return e;
+    ExpandArgs x;
+    x.pool_ids = a.pool_ids; x.Q = a.Q; x.sel = a.sel; x.KP = a.KP; x.first_key = a.first_key;
+    x.tokens = a.tokens;
+    return launch_expand(x, st);
   }
   hipError_t e = hipFuncSetAttribute((const void*)topk_rows_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes);
@@ -625,8 +637,12 @@ hipError_t launch_topk_pools(const TopkPoolsArgs& a, const TopkRowsPlan& pl, hip
   hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)a.Q), dim3(pl.waves * kWave), pl.lds_bytes,
                      st, a.scores, (int)a.P, a.sel, pl.cap, pl.waves, a.pool_ids, a.pool_scores);
   e = hipGetLastError();
-  if (e != hipSuccess || !a.sort) return e;
-  return launch_sort_rows(a.pool_ids, a.pool_scores, a.Q, a.sel, st);
+  if (e == hipSuccess && a.sort) e = launch_sort_rows(a.pool_ids, a.pool_scores, a.Q, a.sel, st);
+  if (e != hipSuccess || !a.tokens) return e;
+  ExpandArgs x;
+  x.pool_ids = a.pool_ids; x.Q = a.Q; x.sel = a.sel; x.KP = a.KP; x.first_key = a.first_key;
+  x.tokens = a.tokens;
+  return launch_expand(x, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -203,6 +203,38 @@ def test_select_and_expand_pipeline(dsai, case):
     assert np.array_equal(ids2.cpu().numpy(), gids)
 
 
+@pytest.mark.parametrize("P,KP,index_topk,first_key", [
+    (16384, 4, 512, 0),       # block select ranks its rows: tokens from the same kernel
+    (16384, 4, 4096, 7),      # select_k > 512: row sort, then the expand kernel
+    (40000, 2, 512, 3),       # streaming select, then the expand kernel
+    (1000, 8, 64, 5),
+    (0, 4, 64, 0),            # no pools: every row padding
+])
+@pytest.mark.parametrize("order", ["score", "index"])
+def test_select_expand_fused(dsai, P, KP, index_topk, first_key, order):
+    """dsai_select_expand gives the ids and scores of dsai_select and the
+    tokens of dsai_expand on them, bit for bit, and the tokens equal the
+    oracle's expansion of the ids."""
+    log(f"[gpu] select_expand P={P} KP={KP} index_topk={index_topk} order={order}")
+    rng = np.random.default_rng(7 + P + KP)
+    Q, H, D = 11, 32, 128
+    ix = dsai.Indexer(heads=H, dim=D, kpool=KP, index_topk=index_topk, first_key=first_key,
+                      order=dsai.DSAI_ORDER_SCORE if order == "score" else dsai.DSAI_ORDER_INDEX)
+    f = lambda shape: bf16_gpu(SY.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32)))
+    q, pk = f((Q, H, D)), f((max(P, 1), D))[:P]
+    w = torch.from_numpy((rng.standard_normal((Q, H)) / np.sqrt(H)).astype(np.float32)).cuda()
+    pv = torch.from_numpy((rng.random(P) < 0.9).astype(np.uint8)).cuda()
+    ids, vals = ix.select(q, w, pk, pv)
+    tok = ix.expand(ids)
+    fids, fvals, ftok = ix.select(q, w, pk, pv, expand=True)
+    torch.cuda.synchronize()
+    gids = ids.cpu().numpy()
+    assert np.array_equal(fids.cpu().numpy(), gids)
+    assert np.array_equal(fvals.cpu().numpy().view(np.uint32), vals.cpu().numpy().view(np.uint32))
+    assert np.array_equal(ftok.cpu().numpy(), tok.cpu().numpy())
+    assert np.array_equal(ftok.cpu().numpy(), oracle.expand_selection(gids, first_key, KP))
+
+
 @pytest.mark.parametrize("KP", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_expand_bit_exact(dsai, KP):
     log(f"[gpu] expand KP={KP}")
