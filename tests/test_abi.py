@@ -311,6 +311,15 @@ def test_pooled_argument_errors(lib):
     assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, 64, 16384, FAKE, FAKE,
                            ctypes.c_void_p(0x10010), need.value, None) == WORKSPACE   # not 256-aligned
     assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, -1, 16384, FAKE, FAKE, FAKE, 0, None) == INVALID
+    # select with expand: select's rules plus the token array
+    se = lambda Q=64, tok=FAKE, ws=FAKE, wsb=need.value: lib.dsai_select_expand(
+        h, FAKE, FAKE, FAKE, FAKE, Q, 16384, FAKE, FAKE, tok, ws, wsb, None)
+    assert se(Q=-1) == INVALID
+    assert se(Q=0) == OK
+    assert se(tok=None) == NULLPTR
+    assert se(tok=ctypes.c_void_p(0x10004)) == INVALID     # tokens 16-byte aligned
+    assert se(wsb=need.value - 1) == WORKSPACE
+    assert se(ws=None) == WORKSPACE
     # expand
     assert lib.dsai_expand(h, FAKE, -1, FAKE, None) == INVALID
     assert lib.dsai_expand(h, FAKE, 0, FAKE, None) == OK
