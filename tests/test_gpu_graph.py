@@ -1,7 +1,7 @@
 """GPU checks that the single-stream calls can be captured in a HIP graph
 (torch.cuda.graph) and replayed: the pooled decode pipeline
-(kpool_compress -> select -> expand), the cache write's k_norm, and the
-fused score + top-k with its row sort.  Every replay, with eager work and
+(kpool_compress -> select -> expand, and select with expand in one call),
+the cache write's k_norm, and the fused score + top-k with its row sort.  Every replay, with eager work and
 synchronisations between replays, must reproduce the eager results bit for
 bit.  (No call here clears memory with hipMemsetAsync, which graphs do not
 replay reliably on this hardware.)"""
@@ -60,13 +60,15 @@ def test_pooled_pipeline_graph(dsai):
     ids = torch.empty((pc.Q, K), dtype=torch.int32, device="cuda")
     sc = torch.empty((pc.Q, K), dtype=torch.float32, device="cuda")
     tok = torch.empty((pc.Q, K * pc.KP), dtype=torch.int32, device="cuda")
+    ids2, sc2, tok2 = torch.empty_like(ids), torch.empty_like(sc), torch.empty_like(tok)
 
     def run():
         ix.kpool_compress(kn, gate, valid, ape, pool_k, pool_tok, pool_valid)
         ix.select(q, w, pool_k, pool_valid, ws, ids, sc)
         ix.expand(ids, tok)
+        ix.select(q, w, pool_k, pool_valid, ws, ids2, sc2, tokens=tok2, expand=True)
 
-    outs = [pool_k, pool_tok, pool_valid, ids, sc, tok]
+    outs = [pool_k, pool_tok, pool_valid, ids, sc, tok, ids2, sc2, tok2]
     run()
     torch.cuda.synchronize()
     eager = [t.clone() for t in outs]
@@ -80,6 +82,8 @@ def test_pooled_pipeline_graph(dsai):
     with torch.cuda.graph(g):
         run()
     replay_and_compare(g, outs, eager)
+    for fused, split in ((ids2, ids), (sc2, sc), (tok2, tok)):  # select with expand = the two calls
+        assert torch.equal(fused.view(torch.uint8), split.view(torch.uint8))
 
 
 def test_score_topk_and_k_norm_graph(dsai):
