@@ -61,7 +61,7 @@ extern "C" {
 /* Largest topk / select_k the fused selection supports (LDS capacity). */
 #define DSAI_MAX_TOPK 8192
 /* Heads and head dims the kernels are compiled for: heads 1..64
- * (zero-padded to 16, 32 or 64 on the matrix cores), dim 32, 64 or 128. */
+ * (zero-padded to 32 or 64 on the matrix cores), dim 32, 64 or 128. */
 #define DSAI_MAX_HEADS 64
 
 /* Order of the entries of a top-k row (dsai_config.order). */
@@ -324,17 +324,23 @@ int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k
  * [0, P)) -> token ids [Q, index_topk] int32 (index_topk = select_k *
  * kpool).  Slot i*kpool + j receives first_key + pool_ids[q,i]*kpool + j,
  * or -1 when pool_ids[q,i] is negative; every slot is written exactly once.
- * Q >= 0. */
+ * Token ids are int32: an id above (2^31 - 1 - first_key + 1) / kpool - 1,
+ * whose token ids would not fit, is written as missing (-1) like a negative
+ * one (ids of a cache of N <= 2^31 - 1 tokens never are).  Q >= 0. */
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,
                 void* stream);
 
 /* dsai_select followed by dsai_expand of its pool ids, in one call: the same
  * pool_ids, pool_scores and tokens [Q, index_topk] int32 (16-byte aligned,
- * DSAI_ERR_INVALID_ARG otherwise), with the same workspace.  Where the
+ * DSAI_ERR_INVALID_ARG otherwise), with the same workspace.  The pools' token
+ * ids must fit int32: first_key + P * kpool - 1 <= 2^31 - 1
+ * (DSAI_ERR_INVALID_ARG otherwise).  Where the
  * selection's rows are final when its kernel ends (P <= 32768, and in score
  * order select_k <= 512), that kernel writes the token ids too, with no
  * separate expand launch (the "Shape of the pipeline" of "Module glm5next_dsa"
- * runs topk_pools then expand_selection; their outputs are unchanged). */
+ * runs topk_pools then expand_selection; their outputs are unchanged).
+ * Every refusal (including DSAI_ERR_UNSUPPORTED for a select_k the
+ * selection cannot hold) comes before the first launch. */
 int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void* pool_k,
                        const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
                        float* pool_scores, int32_t* tokens, void* workspace,

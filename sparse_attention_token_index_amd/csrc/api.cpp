@@ -518,35 +518,55 @@ int dsai_kpool_compress(dsai_handle h, const void* k_normed, const float* gate,
   return hip_status(h, dsai::launch_kpool(a, static_cast<hipStream_t>(stream)));
 }
 
-int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                      const uint8_t* pool_valid, int64_t Q, int64_t P, float* scores,
-                      void* stream) {
-  if (!h) return DSAI_ERR_NULLPTR;
+// Host checks of index_scores' arguments (no HIP call).
+static int check_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                              const uint8_t* pool_valid, int64_t Q, int64_t P, const void* scores) {
   if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
   if (Q == 0 || P == 0) return DSAI_OK;
   if (P * h->cfg.dim * 2 > (int64_t)0xFFFFFFFF) return DSAI_ERR_UNSUPPORTED;  // 32-bit offsets
   if (!q || !w || !pool_k || !pool_valid || !scores) return DSAI_ERR_NULLPTR;
   if (!aligned(q) || !aligned(pool_k)) return DSAI_ERR_INVALID_ARG;
+  return DSAI_OK;
+}
+
+static hipError_t launch_index_scores(dsai_handle h, const void* q, const float* w,
+                                      const void* pool_k, const uint8_t* pool_valid, int64_t Q,
+                                      int64_t P, float* scores, hipStream_t st) {
   dsai::PooledScoresArgs a;
   a.q = static_cast<const uint16_t*>(q); a.w = w;
   a.pool_k = static_cast<const uint16_t*>(pool_k); a.pool_valid = pool_valid;
   a.Q = Q; a.P = P; a.H = h->cfg.heads; a.D = h->cfg.dim; a.scores = scores;
-  return hip_status(h, dsai::launch_pooled_scores(a, static_cast<hipStream_t>(stream)));
+  return dsai::launch_pooled_scores(a, st);
+}
+
+int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                      const uint8_t* pool_valid, int64_t Q, int64_t P, float* scores,
+                      void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  const int st = check_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores);
+  if (st != DSAI_OK || Q == 0 || P == 0) return st;
+  return hip_status(h, launch_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+// Launch plan of topk_pools (queries the device's LDS limit once).
+static int plan_pools(dsai_handle h, int64_t P, dsai::TopkRowsPlan* plan) {
+  hipError_t e = device_limits(h);
+  if (e != hipSuccess) return hip_status(h, e);
+  *plan = dsai::plan_topk_rows(select_k(h->cfg), P, h->lds_limit);
+  return plan->waves < 1 ? DSAI_ERR_UNSUPPORTED : DSAI_OK;
 }
 
 // topk_pools, and with `tokens` the rows expanded to token ids as well.
-static int topk_pools_impl(dsai_handle h, const float* scores, int64_t Q, int64_t P,
-                           int32_t* pool_ids, float* pool_scores, int32_t* tokens, void* stream) {
-  hipError_t e = device_limits(h);
-  if (e != hipSuccess) return hip_status(h, e);
-  const dsai::TopkRowsPlan plan = dsai::plan_topk_rows(select_k(h->cfg), P, h->lds_limit);
-  if (plan.waves < 1) return DSAI_ERR_UNSUPPORTED;
+static hipError_t launch_pools(dsai_handle h, const dsai::TopkRowsPlan& plan, const float* scores,
+                               int64_t Q, int64_t P, int32_t* pool_ids, float* pool_scores,
+                               int32_t* tokens, hipStream_t st) {
   dsai::TopkPoolsArgs a;
   a.scores = scores; a.Q = Q; a.P = P; a.sel = select_k(h->cfg);
   a.pool_ids = pool_ids; a.pool_scores = pool_scores;
   a.sort = h->cfg.order == DSAI_ORDER_SCORE;
   a.tokens = tokens; a.KP = h->cfg.kpool; a.first_key = h->cfg.first_key;
-  return hip_status(h, dsai::launch_topk_pools(a, plan, static_cast<hipStream_t>(stream)));
+  return dsai::launch_topk_pools(a, plan, st);
 }
 
 int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, int32_t* pool_ids,
@@ -555,7 +575,11 @@ int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P, in
   if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
   if (Q == 0) return DSAI_OK;
   if (!pool_ids || !pool_scores || (P > 0 && !scores)) return DSAI_ERR_NULLPTR;
-  return topk_pools_impl(h, scores, Q, P, pool_ids, pool_scores, nullptr, stream);
+  dsai::TopkRowsPlan plan;
+  const int st = plan_pools(h, P, &plan);
+  if (st != DSAI_OK) return st;
+  return hip_status(h, launch_pools(h, plan, scores, Q, P, pool_ids, pool_scores, nullptr,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* bytes) {
@@ -565,22 +589,60 @@ int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* byte
   return DSAI_OK;
 }
 
+// index_scores into `scores` ([Q, P] fp32, device memory the caller
+// provides), then topk_pools (with `tokens`: expanded as well).  Every
+// refusal, the topk_pools plan included, comes before the first launch.
+static int select_into(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                       const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
+                       float* pool_scores, int32_t* tokens, float* scores, void* stream) {
+  int st = check_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores);
+  if (st != DSAI_OK) return st;
+  if (!pool_ids || !pool_scores) return DSAI_ERR_NULLPTR;
+  dsai::TopkRowsPlan plan;
+  if ((st = plan_pools(h, P, &plan)) != DSAI_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (P > 0) {
+    const hipError_t e = launch_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores, s);
+    if (e != hipSuccess) return hip_status(h, e);
+  }
+  return hip_status(h, launch_pools(h, plan, scores, Q, P, pool_ids, pool_scores, tokens, s));
+}
+
+static int check_workspace(dsai_handle h, int64_t Q, int64_t P, const void* workspace,
+                           size_t workspace_bytes) {
+  size_t need = 0;
+  dsai_select_workspace_size(h, Q, P, &need);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return DSAI_ERR_WORKSPACE;
+  return DSAI_OK;
+}
+
 int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k,
                 const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
                 float* pool_scores, void* workspace, size_t workspace_bytes, void* stream) {
   if (!h) return DSAI_ERR_NULLPTR;
   if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
   if (Q == 0) return DSAI_OK;
-  size_t need = 0;
-  dsai_select_workspace_size(h, Q, P, &need);
-  if (need > 0 && (!workspace || workspace_bytes < need ||
-                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
-    return DSAI_ERR_WORKSPACE;
-  int st = dsai_index_scores(h, q, w, pool_k, pool_valid, Q, P, static_cast<float*>(workspace),
-                             stream);
+  const int st = check_workspace(h, Q, P, workspace, workspace_bytes);
   if (st != DSAI_OK) return st;
-  return dsai_topk_pools(h, static_cast<const float*>(workspace), Q, P, pool_ids, pool_scores,
-                         stream);
+  return select_into(h, q, w, pool_k, pool_valid, Q, P, pool_ids, pool_scores, nullptr,
+                     static_cast<float*>(workspace), stream);
+}
+
+// Token ids of the expanded rows are int32: the last token of the last pool,
+// first_key + P * kpool - 1, must fit.
+static bool tokens_fit(const dsai_config& c, int64_t P) {
+  return (int64_t)c.first_key + P * (int64_t)c.kpool - 1 <= kI32;
+}
+
+static int check_select_expand(dsai_handle h, int64_t Q, int64_t P, const int32_t* pool_ids,
+                               const float* pool_scores, const int32_t* tokens) {
+  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
+  if (Q == 0) return DSAI_OK;
+  if (!tokens || !pool_ids || !pool_scores) return DSAI_ERR_NULLPTR;
+  if (!aligned(tokens) || !tokens_fit(h->cfg, P)) return DSAI_ERR_INVALID_ARG;
+  return DSAI_OK;
 }
 
 int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void* pool_k,
@@ -588,20 +650,11 @@ int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void*
                        float* pool_scores, int32_t* tokens, void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (!h) return DSAI_ERR_NULLPTR;
-  if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
-  if (Q == 0) return DSAI_OK;
-  if (!tokens || !pool_ids || !pool_scores) return DSAI_ERR_NULLPTR;
-  if (!aligned(tokens)) return DSAI_ERR_INVALID_ARG;
-  size_t need = 0;
-  dsai_select_workspace_size(h, Q, P, &need);
-  if (need > 0 && (!workspace || workspace_bytes < need ||
-                   reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
-    return DSAI_ERR_WORKSPACE;
-  int st = dsai_index_scores(h, q, w, pool_k, pool_valid, Q, P, static_cast<float*>(workspace),
-                             stream);
-  if (st != DSAI_OK) return st;
-  return topk_pools_impl(h, static_cast<const float*>(workspace), Q, P, pool_ids, pool_scores,
-                         tokens, stream);
+  int st = check_select_expand(h, Q, P, pool_ids, pool_scores, tokens);
+  if (st != DSAI_OK || Q == 0) return st;
+  if ((st = check_workspace(h, Q, P, workspace, workspace_bytes)) != DSAI_OK) return st;
+  return select_into(h, q, w, pool_k, pool_valid, Q, P, pool_ids, pool_scores, tokens,
+                     static_cast<float*>(workspace), stream);
 }
 
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,

@@ -649,17 +649,21 @@ hipError_t launch_topk_pools(const TopkPoolsArgs& a, const TopkRowsPlan& pl, hip
 // expand_selection (glm5next_dsa: writes -1 over the whole index row before
 // any index, so every slot is written).  One thread per (row, selected pool)
 // writes the pool's KP slots: -1 for a missing pool, else the pool's token
-// ids; each output slot is written exactly once, coalesced.
+// ids; each output slot is written exactly once, coalesced.  An id past
+// max_id (its token ids would not fit int32) counts as missing.
 // ---------------------------------------------------------------------------
 template <int KP>
 __global__ __launch_bounds__(256) void expand_kernel(const int32_t* __restrict__ ids, int64_t n,
-                                                     int first_key, int32_t* __restrict__ tok) {
+                                                     int first_key, int32_t max_id,
+                                                     int32_t* __restrict__ tok) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
   const int32_t p = ids[e];
+  const bool ok = p >= 0 && p <= max_id;
+  const int32_t t0 = ok ? first_key + p * KP : 0;  // no overflow: p <= max_id
   int32_t v[KP];
 #pragma unroll
-  for (int j = 0; j < KP; ++j) v[j] = (p < 0) ? -1 : first_key + p * KP + j;
+  for (int j = 0; j < KP; ++j) v[j] = ok ? t0 + j : -1;
   int32_t* o = tok + e * KP;
   if constexpr (KP == 4) {
     *reinterpret_cast<int4*>(o) = make_int4(v[0], v[1], v[2], v[3]);
@@ -677,11 +681,14 @@ __global__ __launch_bounds__(256) void expand_kernel(const int32_t* __restrict__
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t st) {
   const int64_t n = a.Q * a.sel;
   if (n <= 0) return hipSuccess;
+  // largest pool id whose last token id, first_key + id * KP + KP - 1, fits int32
+  const int64_t max_id64 = ((int64_t)2147483647 - a.first_key + 1) / a.KP - 1;
+  const int32_t max_id = (int32_t)(max_id64 < 2147483647 ? max_id64 : 2147483647);
   const unsigned blocks = (unsigned)((n + 255) / 256);
 #define DSAI_KP(kp)                                                                           \
   case kp:                                                                                    \
     hipLaunchKernelGGL(expand_kernel<kp>, dim3(blocks), dim3(256), 0, st, a.pool_ids, n,      \
-                       a.first_key, a.tokens);                                                \
+                       a.first_key, max_id, a.tokens);                                        \
     break;
   switch (a.KP) {
     DSAI_KP(1) DSAI_KP(2) DSAI_KP(3) DSAI_KP(4) DSAI_KP(5) DSAI_KP(6) DSAI_KP(7) DSAI_KP(8)

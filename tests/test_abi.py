@@ -328,6 +328,22 @@ def test_pooled_argument_errors(lib):
     lib.dsai_destroy(h)
 
 
+def test_expanded_token_ids_must_fit_int32(lib):
+    """first_key + P * kpool - 1 above 2^31 - 1 would overflow the int32
+    token ids: select with expand refuses it before any HIP
+    call; one pool fewer passes the check (and then needs a device, so the
+    workspace check is what answers here)."""
+    KP, fk = 8, 2 ** 31 - 1 - 8 * 1000
+    st, h = _create(lib, kpool=KP, index_topk=64, first_key=fk)
+    assert st == OK
+    P_ok = (2 ** 31 - 1 - fk + 1) // KP          # last token = 2^31 - 1
+    se = lambda P, ws=None: lib.dsai_select_expand(h, FAKE, FAKE, FAKE, FAKE, 2, P, FAKE, FAKE,
+                                                   FAKE, ws, 0, None)
+    assert se(P_ok + 1) == INVALID
+    assert se(P_ok) == WORKSPACE                 # past the token check: no workspace given
+    lib.dsai_destroy(h)
+
+
 def test_sort_rows_argument_errors(lib):
     st, h = _create(lib)
     assert st == OK
