@@ -346,6 +346,27 @@ int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void*
                        float* pool_scores, int32_t* tokens, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device array dsai_select_expand_static keeps its
+ * [Q, P] scores in (one array per device). */
+#define DSAI_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (work recorded under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dsai_select_expand with no workspace argument.  The [Q, P] fp32 scores
+ * live in a static device array of DSAI_STATIC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends; its
+ * address is looked up at the first call on a device (with that device
+ * current).  The call allocates nothing (no hipMalloc / hipFree) and clears
+ * nothing: index_scores writes every score before topk_pools reads it.
+ * Outputs, argument rules and errors as dsai_select_expand, plus
+ * DSAI_ERR_WORKSPACE when Q * P * 4 > DSAI_STATIC_SCRATCH_BYTES (before any
+ * HIP call).  Every call on a device shares that device's array: calls that
+ * overlap on one device (other streams, other handles, other host threads)
+ * race on it and must be ordered by the caller. */
+int dsai_select_expand_static(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                              const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
+                              float* pool_scores, int32_t* tokens, void* stream);
+
 /* ---- cache write: the indexer's k_norm ------------------------------------ */
 /* k_norm ("Module glm5next_dsa", "Checkpoint and kernel facts": indexer.k_norm
  * is a LayerNorm with a bias; Constants: the BF16 LayerNorm module): the

@@ -36,6 +36,7 @@ EXPORTS = (
     "dsai_indexer_backward_packed", "dsai_select_expand", "dsai_pool_count", "dsai_kpool_compress", "dsai_index_scores",
     "dsai_topk_pools", "dsai_select_workspace_size", "dsai_select", "dsai_expand",
     "dsai_sort_rows", "dsai_k_norm", "dsai_backward_workspace_size", "dsai_indexer_backward",
+    "dsai_select_expand_static",
 )
 
 DSAI_OK = 0
@@ -43,6 +44,7 @@ DSAI_ORDER_SCORE = 0  # rows by score descending, lower index first on ties
 DSAI_ORDER_INDEX = 1  # rows by ascending index (same set, no sorting pass)
 DSAI_MAX_KPOOL = 8
 DSAI_MAX_TOPK = 8192
+DSAI_STATIC_SCRATCH_BYTES = 16 << 20  # scores array of dsai_select_expand_static
 
 
 class DsaiError(RuntimeError):
@@ -84,6 +86,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_score_topk_packed": [vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp, vp, vp],
         "dsai_backward_packed_workspace_size": [vp, i64, vp, vp, c_int, c_int, vp],
         "dsai_select_expand": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "dsai_select_expand_static": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp],
         "dsai_indexer_backward_packed": [vp, vp, vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp,
                                          vp, vp, ctypes.c_size_t, vp],
         "dsai_pool_count": [vp, i64, ctypes.POINTER(i64)],
@@ -511,6 +514,30 @@ class Indexer:
                                        workspace.numel() * workspace.element_size(), _stream(dev))
         self._check(st, "dsai_select")
         return pool_ids, pool_scores
+
+    def select_expand_static(self, q, w, pool_k, pool_valid, pool_ids, pool_scores, tokens):
+        """dsai_select_expand_static: select with expand whose [Q,P] scores live
+        in the library's static device array (no workspace; the output
+        tensors are the caller's, so the call allocates nothing).  Calls that
+        overlap on one GPU share that array and race."""
+        Q, P = q.shape[0], pool_k.shape[0]
+        H, D, K = self.cfg.heads, self.cfg.dim, self.select_k
+        dev = q.device
+        if pool_valid.dtype == torch.bool:
+            pool_valid = pool_valid.view(torch.uint8)
+        _need(q, "q", torch.bfloat16, (Q, H, D))
+        _need(w, "w", torch.float32, (Q, H), dev)
+        _need(pool_k, "pool_k", torch.bfloat16, (P, D), dev)
+        _need(pool_valid, "pool_valid", torch.uint8, (P,), dev)
+        _need(pool_ids, "pool_ids", torch.int32, (Q, K), dev)
+        _need(pool_scores, "pool_scores", torch.float32, (Q, K), dev)
+        _need(tokens, "tokens", torch.int32, (Q, K * self.cfg.kpool), dev)
+        with torch.cuda.device(dev):
+            st = self._lib.dsai_select_expand_static(
+                self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid), Q, P,
+                _ptr(pool_ids), _ptr(pool_scores), _ptr(tokens), _stream(dev))
+        self._check(st, "dsai_select_expand_static")
+        return pool_ids, pool_scores, tokens
 
     def expand(self, pool_ids, tokens=None):
         """pool_ids [Q,select_k] int32 -> token ids [Q, select_k*kpool] int32 (-1 = invalid)."""

@@ -2,6 +2,7 @@
 // (all on the host, before any HIP call) and dispatch to the kernels.
 #include "dsai.h"
 
+#include <mutex>
 #include <new>
 
 #include <cmath>
@@ -655,6 +656,52 @@ int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void*
   if ((st = check_workspace(h, Q, P, workspace, workspace_bytes)) != DSAI_OK) return st;
   return select_into(h, q, w, pool_k, pool_valid, Q, P, pool_ids, pool_scores, tokens,
                      static_cast<float*>(workspace), stream);
+}
+
+// ---- dsai_select_expand_static: the [Q, P] scores in a static device array --
+// One copy per device, held by the library until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device copy: the
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DSAI_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`.
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+int dsai_select_expand_static(dsai_handle h, const void* q, const float* w, const void* pool_k,
+                              const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
+                              float* pool_scores, int32_t* tokens, void* stream) {
+  if (!h) return DSAI_ERR_NULLPTR;
+  int st = check_select_expand(h, Q, P, pool_ids, pool_scores, tokens);
+  if (st != DSAI_OK || Q == 0) return st;
+  size_t need = 0;
+  dsai_select_workspace_size(h, Q, P, &need);
+  if (need > (size_t)DSAI_STATIC_SCRATCH_BYTES) return DSAI_ERR_WORKSPACE;
+  void* buf = nullptr;
+  const hipError_t e = static_scratch(&buf);
+  if (e != hipSuccess) return hip_status(h, e);
+  return select_into(h, q, w, pool_k, pool_valid, Q, P, pool_ids, pool_scores, tokens,
+                     static_cast<float*>(buf), stream);
 }
 
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,

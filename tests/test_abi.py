@@ -320,6 +320,18 @@ def test_pooled_argument_errors(lib):
     assert se(tok=ctypes.c_void_p(0x10004)) == INVALID     # tokens 16-byte aligned
     assert se(wsb=need.value - 1) == WORKSPACE
     assert se(ws=None) == WORKSPACE
+    # select with expand from the static array: its rules, and no more
+    # scores than the array holds (refused before any HIP call)
+    sst = lambda Q=64, P=16384, tok=FAKE: lib.dsai_select_expand_static(
+        h, FAKE, FAKE, FAKE, FAKE, Q, P, FAKE, FAKE, tok, None)
+    assert sst(Q=-1) == INVALID
+    assert sst(Q=0) == OK
+    assert sst(tok=None) == NULLPTR
+    assert sst(tok=ctypes.c_void_p(0x10004)) == INVALID
+    assert sst(Q=64, P=(16 << 20) // (4 * 64) + 1) == WORKSPACE
+    assert sst(Q=1, P=(16 << 20) // 4 + 1) == WORKSPACE
+    assert lib.dsai_select_expand_static(None, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE,
+                                         None) == NULLPTR
     # expand
     assert lib.dsai_expand(h, FAKE, -1, FAKE, None) == INVALID
     assert lib.dsai_expand(h, FAKE, 0, FAKE, None) == OK
@@ -330,7 +342,7 @@ def test_pooled_argument_errors(lib):
 
 def test_expanded_token_ids_must_fit_int32(lib):
     """first_key + P * kpool - 1 above 2^31 - 1 would overflow the int32
-    token ids: select with expand refuses it before any HIP
+    token ids: select with expand (either form) refuses it before any HIP
     call; one pool fewer passes the check (and then needs a device, so the
     workspace check is what answers here)."""
     KP, fk = 8, 2 ** 31 - 1 - 8 * 1000
@@ -341,6 +353,8 @@ def test_expanded_token_ids_must_fit_int32(lib):
                                                    FAKE, ws, 0, None)
     assert se(P_ok + 1) == INVALID
     assert se(P_ok) == WORKSPACE                 # past the token check: no workspace given
+    assert lib.dsai_select_expand_static(h, FAKE, FAKE, FAKE, FAKE, 2, P_ok + 1, FAKE, FAKE,
+                                         FAKE, None) == INVALID
     lib.dsai_destroy(h)
 
 
