@@ -1,42 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of the DSA lightning-indexer selection path on one MI355X.
 
-One step = one pass of the whole hot path on synthetic inputs already
-resident in device memory:
-  * the unpooled indexer on the prefill workload (B=1, S=Skv=4096, H=64,
-    D=128, topk=2048, causal): the fused score + mask + top-k kernel
-    (rows in index order), then the score-order pass (dsai_sort_rows) -- the
-    same work and result as dsai_score_topk under DSAI_ORDER_SCORE, timed
-    as two launches so the fused kernel has a duration of its own;
-  * the pooled decode selection over one 65536-token indexer cache
-    (kpool_compress -> select with expand: index_scores + topk_pools, whose
-    kernel also writes the expanded token ids (dsai_select_expand);
-    KP=4, 64 query rows, 32 heads, index_topk=512).
-Outside the step, the same top-k rows are rescored through the
-topk_indices form of dsai_score_topk (scores at supplied indices), and the
-cache write's k_norm runs over the 65536 cache rows, and the backward
-(gradients of the selected scores, with seeded incoming gradients) runs at
-the step's top-k rows of whichever indexer workload is chosen, and the
-prefill rows and keys run as 4 packed sequences of 1024 (dsai_score_topk_packed,
-score order); all four are reported in `breakdown`
-(score_at_indices_*, k_norm_*, backward_*: 6*H*D flops per selected entry,
-and the D fp32 key-gradient adds per entry per second; packed_4x1024_*:
-2*H*D flops per visible pair of the four sequences).  The pooled decode
-stages are also captured once in a HIP graph and replayed
-(pooled_decode_graph_ms).
-`value` = prefill query tokens per second of the whole step (the pooled
-stages' time is counted against it as well).  HIP events on the stream the
-library launches on give per-stage times; the fused kernel's roofline is its
-algorithmic matrix-core work (2*H*D flops per visible (query, key) pair)
-over its average launch time against the dense bf16 peak.
+The headline step is one pass of the unpooled indexer over the long-context
+workload (B=1, S=Skv=65536, H=64, D=128, 5% of keys x4, causal, topk=2048,
+query rows in 1024-row chunks): dsai_score_topk in its default score order
+(fused score + causal mask + top-k per chunk, score-descending rows), inputs
+resident in device memory.  `value` = query tokens (B*S) per second of that
+step.  `roofline` is the fused kernel's: 2*H*D flops per visible (query,
+key) pair over the step's device time, against the dense bf16 peak (the
+chunks run two at a time on the library's two streams, so the time per
+launch is the step's time over its launches).
+
+Measured in the same run and reported in `breakdown` (not part of `value`):
+  * the other indexer workloads in the same call and order - prefill
+    (S=Skv=4096, topk=2048) and C4 (B=2, S=16384, Skv=4096, ratio 4,
+    topk=512) - each with its own fraction of the bf16 peak, and every
+    workload in index order (no score ordering);
+  * the pooled decode pipeline over a 65536-token cache (KP=4, Q=64, H=32,
+    index_topk=512): kpool_compress and expand_selection with the device's
+    caches flushed before every timed launch (a 512 MiB read evicts the
+    256 MB last-level cache), as GB/s against HBM peak, also at a scaled
+    size (kpool over 2^20 tokens, expand over 65536 rows); select with
+    expand, its static-scratch form, and the whole decode chain replayed
+    from a HIP graph;
+  * the cache write's k_norm (cold), scores at supplied indices, packed
+    sequences and the backward (prefill workload).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-Profiling helpers (see the summaries under profiles/):
+  --step-only             run and time only the headline step (profiling runs)
   --copy-calibration      also run a plain device copy of known size (the
                           yardstick for the FETCH_SIZE / WRITE_SIZE counters)
   --pmc-summary F W OUT   turn two rocprofv3 --pmc CSV directories (F with
                           FETCH_SIZE, W with WRITE_SIZE) into the traffic
                           summary OUT that later runs report as `traffic`
+  --counter-summary DIR OUT CMD  per-kernel averages of any rocprofv3 --pmc run
   --stats-summary CSV OUT CMD   text table of a rocprofv3 kernel_trace.csv
 """
 from __future__ import annotations
@@ -61,8 +58,13 @@ import synthetic as SY  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz, dense bf16
 PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 1 << 30        # copy calibration: 1 GiB read + 1 GiB written
+FLUSH_BYTES = 512 << 20     # read before each cold launch (> 256 MB last-level cache)
 SCORE_KERNEL = "score_select_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_select_prefill_traffic.txt")
+METRIC = "indexer query tokens/s (score+top-k) and % bf16 MFMA peak; pool/expand GB/s"
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"score_select_{workload}_traffic.txt")
 
 
 def visible_pairs(case) -> int:
@@ -74,6 +76,10 @@ def indexer_flops(case) -> float:
     return 2.0 * case.H * case.D * visible_pairs(case)
 
 
+def launches(case) -> int:
+    return max(1, -(-case.S // case.chunk_rows)) if case.chunk_rows else 1
+
+
 def selected_entries(case) -> int:
     """Usable (row, key) entries of the top-k output: sum over rows of
     min(topk, n_t) - the pairs the gather form scores when fed that output."""
@@ -82,24 +88,20 @@ def selected_entries(case) -> int:
     return int(np.minimum(case.topk, n).sum()) * case.B
 
 
-def kpool_bytes(pc, P) -> int:
+def kpool_bytes(N, D, KP, first_key=0) -> int:
     # read k_normed (bf16) + gate (fp32) + valid (u8) of the pooled tokens + ape;
     # write pool_k (bf16) + pool_tok (i32) + pool_valid (u8)
-    n = P * pc.KP
-    return n * pc.D * 2 + n * pc.D * 4 + n + pc.KP * pc.D * 4 + P * pc.D * 2 + P * 4 + P
+    P = max(0, N - first_key) // KP
+    n = P * KP
+    return n * D * 2 + n * D * 4 + n + KP * D * 4 + P * D * 2 + P * 4 + P
 
 
-def expand_bytes(pc) -> int:
-    sel = pc.index_topk // pc.KP
-    return pc.Q * sel * 4 + pc.Q * pc.index_topk * 4
+def expand_bytes(Q, select_k, KP) -> int:
+    return Q * select_k * 4 + Q * select_k * KP * 4
 
 
 def select_flops(pc, P) -> float:
     return 2.0 * pc.Q * pc.H * pc.D * P
-
-
-def sort_bytes(case) -> int:
-    return 2 * case.B * case.S * case.topk * 8   # read + write (int32 index, fp32 score)
 
 
 def kernel_sources_sha1() -> str:
@@ -114,11 +116,11 @@ def kernel_sources_sha1() -> str:
     return h.hexdigest()
 
 
-def read_traffic():
-    """Bytes per launch of the fused kernel from the committed counter summary,
-    or None when it is missing or was taken on other kernel sources."""
+def read_traffic(workload):
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel sources."""
     try:
-        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line
+        kv = dict(line.split(":", 1) for line in open(traffic_file(workload)) if ":" in line
                   and not line.startswith("#"))
     except OSError:
         return None
@@ -130,6 +132,10 @@ def read_traffic():
     except (KeyError, ValueError):
         return None
 
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output summaries
+# ---------------------------------------------------------------------------
 
 def _pmc_rows(d):
     rows = []
@@ -149,18 +155,15 @@ def _per_dispatch(rows, counter, match):
     return list(vals.values())
 
 
-def pmc_summary(fetch_dir, write_dir, out):
+def pmc_summary(fetch_dir, write_dir, out, workload="long"):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel, each
-    scaled by what the counter reads for the copy of COPY_BYTES."""
+    scaled by what the counter reads for the copy of COPY_BYTES.  The
+    headline run launches only the fused kernel's chunks of one workload, so
+    every dispatch of that kernel is counted (per launch = per chunk)."""
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     is_copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
     is_score = lambda n: SCORE_KERNEL in n
     names = sorted({r["Kernel_Name"] for r in fr if is_score(r["Kernel_Name"])})
-    # the prefill launch: the fused kernel's dispatches with the largest grid
-    # (the packed sequences' launches of the same kernel are smaller)
-    grid = max(int(r["Grid_Size"]) for r in fr + wr if is_score(r["Kernel_Name"]))
-    fr = [r for r in fr if not is_score(r["Kernel_Name"]) or int(r["Grid_Size"]) == grid]
-    wr = [r for r in wr if not is_score(r["Kernel_Name"]) or int(r["Grid_Size"]) == grid]
     f_k, w_k = _per_dispatch(fr, "FETCH_SIZE", is_score), _per_dispatch(wr, "WRITE_SIZE", is_score)
     f_c, w_c = _per_dispatch(fr, "FETCH_SIZE", is_copy), _per_dispatch(wr, "WRITE_SIZE", is_copy)
     if not (f_k and w_k and f_c and w_c):
@@ -170,18 +173,18 @@ def pmc_summary(fetch_dir, write_dir, out):
     fscale = COPY_BYTES / (np.mean(f_c) * 1024)
     wscale = COPY_BYTES / (np.mean(w_c) * 1024)
     fk, wk = np.mean(f_k) * 1024 * fscale, np.mean(w_k) * 1024 * wscale
+    cmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --step-only "
+           f"--no-cpu-baseline --copy-calibration")
     lines = [
-        "# HBM traffic of the fused score + top-k kernel, prefill workload",
-        "# (B=1, S=Skv=4096, H=64, D=128, topk=2048), rocprofv3 --pmc counters.",
+        f"# HBM traffic per launch of the fused score + top-k kernel, workload {workload},",
+        "# rocprofv3 --pmc counters (one counter per pass), scaled by a 1 GiB device copy.",
         "# commands (from the repository root):",
-        "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <F> -o run -- python3 bench.py --steps 3 "
-        "--warmup 1 --no-cpu-baseline --copy-calibration",
-        "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <W> -o run -- python3 bench.py --steps 3 "
-        "--warmup 1 --no-cpu-baseline --copy-calibration",
-        "#   python3 bench.py --pmc-summary <F> <W> profiles/score_select_prefill_traffic.txt",
+        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <F> -o run -- {cmd}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <W> -o run -- {cmd}",
+        f"#   python3 bench.py --pmc-summary <F> <W> profiles/score_select_{workload}_traffic.txt "
+        f"--workload {workload}",
         f"kernel: {names[0] if names else SCORE_KERNEL}",
         f"source_sha1: {kernel_sources_sha1()}",
-        f"grid_threads: {grid}",
         f"dispatches: fetch {len(f_k)}, write {len(w_k)}",
         f"fetch_kib_per_dispatch: {np.mean(f_k):.1f}",
         f"write_kib_per_dispatch: {np.mean(w_k):.1f}",
@@ -199,110 +202,158 @@ def pmc_summary(fetch_dir, write_dir, out):
     print("\n".join(lines))
 
 
-def stats_summary(csv_path, out, command):
-    """Short text table of a rocprofv3 --kernel-trace run (its
-    kernel_trace.csv), one line per kernel and grid size, so launches of one
-    kernel at different sizes (the prefill launch and the packed sequences'
-    launches of the fused kernel) are listed apart."""
-    groups = {}
-    for r in csv.DictReader(open(csv_path)):
-        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        groups.setdefault((r["Kernel_Name"].strip('"'), grid), []).append(dur)
-    total = sum(sum(v) for v in groups.values())
-    lines = ["# rocprofv3 kernel-trace statistics per kernel and grid size (threads)",
-             f"# command: {command}",
-             f"# {'kernel':<64s} {'grid':>8s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
-             f"{'max_us':>9s} {'pct':>6s}"]
-    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        name = name if len(name) <= 64 else name[:61] + "..."
-        lines.append(f"  {name:<64s} {grid:8d} {len(v):6d} {np.mean(v):9.2f} {min(v):9.2f} "
-                     f"{max(v):9.2f} {100 * sum(v) / total:6.2f}")
+def counter_summary(pmc_dir, out, command):
+    """Per-kernel averages (per dispatch) of every counter of a rocprofv3
+    --pmc run, with the derived matrix-core and LDS figures when their
+    counters are present (GRBM_GUI_ACTIVE counts per XCD and is summed over
+    the 8 XCDs; SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs)."""
+    rows = _pmc_rows(pmc_dir)
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        d = per.setdefault(name, {})
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        d.setdefault(r["Counter_Name"], {})
+        d[r["Counter_Name"]][key] = d[r["Counter_Name"]].get(key, 0.0) + float(r["Counter_Value"])
+    lines = ["# rocprofv3 --pmc counters, average per dispatch, per kernel",
+             f"# command: {command}"]
+    for name, cs in sorted(per.items(), key=lambda kv: kv[0]):
+        if "at::" in name:
+            continue
+        nd = max(len(v) for v in cs.values())
+        lines.append(f"kernel: {name[:150]}")
+        lines.append(f"  dispatches: {nd}")
+        avg = {c: float(np.mean(list(v.values()))) for c, v in cs.items()}
+        for c in sorted(avg):
+            lines.append(f"  {c}: {avg[c]:.0f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+            cyc = avg["GRBM_GUI_ACTIVE"] / 8.0
+            lines.append(f"  derived_mfma_busy_frac: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.3f}")
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            lines.append("  derived_lds_bank_conflict_frac: "
+                         f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.3f}")
+        if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
+            lines.append(f"  derived_valu_per_mfma: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def cpu_baseline(case, pc, budget_s=15.0, cap_s=30.0):
-    """The oracle (fp64 NumPy, as it stands) running the same step on the host:
-    every prefill query row against all its visible keys in score order, then
-    the pooled pipeline.  Whole steps are repeated until `budget_s` has
-    passed; if one step would run past `cap_s` the prefill rows stop there and
-    the step time is extrapolated from the rows done."""
+def stats_summary(csv_path, out, command):
+    """Short text table of a rocprofv3 --kernel-trace run (its
+    kernel_trace.csv), one line per kernel and grid size.  `avg_us` is the
+    mean dispatch duration; `union_us` is the time during which at least one
+    dispatch of that line ran, per dispatch (launches that overlap on two
+    streams count once), which is what a host timer around the calls sees."""
+    groups = {}
+    for r in csv.DictReader(open(csv_path)):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        groups.setdefault((r["Kernel_Name"].strip('"'), grid), []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    total = sum(sum(e - s for s, e in v) for v in groups.values())
+    lines = ["# rocprofv3 kernel-trace statistics per kernel and grid size (threads)",
+             f"# command: {command}",
+             f"# {'kernel':<64s} {'grid':>8s} {'calls':>6s} {'avg_us':>9s} {'union_us':>9s} "
+             f"{'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+
+    def union(iv):
+        iv = sorted(iv)
+        tot, cs, ce = 0, iv[0][0], iv[0][1]
+        for s, e in iv[1:]:
+            if s > ce:
+                tot += ce - cs
+                cs, ce = s, e
+            else:
+                ce = max(ce, e)
+        return tot + ce - cs
+
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(e - s for s, e in kv[1])):
+        d = [(e - s) / 1e3 for s, e in v]
+        name = name if len(name) <= 64 else name[:61] + "..."
+        lines.append(f"  {name:<64s} {grid:8d} {len(v):6d} {np.mean(d):9.2f} "
+                     f"{union(v) / 1e3 / len(v):9.2f} {min(d):9.2f} {max(d):9.2f} "
+                     f"{100 * sum(d) * 1e3 / total:6.2f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands
+# ---------------------------------------------------------------------------
+
+def _sample_rows(case, n):
+    """Deterministic spread of query positions over the whole range."""
+    return np.unique(np.linspace(0, case.S - 1, n).round().astype(np.int64))
+
+
+def cpu_baseline(case, budget_s=20.0):
+    """The oracle (fp64 NumPy, as it stands) on a bounded sample of the
+    headline workload: query rows spread over the positions (32 rows from
+    each of 8 evenly spaced 1024-row blocks, so their inputs are drawn
+    without drawing the rest), each scored against all its visible keys and
+    ranked, in a shuffled order until `budget_s` of oracle time has passed.
+    The time per visible (query, key) pair on the rows done, times the
+    workload's visible pairs, gives the step time on the host."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    inp = SY.indexer_inputs(case)
+    k = SY.bf16_bits_to_f32(SY.indexer_k_bits(case)).astype(np.float64)
+    nblk = max(1, case.S // SY.BLOCK)
+    blocks = np.unique(np.linspace(0, nblk - 1, min(8, nblk)).round().astype(np.int64))
+    rows = np.concatenate([b * SY.BLOCK + np.linspace(0, min(SY.BLOCK, case.S - b * SY.BLOCK) - 1,
+                                                      32).round().astype(np.int64)
+                           for b in blocks])
+    rows = np.unique(rows)
+    inp = SY.indexer_inputs(case, rows=rows)
     q = SY.bf16_bits_to_f32(inp["q_bits"]).astype(np.float64)
-    k = SY.bf16_bits_to_f32(inp["k_bits"]).astype(np.float64)
     w = inp["w"].astype(np.float64)
-    pin = SY.pooled_inputs(pc)
-    kn = SY.bf16_bits_to_f32(pin["k_normed_bits"]).astype(np.float64)
-    pq = SY.bf16_bits_to_f32(pin["q_bits"]).astype(np.float64)
-
-    def pooled():
-        ref = oracle.kpool_compress(kn, pin["gate"], pin["valid"], pin["ape"], pc.first_key, pc.KP)
-        s = oracle.pooled_index_scores(pq, pin["w"], ref["pool_k"], ref["pool_valid"])
-        ids, _ = oracle.topk_pools(s, pc.index_topk // pc.KP)
-        oracle.expand_selection(ids, pc.first_key, pc.KP)
-
-    steps, t_rows, rows_done, t_pool, partial = 0, 0.0, 0, 0.0, False
-    t_start = time.perf_counter()
-    while True:
+    order = np.random.default_rng(0).permutation(rows.size)
+    pairs, done, spent = 0, 0, 0.0
+    for i in order:
+        t = int(rows[i])
         t0 = time.perf_counter()
-        for b in range(case.B):
-            for t in range(case.S):
-                oracle.score_topk(q[t:t + 1, b:b + 1], k[:, b:b + 1], w[t:t + 1, b:b + 1],
-                                  case.compress_ratio, case.topk, rows=[t])
-                rows_done += 1
-                if time.perf_counter() - t_start > cap_s:
-                    partial = True
-                    break
-            if partial:
-                break
-        t_rows += time.perf_counter() - t0
-        if partial:
+        oracle.score_topk(q[i:i + 1], k, w[i:i + 1], case.compress_ratio, case.topk, rows=[t])
+        spent += time.perf_counter() - t0
+        done += 1
+        pairs += case.B * oracle.visible_keys(t, case.Skv, case.compress_ratio)
+        if spent > budget_s:
             break
-        t0 = time.perf_counter()
-        pooled()
-        t_pool += time.perf_counter() - t0
-        steps += 1
-        if time.perf_counter() - t_start >= budget_s:
-            break
-    per_row = t_rows / rows_done
-    if steps:
-        step_s = (t_rows + t_pool) / steps
-        sample = (f"{steps} whole step(s): all {case.B * case.S} {case.name} query rows in score "
-                  f"order plus the pooled_decode pipeline, fp64 NumPy, "
-                  f"{t_rows + t_pool:.1f} s")
-    else:
-        t0 = time.perf_counter()
-        pooled()
-        t_pool = time.perf_counter() - t0
-        step_s = per_row * case.B * case.S + t_pool
-        sample = (f"{rows_done} of {case.B * case.S} {case.name} query rows (t=0..) timed and "
-                  f"extrapolated to the step, plus one pooled_decode pipeline, fp64 NumPy")
+    step_s = spent / pairs * visible_pairs(case)
+    sample = (f"{done} of {case.B * case.S} {case.name} query rows (32 from each of "
+              f"{blocks.size} evenly spaced 1024-row blocks, shuffled), each against all its "
+              f"visible keys in score order, fp64 NumPy, {spent:.1f} s; extrapolated to the "
+              f"whole workload by visible (query, key) pairs")
     return {"value": case.B * case.S / step_s, "unit": "query tokens/s", "cores": int(cores),
             "kind": "oracle", "sample": sample}
 
 
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill", choices=sorted(SY.CASES))
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long", choices=sorted(SY.CASES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--counter-summary", nargs=3, metavar=("PMC_DIR", "OUT", "COMMAND"))
     ap.add_argument("--stats-summary", nargs=3, metavar=("KERNEL_TRACE_CSV", "OUT", "COMMAND"))
     args = ap.parse_args()
 
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, workload=args.workload)
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
         return
     if args.stats_summary:
         stats_summary(*args.stats_summary)
@@ -325,16 +376,140 @@ def main():
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # ---- inputs (resident before timing) ----------------------------------
-    case = SY.CASES[args.workload]
-    inp = SY.indexer_inputs(case)
-    q, k = bf16(inp["q_bits"]), bf16(inp["k_bits"])
-    w = torch.from_numpy(inp["w"]).to(dev)
-    ix = dsai.Indexer(heads=case.H, dim=case.D, chunk_rows=case.chunk_rows,
-                      order=dsai.DSAI_ORDER_INDEX)
-    out_idx = torch.empty((case.B, case.S, case.topk), dtype=torch.int32, device=dev)
-    out_sc = torch.empty((case.B, case.S, case.topk), dtype=torch.float32, device=dev)
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
+    def timed(fn, reps, warm=2):
+        """Average ms of fn() over `reps` calls queued back to back (HIP events
+        on torch's current stream, the stream every library call runs on)."""
+        for _ in range(warm):
+            fn()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    flush_buf = None
+
+    def timed_cold(fn, reps):
+        """Average ms of fn() with the caches flushed before each launch: a
+        FLUSH_BYTES read (outside the timed interval, clean lines, so no
+        write-back competes with fn) evicts the last-level cache and the
+        L2s, so fn's inputs come from HBM."""
+        nonlocal flush_buf
+        if flush_buf is None:
+            flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        fn()
+        pairs = [(ev(), ev()) for _ in range(reps)]
+        for a, b in pairs:
+            torch.sum(flush_buf, out=sink)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+    def indexer_case(case, order):
+        inp = SY.indexer_inputs(case)
+        q, k = bf16(inp["q_bits"]), bf16(inp["k_bits"])
+        w = torch.from_numpy(inp["w"]).to(dev)
+        ix = dsai.Indexer(heads=case.H, dim=case.D, chunk_rows=case.chunk_rows, order=order)
+        oi = torch.empty((case.B, case.S, case.topk), dtype=torch.int32, device=dev)
+        osc = torch.empty((case.B, case.S, case.topk), dtype=torch.float32, device=dev)
+        run = lambda: ix.score_topk(q, k, w, case.compress_ratio, case.topk, out_idx=oi,
+                                    out_score=osc)
+        return run, (q, k, w, oi, osc)
+
+    # ---- headline step ------------------------------------------------------
+    case = SY.CASES[args.workload]
+    step, held = indexer_case(case, dsai.DSAI_ORDER_SCORE)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = ev(), ev()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    flops = indexer_flops(case)
+    nl = launches(case)
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": case.B * case.S / (ms_per_step * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "B": case.B, "S": case.S, "Skv": case.Skv,
+                   "H": case.H, "D": case.D, "topk": case.topk,
+                   "compress_ratio": case.compress_ratio, "chunk_rows": case.chunk_rows,
+                   "heavy_keys": f"{case.heavy_frac:g} of keys x{case.heavy_scale:g}",
+                   "order": "score descending", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": f"{SCORE_KERNEL}<64,128,...> (fused score+mask+top-k)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": read_traffic(case.name),
+                     "flops_per_launch": flops / nl, "launches_per_step": nl,
+                     "avg_launch_ms": ms_per_step / nl},
+    }
+    if args.step_only:
+        print(json.dumps(result), flush=True)
+        return
+
+    bd = {"wall_s": wall}
+    # ---- indexer workloads --------------------------------------------------
+    # The headline workload in index order (the fused kernel alone), then the
+    # other workloads in both orders.
+    ix_case = {}
+    for name in ("prefill", "c4", "long"):
+        c = SY.CASES[name]
+        reps = max(3, args.steps) if name == "long" else max(10, 2 * args.steps)
+        ent = {}
+        for order, tag in ((dsai.DSAI_ORDER_SCORE, "score"), (dsai.DSAI_ORDER_INDEX, "index")):
+            if name == case.name and tag == "score":
+                ms = ms_per_step
+            else:
+                run, keep = indexer_case(c, order) if name != case.name else \
+                    (None, None)
+                if run is None:   # the headline workload's inputs are resident already
+                    q, k, w, oi, osc = held
+                    ixo = dsai.Indexer(heads=c.H, dim=c.D, chunk_rows=c.chunk_rows, order=order)
+                    run = lambda: ixo.score_topk(q, k, w, c.compress_ratio, c.topk, out_idx=oi,
+                                                 out_score=osc)
+                ms = timed(run, reps)
+                del run, keep
+            fl = indexer_flops(c)
+            ent[f"{tag}_order_ms"] = ms
+            ent[f"{tag}_order_tokens_per_s"] = c.B * c.S / (ms * 1e-3)
+            ent[f"{tag}_order_frac"] = fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+        ent["gflop"] = indexer_flops(c) / 1e9
+        ix_case[name] = ent
+        torch.cuda.empty_cache()
+    bd["indexer"] = ix_case
+
+    # ---- pooled decode pipeline ----------------------------------------------
     pc = SY.POOLED_CASES["pooled_decode"]
     pin = SY.pooled_inputs(pc)
     pix = dsai.Indexer(heads=pc.H, dim=pc.D, kpool=pc.KP, index_topk=pc.index_topk,
@@ -351,130 +526,47 @@ def main():
     pids = torch.empty((pc.Q, sel), dtype=torch.int32, device=dev)
     pscores = torch.empty((pc.Q, sel), dtype=torch.float32, device=dev)
     toks = torch.empty((pc.Q, pc.index_topk), dtype=torch.int32, device=dev)
+    reps = max(10, args.steps)
 
-    stages = ["score_topk", "sort_rows", "kpool_compress", "select_expand"]
+    kp_run = lambda: pix.kpool_compress(kn, gate, valid, ape, pool_k=pool_k, pool_tok=pool_tok,
+                                        pool_valid=pool_valid)
+    kp_ms = timed_cold(kp_run, reps)
+    kb = kpool_bytes(pc.N, pc.D, pc.KP, pc.first_key)
+    sel_run = lambda: pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids,
+                                 pool_scores=pscores, tokens=toks, expand=True)
+    sel_ms = timed(sel_run, reps)
+    st_run = lambda: pix.select_expand_static(pq, pw, pool_k, pool_valid, pids, pscores, toks)
+    st_ms = timed(st_run, reps)
+    ex_run = lambda: pix.expand(pids, tokens=toks)
+    ex_ms = timed_cold(ex_run, reps)
+    eb = expand_bytes(pc.Q, sel, pc.KP)
 
-    def step(ev=None):
-        e = ev or {}
+    # scaled diagnostics: kpool over 2^20 tokens, expand over 65536 rows
+    NB = 1 << 20
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    kn_b = torch.randn((NB, pc.D), generator=g, device=dev).to(torch.bfloat16)
+    gate_b = torch.randn((NB, pc.D), generator=g, device=dev)
+    valid_b = (torch.rand((NB,), generator=g, device=dev) < pc.valid_p).to(torch.uint8)
+    PB = pix.pool_count(NB)
+    pk_b = torch.empty((PB, pc.D), dtype=torch.bfloat16, device=dev)
+    pt_b = torch.empty((PB,), dtype=torch.int32, device=dev)
+    pv_b = torch.empty((PB,), dtype=torch.uint8, device=dev)
+    kpb_ms = timed_cold(lambda: pix.kpool_compress(kn_b, gate_b, valid_b, ape, pool_k=pk_b,
+                                                   pool_tok=pt_b, pool_valid=pv_b), reps)
+    kbb = kpool_bytes(NB, pc.D, pc.KP, pc.first_key)
+    del kn_b, gate_b, valid_b, pk_b, pt_b, pv_b
+    QB = 65536
+    ids_b = torch.randint(-1, P, (QB, sel), generator=g, device=dev, dtype=torch.int32)
+    tok_b = torch.empty((QB, pc.index_topk), dtype=torch.int32, device=dev)
+    exb_ms = timed_cold(lambda: pix.expand(ids_b, tokens=tok_b), reps)
+    ebb = expand_bytes(QB, sel, pc.KP)
+    del ids_b, tok_b
 
-        def mark(name, i):
-            if e:
-                e[name][i].record()
-        mark("score_topk", 0)
-        ix.score_topk(q, k, w, case.compress_ratio, case.topk, out_idx=out_idx, out_score=out_sc)
-        mark("score_topk", 1)
-        mark("sort_rows", 0)
-        ix.sort_rows(out_idx, out_sc)
-        mark("sort_rows", 1)
-        mark("kpool_compress", 0)
-        pix.kpool_compress(kn, gate, valid, ape, pool_k=pool_k, pool_tok=pool_tok, pool_valid=pool_valid)
-        mark("kpool_compress", 1)
-        mark("select_expand", 0)   # index_scores + topk_pools + expand_selection
-        pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids, pool_scores=pscores,
-                   tokens=toks, expand=True)
-        mark("select_expand", 1)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # whole-step timing
-    t0 = time.perf_counter()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
-
-    # per-stage timing: HIP events on the stream the library launches on
-    # (torch's current stream, which the binding passes to every call); the
-    # steps are queued back to back so no event waits on the host
-    per = {s: [] for s in stages}
-    evs = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for s in stages} for _ in range(args.steps + 1)]
-    for ev in evs:
-        step(ev)
-    torch.cuda.synchronize()
-    for ev in evs[1:]:   # the first step of the batch starts from an idle queue
-        for s in stages:
-            per[s].append(ev[s][0].elapsed_time(ev[s][1]))
-    avg = {s: float(np.mean(v)) for s, v in per.items()}
-    med = {s: float(np.median(v)) for s, v in per.items()}
-
-    # scores at supplied indices (the topk_indices form; not part of the
-    # step): the step's own top-k rows rescored (prefill workload only)
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    at_ms = at_flops = None
-    if case.name == "prefill":
-        at_ix = dsai.Indexer(heads=case.H, dim=case.D, chunk_rows=case.chunk_rows)
-        at_idx, at_sc = torch.empty_like(out_idx), torch.empty_like(out_sc)
-        for _ in range(2):
-            at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
-                             out_idx=at_idx, out_score=at_sc)
-        a0.record()
-        for _ in range(args.steps):
-            at_ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=out_idx,
-                             out_idx=at_idx, out_score=at_sc)
-        a1.record()
-        torch.cuda.synchronize()
-        at_ms = a0.elapsed_time(a1) / args.steps
-        at_flops = 2.0 * case.H * case.D * selected_entries(case)
-
-    # packed sequences (not part of the step): the prefill rows and keys cut
-    # into 4 sequences of S/4, each causal on its own keys (prefill only)
-    pk_ms = pk_flops = None
-    if case.name == "prefill":
-        nseq = 4
-        cu = np.arange(nseq + 1, dtype=np.int64) * (case.S // nseq)
-        pk_ix = dsai.Indexer(heads=case.H, dim=case.D)
-        pq_, pk_, pw_ = q[:, 0], k[:, 0], w[:, 0]
-        pk_i = torch.empty((case.S, case.topk), dtype=torch.int32, device=dev)
-        pk_s = torch.empty((case.S, case.topk), dtype=torch.float32, device=dev)
-        for _ in range(2):
-            pk_ix.score_topk_packed(pq_, pk_, pw_, cu, cu, case.compress_ratio, case.topk,
-                                    out_idx=pk_i, out_score=pk_s)
-        a0.record()
-        for _ in range(args.steps):
-            pk_ix.score_topk_packed(pq_, pk_, pw_, cu, cu, case.compress_ratio, case.topk,
-                                    out_idx=pk_i, out_score=pk_s)
-        a1.record()
-        torch.cuda.synchronize()
-        pk_ms = a0.elapsed_time(a1) / args.steps
-        t = np.arange(case.S // nseq, dtype=np.int64)
-        pk_flops = 2.0 * case.H * case.D * nseq * float(
-            np.minimum(case.S // nseq, (t + 1) // case.compress_ratio).sum())
-
-    # the backward (gradients of the selected scores) at the step's own top-k
-    # rows, with seeded incoming gradients (not part of the step)
-    bw_ix = dsai.Indexer(heads=case.H, dim=case.D)
-    bw_g = torch.from_numpy(SY.score_grads(case.seed, case.B, case.S, case.topk)).to(dev)
-    bw_ws = torch.empty(bw_ix.backward_workspace_size(case.S, case.Skv, case.B, case.topk,
-                                                      case.compress_ratio), dtype=torch.uint8,
-                        device=dev)
-    bw_out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w))
-    for _ in range(2):
-        bw_ix.indexer_backward(q, k, w, out_idx, bw_g, case.compress_ratio, workspace=bw_ws,
-                               grad_q=bw_out[0], grad_k=bw_out[1], grad_weights=bw_out[2])
-    a0.record()
-    for _ in range(args.steps):
-        bw_ix.indexer_backward(q, k, w, out_idx, bw_g, case.compress_ratio, workspace=bw_ws,
-                               grad_q=bw_out[0], grad_k=bw_out[1], grad_weights=bw_out[2])
-    a1.record()
-    torch.cuda.synchronize()
-    bw_ms = a0.elapsed_time(a1) / args.steps
-    bw_entries = selected_entries(case)
-    del bw_ws, bw_out
-
-    # the pooled decode stages (kpool_compress -> select with expand) captured
-    # once in a HIP graph and replayed: the decode step's latency without
-    # per-call launch work (not part of the step)
+    # the decode chain (kpool -> select with expand) captured once and replayed
     def pooled():
-        pix.kpool_compress(kn, gate, valid, ape, pool_k=pool_k, pool_tok=pool_tok, pool_valid=pool_valid)
-        pix.select(pq, pw, pool_k, pool_valid, workspace=ws, pool_ids=pids, pool_scores=pscores,
-                   tokens=toks, expand=True)
+        kp_run()
+        sel_run()
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -485,91 +577,79 @@ def main():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         pooled()
-    graph.replay()
-    torch.cuda.synchronize()
-    a0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    a1.record()
-    torch.cuda.synchronize()
-    pooled_graph_ms = a0.elapsed_time(a1) / args.steps
+    graph_ms = timed(graph.replay, reps)
     del graph
 
-    # the cache write's k_norm (LayerNorm with a bias) over the pooled
-    # workload's 65536 cache rows (not part of the step)
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    bd["pooled_decode"] = {
+        "N": pc.N, "KP": pc.KP, "Q": pc.Q, "H": pc.H, "index_topk": pc.index_topk, "P": P,
+        "kpool_cold_ms": kp_ms, "kpool_bytes": kb, "kpool_cold_GBps": gbs(kb, kp_ms),
+        "kpool_cold_frac_hbm": gbs(kb, kp_ms) / PEAK_HBM_GBS,
+        "kpool_2p20_cold_ms": kpb_ms, "kpool_2p20_bytes": kbb,
+        "kpool_2p20_cold_GBps": gbs(kbb, kpb_ms), "kpool_2p20_cold_frac_hbm": gbs(kbb, kpb_ms) / PEAK_HBM_GBS,
+        "select_expand_ms": sel_ms,
+        "select_expand_TFLOPs": select_flops(pc, P) / (sel_ms * 1e-3) / 1e12,
+        "select_expand_static_ms": st_ms,
+        "expand_cold_ms": ex_ms, "expand_bytes": eb, "expand_cold_GBps": gbs(eb, ex_ms),
+        "expand_q65536_cold_ms": exb_ms, "expand_q65536_bytes": ebb,
+        "expand_q65536_cold_GBps": gbs(ebb, exb_ms),
+        "expand_q65536_cold_frac_hbm": gbs(ebb, exb_ms) / PEAK_HBM_GBS,
+        "decode_graph_ms": graph_ms,
+        "decode_tokens_per_s": pc.Q / (graph_ms * 1e-3),
+    }
+
+    # the cache write's k_norm (LayerNorm with a bias) over the 65536 cache rows
     ln_g = torch.ones((pc.D,), dtype=torch.bfloat16, device=dev)
     ln_b = torch.zeros((pc.D,), dtype=torch.bfloat16, device=dev)
     ln_out = torch.empty_like(kn)
-    for _ in range(2):
-        pix.k_norm(kn, ln_g, ln_b, 1e-5, out=ln_out)
-    a0.record()
-    for _ in range(args.steps):
-        pix.k_norm(kn, ln_g, ln_b, 1e-5, out=ln_out)
-    a1.record()
-    torch.cuda.synchronize()
-    ln_ms = a0.elapsed_time(a1) / args.steps
+    ln_ms = timed_cold(lambda: pix.k_norm(kn, ln_g, ln_b, 1e-5, out=ln_out), reps)
     ln_bytes = 2 * kn.numel() * 2 + 2 * pc.D * 2
+    bd["k_norm"] = {"rows": pc.N, "cold_ms": ln_ms, "bytes": ln_bytes,
+                    "cold_GBps": gbs(ln_bytes, ln_ms), "cold_frac_hbm": gbs(ln_bytes, ln_ms) / PEAK_HBM_GBS}
+    del held
+    torch.cuda.empty_cache()
 
-    if args.copy_calibration:
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    flops = indexer_flops(case)
-    launches = max(1, -(-case.S // case.chunk_rows)) if case.chunk_rows else 1
-    launch_ms = avg["score_topk"] / launches
-    achieved = flops / launches / (launch_ms * 1e-3) / 1e12
-    kb, eb, sb = kpool_bytes(pc, P), expand_bytes(pc), sort_bytes(case)
-    tokens = case.B * case.S
-    result = {
-        "metric": "indexer query tokens/s (score+top-k) and % bf16 MFMA peak; pool/expand GB/s",
-        "value": tokens / (ms_per_step * 1e-3),
-        "unit": "query tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{case.name}+pooled_decode", "B": case.B, "S": case.S,
-                   "Skv": case.Skv, "H": case.H, "D": case.D, "topk": case.topk,
-                   "compress_ratio": case.compress_ratio, "chunk_rows": case.chunk_rows,
-                   "order": "score descending",
-                   "pooled": {"N": pc.N, "KP": pc.KP, "Q": pc.Q, "H": pc.H, "D": pc.D,
-                              "index_topk": pc.index_topk, "P": P},
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": f"{SCORE_KERNEL}<64,128> (fused score+mask+top-k)",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": read_traffic(),
-                     "flops_per_launch": flops / launches, "avg_launch_ms": launch_ms},
-        "breakdown": {
-            "score_topk_ms": avg["score_topk"], "score_topk_median_ms": med["score_topk"],
-            "sort_rows_ms": avg["sort_rows"], "sort_rows_GBps": sb / (avg["sort_rows"] * 1e-3) / 1e9,
-            "kpool_ms": avg["kpool_compress"], "kpool_GBps": kb / (avg["kpool_compress"] * 1e-3) / 1e9,
-            "kpool_bytes": kb,
-            "select_expand_ms": avg["select_expand"],
-            "select_expand_TFLOPs": select_flops(pc, P) / (avg["select_expand"] * 1e-3) / 1e12,
-            "expand_bytes": eb, "wall_s": wall,
-            "score_at_indices_ms": at_ms,
-            "score_at_indices_TFLOPs": (at_flops / (at_ms * 1e-3) / 1e12) if at_ms else None,
-            "k_norm_ms": ln_ms, "k_norm_GBps": ln_bytes / (ln_ms * 1e-3) / 1e9,
-            "k_norm_bytes": ln_bytes,
-            "pooled_decode_graph_ms": pooled_graph_ms,
-            "packed_4x1024_ms": pk_ms,
-            "packed_4x1024_TFLOPs": (pk_flops / (pk_ms * 1e-3) / 1e12) if pk_ms else None,
-            "backward_ms": bw_ms,
-            "backward_TFLOPs": 6.0 * case.H * case.D * bw_entries / (bw_ms * 1e-3) / 1e12,
-            "backward_key_adds_G_per_s": case.D * bw_entries / (bw_ms * 1e-3) / 1e9,
-        },
+    # ---- prefill-workload extras: supplied indices, packed, backward ----------
+    pcase = SY.CASES["prefill"]
+    prun, (q, k, w, oi, osc) = indexer_case(pcase, dsai.DSAI_ORDER_INDEX)
+    prun()
+    at_ix = dsai.Indexer(heads=pcase.H, dim=pcase.D)
+    at_idx, at_sc = torch.empty_like(oi), torch.empty_like(osc)
+    at_ms = timed(lambda: at_ix.score_topk(q, k, w, pcase.compress_ratio, pcase.topk,
+                                           topk_indices=oi, out_idx=at_idx, out_score=at_sc), reps)
+    at_flops = 2.0 * pcase.H * pcase.D * selected_entries(pcase)
+    nseq = 4
+    cu = np.arange(nseq + 1, dtype=np.int64) * (pcase.S // nseq)
+    pk_ix = dsai.Indexer(heads=pcase.H, dim=pcase.D)
+    pk_i = torch.empty((pcase.S, pcase.topk), dtype=torch.int32, device=dev)
+    pk_s = torch.empty((pcase.S, pcase.topk), dtype=torch.float32, device=dev)
+    pk_ms = timed(lambda: pk_ix.score_topk_packed(q[:, 0], k[:, 0], w[:, 0], cu, cu,
+                                                  pcase.compress_ratio, pcase.topk,
+                                                  out_idx=pk_i, out_score=pk_s), reps)
+    t = np.arange(pcase.S // nseq, dtype=np.int64)
+    pk_flops = 2.0 * pcase.H * pcase.D * nseq * float(
+        np.minimum(pcase.S // nseq, (t + 1) // pcase.compress_ratio).sum())
+    bw_g = torch.from_numpy(SY.score_grads(pcase.seed, pcase.B, pcase.S, pcase.topk)).to(dev)
+    bw_ws = torch.empty(at_ix.backward_workspace_size(pcase.S, pcase.Skv, pcase.B, pcase.topk,
+                                                      pcase.compress_ratio),
+                        dtype=torch.uint8, device=dev)
+    bw_out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w))
+    bw_ms = timed(lambda: at_ix.indexer_backward(q, k, w, oi, bw_g, pcase.compress_ratio,
+                                                 workspace=bw_ws, grad_q=bw_out[0],
+                                                 grad_k=bw_out[1], grad_weights=bw_out[2]), reps)
+    bw_entries = selected_entries(pcase)
+    bd["prefill_extras"] = {
+        "score_at_indices_ms": at_ms,
+        "score_at_indices_TFLOPs": at_flops / (at_ms * 1e-3) / 1e12,
+        "packed_4x1024_ms": pk_ms,
+        "packed_4x1024_TFLOPs": pk_flops / (pk_ms * 1e-3) / 1e12,
+        "backward_ms": bw_ms,
+        "backward_TFLOPs": 6.0 * pcase.H * pcase.D * bw_entries / (bw_ms * 1e-3) / 1e12,
+        "backward_key_adds_G_per_s": pcase.D * bw_entries / (bw_ms * 1e-3) / 1e9,
     }
+    result["breakdown"] = bd
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, pc)
+        result["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(result), flush=True)
 
 

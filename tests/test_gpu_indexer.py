@@ -122,6 +122,82 @@ def test_integer_inputs_bit_exact(dsai, case):
     assert np.array_equal(gsc.astype(np.float64), ovals)   # -0.0 == +0.0
 
 
+def _tie_inputs(case, lo, hi, w_zero=False):
+    """Integer q, k drawn from [lo, hi] and weights from {+-1, +-1/2, +-1/4}
+    (or all zero): every fp32 step of the GPU is exact, and the narrow range
+    makes equal scores frequent."""
+    rng = np.random.default_rng(case.seed + 500)
+    q = rng.integers(lo, hi + 1, (case.S, case.B, case.H, case.D)).astype(np.float32)
+    k = rng.integers(lo, hi + 1, (case.Skv, case.B, case.D)).astype(np.float32)
+    w = (rng.choice([-1.0, -0.5, -0.25, 0.25, 0.5, 1.0], (case.S, case.B, case.H))
+         .astype(np.float32))
+    if w_zero:
+        w[:] = 0.0
+    return {"q_bits": SY.f32_to_bf16_bits(q), "k_bits": SY.f32_to_bf16_bits(k), "w": w}
+
+
+def _exact_rows(case, gidx, gsc, inp, rows):
+    oidx, ovals, _ = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
+    for b in range(case.B):
+        g_i, g_s = gidx[b, rows], gsc[b, rows]
+        bad = np.argwhere(g_i != oidx[b])
+        assert bad.size == 0, f"b={b}: first differing (row, slot) {[(rows[r], c) for r, c in bad[:5]]}"
+        assert np.array_equal(g_s.astype(np.float64), ovals[b])   # -0.0 == +0.0
+        assert not np.any(g_s.view(np.uint32) == 0x80000000)       # the GPU writes +0
+
+
+FILTER_TIES = [
+    # rows longer than any dense store (D = 128: more than 4608 keys), topk =
+    # 2048, integer inputs in [-4, 4]: the filter store fills and cuts
+    # several times; 16-bit stored indices
+    (SY.IndexerCase("filter_int_h64d128_k2048", B=1, S=6000, Skv=6000, H=64, D=128,
+                    compress_ratio=1, topk=2048, w_var=0, seed=61), -4, 4, False),
+    # the same with q, k in [-1, 1]: scores on a coarse grid, heavy ties at
+    # the k-th value on every cut
+    (SY.IndexerCase("filter_ties_h64d128_k2048", B=1, S=6000, Skv=6000, H=64, D=128,
+                    compress_ratio=1, topk=2048, w_var=0, seed=62), -1, 1, False),
+    # every score is zero: each cut keeps the lowest indices
+    (SY.IndexerCase("filter_zero_h64d128_k2048", B=1, S=6000, Skv=6000, H=64, D=128,
+                    compress_ratio=1, topk=2048, w_var=0, seed=63), -4, 4, True),
+    # more than 65536 keys: 32-bit stored indices (H = 4, D = 32)
+    (SY.IndexerCase("filter_ties_wide_h4d32_k1024", B=1, S=70000, Skv=70000, H=4, D=32,
+                    compress_ratio=1, topk=1024, w_var=0, seed=64), -1, 1, False),
+]
+
+
+@pytest.mark.parametrize("case,lo,hi,w_zero", FILTER_TIES, ids=[c[0].name for c in FILTER_TIES])
+def test_filter_store_ties_bit_exact(dsai, case, lo, hi, w_zero):
+    """Exact-arithmetic inputs on rows long enough for the filtering store:
+    indices, their order, scores and +-0 equal the oracle's bit for bit on
+    every sampled row (ends, the rows where n_t crosses topk, every 13th
+    row), so the lower-index-wins rule is pinned across repeated cuts, in
+    score order and in index order."""
+    log(f"[gpu] filter-store ties {case.name}")
+    inp = _tie_inputs(case, lo, hi, w_zero)
+    k = case.topk
+    rows = sorted(set(range(0, 8)) | set(range(k - 4, k + 4)) | set(range(case.S - 8, case.S)) |
+                  set(range(0, case.S, 13 if case.S < 10000 else 1750)) |
+                  ({65534, 65535, 65536, 65537} if case.S > 65536 else set()))
+    gidx, gsc = run_gpu(dsai, case, inp)
+    if w_zero:   # closed form: the lowest min(topk, n_t) indices, score +0
+        for t in rows:
+            m = min(k, t + 1)
+            assert gidx[0, t, :m].tolist() == list(range(m)), t
+            assert np.all(gsc[0, t, :m].view(np.uint32) == 0)
+    _exact_rows(case, gidx, gsc, inp, rows)
+    # index order: the same set, ascending
+    ix = dsai.Indexer(heads=case.H, dim=case.D, order=dsai.DSAI_ORDER_INDEX)
+    ii, isc = ix.score_topk(to_gpu_bf16(inp["q_bits"]), to_gpu_bf16(inp["k_bits"]),
+                            torch.from_numpy(inp["w"]).cuda(), case.compress_ratio, k)
+    torch.cuda.synchronize()
+    ii, isc = ii.cpu().numpy(), isc.cpu().numpy()
+    for t in rows:
+        m = int((gidx[0, t] >= 0).sum())
+        order = np.argsort(gidx[0, t, :m], kind="stable")
+        assert np.array_equal(ii[0, t, :m], gidx[0, t, :m][order]), t
+        assert np.array_equal(isc[0, t, :m].view(np.uint32), gsc[0, t, :m][order].view(np.uint32)), t
+
+
 def test_chunked_launches_match_single_launch(dsai):
     case = MEDIUM[0]
     log("[gpu] chunking")
@@ -282,7 +358,12 @@ def test_config_parity(dsai, name):
     inp = SY.indexer_inputs(case)
     log(f"[gpu] config parity {name}: running")
     gidx, gsc = run_gpu(dsai, case, inp)
-    rows = list(range(case.S)) if name == "tiny" else _sample_rows(case)
+    if name == "tiny":
+        rows = list(range(case.S))
+    elif name == "long":   # every 64th row as well
+        rows = sorted(set(_sample_rows(case)) | set(range(0, case.S, 64)))
+    else:
+        rows = _sample_rows(case)
     log(f"[gpu] config parity {name}: oracle on {len(rows)} rows x {case.B} batches")
     _, _, full = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
     compare(case, gidx, gsc, rows, full)

@@ -258,3 +258,39 @@ def test_pooled_decode_full_size_counts(dsai):
     pvv = pv.cpu().numpy()
     assert pvv.shape == (16384,)
     assert not pvv[16374:].any()
+
+
+def test_pooled_kp1_equals_unpooled(dsai):
+    """Two GPU paths against each other: with KP = 1, ape = 0 and every token
+    valid, a pool key is its token's key exactly (a one-slot softmax is 1), so
+    the pooled selection of a decode query over N cached keys must equal the
+    unpooled selection of a query row that sees all N keys (the row at
+    position N - 1 of a causal batch): the same ids in the same order and
+    equal scores."""
+    N, H, D, Q, sel = 3000, 32, 128, 6, 256
+    log(f"[gpu] pooled KP=1 vs unpooled N={N}")
+    rng = np.random.default_rng(77)
+    k_bits = SY.f32_to_bf16_bits(rng.standard_normal((N, D)).astype(np.float32))
+    qd_bits = SY.f32_to_bf16_bits(rng.standard_normal((Q, H, D)).astype(np.float32))
+    wd = (rng.standard_normal((Q, H)) / np.sqrt(H)).astype(np.float32)
+    pix = dsai.Indexer(heads=H, dim=D, kpool=1, index_topk=sel)
+    pk, pt, pv = pix.kpool_compress(bf16_gpu(k_bits),
+                                    torch.from_numpy(rng.standard_normal((N, D)).astype(np.float32)).cuda(),
+                                    torch.ones(N, dtype=torch.uint8, device="cuda"),
+                                    torch.zeros((1, D), dtype=torch.float32, device="cuda"))
+    ids, vals = pix.select(bf16_gpu(qd_bits), torch.from_numpy(wd).cuda(), pk, pv)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(pk), k_bits)
+    # unpooled: S = N + Q - 1 rows, the last Q of them the decode queries
+    S = N + Q - 1
+    q_bits = np.zeros((S, 1, H, D), dtype=np.uint16)
+    q_bits[N - 1:, 0] = qd_bits
+    w = np.zeros((S, 1, H), dtype=np.float32)
+    w[N - 1:, 0] = wd
+    ix = dsai.Indexer(heads=H, dim=D)
+    ui, us = ix.score_topk(bf16_gpu(q_bits), bf16_gpu(k_bits.reshape(N, 1, D)),
+                           torch.from_numpy(w).cuda(), 1, sel)
+    torch.cuda.synchronize()
+    ui, us = ui.cpu().numpy()[0, N - 1:], us.cpu().numpy()[0, N - 1:]
+    assert np.array_equal(ids.cpu().numpy(), ui)
+    assert np.array_equal(vals.cpu().numpy().astype(np.float64), us.astype(np.float64))
