@@ -294,10 +294,17 @@ int dsai_kpool_compress(dsai_handle h, const void* k_normed, const float* gate,
  *   q [Q, H, D] bf16, w [Q, H] fp32, pool_k [P, D] bf16, pool_valid [P] uint8
  *   scores[q, p] = sum_h w[q,h] * max(0, q[q,h,:] . pool_k[p,:]) if
  *   pool_valid[p], else -inf (an invalid candidate).  No causal mask.
+ *   pool_limit: NULL (every row sees every pool) or [Q] int32 device array,
+ *   4-byte aligned: row q's pools p >= pool_limit[q] are invalid candidates
+ *   for that row (-inf), e.g. the pools not wholly before a query of a
+ *   multi-token decode step; a bound below 0 acts as 0, above P as P.
+ *   (The page "Module glm5next_dsa" has index_scores return [Q, P] scores
+ *   plus candidate validity; the per-row bound is this library's reading of
+ *   validity for rows at different positions.)
  * Q, P >= 0; P < 2^31. */
 int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                      const uint8_t* pool_valid, int64_t Q, int64_t P, float* scores,
-                      void* stream);
+                      const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q, int64_t P,
+                      float* scores, void* stream);
 
 /* topk_pools: per row of scores [Q, P] (from dsai_index_scores), the
  * select_k = index_topk / kpool pools with the largest finite scores, by
@@ -312,13 +319,15 @@ int dsai_topk_pools(dsai_handle h, const float* scores, int64_t Q, int64_t P,
  * fp32 score matrix).  Host-only. */
 int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* bytes);
 
-/* dsai_index_scores followed by dsai_topk_pools on one stream, with the
- * [Q, P] scores held in the caller's `workspace` (at least
+/* dsai_index_scores (with its optional per-row pool_limit) followed by
+ * dsai_topk_pools on one stream, with the [Q, P] scores held in the caller's
+ * `workspace` (at least
  * dsai_select_workspace_size bytes, 256-byte aligned; DSAI_ERR_WORKSPACE
  * otherwise).  The workspace is free again once the stream passes the call. */
 int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
-                float* pool_scores, void* workspace, size_t workspace_bytes, void* stream);
+                const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q, int64_t P,
+                int32_t* pool_ids, float* pool_scores, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /* expand_selection: pool ids [Q, select_k] int32 (each -1 or a pool id in
  * [0, P)) -> token ids [Q, index_topk] int32 (index_topk = select_k *
@@ -342,9 +351,9 @@ int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* toke
  * Every refusal (including DSAI_ERR_UNSUPPORTED for a select_k the
  * selection cannot hold) comes before the first launch. */
 int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                       const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
-                       float* pool_scores, int32_t* tokens, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q,
+                       int64_t P, int32_t* pool_ids, float* pool_scores, int32_t* tokens,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of the static device array dsai_select_expand_static keeps its
  * [Q, P] scores in (one array per device). */
@@ -364,8 +373,9 @@ int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void*
  * overlap on one device (other streams, other handles, other host threads)
  * race on it and must be ordered by the caller. */
 int dsai_select_expand_static(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                              const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
-                              float* pool_scores, int32_t* tokens, void* stream);
+                              const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q,
+                              int64_t P, int32_t* pool_ids, float* pool_scores, int32_t* tokens,
+                              void* stream);
 
 /* ---- cache write: the indexer's k_norm ------------------------------------ */
 /* k_norm ("Module glm5next_dsa", "Checkpoint and kernel facts": indexer.k_norm

@@ -26,6 +26,7 @@ from .indexer import (  # noqa: F401
     pool_count,
     kpool_compress,
     pooled_index_scores,
+    visible_pools,
     topk_pools,
     expand_selection,
 )

@@ -454,12 +454,28 @@ def kpool_compress(k_normed: np.ndarray, gate: np.ndarray, valid: np.ndarray,
             "pool_tok": pt, "pool_valid": pv}
 
 
+def visible_pools(P: int, limit) -> np.ndarray:
+    """Pools a decode row may select under a per-row visible-pool bound:
+    p < limit, the bound clamped to [0, P] (None: every pool).  Reading for
+    multi-token decode, where rows of one step sit at different positions:
+    the "Module glm5next_dsa" page has index_scores return [Q, P] scores
+    plus candidate validity, and its topk_pools select from valid
+    candidates; a row's bound makes the pools at or past it invalid
+    candidates for that row only."""
+    if limit is None:
+        return np.ones(P, dtype=bool)
+    lim = min(max(int(limit), 0), P)
+    return np.arange(P) < lim
+
+
 def pooled_index_scores(q: np.ndarray, w: np.ndarray, pool_k: np.ndarray,
-                        pool_valid: np.ndarray) -> np.ndarray:
+                        pool_valid: np.ndarray, pool_limit=None) -> np.ndarray:
     """[Q, P] scores of decode queries against pool keys (glm5next_dsa: index_scores).
 
     S[q, p] = sum_h w[q, h] * ReLU(q[q, h, :] . pool_k[p, :]) for valid pools;
-    -inf marks an invalid candidate.  No causal mask.
+    -inf marks an invalid candidate.  No causal mask.  With pool_limit
+    ([Q] ints), row i's pools at or past pool_limit[i] are invalid
+    candidates too (visible_pools).
     q [Q, H, D], w [Q, H], pool_k [P, D], pool_valid [P].
     """
     Q = q.shape[0]
@@ -467,6 +483,7 @@ def pooled_index_scores(q: np.ndarray, w: np.ndarray, pool_k: np.ndarray,
     out = np.empty((Q, P), dtype=np.float64)
     for i in range(Q):
         out[i] = head_scores(q[i], pool_k, w[i])
+        out[i, ~visible_pools(P, None if pool_limit is None else pool_limit[i])] = NEG_INF
     out[:, np.asarray(pool_valid) == 0] = NEG_INF
     return out
 

@@ -85,16 +85,17 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "dsai_score_topk": [vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, vp, vp, vp],
         "dsai_score_topk_packed": [vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp, vp, vp],
         "dsai_backward_packed_workspace_size": [vp, i64, vp, vp, c_int, c_int, vp],
-        "dsai_select_expand": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
-        "dsai_select_expand_static": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp],
+        "dsai_select_expand": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t,
+                               vp],
+        "dsai_select_expand_static": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp],
         "dsai_indexer_backward_packed": [vp, vp, vp, vp, vp, vp, i64, vp, vp, c_int, c_int, vp, vp,
                                          vp, vp, ctypes.c_size_t, vp],
         "dsai_pool_count": [vp, i64, ctypes.POINTER(i64)],
         "dsai_kpool_compress": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp],
-        "dsai_index_scores": [vp, vp, vp, vp, vp, i64, i64, vp, vp],
+        "dsai_index_scores": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp],
         "dsai_topk_pools": [vp, vp, i64, i64, vp, vp, vp],
         "dsai_select_workspace_size": [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
-        "dsai_select": [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp],
+        "dsai_select": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "dsai_expand": [vp, vp, i64, vp, vp],
         "dsai_sort_rows": [vp, vp, vp, i64, c_int, vp],
         "dsai_k_norm": [vp, vp, vp, vp, ctypes.c_float, i64, vp, vp],
@@ -428,8 +429,10 @@ class Indexer:
         self._check(st, "dsai_kpool_compress")
         return pool_k, pool_tok, pool_valid
 
-    def index_scores(self, q, w, pool_k, pool_valid, out=None):
-        """q [Q,H,D] bf16, w [Q,H] fp32, pool_k [P,D] bf16, pool_valid [P] uint8 -> [Q,P] fp32."""
+    def index_scores(self, q, w, pool_k, pool_valid, out=None, pool_limit=None):
+        """q [Q,H,D] bf16, w [Q,H] fp32, pool_k [P,D] bf16, pool_valid [P] uint8 -> [Q,P] fp32.
+        pool_limit: optional [Q] int32 per-row bound; row q's pools p >= it are
+        invalid candidates (-inf) for that row."""
         Q, P = q.shape[0], pool_k.shape[0]
         H, D = self.cfg.heads, self.cfg.dim
         dev = q.device
@@ -439,12 +442,15 @@ class Indexer:
         _need(w, "w", torch.float32, (Q, H), dev)
         _need(pool_k, "pool_k", torch.bfloat16, (P, D), dev)
         _need(pool_valid, "pool_valid", torch.uint8, (P,), dev)
+        if pool_limit is not None:
+            _need(pool_limit, "pool_limit", torch.int32, (Q,), dev)
         if out is None:
             out = torch.empty((Q, P), dtype=torch.float32, device=dev)
         _need(out, "scores", torch.float32, (Q, P), dev)
         with torch.cuda.device(dev):
             st = self._lib.dsai_index_scores(self._h, _ptr(q), _ptr(w), _ptr(pool_k),
-                                             _ptr(pool_valid), Q, P, _ptr(out), _stream(dev))
+                                             _ptr(pool_valid), _ptr(pool_limit), Q, P, _ptr(out),
+                                             _stream(dev))
         self._check(st, "dsai_index_scores")
         return out
 
@@ -473,7 +479,7 @@ class Indexer:
         return n.value
 
     def select(self, q, w, pool_k, pool_valid, workspace=None, pool_ids=None, pool_scores=None,
-               tokens=None, expand=False):
+               tokens=None, expand=False, pool_limit=None):
         """index_scores + topk_pools with the [Q,P] scores in `workspace` (uint8
         tensor) -> (pool_ids, pool_scores); with expand=True also the token ids
         [Q, select_k*kpool] (dsai_select_expand) -> (pool_ids, pool_scores,
@@ -488,6 +494,8 @@ class Indexer:
         _need(w, "w", torch.float32, (Q, H), dev)
         _need(pool_k, "pool_k", torch.bfloat16, (P, D), dev)
         _need(pool_valid, "pool_valid", torch.uint8, (P,), dev)
+        if pool_limit is not None:
+            _need(pool_limit, "pool_limit", torch.int32, (Q,), dev)
         need = self.select_workspace_size(Q, P)
         if workspace is None:
             workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -503,19 +511,20 @@ class Indexer:
             _need(tokens, "tokens", torch.int32, (Q, K * self.cfg.kpool), dev)
             with torch.cuda.device(dev):
                 st = self._lib.dsai_select_expand(
-                    self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid), Q, P,
+                    self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid), _ptr(pool_limit), Q, P,
                     _ptr(pool_ids), _ptr(pool_scores), _ptr(tokens), _ptr(workspace),
                     workspace.numel() * workspace.element_size(), _stream(dev))
             self._check(st, "dsai_select_expand")
             return pool_ids, pool_scores, tokens
         with torch.cuda.device(dev):
             st = self._lib.dsai_select(self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid),
-                                       Q, P, _ptr(pool_ids), _ptr(pool_scores), _ptr(workspace),
+                                       _ptr(pool_limit), Q, P, _ptr(pool_ids), _ptr(pool_scores), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(dev))
         self._check(st, "dsai_select")
         return pool_ids, pool_scores
 
-    def select_expand_static(self, q, w, pool_k, pool_valid, pool_ids, pool_scores, tokens):
+    def select_expand_static(self, q, w, pool_k, pool_valid, pool_ids, pool_scores, tokens,
+                             pool_limit=None):
         """dsai_select_expand_static: select with expand whose [Q,P] scores live
         in the library's static device array (no workspace; the output
         tensors are the caller's, so the call allocates nothing).  Calls that
@@ -532,9 +541,11 @@ class Indexer:
         _need(pool_ids, "pool_ids", torch.int32, (Q, K), dev)
         _need(pool_scores, "pool_scores", torch.float32, (Q, K), dev)
         _need(tokens, "tokens", torch.int32, (Q, K * self.cfg.kpool), dev)
+        if pool_limit is not None:
+            _need(pool_limit, "pool_limit", torch.int32, (Q,), dev)
         with torch.cuda.device(dev):
             st = self._lib.dsai_select_expand_static(
-                self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid), Q, P,
+                self._h, _ptr(q), _ptr(w), _ptr(pool_k), _ptr(pool_valid), _ptr(pool_limit), Q, P,
                 _ptr(pool_ids), _ptr(pool_scores), _ptr(tokens), _stream(dev))
         self._check(st, "dsai_select_expand_static")
         return pool_ids, pool_scores, tokens

@@ -521,32 +521,36 @@ int dsai_kpool_compress(dsai_handle h, const void* k_normed, const float* gate,
 
 // Host checks of index_scores' arguments (no HIP call).
 static int check_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                              const uint8_t* pool_valid, int64_t Q, int64_t P, const void* scores) {
+                              const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q,
+                              int64_t P, const void* scores) {
   if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
   if (Q == 0 || P == 0) return DSAI_OK;
   if (P * h->cfg.dim * 2 > (int64_t)0xFFFFFFFF) return DSAI_ERR_UNSUPPORTED;  // 32-bit offsets
   if (!q || !w || !pool_k || !pool_valid || !scores) return DSAI_ERR_NULLPTR;
-  if (!aligned(q) || !aligned(pool_k)) return DSAI_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(pool_k) || reinterpret_cast<uintptr_t>(pool_limit) % 4 != 0)
+    return DSAI_ERR_INVALID_ARG;
   return DSAI_OK;
 }
 
 static hipError_t launch_index_scores(dsai_handle h, const void* q, const float* w,
-                                      const void* pool_k, const uint8_t* pool_valid, int64_t Q,
-                                      int64_t P, float* scores, hipStream_t st) {
+                                      const void* pool_k, const uint8_t* pool_valid,
+                                      const int32_t* pool_limit, int64_t Q, int64_t P,
+                                      float* scores, hipStream_t st) {
   dsai::PooledScoresArgs a;
   a.q = static_cast<const uint16_t*>(q); a.w = w;
   a.pool_k = static_cast<const uint16_t*>(pool_k); a.pool_valid = pool_valid;
+  a.limit = pool_limit;
   a.Q = Q; a.P = P; a.H = h->cfg.heads; a.D = h->cfg.dim; a.scores = scores;
   return dsai::launch_pooled_scores(a, st);
 }
 
 int dsai_index_scores(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                      const uint8_t* pool_valid, int64_t Q, int64_t P, float* scores,
-                      void* stream) {
+                      const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q, int64_t P,
+                      float* scores, void* stream) {
   if (!h) return DSAI_ERR_NULLPTR;
-  const int st = check_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores);
+  const int st = check_index_scores(h, q, w, pool_k, pool_valid, pool_limit, Q, P, scores);
   if (st != DSAI_OK || Q == 0 || P == 0) return st;
-  return hip_status(h, launch_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores,
+  return hip_status(h, launch_index_scores(h, q, w, pool_k, pool_valid, pool_limit, Q, P, scores,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -594,16 +598,18 @@ int dsai_select_workspace_size(dsai_handle h, int64_t Q, int64_t P, size_t* byte
 // provides), then topk_pools (with `tokens`: expanded as well).  Every
 // refusal, the topk_pools plan included, comes before the first launch.
 static int select_into(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                       const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
-                       float* pool_scores, int32_t* tokens, float* scores, void* stream) {
-  int st = check_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores);
+                       const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q,
+                       int64_t P, int32_t* pool_ids, float* pool_scores, int32_t* tokens,
+                       float* scores, void* stream) {
+  int st = check_index_scores(h, q, w, pool_k, pool_valid, pool_limit, Q, P, scores);
   if (st != DSAI_OK) return st;
   if (!pool_ids || !pool_scores) return DSAI_ERR_NULLPTR;
   dsai::TopkRowsPlan plan;
   if ((st = plan_pools(h, P, &plan)) != DSAI_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (P > 0) {
-    const hipError_t e = launch_index_scores(h, q, w, pool_k, pool_valid, Q, P, scores, s);
+    const hipError_t e =
+        launch_index_scores(h, q, w, pool_k, pool_valid, pool_limit, Q, P, scores, s);
     if (e != hipSuccess) return hip_status(h, e);
   }
   return hip_status(h, launch_pools(h, plan, scores, Q, P, pool_ids, pool_scores, tokens, s));
@@ -620,15 +626,16 @@ static int check_workspace(dsai_handle h, int64_t Q, int64_t P, const void* work
 }
 
 int dsai_select(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
-                float* pool_scores, void* workspace, size_t workspace_bytes, void* stream) {
+                const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q, int64_t P,
+                int32_t* pool_ids, float* pool_scores, void* workspace, size_t workspace_bytes,
+                void* stream) {
   if (!h) return DSAI_ERR_NULLPTR;
   if (Q < 0 || P < 0 || Q > kI32 || P > kI32) return DSAI_ERR_INVALID_ARG;
   if (Q == 0) return DSAI_OK;
   const int st = check_workspace(h, Q, P, workspace, workspace_bytes);
   if (st != DSAI_OK) return st;
-  return select_into(h, q, w, pool_k, pool_valid, Q, P, pool_ids, pool_scores, nullptr,
-                     static_cast<float*>(workspace), stream);
+  return select_into(h, q, w, pool_k, pool_valid, pool_limit, Q, P, pool_ids, pool_scores,
+                     nullptr, static_cast<float*>(workspace), stream);
 }
 
 // Token ids of the expanded rows are int32: the last token of the last pool,
@@ -647,15 +654,15 @@ static int check_select_expand(dsai_handle h, int64_t Q, int64_t P, const int32_
 }
 
 int dsai_select_expand(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                       const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
-                       float* pool_scores, int32_t* tokens, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q,
+                       int64_t P, int32_t* pool_ids, float* pool_scores, int32_t* tokens,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!h) return DSAI_ERR_NULLPTR;
   int st = check_select_expand(h, Q, P, pool_ids, pool_scores, tokens);
   if (st != DSAI_OK || Q == 0) return st;
   if ((st = check_workspace(h, Q, P, workspace, workspace_bytes)) != DSAI_OK) return st;
-  return select_into(h, q, w, pool_k, pool_valid, Q, P, pool_ids, pool_scores, tokens,
-                     static_cast<float*>(workspace), stream);
+  return select_into(h, q, w, pool_k, pool_valid, pool_limit, Q, P, pool_ids, pool_scores,
+                     tokens, static_cast<float*>(workspace), stream);
 }
 
 // ---- dsai_select_expand_static: the [Q, P] scores in a static device array --
@@ -689,8 +696,9 @@ hipError_t static_scratch(void** out) {
 }  // namespace
 
 int dsai_select_expand_static(dsai_handle h, const void* q, const float* w, const void* pool_k,
-                              const uint8_t* pool_valid, int64_t Q, int64_t P, int32_t* pool_ids,
-                              float* pool_scores, int32_t* tokens, void* stream) {
+                              const uint8_t* pool_valid, const int32_t* pool_limit, int64_t Q,
+                              int64_t P, int32_t* pool_ids, float* pool_scores, int32_t* tokens,
+                              void* stream) {
   if (!h) return DSAI_ERR_NULLPTR;
   int st = check_select_expand(h, Q, P, pool_ids, pool_scores, tokens);
   if (st != DSAI_OK || Q == 0) return st;
@@ -700,8 +708,8 @@ int dsai_select_expand_static(dsai_handle h, const void* q, const float* w, cons
   void* buf = nullptr;
   const hipError_t e = static_scratch(&buf);
   if (e != hipSuccess) return hip_status(h, e);
-  return select_into(h, q, w, pool_k, pool_valid, Q, P, pool_ids, pool_scores, tokens,
-                     static_cast<float*>(buf), stream);
+  return select_into(h, q, w, pool_k, pool_valid, pool_limit, Q, P, pool_ids, pool_scores,
+                     tokens, static_cast<float*>(buf), stream);
 }
 
 int dsai_expand(dsai_handle h, const int32_t* pool_ids, int64_t Q, int32_t* tokens,

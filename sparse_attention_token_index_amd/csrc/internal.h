@@ -49,6 +49,7 @@ struct PooledScoresArgs {
   const float* w;     // [Q, H]
   const uint16_t* pool_k;
   const uint8_t* pool_valid;
+  const int32_t* limit;  // [Q] visible-pool bound per row, or null (all pools)
   int64_t Q, P;
   int H, D;
   float* scores;  // [Q, P]

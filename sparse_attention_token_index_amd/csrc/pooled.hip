@@ -118,7 +118,8 @@ template <int HP, int D>
 __global__ __launch_bounds__(kPoolRows * 64) __attribute__((amdgpu_waves_per_eu(2))) void
 pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                      const uint16_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_valid,
-                     int Q, int P, int H, int pool_blocks, float* __restrict__ scores) {
+                     const int32_t* __restrict__ limit, int Q, int P, int H, int pool_blocks,
+                     float* __restrict__ scores) {
   using G = TileGeom<D>;
   using Scorer = TileScorer<HP, D>;
   using Acc = typename Scorer::Acc;
@@ -134,6 +135,9 @@ pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   const bool active = row < Q;
   const int p0 = pb * kPer;
   const int np = min(kPer, P - p0);
+  // the row's visible pools: p < its bound (clamped to [0, P]), all if none
+  const int lim = (limit && active) ? min(max(limit[row], 0), P) : P;
+  const int np_row = max(0, min(np, lim - p0));  // this block's pools the row sees
   const int ntiles = (np + G::kTileKeys - 1) / G::kTileKeys;
 
   Scorer sc;
@@ -150,7 +154,7 @@ pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   auto finish = [&](int it_rec) {
     const float s = Scorer::combine(part);
     const int i = it_rec * G::kTileKeys + (lane & 31);
-    if (active && lane < 32 && i < np) srow[i] = valid_s[i] ? s : -__builtin_inff();
+    if (active && lane < 32 && i < np) srow[i] = (valid_s[i] && i < np_row) ? s : -__builtin_inff();
   };
   // ld holds tile it + 2 (loaded two steps earlier), then takes tile it + 4
   auto step = [&](int it, TileLoader<D, kPoolRows * 64>& ld, Frag& fcur, Frag& fnext, Acc& cur,
@@ -195,7 +199,7 @@ static hipError_t launch_scores_t(const PooledScoresArgs& a, hipStream_t st) {
   const int64_t blocks = pool_blocks * ((a.Q + kPoolRows - 1) / kPoolRows);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((pooled_scores_kernel<HP, D>), dim3((unsigned)blocks), dim3(kPoolRows * 64),
-                     0, st, a.q, a.w, a.pool_k, a.pool_valid, (int)a.Q, (int)a.P, a.H,
+                     0, st, a.q, a.w, a.pool_k, a.pool_valid, a.limit, (int)a.Q, (int)a.P, a.H,
                      (int)pool_blocks, a.scores);
   return hipGetLastError();
 }

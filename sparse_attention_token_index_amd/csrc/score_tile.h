@@ -183,6 +183,26 @@ struct TileScorer {
           acc[rr][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rr][m][j], bf[j], acc[rr][m], 0, 0, 0);
   }
 
+  // mma() with a rolling fragment buffer: once k-step j's products have been
+  // issued, bf[j] is refilled with k-step j of the tile at `next`, so the next
+  // tile's reads overlap this tile's remaining products and one set of
+  // fragment registers serves both tiles.
+  __device__ __forceinline__ void mma_fetch(Frag& bf, const lds_char* next, Acc& acc) const {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[rr][m] = floatx16{};
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[rr][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rr][m][j], bf[j], acc[rr][m], 0, 0, 0);
+      bf[j] = *reinterpret_cast<const DSAI_LDS bf16x8*>(next + frag_offset(j));
+    }
+  }
+
   __device__ __forceinline__ void mma(const lds_char* tile, Acc& acc) const {
     Frag bf;
     fetch(tile, bf);

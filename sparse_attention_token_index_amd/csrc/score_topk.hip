@@ -19,8 +19,9 @@
 //           s (no indices, no selection until the end);
 //   filter  otherwise: keys beating the row's running threshold are appended
 //           (order key and index); when a store fills, every wavefront of
-//           the block cuts its rows to the top k by a radix select together,
-//           which raises the thresholds.
+//           the block whose store is past half its slack cuts it together
+//           (a bin-edge cut: at least k entries kept, none of the top k
+//           lost), which raises the thresholds.
 // After the last tile the row's top k is selected exactly and written in
 // ascending index order; no score goes to device memory.  With supplied
 // indices (dense store only) the row's entries are read from its store
@@ -33,12 +34,21 @@
 
 namespace dsai {
 
-// LDS bytes per wavefront of the dense store's final select (histogram and
-// side list); they live in the tile buffers once the key loop is done.
+// LDS bytes per wavefront of the final select (histogram and side list);
+// they live in the tile buffers once the key loop is done.
 constexpr int kDenseScratch = 2048;
+
+// LDS bytes per wavefront the filter store's cuts use during the key loop
+// (one 256-bin histogram; the bin-edge cut needs no side list).
+constexpr int kCutScratch = 1024;
 
 // Static LDS of the filter-store kernels (cut_flag), rounded up.
 constexpr int64_t kStaticLds = 128;
+
+// A filter store asks for a cut once fewer than this many slots are free:
+// the request is served within four more tiles (32 keys each) after the
+// one that raised it.
+constexpr int kCutRequest = 6 * 32;
 
 template <int D, int NW>
 struct ScoreLds {
@@ -67,10 +77,16 @@ __device__ __forceinline__ void score_select_body(
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform
   const int lane = lane_id();
   const int row_bytes = DENSE ? cap * 4 : cap * 4 + ((cap * (int)sizeof(IdxT) + 15) & ~15);
-  const int region = DENSE ? L::kDenseRegion : L::kTiles + NW * kSelScratchBytes;
+  const int region = DENSE ? L::kDenseRegion : L::kTiles + NW * kCutScratch;
 
+  // dense: the final select's histogram and side list, in the tile buffers;
+  // filter: the cuts' histogram (its own region), and after the key loop the
+  // final select's side list in the tile buffers (2 KB per wavefront)
   lds_u32* scratch = DENSE ? (lds_u32*)(smem + wave * kDenseScratch)
-                           : (lds_u32*)(smem + L::kTiles + wave * kSelScratchBytes);
+                           : (lds_u32*)(smem + L::kTiles + wave * kCutScratch);
+  lds_u32* side = DENSE ? scratch + 256 : (lds_u32*)(smem + wave * (L::kTiles / NW));
+  constexpr uint32_t kSideCap =
+      DENSE ? 256u : ((L::kTiles / NW) / 4 < 256 ? (L::kTiles / NW) / 4 : 256u);
 
   // Rows of the block: t0 .. t0 + R - 1; wavefront `wave` owns rows
   // t0 + wave * NR + rr, rr < NR, each with its own LDS row store.
@@ -97,13 +113,16 @@ __device__ __forceinline__ void score_select_body(
     n_t[rr] = active[rr] ? min(Skv, (t[rr] + 1) / ratio) : 0;
     n_w = max(n_w, n_t[rr]);
     lds_char* mine = smem + region + slot * row_bytes;
-    rs[rr] = RowStore<IdxT>{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4), scratch,
-                            scratch + 256, 256u};
+    rs[rr] = RowStore<IdxT>{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4), scratch, side,
+                            kSideCap};
     const int64_t row = (int64_t)(active[rr] ? t[rr] : 0) * B + b;
     sc.load_row(rr, q + row * H * D, w + row * H, H, active[rr]);
   }
 
   uint32_t count[NR], tau[NR];       // filter store: entries, running threshold
+  // a bin-edge cut may keep a few entries past k; one that would keep more
+  // than a quarter of the store's slack cuts exactly instead
+  const uint32_t max_keep = (uint32_t)topk + (uint32_t)(cap - topk) / 4u;
   float smin[NR], smax[NR];           // dense store: this lane's extreme scores
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
@@ -152,96 +171,129 @@ __device__ __forceinline__ void score_select_body(
       } else {
         const uint32_t u = ord_key(x);
         wave_append(rs[rr], count[rr], lane < 32 && vis && u > tau[rr], u, key);
-        if (__builtin_expect(count[rr] > (uint32_t)(cap - G::kTileKeys), 0))  // rare: store full
-          count[rr] = wave_keep_topk(rs[rr], count[rr], topk, &tau[rr]);
       }
     }
     if constexpr (!DENSE) {
-      // Ask for a block-wide cut once a store could not take two more tiles
+      // Ask for a cut once a store has fewer than kCutRequest free slots
       // (read by every wavefront after the next barrier).
       bool need = false;
 #pragma unroll
-      for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - 2 * G::kTileKeys);
+      for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - kCutRequest);
       if (lane == 0) cut_flag[it_rec & 1][wave] = need ? 1u : 0u;
     }
-  };
-  // Filter store: cut every wavefront's rows to the top k together when any
-  // of them asked for it after the previous barrier, so the block's waves
-  // spend one cut's time at the next barrier rather than one after another.
-  // The flags alternate between two slots, so a wavefront's next request
-  // never overwrites one that another wavefront has yet to read.
-  auto cut_together = [&](int it_req) {
-    uint32_t any = 0u;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) any |= cut_flag[it_req & 1][w2];
-    if (any) {
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-        if (count[rr] > (uint32_t)topk) count[rr] = wave_keep_topk(rs[rr], count[rr], topk, &tau[rr]);
-    }
-  };
-  auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
-                  bool red) {
-    __syncthreads();
-    // Scheduling fences: the compiler may not hoist the next iteration's
-    // products above this barrier or sink this one's below the next, which
-    // would put a reduction right behind the products it reads.
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (DENSE) {
-      sc.fetch(buf(it + 1), fnext);
-      if (fin) finish(it - 2);
-      ld.store(buf(it + 2));
-      ld.load((uint32_t)(it + 3) * G::kTileKeys);
-      sc.mma(fcur, cur);
-    } else {
-      // The filter store's cut is a call: one fragment buffer (fcur, refilled
-      // with tile it + 1 once tile it's products have read it) keeps the
-      // registers that must survive it within the budget.
-      if (it >= 3) cut_together(it - 3);  // requests of the previous iteration's finish
-      if (fin) finish(it - 2);
-      ld.store(buf(it + 2));
-      ld.load((uint32_t)(it + 3) * G::kTileKeys);
-      sc.mma(fcur, cur);
-    }
-    if (red) {
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
-    }
-    if constexpr (!DENSE) sc.fetch(buf(it + 1), fcur);
-    __builtin_amdgcn_sched_barrier(0);
   };
   if (ntiles > 0) {
     ld.load(0u);
     ld.store(buf(0));
     ld.load((uint32_t)G::kTileKeys);
     ld.store(buf(1));
-    ld.load((uint32_t)(2 * G::kTileKeys));
-    __syncthreads();
-    sc.fetch(buf(0), f0);
-    // dense: fragments alternate between f0 and f1; filter: f0 only
-    Frag& fb = DENSE ? f1 : f0;
-    step(0, f0, fb, acc0, acc1, false, false);
-    int it = 1;
-    if (ntiles > 1) {
-      step(1, fb, f0, acc1, acc0, false, true);
-      for (it = 2; it + 1 < ntiles; it += 2) {
-        step(it, f0, fb, acc0, acc1, true, true);
-        step(it + 1, fb, f0, acc1, acc0, true, true);
-      }
-      if (it < ntiles) step(it, f0, fb, acc0, acc1, true, true);
-      finish(ntiles - 2);
-    }
+    if constexpr (DENSE) {
+      auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
+                      bool red) {
+        __syncthreads();
+        // Scheduling fences: the compiler may not hoist the next iteration's
+        // products above this barrier or sink this one's below the next,
+        // which would put a reduction right behind the products it reads.
+        __builtin_amdgcn_sched_barrier(0);
+        sc.fetch(buf(it + 1), fnext);
+        if (fin) finish(it - 2);
+        ld.store(buf(it + 2));
+        ld.load((uint32_t)(it + 3) * G::kTileKeys);
+        sc.mma(fcur, cur);
+        if (red) {
 #pragma unroll
-    for (int rr = 0; rr < NR; ++rr)
-      part[rr] = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, rr);
-    finish(ntiles - 1);
+          for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      ld.load((uint32_t)(2 * G::kTileKeys));
+      __syncthreads();
+      sc.fetch(buf(0), f0);
+      step(0, f0, f1, acc0, acc1, false, false);
+      int it = 1;
+      if (ntiles > 1) {
+        step(1, f1, f0, acc1, acc0, false, true);
+        for (it = 2; it + 1 < ntiles; it += 2) {
+          step(it, f0, f1, acc0, acc1, true, true);
+          step(it + 1, f1, f0, acc1, acc0, true, true);
+        }
+        if (it < ntiles) step(it, f0, f1, acc0, acc1, true, true);
+        finish(ntiles - 2);
+      }
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+        part[rr] = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, rr);
+      finish(ntiles - 1);
+    } else {
+      // Filter store: the same pipeline, run from tile s until a wavefront
+      // of the block asks for a cut.  The cut is a call and needs registers
+      // the pipeline holds, so it never runs inside the loop: every
+      // wavefront sees the request after the same barrier, drains (records
+      // the last two tiles), and after one more barrier cuts its store if
+      // it is past half its slack, or nearly full; then the pipeline
+      // restarts at the next tile, whose tile and the one after it are
+      // already staged in LDS.  A request waits at most four tiles, which
+      // kCutRequest leaves room for.  Request flags alternate between two
+      // slots, so a wavefront's next request never overwrites one another
+      // wavefront has yet to read; flags of a finished run are not read.
+      int s = 0;  // first tile of the current run
+      // One fragment buffer, refilled with tile it + 1 as tile it's products
+      // are issued (registers for the store's bookkeeping).
+      auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
+                      bool red) -> bool {
+        (void)fnext;
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t any = 0u;
+        if (it >= s + 3) {  // the request of finish(it - 3), in this run
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) any |= cut_flag[(it - 3) & 1][w2];
+        }
+        if (fin) finish(it - 2);
+        ld.store(buf(it + 2));
+        ld.load((uint32_t)(it + 3) * G::kTileKeys);
+        sc.mma_fetch(fcur, buf(it + 1), cur);
+        if (red) {
+#pragma unroll
+          for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return any != 0u;
+      };
+      const uint32_t cut_at = min((uint32_t)(topk + cap) / 2u, (uint32_t)(cap - kCutRequest - 32));
+      for (;;) {
+        ld.load((uint32_t)(s + 2) * G::kTileKeys);
+        __syncthreads();
+        sc.fetch(buf(s), f0);
+        // Steps go in pairs (products in acc0, then acc1), so a run always
+        // ends with its last products in acc1; a pair may run one tile past
+        // the last (zero keys past the range, never recorded).
+        int it = s;
+        for (;;) {
+          const bool more = it > s;
+          bool want = step(it, f0, f0, acc0, acc1, more, more);
+          want |= step(it + 1, f0, f0, acc1, acc0, more, true);
+          it += 2;
+          if (want || it >= ntiles) break;
+        }
+        // drain: record tiles it - 2 (reduced in the last step) and it - 1
+        finish(it - 2);
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(acc1, rr);
+        finish(it - 1);
+        if (it >= ntiles) break;
+        __syncthreads();  // every wavefront drained; tiles it and it + 1 are staged
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr)
+          if (count[rr] > cut_at) count[rr] = wave_cut(rs[rr], count[rr], (uint32_t)topk, max_keep, &tau[rr]);
+        s = it;
+      }
+    }
   }
-  if constexpr (DENSE) {
-    // The final select's scratch lies in the tile buffers, which the last
-    // iteration of a slower wavefront may still be writing (its store of the
-    // unused tile past the end).
-    __syncthreads();
-  }
+  // The final select's scratch lies in the tile buffers, which the last
+  // iteration of a slower wavefront may still be writing (its store of the
+  // unused tile past the end).
+  __syncthreads();
 
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
@@ -314,9 +366,9 @@ bool plan_filter(int D, int NW, int NR, int topk, int64_t Skv, int64_t budget, i
                  ScoreSelectPlan* p) {
   const int64_t tiles = 2 * (int64_t)tile_bytes_for(D);
   const int idx_bytes = Skv <= 65536 ? 2 : 4;
-  const int need = topk + 8 * 32;
+  const int need = topk + 16 * 32;  // slack for a cut request and a bin-edge cut's extra entries
   for (int R = NW * NR; R >= min_rows; --R) {
-    const int64_t per_row = (budget - tiles - (int64_t)NW * kSelScratchBytes) / R;
+    const int64_t per_row = (budget - tiles - (int64_t)NW * kCutScratch) / R;
     if (per_row <= 0) continue;
     int cap = (int)(per_row / (4 + idx_bytes)) & ~63;
     while (cap > 0 && store_row_bytes(cap, idx_bytes) > per_row) cap -= 64;
@@ -327,7 +379,7 @@ bool plan_filter(int D, int NW, int NR, int topk, int64_t Skv, int64_t budget, i
     p->cap = cap;
     p->dense = false;
     p->idx_bytes = idx_bytes;
-    p->lds_bytes = (size_t)(tiles + (int64_t)NW * kSelScratchBytes +
+    p->lds_bytes = (size_t)(tiles + (int64_t)NW * kCutScratch +
                             (int64_t)R * store_row_bytes(cap, idx_bytes));
     return true;
   }

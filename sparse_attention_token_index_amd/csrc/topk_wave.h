@@ -243,6 +243,135 @@ __device__ __noinline__ uint32_t wave_compact(RowStore<IdxT> rs, uint32_t n, uin
   return wpos;
 }
 
+// Keep, in store order, the entries with key >= t.  Returns the new count.
+template <typename IdxT>
+__device__ __noinline__ uint32_t wave_compact_ge(RowStore<IdxT> rs, uint32_t n, uint32_t t) {
+  const int lane = lane_id();
+  uint32_t wpos = 0u;
+  constexpr int kB = 4;
+  for (uint32_t base = 0; base < n; base += kWave * kB) {
+    uint32_t u[kB], x[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      u[j] = i < n ? rs.key[i] : 0u;
+      x[j] = i < n ? (uint32_t)rs.idx[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      const bool keep = i < n && u[j] >= t;
+      const uint64_t mk = ballot(keep);
+      if (keep) {
+        const uint32_t p = wpos + lanes_below(mk);
+        rs.key[p] = u[j];
+        rs.idx[p] = (IdxT)x[j];
+      }
+      wpos = uniform(wpos + (uint32_t)__popcll(mk));
+    }
+  }
+  wave_lds_sync();
+  return wpos;
+}
+
+// Bin-edge cut of a store holding n > k entries: a threshold t such that at
+// least k entries have key >= t, found from one 256-bin histogram of the
+// keys over [min, max] (and, when the bin holding rank k has more than
+// kCutRefine keys, a second histogram inside that bin), then the entries
+// with key >= t kept in store order.  Any t no larger than the k-th largest
+// key keeps the row's top k; a later key equal to t can never displace one
+// of the >= k kept keys (they are at least as large and come first), so t
+// becomes the admission threshold (keys must exceed it).  That keeps k plus
+// the part of t's bin below rank k - a few dozen entries more than an exact
+// cut - for two passes over the store fewer and no side list.  When it would
+// keep more than `max_keep` (many equal keys at the boundary), the exact cut
+// runs instead (to exactly k, ties to the earlier entries), without a side
+// list: `side` may be memory other wavefronts are using.
+constexpr uint32_t kCutRefine = 64;
+
+template <typename IdxT>
+__device__ __noinline__ uint32_t wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_t k,
+                                          uint32_t max_keep, uint32_t* tau) {
+  const int lane = lane_id();
+  wave_lds_sync();
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
+    uint32_t u[kSelBatch];
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      u[j] = i < n ? rs.key[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+      const uint32_t i = base + j * kWave + lane;
+      if (i < n) {
+        mn = min(mn, u[j]);
+        mx = max(mx, u[j]);
+      }
+    }
+  }
+  const uint32_t lo = uniform(wave_min(mn));
+  mx = uniform(wave_max(mx));
+  const uint32_t range = mx - lo;
+  uint32_t t = lo, kept = n;
+  if (range != 0u) {
+    const int rbits = 32 - __clz(range);
+    const int shift = rbits > 8 ? rbits - 8 : 0;
+    clear_hist(rs.hist);
+    for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
+      uint32_t u[kSelBatch];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) {
+        const uint32_t i = base + j * kWave + lane;
+        u[j] = i < n ? rs.key[i] : lo;
+      }
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) {
+        const uint32_t i = base + j * kWave + lane;
+        if (i < n) hist_add(rs.hist, (u[j] - lo) >> shift);
+      }
+    }
+    wave_lds_sync();
+    const uint2 fb = find_bin(rs.hist, k);
+    const uint32_t cnt_bin = uniform(rs.hist[fb.x]);
+    t = lo + (fb.x << shift);
+    kept = fb.y + cnt_bin;
+    wave_lds_sync();
+    if (cnt_bin > kCutRefine && shift > 0) {
+      // second round inside the bin: 8 more bits (or all that remain)
+      const int shift2 = shift > 8 ? shift - 8 : 0;
+      const uint32_t bin_hi = t + ((1u << shift) - 1u);  // no wrap: bin b lies in [lo, mx]
+      clear_hist(rs.hist);
+      for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
+        uint32_t u[kSelBatch];
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+          const uint32_t i = base + j * kWave + lane;
+          u[j] = i < n ? rs.key[i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+          const uint32_t i = base + j * kWave + lane;
+          if (i < n && u[j] >= t && u[j] <= bin_hi) hist_add(rs.hist, (u[j] - t) >> shift2);
+        }
+      }
+      wave_lds_sync();
+      const uint2 fb2 = find_bin(rs.hist, k - fb.y);
+      t += fb2.x << shift2;
+      kept = fb.y + fb2.y + uniform(rs.hist[fb2.x]);
+      wave_lds_sync();
+    }
+  }
+  if (kept > max_keep) {
+    const uint2 sel = wave_radix_select(rs.key, rs.hist, rs.side, 0u, n, k);
+    *tau = sel.x;
+    return wave_compact(rs, n, sel.x, sel.y);
+  }
+  *tau = t;
+  return wave_compact_ge(rs, n, t);
+}
+
 // Reduce the store to its top k (stable) if it holds more than k entries;
 // *tau receives the k-th largest key (the new admission threshold).
 template <typename IdxT>

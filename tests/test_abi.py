@@ -294,9 +294,12 @@ def test_pooled_argument_errors(lib):
     assert lib.dsai_kpool_compress(h, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == NULLPTR
     assert lib.dsai_kpool_compress(h, FAKE, FAKE, FAKE, FAKE, 64, None, FAKE, FAKE, None) == NULLPTR
     # index_scores
-    assert lib.dsai_index_scores(h, FAKE, FAKE, FAKE, FAKE, -1, 5, FAKE, None) == INVALID
-    assert lib.dsai_index_scores(h, FAKE, FAKE, FAKE, FAKE, 0, 5, FAKE, None) == OK
-    assert lib.dsai_index_scores(h, None, FAKE, FAKE, FAKE, 2, 5, FAKE, None) == NULLPTR
+    assert lib.dsai_index_scores(h, FAKE, FAKE, FAKE, FAKE, None, -1, 5, FAKE, None) == INVALID
+    assert lib.dsai_index_scores(h, FAKE, FAKE, FAKE, FAKE, None, 0, 5, FAKE, None) == OK
+    assert lib.dsai_index_scores(h, None, FAKE, FAKE, FAKE, None, 2, 5, FAKE, None) == NULLPTR
+    # pool_limit: an int32 array (4-byte aligned) or NULL
+    assert lib.dsai_index_scores(h, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10002), 2, 5, FAKE,
+                                 None) == INVALID
     # topk_pools
     assert lib.dsai_topk_pools(h, FAKE, -2, 5, FAKE, FAKE, None) == INVALID
     assert lib.dsai_topk_pools(h, FAKE, 0, 5, FAKE, FAKE, None) == OK
@@ -305,15 +308,15 @@ def test_pooled_argument_errors(lib):
     need = ctypes.c_size_t()
     assert lib.dsai_select_workspace_size(h, 64, 16384, ctypes.byref(need)) == OK
     assert need.value == 64 * 16384 * 4
-    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, 64, 16384, FAKE, FAKE, None, 0, None) == WORKSPACE
-    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, 64, 16384, FAKE, FAKE, FAKE, need.value - 1,
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, None, 64, 16384, FAKE, FAKE, None, 0, None) == WORKSPACE
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, None, 64, 16384, FAKE, FAKE, FAKE, need.value - 1,
                            None) == WORKSPACE
-    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, 64, 16384, FAKE, FAKE,
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, None, 64, 16384, FAKE, FAKE,
                            ctypes.c_void_p(0x10010), need.value, None) == WORKSPACE   # not 256-aligned
-    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, -1, 16384, FAKE, FAKE, FAKE, 0, None) == INVALID
+    assert lib.dsai_select(h, FAKE, FAKE, FAKE, FAKE, None, -1, 16384, FAKE, FAKE, FAKE, 0, None) == INVALID
     # select with expand: select's rules plus the token array
     se = lambda Q=64, tok=FAKE, ws=FAKE, wsb=need.value: lib.dsai_select_expand(
-        h, FAKE, FAKE, FAKE, FAKE, Q, 16384, FAKE, FAKE, tok, ws, wsb, None)
+        h, FAKE, FAKE, FAKE, FAKE, None, Q, 16384, FAKE, FAKE, tok, ws, wsb, None)
     assert se(Q=-1) == INVALID
     assert se(Q=0) == OK
     assert se(tok=None) == NULLPTR
@@ -323,14 +326,14 @@ def test_pooled_argument_errors(lib):
     # select with expand from the static array: its rules, and no more
     # scores than the array holds (refused before any HIP call)
     sst = lambda Q=64, P=16384, tok=FAKE: lib.dsai_select_expand_static(
-        h, FAKE, FAKE, FAKE, FAKE, Q, P, FAKE, FAKE, tok, None)
+        h, FAKE, FAKE, FAKE, FAKE, None, Q, P, FAKE, FAKE, tok, None)
     assert sst(Q=-1) == INVALID
     assert sst(Q=0) == OK
     assert sst(tok=None) == NULLPTR
     assert sst(tok=ctypes.c_void_p(0x10004)) == INVALID
     assert sst(Q=64, P=(16 << 20) // (4 * 64) + 1) == WORKSPACE
     assert sst(Q=1, P=(16 << 20) // 4 + 1) == WORKSPACE
-    assert lib.dsai_select_expand_static(None, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE,
+    assert lib.dsai_select_expand_static(None, FAKE, FAKE, FAKE, FAKE, None, 1, 1, FAKE, FAKE, FAKE,
                                          None) == NULLPTR
     # expand
     assert lib.dsai_expand(h, FAKE, -1, FAKE, None) == INVALID
@@ -349,11 +352,11 @@ def test_expanded_token_ids_must_fit_int32(lib):
     st, h = _create(lib, kpool=KP, index_topk=64, first_key=fk)
     assert st == OK
     P_ok = (2 ** 31 - 1 - fk + 1) // KP          # last token = 2^31 - 1
-    se = lambda P, ws=None: lib.dsai_select_expand(h, FAKE, FAKE, FAKE, FAKE, 2, P, FAKE, FAKE,
+    se = lambda P, ws=None: lib.dsai_select_expand(h, FAKE, FAKE, FAKE, FAKE, None, 2, P, FAKE, FAKE,
                                                    FAKE, ws, 0, None)
     assert se(P_ok + 1) == INVALID
     assert se(P_ok) == WORKSPACE                 # past the token check: no workspace given
-    assert lib.dsai_select_expand_static(h, FAKE, FAKE, FAKE, FAKE, 2, P_ok + 1, FAKE, FAKE,
+    assert lib.dsai_select_expand_static(h, FAKE, FAKE, FAKE, FAKE, None, 2, P_ok + 1, FAKE, FAKE,
                                          FAKE, None) == INVALID
     lib.dsai_destroy(h)
 

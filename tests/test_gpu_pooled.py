@@ -294,3 +294,53 @@ def test_pooled_kp1_equals_unpooled(dsai):
     ui, us = ui.cpu().numpy()[0, N - 1:], us.cpu().numpy()[0, N - 1:]
     assert np.array_equal(ids.cpu().numpy(), ui)
     assert np.array_equal(vals.cpu().numpy().astype(np.float64), us.astype(np.float64))
+
+
+@pytest.mark.parametrize("P,KP,index_topk", [(16384, 4, 512), (3001, 2, 64), (40000, 4, 512)])
+@pytest.mark.parametrize("order", ["score", "index"])
+def test_select_with_pool_limits(dsai, P, KP, index_topk, order):
+    """Per-row visible-pool bounds (multi-token decode): each row selects only
+    among its pools p < bound (bounds below 0 act as 0, above P as P).  The
+    GPU's selection on the oracle's pool keys keeps the top-k parity rules
+    against the oracle with the same bounds; the expanded token ids are the
+    oracle's expansion of the GPU's ids; bounds of P for every row give the
+    unbounded call's bits; a bound of 0 gives a padding row."""
+    log(f"[gpu] pool limits P={P} KP={KP} order={order}")
+    rng = np.random.default_rng(P + KP)
+    Q, H, D = 13, 32, 128
+    ix = dsai.Indexer(heads=H, dim=D, kpool=KP, index_topk=index_topk,
+                      order=dsai.DSAI_ORDER_SCORE if order == "score" else dsai.DSAI_ORDER_INDEX)
+    qb = SY.f32_to_bf16_bits(rng.standard_normal((Q, H, D)).astype(np.float32))
+    pkb = SY.f32_to_bf16_bits(rng.standard_normal((P, D)).astype(np.float32))
+    w = (rng.standard_normal((Q, H)) / np.sqrt(H)).astype(np.float32)
+    pv = (rng.random(P) < 0.9).astype(np.uint8)
+    lim = rng.integers(0, P + 1, size=Q).astype(np.int32)
+    lim[:5] = [-3, 0, 1, P, P + 9]
+    q, pk, wg, pvg = bf16_gpu(qb), bf16_gpu(pkb), torch.from_numpy(w).cuda(), torch.from_numpy(pv).cuda()
+    limg = torch.from_numpy(lim).cuda()
+    ids, vals, tok = ix.select(q, wg, pk, pvg, expand=True, pool_limit=limg)
+    u_ids, u_vals = ix.select(q, wg, pk, pvg)
+    f_ids, f_vals = ix.select(q, wg, pk, pvg, pool_limit=torch.full((Q,), P, dtype=torch.int32,
+                                                                     device="cuda"))
+    torch.cuda.synchronize()
+    gids, gv = ids.cpu().numpy(), vals.cpu().numpy()
+    assert np.array_equal(f_ids.cpu().numpy(), u_ids.cpu().numpy())
+    assert np.array_equal(f_vals.cpu().numpy().view(np.uint32), u_vals.cpu().numpy().view(np.uint32))
+    assert np.all(gids[1] == -1) and np.all(np.isneginf(gv[1]))      # bound 0
+    assert np.all(gids[0] == -1)                                     # bound < 0
+    assert np.array_equal(tok.cpu().numpy(), oracle.expand_selection(gids, 0, KP))
+    sel = index_topk // KP
+    o = oracle.pooled_index_scores(f64(qb), w, f64(pkb), pv, pool_limit=lim)
+    for r in range(Q):
+        vis = np.nonzero(np.isfinite(o[r]))[0]
+        pos = np.full(P, -1, dtype=np.int64)
+        pos[vis] = np.arange(vis.size)
+        gi = np.where(gids[r] >= 0, pos[np.maximum(gids[r], 0)], -1)
+        if order == "index":   # same set in pool-id order: compare in score order
+            m = int((gids[r] >= 0).sum())
+            srt = np.lexsort((gids[r][:m], -gv[r][:m].astype(np.float64)))
+            gi = np.concatenate([gi[:m][srt], gi[m:]])
+            gvr = np.concatenate([gv[r][:m][srt], gv[r][m:]])
+        else:
+            gvr = gv[r]
+        check_topk_rows(gi[None], gvr[None], [o[r][vis]], sel, [f"row {r} bound {lim[r]}"])

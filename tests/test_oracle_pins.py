@@ -373,6 +373,61 @@ def test_bruteforce_pooled():
     check_bruteforce_pooled()
 
 
+def check_bruteforce_pool_limits(n_cases=12, seed=31):
+    """Per-row visible-pool bounds: each row selects, by exact rational
+    arithmetic, only among valid pools p < its bound (bounds below 0 act as
+    0, above P as P); the selection is the brute-force one, ties to the lower
+    pool id, padding where too few pools remain."""
+    rng = np.random.default_rng(seed)
+    F = lambda x: Fraction(float(x))
+    for c in range(n_cases):
+        P, D, H, Q = int(rng.integers(1, 9)), int(rng.integers(1, 4)), int(rng.integers(1, 3)), 5
+        pk = rng.choice(_QK_SET, (P, D)).astype(np.float64)
+        pv = (rng.random(P) < 0.8).astype(np.uint8)
+        q = rng.choice(_QK_SET, (Q, H, D)).astype(np.float64)
+        w = rng.choice(_W_SET, (Q, H)).astype(np.float64)
+        lim = rng.integers(-2, P + 3, size=Q)
+        sc = oracle.pooled_index_scores(q, w, pk, pv, pool_limit=lim)
+        for sel in (1, 2, P + 1):
+            ids, vals = oracle.topk_pools(sc, sel)
+            for i in range(Q):
+                scores = {}
+                for p_ in range(min(max(int(lim[i]), 0), P)):
+                    if not pv[p_]:
+                        continue
+                    tot = Fraction(0)
+                    for h in range(H):
+                        dot = sum((F(q[i, h, d]) * F(pk[p_, d]) for d in range(D)), Fraction(0))
+                        tot += F(w[i, h]) * max(dot, Fraction(0))
+                    scores[p_] = tot
+                chosen = _brute_pick(scores, sel)
+                assert ids[i].tolist() == chosen + [-1] * (sel - len(chosen)), (c, i)
+                for j, p_ in enumerate(chosen):
+                    assert F(vals[i, j]) == scores[p_]
+
+
+def check_pool_limit_reduces_to_unbounded(seed=32):
+    """A bound of P (or more) for every row is the call without bounds."""
+    rng = np.random.default_rng(seed)
+    P, D, H, Q = 40, 8, 4, 6
+    pk = rng.standard_normal((P, D))
+    pv = (rng.random(P) < 0.9).astype(np.uint8)
+    q, w = rng.standard_normal((Q, H, D)), rng.standard_normal((Q, H))
+    ref = oracle.pooled_index_scores(q, w, pk, pv)
+    for lim in (np.full(Q, P), np.full(Q, P + 7)):
+        assert np.array_equal(oracle.pooled_index_scores(q, w, pk, pv, pool_limit=lim), ref)
+    none = oracle.pooled_index_scores(q, w, pk, pv, pool_limit=np.zeros(Q, np.int64))
+    assert np.all(np.isneginf(none))
+
+
+def test_bruteforce_pool_limits():
+    check_bruteforce_pool_limits()
+
+
+def test_pool_limit_reduces_to_unbounded():
+    check_pool_limit_reduces_to_unbounded()
+
+
 # ---------------------------------------------------------------------------
 # Special cases, closed forms, invariants
 # ---------------------------------------------------------------------------
@@ -843,7 +898,8 @@ ALL_CHECKS = [check_golden_indexer, check_golden_kpool, check_golden_pooled,
               check_k_norm_hand_example, check_k_norm_properties,
               lambda: check_backward_finite_differences(2), check_backward_euler,
               check_backward_dense_form, check_backward_gate_at_zero,
-              lambda: check_bruteforce_packed(6), lambda: check_backward_packed_finite_differences(1)]
+              lambda: check_bruteforce_packed(6), lambda: check_backward_packed_finite_differences(1),
+              check_bruteforce_pool_limits, check_pool_limit_reduces_to_unbounded]
 
 
 def _some_check_fails():
@@ -892,6 +948,11 @@ MUTANTS = {
         (int(cq[i]), int(cq[i + 1]), 0, int(ck[i + 1] - ck[i])) for i in range(len(cq) - 1)]),
     "packed rows see the keys before them": ("_sequence_spans", lambda cq, ck: [
         (int(cq[i]), int(cq[i + 1]), 0, int(ck[i + 1])) for i in range(len(cq) - 1)]),
+    "pool bound admits p == limit": ("visible_pools", lambda P, lim: (
+        np.ones(P, dtype=bool) if lim is None else np.arange(P) <= min(max(int(lim), 0), P))),
+    "pool bound ignored": ("visible_pools", lambda P, lim: np.ones(P, dtype=bool)),
+    "negative pool bound wraps": ("visible_pools", lambda P, lim: (
+        np.ones(P, dtype=bool) if lim is None else np.arange(P) < (int(lim) % (P + 1)))),
     "round toward zero": ("round_to_bf16", lambda x: (
         np.ldexp(np.trunc(np.ldexp(np.frexp(x)[0], 8)), np.frexp(x)[1] - 8),
         (np.ldexp(np.trunc(np.ldexp(np.frexp(x)[0], 8)), np.frexp(x)[1] - 8)
