@@ -42,7 +42,7 @@ constexpr int kDenseScratch = 2048;
 // (one 256-bin histogram; the bin-edge cut needs no side list).
 constexpr int kCutScratch = 1024;
 
-// Static LDS of the filter-store kernels (cut_flag), rounded up.
+// Static LDS of the filter-store kernels (cut requests), rounded up.
 constexpr int64_t kStaticLds = 128;
 
 // A filter store asks for a cut once fewer than this many slots are free:
@@ -66,7 +66,9 @@ __device__ __forceinline__ void score_select_body(
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup) {
   extern __shared__ __align__(16) char smem_raw[];
-  __shared__ uint32_t cut_flag[2][8];  // filter store: per-wavefront cut requests
+  // filter store: cut requests, one word per tile modulo 3 (set by any
+  // wavefront whose store is nearly full after recording that tile)
+  __shared__ uint32_t cut_req[3];
   lds_char* smem = (lds_char*)smem_raw;
   using G = TileGeom<D>;
   using L = ScoreLds<D, NW>;
@@ -119,6 +121,7 @@ __device__ __forceinline__ void score_select_body(
     sc.load_row(rr, q + row * H * D, w + row * H, H, active[rr]);
   }
 
+  if (!DENSE && threadIdx.x < 3) cut_req[threadIdx.x] = 0u;  // published by the loop's first barrier
   uint32_t count[NR], tau[NR];       // filter store: entries, running threshold
   // a bin-edge cut may keep a few entries past k; one that would keep more
   // than a quarter of the store's slack cuts exactly instead
@@ -175,11 +178,11 @@ __device__ __forceinline__ void score_select_body(
     }
     if constexpr (!DENSE) {
       // Ask for a cut once a store has fewer than kCutRequest free slots
-      // (read by every wavefront after the next barrier).
+      // (read by every wavefront after a later barrier).
       bool need = false;
 #pragma unroll
       for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - kCutRequest);
-      if (lane == 0) cut_flag[it_rec & 1][wave] = need ? 1u : 0u;
+      if (need && lane == 0) cut_req[it_rec % 3] = 1u;
     }
   };
   if (ntiles > 0) {
@@ -233,9 +236,9 @@ __device__ __forceinline__ void score_select_body(
       // it is past half its slack, or nearly full; then the pipeline
       // restarts at the next tile, whose tile and the one after it are
       // already staged in LDS.  A request waits at most four tiles, which
-      // kCutRequest leaves room for.  Request flags alternate between two
-      // slots, so a wavefront's next request never overwrites one another
-      // wavefront has yet to read; flags of a finished run are not read.
+      // kCutRequest leaves room for.  Requests rotate over three words, so a
+      // word is cleared only after every wavefront read it and before it is
+      // set again; words of a finished run are not read.
       int s = 0;  // first tile of the current run
       // One fragment buffer, refilled with tile it + 1 as tile it's products
       // are issued (registers for the store's bookkeeping).
@@ -244,11 +247,11 @@ __device__ __forceinline__ void score_select_body(
         (void)fnext;
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        uint32_t any = 0u;
-        if (it >= s + 3) {  // the request of finish(it - 3), in this run
-#pragma unroll
-          for (int w2 = 0; w2 < NW; ++w2) any |= cut_flag[(it - 3) & 1][w2];
-        }
+        // the requests of finish(it - 3), in this run; the word of
+        // finish(it - 4) is cleared for finish(it - 1) (every wavefront read
+        // it before this barrier, none writes it again before the next)
+        const uint32_t any = it >= s + 3 ? cut_req[it % 3] : 0u;
+        if (wave == 0 && lane == 0) cut_req[(it + 2) % 3] = 0u;
         if (fin) finish(it - 2);
         ld.store(buf(it + 2));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
