@@ -406,7 +406,7 @@ def main():
         fn()
         pairs = [(ev(), ev()) for _ in range(reps)]
         for a, b in pairs:
-            torch.sum(flush_buf, out=sink)
+            torch.sum(flush_buf, dim=0, out=sink)
             a.record()
             fn()
             b.record()
