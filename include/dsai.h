@@ -77,7 +77,8 @@ typedef struct dsai_config {
                      kpool (config invariant on the "Module glm5next_dsa"
                      page); select_k = index_topk / kpool pools per row       */
   int first_key;  /* first cached token that pools (>= 0)                      */
-  int chunk_rows; /* query rows per dsai_score_topk launch; 0 = one launch     */
+  int chunk_rows; /* query rows per launch of the scores at supplied
+                     indices (0: all rows in one launch)                     */
   int order;      /* DSAI_ORDER_SCORE (default 0) or DSAI_ORDER_INDEX: order of
                      the entries of each dsai_score_topk / dsai_topk_pools /
                      dsai_select row (padding is always at the tail)         */
@@ -124,14 +125,13 @@ int dsai_last_hip_error(dsai_handle h);
  * S, Skv, B >= 0 (S == 0 or B == 0: nothing is written or launched);
  * Skv < 2^31; compress_ratio >= 1; 1 <= topk <= DSAI_MAX_TOPK
  * (DSAI_ERR_INVALID_ARG otherwise); index_k must span < 4 GiB
- * (Skv * B * D * 2 bytes; DSAI_ERR_UNSUPPORTED otherwise).  Query rows are
- * processed in launches of cfg.chunk_rows rows (all rows if 0); no scratch
- * memory is used.  With more than one chunk, consecutive chunks run on two
- * streams the handle owns, forked from `stream` (after the work already on
- * it) and joined back to it (work enqueued on `stream` later waits for every
- * chunk), so that two chunks are in flight; the streams and their events
- * are created at the first such call on a device and released by
- * dsai_destroy.
+ * (Skv * B * D * 2 bytes; DSAI_ERR_UNSUPPORTED otherwise).  The selection
+ * runs as one launch on `stream` (plus the row-sort launch in score order);
+ * no scratch memory is used and no score matrix is formed, at any size.
+ * cfg.chunk_rows does not apply to the selection: the one launch covers
+ * every row, its workgroups numbered from the last (longest) rows to the
+ * first, so no chunk boundary leaves the GPU idle while a chunk's longest
+ * rows finish.
  *
  * Scores at supplied indices (the page's optional topk_indices
  * [batch, seqlen, topk] int32, and pytorch_extract_topk_scores): when
@@ -141,7 +141,13 @@ int dsai_last_hip_error(dsai_handle h);
  * bit-identical to the score the selection reports for that key.
  * topk_indices is device memory, 16-byte aligned (DSAI_ERR_INVALID_ARG
  * otherwise), and may be out_idx itself (in place); cfg.order does not
- * apply; index_k has no 4 GiB limit on this form. */
+ * apply; index_k has no 4 GiB limit on this form.  Its rows are scored in
+ * launches of cfg.chunk_rows rows (all rows if 0); with more than one
+ * chunk, consecutive chunks run on two streams the handle owns, forked from
+ * `stream` (after the work already on it) and joined back to it (work
+ * enqueued on `stream` later waits for every chunk); the streams and their
+ * events are created at the first such call on a device and released by
+ * dsai_destroy. */
 int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
                     const float* weights, int64_t S, int64_t Skv, int64_t B,
                     int compress_ratio, int topk, const int32_t* topk_indices,
@@ -177,10 +183,11 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
  * (DSAI_ERR_INVALID_ARG otherwise); a sequence whose keys span 4 GiB or
  * more, or a topk the selection cannot hold, gives DSAI_ERR_UNSUPPORTED;
  * every refusal comes before the first launch.  One launch per non-empty
- * sequence (one per cfg.chunk_rows rows of it, in order, if chunked);
- * consecutive sequences alternate between the handle's two streams, forked
- * from `stream` and joined back to it as for chunked dsai_score_topk calls;
- * then, in score order, one row sort over all Tq rows on `stream`. */
+ * sequence (with supplied indices, one per cfg.chunk_rows rows of it, in
+ * order, if chunked); consecutive sequences alternate between the handle's
+ * two streams, forked from `stream` and joined back to it as for chunked
+ * scores at supplied indices; then, in score order, one row sort over all
+ * Tq rows on `stream`. */
 int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index_k,
                            const float* weights, int64_t nseq, const int64_t* cu_seqlens_q,
                            const int64_t* cu_seqlens_k, int compress_ratio, int topk,

@@ -266,14 +266,9 @@ static int score_topk_one(dsai_handle h, const void* index_q, const void* index_
   a.chunk_rows = h->cfg.chunk_rows;
   a.sort = sort;
   a.out_idx = out_idx; a.out_score = out_score;
+  // one launch on the caller's stream whatever cfg.chunk_rows is
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t le;
-  if (a.chunk_rows > 0 && S > a.chunk_rows)
-    le = on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
-      return dsai::launch_score_topk(a, plan, s0, s1);
-    });
-  else
-    le = dsai::launch_score_topk(a, plan, st, nullptr);
+  hipError_t le = dsai::launch_score_topk(a, plan, st, nullptr);
   if (le != hipSuccess) return hip_status(h, le);
   if (a.sort) le = dsai::launch_sort_rows(out_idx, out_score, B * S, topk, st);
   return hip_status(h, le);

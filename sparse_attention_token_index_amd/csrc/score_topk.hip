@@ -422,7 +422,11 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
                                      (int)p.lds_bytes);
   if (e != hipSuccess) return e;
   const int R = p.rows_per_block;
-  const int64_t chunk = a.chunk_rows > 0 ? a.chunk_rows : a.S;
+  // The selection covers every row in one launch, workgroups numbered
+  // heaviest rows first: no [chunk, Skv] scores exist, so a chunk would bound
+  // no memory, and one launch has no per-chunk tail.  Scores at supplied
+  // indices keep one launch per chunk_rows rows.
+  const int64_t chunk = (at && a.chunk_rows > 0) ? a.chunk_rows : a.S;
   int64_t ci = 0;
   for (int64_t r0 = 0; r0 < a.S; r0 += chunk, ++ci) {
     const int64_t r1 = (r0 + chunk < a.S) ? r0 + chunk : a.S;

@@ -134,7 +134,9 @@ CASES = {
     # C4 compressed-KV indexer: B=2, S=16384 queries, Skv=4096 keys, ratio 4, topk=512.
     "c4": IndexerCase("c4", B=2, S=16384, Skv=4096, H=64, D=128, compress_ratio=4,
                       topk=512, w_var=1.0 / 64),
-    # Long-context stress: S=Skv=65536, 5% of keys x4, topk=2048, 1024-row chunks.
+    # Long-context stress: S=Skv=65536, 5% of keys x4, topk=2048, 1024-row chunks
+    # (chunk_rows bounds the launches of scores at supplied indices; the fused
+    # selection forms no score matrix and runs as one launch).
     "long": IndexerCase("long", B=1, S=65536, Skv=65536, H=64, D=128, compress_ratio=1,
                         topk=2048, w_var=1.0 / 64, heavy_frac=0.05, heavy_scale=4.0,
                         chunk_rows=1024),
