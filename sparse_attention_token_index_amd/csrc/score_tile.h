@@ -76,7 +76,9 @@ struct TileLoader {
   }
 
   __device__ __forceinline__ void load(uint32_t row0) {
-    const uint32_t soff = row0 * row_bytes;
+    // the stage offset is wave-uniform; saying so keeps it scalar where the
+    // compiler cannot prove it (a buffer load needs it in a scalar register)
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * row_bytes);
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0));

@@ -66,9 +66,10 @@ __device__ __forceinline__ void score_select_body(
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup) {
   extern __shared__ __align__(16) char smem_raw[];
-  // filter store: cut requests, one word per tile modulo 3 (set by any
-  // wavefront whose store is nearly full after recording that tile)
-  __shared__ uint32_t cut_req[3];
+  // filter store: cut requests, one 8-byte word per tile modulo 3, byte w
+  // written by wavefront w after recording that tile (1: its store is nearly
+  // full)
+  __shared__ uint64_t cut_req[3];
   lds_char* smem = (lds_char*)smem_raw;
   using G = TileGeom<D>;
   using L = ScoreLds<D, NW>;
@@ -173,16 +174,18 @@ __device__ __forceinline__ void score_select_body(
         smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
       } else {
         const uint32_t u = ord_key(x);
-        wave_append(rs[rr], count[rr], lane < 32 && vis && u > tau[rr], u, key);
+        // (non-short-circuit: no branch)
+        wave_append_all(rs[rr], count[rr], (lane < 32) & vis & (u > tau[rr]), u, key);
       }
     }
     if constexpr (!DENSE) {
       // Ask for a cut once a store has fewer than kCutRequest free slots
-      // (read by every wavefront after a later barrier).
+      // (read by every wavefront after a later barrier): every lane writes
+      // the wavefront's own byte, so no branch and no clearing.
       bool need = false;
 #pragma unroll
       for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - kCutRequest);
-      if (need && lane == 0) cut_req[it_rec % 3] = 1u;
+      ((DSAI_LDS uint8_t*)&cut_req[it_rec % 3])[wave] = need ? 1u : 0u;
     }
   };
   if (ntiles > 0) {
@@ -236,22 +239,20 @@ __device__ __forceinline__ void score_select_body(
       // it is past half its slack, or nearly full; then the pipeline
       // restarts at the next tile, whose tile and the one after it are
       // already staged in LDS.  A request waits at most four tiles, which
-      // kCutRequest leaves room for.  Requests rotate over three words, so a
-      // word is cleared only after every wavefront read it and before it is
-      // set again; words of a finished run are not read.
+      // kCutRequest leaves room for: a store holds at most cap - 64 entries
+      // before any tile is recorded, the room wave_append_all needs.
+      // Requests rotate over three words: the word step `it` reads was
+      // written by finish(it - 3) (before this barrier) and is written
+      // again by finish(it) (after the next); words of a finished run are
+      // not read.  The steady-state steps have no branch, so the compiler
+      // interleaves the record of tile it - 2 with tile it's products.
       int s = 0;  // first tile of the current run
       // One fragment buffer, refilled with tile it + 1 as tile it's products
       // are issued (registers for the store's bookkeeping).
-      auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
-                      bool red) -> bool {
-        (void)fnext;
+      auto step = [&](int it, Frag& fcur, Acc& cur, const Acc& old, bool fin, bool red) -> bool {
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        // the requests of finish(it - 3), in this run; the word of
-        // finish(it - 4) is cleared for finish(it - 1) (every wavefront read
-        // it before this barrier, none writes it again before the next)
-        const uint32_t any = it >= s + 3 ? cut_req[it % 3] : 0u;
-        if (wave == 0 && lane == 0) cut_req[(it + 2) % 3] = 0u;
+        const uint64_t req = cut_req[it % 3];  // used at the end of the step
         if (fin) finish(it - 2);
         ld.store(buf(it + 2));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
@@ -260,8 +261,18 @@ __device__ __forceinline__ void score_select_body(
 #pragma unroll
           for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
         }
+        // Issue order: each matrix-core product followed by a few vector
+        // instructions (the record, the reduction), so that a wavefront
+        // whose products wait for the matrix core still has vector work
+        // queued behind them rather than in one block after the last.
+#pragma unroll
+        for (int g = 0; g < Scorer::KS * Scorer::MT * NR; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
+        }
         __builtin_amdgcn_sched_barrier(0);
-        return any != 0u;
+        // (uniform and with no branch: `&`, not `&&`)
+        return (it >= s + 3) & (uniform((uint32_t)req | (uint32_t)(req >> 32)) != 0u);
       };
       const uint32_t cut_at = min((uint32_t)(topk + cap) / 2u, (uint32_t)(cap - kCutRequest - 32));
       for (;;) {
@@ -270,14 +281,17 @@ __device__ __forceinline__ void score_select_body(
         sc.fetch(buf(s), f0);
         // Steps go in pairs (products in acc0, then acc1), so a run always
         // ends with its last products in acc1; a pair may run one tile past
-        // the last (zero keys past the range, never recorded).
-        int it = s;
-        for (;;) {
-          const bool more = it > s;
-          bool want = step(it, f0, f0, acc0, acc1, more, more);
-          want |= step(it + 1, f0, f0, acc1, acc0, more, true);
+        // the last (zero keys past the range, never recorded).  The first
+        // pair of a run (nothing to record yet, no request to read) is
+        // peeled, so the flags of the steady-state steps are constants.
+        step(s, f0, acc0, acc1, false, false);
+        step(s + 1, f0, acc1, acc0, false, true);
+        int it = s + 2;
+        while (it < ntiles) {
+          bool want = step(it, f0, acc0, acc1, true, true);
+          want |= step(it + 1, f0, acc1, acc0, true, true);
           it += 2;
-          if (want || it >= ntiles) break;
+          if (want) break;
         }
         // drain: record tiles it - 2 (reduced in the last step) and it - 1
         finish(it - 2);
@@ -287,8 +301,13 @@ __device__ __forceinline__ void score_select_body(
         if (it >= ntiles) break;
         __syncthreads();  // every wavefront drained; tiles it and it + 1 are staged
 #pragma unroll
-        for (int rr = 0; rr < NR; ++rr)
-          if (count[rr] > cut_at) count[rr] = wave_cut(rs[rr], count[rr], (uint32_t)topk, max_keep, &tau[rr]);
+        for (int rr = 0; rr < NR; ++rr) {
+          if (count[rr] > cut_at) {
+            const uint2 c = wave_cut(rs[rr], count[rr], (uint32_t)topk, max_keep);
+            count[rr] = uniform(c.x);
+            tau[rr] = uniform(c.y);
+          }
+        }
         s = it;
       }
     }

@@ -51,6 +51,22 @@ __device__ __forceinline__ void wave_append(const RowStore<IdxT>& rs, uint32_t& 
   count = uniform(count + (uint32_t)__popcll(m));
 }
 
+// wave_append with no branch, so the compiler can interleave it with other
+// work: every lane stores, the passing lanes after the current entries in
+// lane order and the others into the slots right after those (slots past the
+// count hold nothing), so the store needs 64 free slots past `count`.
+template <typename IdxT>
+__device__ __forceinline__ void wave_append_all(const RowStore<IdxT>& rs, uint32_t& count,
+                                                bool pass, uint32_t u, uint32_t id) {
+  const uint64_t m = ballot(pass);
+  const uint32_t below = lanes_below(m);
+  const uint32_t np = (uint32_t)__popcll(m);
+  const uint32_t p = count + (pass ? below : np + (uint32_t)lane_id() - below);
+  rs.key[p] = u;
+  rs.idx[p] = (IdxT)id;
+  count = uniform(count + np);
+}
+
 // LDS bytes per wavefront for the select: a 256-bin histogram and a 256-key
 // side list.
 constexpr int kSelScratchBytes = 2048;
@@ -286,12 +302,13 @@ __device__ __noinline__ uint32_t wave_compact_ge(RowStore<IdxT> rs, uint32_t n, 
 // cut - for two passes over the store fewer and no side list.  When it would
 // keep more than `max_keep` (many equal keys at the boundary), the exact cut
 // runs instead (to exactly k, ties to the earlier entries), without a side
-// list: `side` may be memory other wavefronts are using.
+// list: `side` may be memory other wavefronts are using.  Returns (entries
+// kept, new threshold), so the caller's threshold can stay in a register.
 constexpr uint32_t kCutRefine = 64;
 
 template <typename IdxT>
-__device__ __noinline__ uint32_t wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_t k,
-                                          uint32_t max_keep, uint32_t* tau) {
+__device__ __noinline__ uint2 wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_t k,
+                                       uint32_t max_keep) {
   const int lane = lane_id();
   wave_lds_sync();
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -365,11 +382,9 @@ __device__ __noinline__ uint32_t wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_
   }
   if (kept > max_keep) {
     const uint2 sel = wave_radix_select(rs.key, rs.hist, rs.side, 0u, n, k);
-    *tau = sel.x;
-    return wave_compact(rs, n, sel.x, sel.y);
+    return make_uint2(wave_compact(rs, n, sel.x, sel.y), sel.x);
   }
-  *tau = t;
-  return wave_compact_ge(rs, n, t);
+  return make_uint2(wave_compact_ge(rs, n, t), t);
 }
 
 // Reduce the store to its top k (stable) if it holds more than k entries;
