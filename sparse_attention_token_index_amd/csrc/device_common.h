@@ -27,7 +27,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+// (the compiler builtin takes the predicate as a lane mask, so a compare
+// feeds it directly)
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // Make LDS writes of this wave visible to its other lanes and keep the
 // compiler from moving LDS accesses across this point.
@@ -44,6 +46,12 @@ __device__ __forceinline__ uint32_t ord_key(float s) {
   uint32_t b = __float_as_uint(s);
   if (b == 0x80000000u) b = 0u;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// ord_key of a score known not to be -0.
+__device__ __forceinline__ uint32_t ord_key_nz(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return (int32_t)b < 0 ? ~b : (b | 0x80000000u);
 }
 
 __device__ __forceinline__ float ord_to_float(uint32_t u) {

@@ -158,7 +158,11 @@ __device__ __forceinline__ void score_select_body(
   // Every LDS access is issued early in its iteration, so the next barrier
   // does not wait on a recent one.
   using Frag = typename Scorer::Frag;
-  auto buf = [&](int it) { return smem + (it & 1) * L::kTileBytes; };
+  // Buffer of a tile of parity p.  Every step knows the parity of its tile
+  // at compile time (tile it's products go to acc0 when it is even, acc1
+  // when odd, and a run of the filter loop starts at an even tile), so the
+  // buffers' LDS addresses fold into the instructions' offsets.
+  auto buf = [&](int p) { return smem + p * L::kTileBytes; };
   Acc acc0, acc1;
   Frag f0, f1;
   float part[NR];  // reduce_half of the tile awaiting finish()
@@ -173,7 +177,7 @@ __device__ __forceinline__ void score_select_body(
         smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
         smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
       } else {
-        const uint32_t u = ord_key(x);
+        const uint32_t u = ord_key_nz(x);  // x + 0 is never -0
         // (non-short-circuit: no branch)
         wave_append_all(rs[rr], count[rr], (lane < 32) & vis & (u > tau[rr]), u, key);
       }
@@ -194,16 +198,16 @@ __device__ __forceinline__ void score_select_body(
     ld.load((uint32_t)G::kTileKeys);
     ld.store(buf(1));
     if constexpr (DENSE) {
-      auto step = [&](int it, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old, bool fin,
-                      bool red) {
+      auto step = [&](int it, int par, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old,
+                      bool fin, bool red) {
         __syncthreads();
         // Scheduling fences: the compiler may not hoist the next iteration's
         // products above this barrier or sink this one's below the next,
         // which would put a reduction right behind the products it reads.
         __builtin_amdgcn_sched_barrier(0);
-        sc.fetch(buf(it + 1), fnext);
+        sc.fetch(buf(par ^ 1), fnext);
         if (fin) finish(it - 2);
-        ld.store(buf(it + 2));
+        ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
         sc.mma(fcur, cur);
         if (red) {
@@ -215,15 +219,15 @@ __device__ __forceinline__ void score_select_body(
       ld.load((uint32_t)(2 * G::kTileKeys));
       __syncthreads();
       sc.fetch(buf(0), f0);
-      step(0, f0, f1, acc0, acc1, false, false);
+      step(0, 0, f0, f1, acc0, acc1, false, false);
       int it = 1;
       if (ntiles > 1) {
-        step(1, f1, f0, acc1, acc0, false, true);
+        step(1, 1, f1, f0, acc1, acc0, false, true);
         for (it = 2; it + 1 < ntiles; it += 2) {
-          step(it, f0, f1, acc0, acc1, true, true);
-          step(it + 1, f1, f0, acc1, acc0, true, true);
+          step(it, 0, f0, f1, acc0, acc1, true, true);
+          step(it + 1, 1, f1, f0, acc1, acc0, true, true);
         }
-        if (it < ntiles) step(it, f0, f1, acc0, acc1, true, true);
+        if (it < ntiles) step(it, 0, f0, f1, acc0, acc1, true, true);
         finish(ntiles - 2);
       }
 #pragma unroll
@@ -249,14 +253,15 @@ __device__ __forceinline__ void score_select_body(
       int s = 0;  // first tile of the current run
       // One fragment buffer, refilled with tile it + 1 as tile it's products
       // are issued (registers for the store's bookkeeping).
-      auto step = [&](int it, Frag& fcur, Acc& cur, const Acc& old, bool fin, bool red) -> bool {
+      auto step = [&](int it, int par, Frag& fcur, Acc& cur, const Acc& old, bool fin,
+                      bool red) -> bool {
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         const uint64_t req = cut_req[it % 3];  // used at the end of the step
         if (fin) finish(it - 2);
-        ld.store(buf(it + 2));
+        ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
-        sc.mma_fetch(fcur, buf(it + 1), cur);
+        sc.mma_fetch(fcur, buf(par ^ 1), cur);
         if (red) {
 #pragma unroll
           for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
@@ -278,18 +283,18 @@ __device__ __forceinline__ void score_select_body(
       for (;;) {
         ld.load((uint32_t)(s + 2) * G::kTileKeys);
         __syncthreads();
-        sc.fetch(buf(s), f0);
+        sc.fetch(buf(0), f0);  // s is even
         // Steps go in pairs (products in acc0, then acc1), so a run always
         // ends with its last products in acc1; a pair may run one tile past
         // the last (zero keys past the range, never recorded).  The first
         // pair of a run (nothing to record yet, no request to read) is
         // peeled, so the flags of the steady-state steps are constants.
-        step(s, f0, acc0, acc1, false, false);
-        step(s + 1, f0, acc1, acc0, false, true);
+        step(s, 0, f0, acc0, acc1, false, false);
+        step(s + 1, 1, f0, acc1, acc0, false, true);
         int it = s + 2;
         while (it < ntiles) {
-          bool want = step(it, f0, acc0, acc1, true, true);
-          want |= step(it + 1, f0, acc1, acc0, true, true);
+          bool want = step(it, 0, f0, acc0, acc1, true, true);
+          want |= step(it + 1, 1, f0, acc1, acc0, true, true);
           it += 2;
           if (want) break;
         }
