@@ -232,6 +232,18 @@ def counter_summary(pmc_dir, out, command):
                          f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.3f}")
         if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
             lines.append(f"  derived_valu_per_mfma: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}")
+        if "GRBM_GUI_ACTIVE" in avg:
+            simd_cyc = avg["GRBM_GUI_ACTIVE"] / 8.0 * 1024
+            # SQ_ACTIVE_INST_VALU counts quad-cycles summed over the SIMDs
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                lines.append("  derived_valu_busy_frac: "
+                             f"{4.0 * avg['SQ_ACTIVE_INST_VALU'] / simd_cyc:.3f}")
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+                lines.append("  derived_valu_mfma_coexec_frac: "
+                             f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd_cyc:.3f}")
+        if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES"):
+            lines.append("  derived_wave_wait_frac: "
+                         f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.3f}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -287,7 +299,7 @@ def _sample_rows(case, n):
 
 def cpu_baseline(case, budget_s=20.0):
     """The oracle (fp64 NumPy, as it stands) on a bounded sample of the
-    headline workload: query rows spread over the positions (32 rows from
+    headline workload: query rows spread over the positions (256 rows from
     each of 8 evenly spaced 1024-row blocks, so their inputs are drawn
     without drawing the rest), each scored against all its visible keys and
     ranked, in a shuffled order until `budget_s` of oracle time has passed.
@@ -303,7 +315,7 @@ def cpu_baseline(case, budget_s=20.0):
     nblk = max(1, case.S // SY.BLOCK)
     blocks = np.unique(np.linspace(0, nblk - 1, min(8, nblk)).round().astype(np.int64))
     rows = np.concatenate([b * SY.BLOCK + np.linspace(0, min(SY.BLOCK, case.S - b * SY.BLOCK) - 1,
-                                                      32).round().astype(np.int64)
+                                                      256).round().astype(np.int64)
                            for b in blocks])
     rows = np.unique(rows)
     inp = SY.indexer_inputs(case, rows=rows)
@@ -321,7 +333,7 @@ def cpu_baseline(case, budget_s=20.0):
         if spent > budget_s:
             break
     step_s = spent / pairs * visible_pairs(case)
-    sample = (f"{done} of {case.B * case.S} {case.name} query rows (32 from each of "
+    sample = (f"{done} of {case.B * case.S} {case.name} query rows (up to 256 from each of "
               f"{blocks.size} evenly spaced 1024-row blocks, shuffled), each against all its "
               f"visible keys in score order, fp64 NumPy, {spent:.1f} s; extrapolated to the "
               f"whole workload by visible (query, key) pairs")

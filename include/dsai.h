@@ -182,12 +182,14 @@ int dsai_score_topk(dsai_handle h, const void* index_q, const void* index_k,
  * >= 0, offsets as above, Tq and Tk < 2^31, compress_ratio >= 1
  * (DSAI_ERR_INVALID_ARG otherwise); a sequence whose keys span 4 GiB or
  * more, or a topk the selection cannot hold, gives DSAI_ERR_UNSUPPORTED;
- * every refusal comes before the first launch.  One launch per non-empty
- * sequence (with supplied indices, one per cfg.chunk_rows rows of it, in
- * order, if chunked); consecutive sequences alternate between the handle's
- * two streams, forked from `stream` and joined back to it as for chunked
- * scores at supplied indices; then, in score order, one row sort over all
- * Tq rows on `stream`. */
+ * every refusal comes before the first launch.  The selection runs as one
+ * launch per 64 non-empty sequences, on `stream`, sequences taken from the
+ * longest row down (a table in the launch arguments maps each workgroup to
+ * its sequence); then, in score order, one row sort over all Tq rows on
+ * `stream`.  With supplied indices: one launch per non-empty sequence (one
+ * per cfg.chunk_rows rows of it, in order, if chunked), consecutive
+ * sequences alternating between the handle's two streams, forked from
+ * `stream` and joined back to it. */
 int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index_k,
                            const float* weights, int64_t nseq, const int64_t* cu_seqlens_q,
                            const int64_t* cu_seqlens_k, int compress_ratio, int topk,

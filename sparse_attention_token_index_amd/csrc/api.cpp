@@ -2,8 +2,10 @@
 // (all on the host, before any HIP call) and dispatch to the kernels.
 #include "dsai.h"
 
+#include <algorithm>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include <cmath>
 
@@ -315,46 +317,77 @@ int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index
     }
   }
   // Sequence i is the one-sample problem on its own rows and keys (topk % 4
-  // == 0 keeps each sequence's output rows 16-byte aligned).  Consecutive
-  // non-empty sequences alternate between the handle's two streams, so two
-  // are in flight; a sequence longer than cfg.chunk_rows runs its chunks in
-  // order on its stream.
+  // == 0 keeps each sequence's output rows 16-byte aligned).
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t le = on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
-    int64_t j = 0;
-    for (int64_t i = 0; i < nseq; ++i) {
-      const int64_t q0 = cu_seqlens_q[i], k0 = cu_seqlens_k[i];
-      const int64_t S = cu_seqlens_q[i + 1] - q0, Skv = cu_seqlens_k[i + 1] - k0;
-      if (S == 0) continue;
-      const hipStream_t sj = (j++ & 1) ? s1 : s0;
-      const uint16_t* q = static_cast<const uint16_t*>(index_q) + q0 * H * D;
-      const uint16_t* k = Skv > 0 ? static_cast<const uint16_t*>(index_k) + k0 * D : nullptr;
-      hipError_t e;
-      if (topk_indices) {
+  hipError_t le = hipSuccess;
+  if (topk_indices) {
+    // Scores at supplied indices: one launch per sequence (per chunk of
+    // cfg.chunk_rows rows), consecutive sequences alternating between the
+    // handle's two streams so that two are in flight.
+    le = on_side_streams(h, st, [&](hipStream_t s0, hipStream_t s1) {
+      int64_t j = 0;
+      for (int64_t i = 0; i < nseq; ++i) {
+        const int64_t q0 = cu_seqlens_q[i], k0 = cu_seqlens_k[i];
+        const int64_t S = cu_seqlens_q[i + 1] - q0, Skv = cu_seqlens_k[i + 1] - k0;
+        if (S == 0) continue;
+        const hipStream_t sj = (j++ & 1) ? s1 : s0;
         dsai::ScoreAtArgs a;
-        a.q = q; a.k = k; a.w = weights + q0 * H;
+        a.q = static_cast<const uint16_t*>(index_q) + q0 * H * D;
+        a.k = Skv > 0 ? static_cast<const uint16_t*>(index_k) + k0 * D : nullptr;
+        a.w = weights + q0 * H;
         a.S = S; a.Skv = Skv; a.B = 1;
         a.H = (int)H; a.D = (int)D; a.ratio = compress_ratio; a.n = topk;
         a.chunk_rows = h->cfg.chunk_rows;
         a.sup = topk_indices + q0 * topk;
         a.out_idx = out_idx + q0 * topk; a.out_score = out_score + q0 * topk;
-        e = launch_scores_at(h, a, sj, nullptr);
-      } else {
-        const dsai::ScoreSelectPlan plan =
-            dsai::plan_score_select(H <= 32 ? 32 : 64, (int)D, topk, Skv, h->lds_limit);
-        dsai::ScoreTopkArgs a;
-        a.q = q; a.k = k; a.w = weights + q0 * H;
-        a.S = S; a.Skv = Skv; a.B = 1;
-        a.H = (int)H; a.D = (int)D; a.ratio = compress_ratio; a.topk = topk;
-        a.chunk_rows = h->cfg.chunk_rows;
-        a.sort = false;
-        a.out_idx = out_idx + q0 * topk; a.out_score = out_score + q0 * topk;
-        e = dsai::launch_score_topk(a, plan, sj, nullptr);
+        const hipError_t e = launch_scores_at(h, a, sj, nullptr);
+        if (e != hipSuccess) return e;
       }
-      if (e != hipSuccess) return e;
+      return hipSuccess;
+    });
+  } else {
+    // Selection: sequences in order of their longest row (most keys first,
+    // stable), up to kPackedMax per launch of the fused kernel, all on
+    // `stream`; each launch's plan is the one of its longest key range.
+    std::vector<int64_t> order;
+    order.reserve((size_t)nseq);
+    for (int64_t i = 0; i < nseq; ++i)
+      if (cu_seqlens_q[i + 1] > cu_seqlens_q[i]) order.push_back(i);
+    auto heaviest = [&](int64_t i) {
+      const int64_t S = cu_seqlens_q[i + 1] - cu_seqlens_q[i];
+      const int64_t Skv = cu_seqlens_k[i + 1] - cu_seqlens_k[i];
+      return std::min(Skv, S / compress_ratio);
+    };
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t x, int64_t y) { return heaviest(x) > heaviest(y); });
+    dsai::PackedTopkArgs a;
+    a.q = static_cast<const uint16_t*>(index_q);
+    a.k = static_cast<const uint16_t*>(index_k);
+    a.w = weights;
+    a.H = (int)H; a.D = (int)D; a.ratio = compress_ratio; a.topk = topk;
+    a.out_idx = out_idx; a.out_score = out_score;
+    for (size_t g0 = 0; g0 < order.size() && le == hipSuccess; g0 += dsai::kPackedMax) {
+      const size_t g1 = std::min(order.size(), g0 + (size_t)dsai::kPackedMax);
+      int64_t skv_max = 0;
+      for (size_t j = g0; j < g1; ++j)
+        skv_max = std::max(skv_max, cu_seqlens_k[order[j] + 1] - cu_seqlens_k[order[j]]);
+      const dsai::ScoreSelectPlan plan =
+          dsai::plan_score_select(H <= 32 ? 32 : 64, (int)D, topk, skv_max, h->lds_limit);
+      dsai::PackedSeqs t;
+      t.n = (int)(g1 - g0);
+      for (int m = 0; m <= dsai::kPackedMax; ++m) t.blk_begin[m] = INT32_MAX;
+      t.blk_begin[0] = 0;
+      for (size_t j = g0; j < g1; ++j) {
+        const int64_t i = order[j], m = (int64_t)(j - g0);
+        t.q0[m] = (int)cu_seqlens_q[i];
+        t.k0[m] = (int)cu_seqlens_k[i];
+        t.S[m] = (int)(cu_seqlens_q[i + 1] - cu_seqlens_q[i]);
+        t.Skv[m] = (int)(cu_seqlens_k[i + 1] - cu_seqlens_k[i]);
+        t.blk_begin[m + 1] = t.blk_begin[m] + (t.S[m] + plan.rows_per_block - 1) / plan.rows_per_block;
+      }
+      le = dsai::launch_score_topk_packed(a, t, plan, st);
     }
-    return hipSuccess;
-  });
+  }
   if (le == hipSuccess && sort) le = dsai::launch_sort_rows(out_idx, out_score, Tq, topk, st);
   return hip_status(h, le);
 }

@@ -83,6 +83,29 @@ struct TopkRowsPlan {
 ScoreSelectPlan plan_score_select(int HP, int D, int topk, int64_t Skv, size_t lds_limit);
 TopkRowsPlan plan_topk_rows(int sel, int64_t P, size_t lds_limit);
 
+// Packed sequences in one launch of the fused kernel: up to kPackedMax
+// sequences, each the B = 1 problem on its own rows and keys (rows and keys
+// counted from q0 / k0 of the packed tensors).  Workgroups blk_begin[i] ..
+// blk_begin[i + 1] - 1 belong to sequence i; blk_begin[n] is the grid and
+// the entries after it hold INT_MAX.  The table travels in the kernel
+// arguments.
+constexpr int kPackedMax = 64;
+struct PackedSeqs {
+  int n;
+  int blk_begin[kPackedMax + 1];
+  int q0[kPackedMax], k0[kPackedMax], S[kPackedMax], Skv[kPackedMax];
+};
+struct PackedTopkArgs {
+  const uint16_t* q;  // [Tq, H, D] bf16
+  const uint16_t* k;  // [Tk, D] bf16
+  const float* w;     // [Tq, H]
+  int H, D, ratio, topk;
+  int32_t* out_idx;   // [Tq, topk], ascending index order
+  float* out_score;
+};
+hipError_t launch_score_topk_packed(const PackedTopkArgs& a, const PackedSeqs& seqs,
+                                    const ScoreSelectPlan& p, hipStream_t st);
+
 // Chunk launches (ScoreTopkArgs::chunk_rows) alternate between st and st2
 // when st2 is not null (two chunks in flight); the score-order pass is the
 // caller's (launch_sort_rows on the joined stream).

@@ -64,7 +64,7 @@ template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
 __device__ __forceinline__ void score_select_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup, int bid) {
   extern __shared__ __align__(16) char smem_raw[];
   // filter store: cut requests, one 8-byte word per tile modulo 3, byte w
   // written by wavefront w after recording that tile (1: its store is nearly
@@ -95,8 +95,8 @@ __device__ __forceinline__ void score_select_body(
   // t0 + wave * NR + rr, rr < NR, each with its own LDS row store.
   const int nrow = row_end - row_begin;
   const int nrb = (nrow + R - 1) / R;
-  const int jb = blockIdx.x / B;
-  const int b = blockIdx.x - jb * B;
+  const int jb = bid / B;
+  const int b = bid - jb * B;
   const int t0 = row_begin + (nrb - 1 - jb) * R;
   const int t_last = min(t0 + R, row_end) - 1;
   const int n_max = min(Skv, (t_last + 1) / ratio);
@@ -353,7 +353,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   score_select_body<HP, D, NW, NR, DENSE, IdxT>(q, k, w, S, Skv, B, H, ratio, topk, row_begin,
-                                                row_end, R, cap, out_idx, out_score, nullptr);
+                                                row_end, R, cap, out_idx, out_score, nullptr,
+                                                (int)blockIdx.x);
+}
+
+// Packed sequences: the workgroup's sequence is the number of sequence
+// starts at or below its index (a fixed-length scan over the table, whose
+// loads the compiler batches; starts past the last sequence hold INT_MAX),
+// then the one-sample problem of that sequence.
+template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_select_packed_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
+    int H, int ratio, int topk, int R, int cap, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_score, const PackedSeqs seqs) {
+  const int bid = (int)blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kPackedMax; ++j) i += bid >= seqs.blk_begin[j] ? 1 : 0;
+  const int64_t q0 = seqs.q0[i];
+  score_select_body<HP, D, NW, NR, DENSE, IdxT>(
+      q + q0 * H * D, k + (int64_t)seqs.k0[i] * D, w + q0 * H, seqs.S[i], seqs.Skv[i], 1, H, ratio,
+      topk, 0, seqs.S[i], R, cap, out_idx + q0 * topk, out_score + q0 * topk, nullptr,
+      bid - seqs.blk_begin[i]);
 }
 
 // Scores at supplied indices through the dense store (its own kernel, so
@@ -364,7 +385,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
     int32_t* out_idx, float* __restrict__ out_score, const int32_t* sup) {
   score_select_body<HP, D, NW, NR, true, uint16_t>(q, k, w, S, Skv, B, H, ratio, topk, row_begin,
-                                                   row_end, R, cap, out_idx, out_score, sup);
+                                                   row_end, R, cap, out_idx, out_score, sup,
+                                                   (int)blockIdx.x);
 }
 
 namespace {
@@ -484,6 +506,42 @@ template <int HP, int D>
 static hipError_t launch_hd(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,
                             hipStream_t st2) {
   return p.waves == 4 ? launch_w<HP, D, 4, 1>(a, p, st, st2) : launch_w<HP, D, 8, 1>(a, p, st, st2);
+}
+
+template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
+static hipError_t launch_packed_t(const PackedTopkArgs& a, const PackedSeqs& seqs,
+                                  const ScoreSelectPlan& p, hipStream_t st) {
+  const void* kern = (const void*)score_select_packed_kernel<HP, D, NW, NR, DENSE, IdxT>;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)p.lds_bytes);
+  if (e != hipSuccess) return e;
+  const int blocks = seqs.blk_begin[seqs.n];
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((score_select_packed_kernel<HP, D, NW, NR, DENSE, IdxT>), dim3((unsigned)blocks),
+                     dim3(NW * 64), p.lds_bytes, st, a.q, a.k, a.w, a.H, a.ratio, a.topk,
+                     p.rows_per_block, p.cap, a.out_idx, a.out_score, seqs);
+  return hipGetLastError();
+}
+
+template <int HP, int D, int NW>
+static hipError_t launch_packed_w(const PackedTopkArgs& a, const PackedSeqs& seqs,
+                                  const ScoreSelectPlan& p, hipStream_t st) {
+  if (p.dense) return launch_packed_t<HP, D, NW, 1, true, uint16_t>(a, seqs, p, st);
+  return p.idx_bytes == 2 ? launch_packed_t<HP, D, NW, 1, false, uint16_t>(a, seqs, p, st)
+                          : launch_packed_t<HP, D, NW, 1, false, uint32_t>(a, seqs, p, st);
+}
+
+hipError_t launch_score_topk_packed(const PackedTopkArgs& a, const PackedSeqs& seqs,
+                                    const ScoreSelectPlan& p, hipStream_t st) {
+  const int HP = a.H <= 32 ? 32 : 64;
+#define DSAI_CASE(hp, d)                                                        \
+  if (HP == hp && a.D == d)                                                     \
+    return p.waves == 4 ? launch_packed_w<hp, d, 4>(a, seqs, p, st)             \
+                        : launch_packed_w<hp, d, 8>(a, seqs, p, st);
+  DSAI_CASE(32, 32) DSAI_CASE(32, 64) DSAI_CASE(32, 128)
+  DSAI_CASE(64, 32) DSAI_CASE(64, 64) DSAI_CASE(64, 128)
+#undef DSAI_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_score_topk(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hipStream_t st,

@@ -89,6 +89,55 @@ def test_packed_matches_oracle(dsai, name, cu_q, cu_k, H, D, r, topk, integer, c
         assert np.array_equal(ss.cpu().numpy()[0].view(np.uint32), gs[q0:q1].view(np.uint32))
 
 
+def _ragged_offsets(rng, nseq, max_q, max_k):
+    """Cumulative offsets of nseq sequences with 0..max_q rows and 0..max_k
+    keys each (some sequences empty on one side or both)."""
+    lq = rng.integers(0, max_q + 1, nseq)
+    lk = rng.integers(0, max_k + 1, nseq)
+    lq[rng.random(nseq) < 0.1] = 0
+    lk[rng.random(nseq) < 0.1] = 0
+    return (np.concatenate([[0], np.cumsum(lq)]).astype(np.int64),
+            np.concatenate([[0], np.cumsum(lk)]).astype(np.int64))
+
+
+PACKED_MANY = [
+    # name, nseq, max rows, max keys, H, D, ratio, topk, extra long sequence
+    ("many_256", 256, 40, 60, 4, 32, 1, 16, 0),
+    ("many_c2", 150, 50, 40, 4, 64, 2, 12, 0),
+    # one sequence past the dense store: its launch uses the filter store
+    # for every sequence it holds
+    ("long_and_short", 70, 30, 50, 4, 32, 1, 16, 6000),
+]
+
+
+@pytest.mark.parametrize("name,nseq,max_q,max_k,H,D,r,topk,extra", PACKED_MANY)
+def test_packed_many_sequences(dsai, name, nseq, max_q, max_k, H, D, r, topk, extra):
+    """Hundreds of ragged sequences (several launches of up to 64
+    sequences, taken longest first), integer inputs: bit-exact against the
+    packed oracle, order and ties included."""
+    log(f"[gpu] packed many {name}")
+    rng = np.random.default_rng(len(name) + nseq)
+    cu_q, cu_k = _ragged_offsets(rng, nseq, max_q, max_k)
+    if extra:
+        at = nseq // 3  # the long sequence sits in the middle of the batch
+        lq, lk = np.diff(cu_q), np.diff(cu_k)
+        lq[at], lk[at] = extra, extra
+        cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+        cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    qb, kb, w = packed_inputs(name, cu_q, cu_k, H, D, r, topk, True, seed=nseq)
+    ix = dsai.Indexer(heads=H, dim=D)
+    gi, gs = ix.score_topk_packed(bf16(qb), bf16(kb), torch.from_numpy(w).cuda(), cu_q, cu_k, r,
+                                  topk)
+    torch.cuda.synchronize()
+    oi, ov = oracle.score_topk_packed(SY.bf16_bits_to_f32(qb).astype(np.float64),
+                                      SY.bf16_bits_to_f32(kb).astype(np.float64),
+                                      w.astype(np.float64), cu_q, cu_k, r, topk)
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
+    bad = np.nonzero((gi != oi).any(axis=1))[0]
+    assert bad.size == 0, f"{name}: {bad.size} rows differ, first {bad[:5]}"
+    assert np.array_equal(gs.astype(np.float64), ov.astype(np.float32).astype(np.float64))
+
+
 def test_packed_backward_exact(dsai):
     """dsai_indexer_backward_packed on integer inputs (every GPU step exact):
     bit-identical to the fp64 packed oracle rounded to bf16, and to one
