@@ -644,6 +644,17 @@ def main():
     pk_ms = timed(lambda: pk_ix.score_topk_packed(q[:, 0], k[:, 0], w[:, 0], cu, cu,
                                                   pcase.compress_ratio, pcase.topk,
                                                   out_idx=pk_i, out_score=pk_s), reps)
+    # the same rows as one batched call (B = 4 samples of 1024 rows: the
+    # single-launch form of the packed problem)
+    L = pcase.S // nseq
+    q4 = q[:, 0].reshape(nseq, L, pcase.H, pcase.D).transpose(0, 1).contiguous()
+    k4 = k[:, 0].reshape(nseq, L, pcase.D).transpose(0, 1).contiguous()
+    w4 = w[:, 0].reshape(nseq, L, pcase.H).transpose(0, 1).contiguous()
+    b4_i = pk_i.view(nseq, L, pcase.topk)
+    b4_s = pk_s.view(nseq, L, pcase.topk)
+    b4_ms = timed(lambda: pk_ix.score_topk(q4, k4, w4, pcase.compress_ratio, pcase.topk,
+                                           out_idx=b4_i, out_score=b4_s), reps)
+    del q4, k4, w4
     t = np.arange(pcase.S // nseq, dtype=np.int64)
     pk_flops = 2.0 * pcase.H * pcase.D * nseq * float(
         np.minimum(pcase.S // nseq, (t + 1) // pcase.compress_ratio).sum())
@@ -661,6 +672,8 @@ def main():
         "score_at_indices_TFLOPs": at_flops / (at_ms * 1e-3) / 1e12,
         "packed_4x1024_ms": pk_ms,
         "packed_4x1024_TFLOPs": pk_flops / (pk_ms * 1e-3) / 1e12,
+        "batched_4x1024_ms": b4_ms,
+        "packed_vs_batched_rate": b4_ms / pk_ms,
         "backward_ms": bw_ms,
         "backward_TFLOPs": 6.0 * pcase.H * pcase.D * bw_entries / (bw_ms * 1e-3) / 1e12,
         "backward_key_adds_G_per_s": pcase.D * bw_entries / (bw_ms * 1e-3) / 1e9,

@@ -211,26 +211,37 @@ def test_chunked_launches_match_single_launch(dsai):
 
 
 def test_chunk_streams_join_the_callers_stream(dsai):
-    """Chunked launches run on the handle's two streams: work the caller
-    enqueues on its own stream right after the call (no host sync) must see
-    every chunk's output, and a non-default caller stream must work too."""
+    """Scores at supplied indices in chunks run on the handle's two streams:
+    work the caller enqueues on its own stream right after the call (no host
+    sync) must see every chunk's output.  The selection (one launch whatever
+    chunk_rows is) on the same non-default caller stream too."""
     case = MEDIUM[0]
     inp = SY.indexer_inputs(case)
     q, k = to_gpu_bf16(inp["q_bits"]), to_gpu_bf16(inp["k_bits"])
     w = torch.from_numpy(inp["w"]).cuda()
     ref = run_gpu(dsai, case, inp, chunk_rows=0)
+    sup = torch.from_numpy(ref[0]).cuda()
     ix = dsai.Indexer(heads=case.H, dim=case.D, chunk_rows=50)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
+    shape = (case.B, case.S, case.topk)
     with torch.cuda.stream(side):
         for _ in range(3):   # the same outputs rewritten, each read right after
-            oi = torch.full((case.B, case.S, case.topk), -7, dtype=torch.int32, device="cuda")
-            os_ = torch.zeros((case.B, case.S, case.topk), dtype=torch.float32, device="cuda")
+            oi = torch.full(shape, -7, dtype=torch.int32, device="cuda")
+            os_ = torch.zeros(shape, dtype=torch.float32, device="cuda")
             ix.score_topk(q, k, w, case.compress_ratio, case.topk, out_idx=oi, out_score=os_)
             ci, cs = oi.clone(), os_.clone()   # enqueued on `side` after the call
+            ai = torch.full(shape, -7, dtype=torch.int32, device="cuda")
+            as_ = torch.zeros(shape, dtype=torch.float32, device="cuda")
+            ix.score_topk(q, k, w, case.compress_ratio, case.topk, topk_indices=sup, out_idx=ai,
+                          out_score=as_)
+            di, ds = ai.clone(), as_.clone()
     torch.cuda.synchronize()
     assert np.array_equal(ci.cpu().numpy(), ref[0])
     assert np.array_equal(cs.cpu().numpy().view(np.uint32), ref[1].view(np.uint32))
+    # the selection's own entries rescored: the same indices and score bits
+    assert np.array_equal(di.cpu().numpy(), ref[0])
+    assert np.array_equal(ds.cpu().numpy().view(np.uint32), ref[1].view(np.uint32))
 
 
 def test_deterministic_and_every_slot_written(dsai):
