@@ -240,6 +240,15 @@ struct TileScorer {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
 
+  // combine() of two tiles at once: lanes 0-31 get tile a's scores (key
+  // l), lanes 32-63 tile b's (key l - 32), each with the operands in the
+  // order combine() adds them (identical bits).
+  static __device__ __forceinline__ float combine2(float half_a, float half_b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(half_a), __float_as_uint(half_b),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+
   // Full score of key `lane % 32` of the staged tile (in lanes l and l + 32).
   __device__ __forceinline__ float score(const lds_char* tile) const {
     Acc acc;

@@ -172,24 +172,9 @@ __device__ __forceinline__ void score_select_body(
     for (int rr = 0; rr < NR; ++rr) {
       const float x = Scorer::combine(part[rr]) + 0.f;  // -0 -> +0
       const bool vis = key < (uint32_t)n_t[rr];
-      if constexpr (DENSE) {
-        rs[rr].key[key] = __float_as_uint(x);  // lanes l and l + 32 store the same value
-        smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
-        smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
-      } else {
-        const uint32_t u = ord_key_nz(x);  // x + 0 is never -0
-        // (non-short-circuit: no branch)
-        wave_append_all(rs[rr], count[rr], (lane < 32) & vis & (u > tau[rr]), u, key);
-      }
-    }
-    if constexpr (!DENSE) {
-      // Ask for a cut once a store has fewer than kCutRequest free slots
-      // (read by every wavefront after a later barrier): every lane writes
-      // the wavefront's own byte, so no branch and no clearing.
-      bool need = false;
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - kCutRequest);
-      ((DSAI_LDS uint8_t*)&cut_req[it_rec % 3])[wave] = need ? 1u : 0u;
+      rs[rr].key[key] = __float_as_uint(x);  // lanes l and l + 32 store the same value
+      smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
+      smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
     }
   };
   if (ntiles > 0) {
@@ -236,35 +221,65 @@ __device__ __forceinline__ void score_select_body(
       finish(ntiles - 1);
     } else {
       // Filter store: the same pipeline, run from tile s until a wavefront
-      // of the block asks for a cut.  The cut is a call and needs registers
-      // the pipeline holds, so it never runs inside the loop: every
-      // wavefront sees the request after the same barrier, drains (records
-      // the last two tiles), and after one more barrier cuts its store if
-      // it is past half its slack, or nearly full; then the pipeline
-      // restarts at the next tile, whose tile and the one after it are
-      // already staged in LDS.  A request waits at most four tiles, which
-      // kCutRequest leaves room for: a store holds at most cap - 64 entries
-      // before any tile is recorded, the room wave_append_all needs.
-      // Requests rotate over three words: the word step `it` reads was
-      // written by finish(it - 3) (before this barrier) and is written
-      // again by finish(it) (after the next); words of a finished run are
-      // not read.  The steady-state steps have no branch, so the compiler
-      // interleaves the record of tile it - 2 with tile it's products.
-      int s = 0;  // first tile of the current run
+      // of the block asks for a cut.  Tiles are recorded two at a time, in
+      // the odd step of each pair: one cross-half exchange leaves tile
+      // it - 2's scores in lanes 0-31 and tile it - 1's in lanes 32-63, so
+      // every lane of the record carries a key.  The cut is a call and
+      // needs registers the pipeline holds, so it never runs inside the
+      // loop: every wavefront sees the request after the same barrier,
+      // drains (records the last two tiles), and after one more barrier
+      // cuts its store if it is past half its slack, or nearly full; then
+      // the pipeline restarts at the next tile, whose tile and the one
+      // after it are already staged in LDS.  After the record that raises
+      // a request at most two more records (128 keys) run before the cut,
+      // which kCutRequest leaves room for: a store holds at most cap - 64
+      // entries before any record, the room wave_append_all needs.
+      // Requests rotate over three words: the even step of tile `it` reads
+      // the word of the record of tiles it - 4 and it - 3 (written in the
+      // previous step, before this barrier); that word is written again
+      // three records later; words of a finished run are not read.  The
+      // steady-state steps have no branch, so the compiler interleaves the
+      // record with the tile's products.
+      int s = 0;  // first tile of the current run (always even)
+      float part_b[NR];  // reduce_half of the odd tile of the pair awaiting its record
+      auto record2 = [&](int it_a) {  // tiles it_a (in part) and it_a + 1 (in part_b)
+        const uint32_t key = (uint32_t)(it_a * G::kTileKeys + lane);
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) {
+          const float x = Scorer::combine2(part[rr], part_b[rr]) + 0.f;  // -0 -> +0
+          const uint32_t u = ord_key_nz(x);  // x + 0 is never -0
+          // (non-short-circuit: no branch)
+          wave_append_all(rs[rr], count[rr], (key < (uint32_t)n_t[rr]) & (u > tau[rr]), u, key);
+        }
+        // Ask for a cut once a store has fewer than kCutRequest free slots:
+        // every lane writes the wavefront's own byte, so no branch and no
+        // clearing.
+        bool need = false;
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - kCutRequest);
+        ((DSAI_LDS uint8_t*)&cut_req[(it_a >> 1) % 3])[wave] = need ? 1u : 0u;
+      };
       // One fragment buffer, refilled with tile it + 1 as tile it's products
-      // are issued (registers for the store's bookkeeping).
+      // are issued (registers for the store's bookkeeping).  Even steps
+      // reduce the previous (odd) tile into part_b and read the request
+      // word; odd steps record the previous pair and reduce the even tile
+      // into part.
       auto step = [&](int it, int par, Frag& fcur, Acc& cur, const Acc& old, bool fin,
                       bool red) -> bool {
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        const uint64_t req = cut_req[it % 3];  // used at the end of the step
-        if (fin) finish(it - 2);
+        uint64_t req = 0;
+        if (par == 0) req = cut_req[((it >> 1) + 1) % 3];  // used at the end of the step
+        if (fin) record2(it - 3);
         ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
         sc.mma_fetch(fcur, buf(par ^ 1), cur);
         if (red) {
 #pragma unroll
-          for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
+          for (int rr = 0; rr < NR; ++rr) {
+            if (par == 0) part_b[rr] = sc.reduce_half(old, rr);
+            else part[rr] = sc.reduce_half(old, rr);
+          }
         }
         // Issue order: each matrix-core product followed by a few vector
         // instructions (the record, the reduction), so that a wavefront
@@ -277,7 +292,7 @@ __device__ __forceinline__ void score_select_body(
         }
         __builtin_amdgcn_sched_barrier(0);
         // (uniform and with no branch: `&`, not `&&`)
-        return (it >= s + 3) & (uniform((uint32_t)req | (uint32_t)(req >> 32)) != 0u);
+        return (it >= s + 4) & (uniform((uint32_t)req | (uint32_t)(req >> 32)) != 0u);
       };
       const uint32_t cut_at = min((uint32_t)(topk + cap) / 2u, (uint32_t)(cap - kCutRequest - 32));
       for (;;) {
@@ -293,16 +308,15 @@ __device__ __forceinline__ void score_select_body(
         step(s + 1, 1, f0, acc1, acc0, false, true);
         int it = s + 2;
         while (it < ntiles) {
-          bool want = step(it, 0, f0, acc0, acc1, true, true);
-          want |= step(it + 1, 1, f0, acc1, acc0, true, true);
+          const bool want = step(it, 0, f0, acc0, acc1, false, true);
+          step(it + 1, 1, f0, acc1, acc0, true, true);
           it += 2;
           if (want) break;
         }
         // drain: record tiles it - 2 (reduced in the last step) and it - 1
-        finish(it - 2);
 #pragma unroll
-        for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(acc1, rr);
-        finish(it - 1);
+        for (int rr = 0; rr < NR; ++rr) part_b[rr] = sc.reduce_half(acc1, rr);
+        record2(it - 2);
         if (it >= ntiles) break;
         __syncthreads();  // every wavefront drained; tiles it and it + 1 are staged
 #pragma unroll
