@@ -164,17 +164,47 @@ __device__ __forceinline__ void score_select_body(
   // buffers' LDS addresses fold into the instructions' offsets.
   auto buf = [&](int p) { return smem + p * L::kTileBytes; };
   Acc acc0, acc1;
-  Frag f0, f1;
-  float part[NR];  // reduce_half of the tile awaiting finish()
-  auto finish = [&](int it_rec) {
-    const uint32_t key = (uint32_t)(it_rec * G::kTileKeys + (lane & 31));
+  Frag f0;  // one fragment buffer, refilled as each tile's products are issued
+  float part[NR];    // reduce_half of the even tile of the pair awaiting its record
+  float part_b[NR];  // ... and of its odd tile
+  // Tiles are recorded two at a time: one cross-half exchange leaves tile
+  // it_a's scores in lanes 0-31 and tile it_a + 1's in lanes 32-63, so every
+  // lane of the record carries its own key (it_a * 32 + lane).
+  // dense: the score goes to its key's slot (slots past the row's keys are
+  // written but never read); filter: appended if it beats the threshold.
+  auto record2 = [&](int it_a) {
+    const uint32_t key = (uint32_t)(it_a * G::kTileKeys + lane);
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
-      const float x = Scorer::combine(part[rr]) + 0.f;  // -0 -> +0
+      const float x = Scorer::combine2(part[rr], part_b[rr]) + 0.f;  // -0 -> +0
       const bool vis = key < (uint32_t)n_t[rr];
-      rs[rr].key[key] = __float_as_uint(x);  // lanes l and l + 32 store the same value
-      smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
-      smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
+      if constexpr (DENSE) {
+        rs[rr].key[key] = __float_as_uint(x);
+        smin[rr] = fminf(smin[rr], vis ? x : __builtin_inff());
+        smax[rr] = fmaxf(smax[rr], vis ? x : -__builtin_inff());
+      } else {
+        const uint32_t u = ord_key_nz(x);  // x + 0 is never -0
+        // (non-short-circuit: no branch)
+        wave_append_all(rs[rr], count[rr], vis & (u > tau[rr]), u, key);
+      }
+    }
+    if constexpr (!DENSE) {
+      // Ask for a cut once a store has fewer than kCutRequest free slots:
+      // every lane writes the wavefront's own byte, so no branch and no
+      // clearing.
+      bool need = false;
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - kCutRequest);
+      ((DSAI_LDS uint8_t*)&cut_req[(it_a >> 1) % 3])[wave] = need ? 1u : 0u;
+    }
+  };
+  // Head reduction of a tile's products: the even tile of a pair into part,
+  // the odd one into part_b.
+  auto reduce_into = [&](int par, const Acc& a) {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      if (par == 0) part[rr] = sc.reduce_half(a, rr);
+      else part_b[rr] = sc.reduce_half(a, rr);
     }
   };
   if (ntiles > 0) {
@@ -183,42 +213,48 @@ __device__ __forceinline__ void score_select_body(
     ld.load((uint32_t)G::kTileKeys);
     ld.store(buf(1));
     if constexpr (DENSE) {
-      auto step = [&](int it, int par, Frag& fcur, Frag& fnext, Acc& cur, const Acc& old,
-                      bool fin, bool red) {
+      // Step `it` (parity par): tile it's products (the fragment registers
+      // refilled with tile it + 1 as they are issued); the reduction of tile
+      // it - 1; in odd steps the record of tiles it - 3 and it - 2.
+      auto step = [&](int it, int par, Acc& cur, const Acc& old, bool fin, bool red) {
         __syncthreads();
         // Scheduling fences: the compiler may not hoist the next iteration's
         // products above this barrier or sink this one's below the next,
         // which would put a reduction right behind the products it reads.
         __builtin_amdgcn_sched_barrier(0);
-        sc.fetch(buf(par ^ 1), fnext);
-        if (fin) finish(it - 2);
+        if (fin) record2(it - 3);
         ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
-        sc.mma(fcur, cur);
-        if (red) {
-#pragma unroll
-          for (int rr = 0; rr < NR; ++rr) part[rr] = sc.reduce_half(old, rr);
-        }
+        sc.mma_fetch(f0, buf(par ^ 1), cur);
+        if (red) reduce_into(par ^ 1, old);
         __builtin_amdgcn_sched_barrier(0);
       };
       ld.load((uint32_t)(2 * G::kTileKeys));
       __syncthreads();
       sc.fetch(buf(0), f0);
-      step(0, 0, f0, f1, acc0, acc1, false, false);
-      int it = 1;
-      if (ntiles > 1) {
-        step(1, 1, f1, f0, acc1, acc0, false, true);
-        for (it = 2; it + 1 < ntiles; it += 2) {
-          step(it, 0, f0, f1, acc0, acc1, true, true);
-          step(it + 1, 1, f1, f0, acc1, acc0, true, true);
+      step(0, 0, acc0, acc1, false, false);
+      if (ntiles == 1) {
+        reduce_into(0, acc0);
+        reduce_into(1, acc0);  // the pair's odd half: keys past the row, never read
+        record2(0);
+      } else {
+        step(1, 1, acc1, acc0, false, true);
+        int it = 2;
+        for (; it + 1 < ntiles; it += 2) {
+          step(it, 0, acc0, acc1, false, true);
+          step(it + 1, 1, acc1, acc0, true, true);
         }
-        if (it < ntiles) step(it, 0, f0, f1, acc0, acc1, true, true);
-        finish(ntiles - 2);
+        if (it < ntiles) {  // an odd number of tiles: tile it is the last
+          step(it, 0, acc0, acc1, false, true);
+          record2(it - 2);
+          reduce_into(0, acc0);
+          reduce_into(1, acc0);  // (slots past the last tile, within the store)
+          record2(it);
+        } else {
+          reduce_into(1, acc1);
+          record2(it - 2);
+        }
       }
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-        part[rr] = sc.reduce_half(((ntiles - 1) & 1) ? acc1 : acc0, rr);
-      finish(ntiles - 1);
     } else {
       // Filter store: the same pipeline, run from tile s until a wavefront
       // of the block asks for a cut.  Tiles are recorded two at a time, in
@@ -241,24 +277,6 @@ __device__ __forceinline__ void score_select_body(
       // steady-state steps have no branch, so the compiler interleaves the
       // record with the tile's products.
       int s = 0;  // first tile of the current run (always even)
-      float part_b[NR];  // reduce_half of the odd tile of the pair awaiting its record
-      auto record2 = [&](int it_a) {  // tiles it_a (in part) and it_a + 1 (in part_b)
-        const uint32_t key = (uint32_t)(it_a * G::kTileKeys + lane);
-#pragma unroll
-        for (int rr = 0; rr < NR; ++rr) {
-          const float x = Scorer::combine2(part[rr], part_b[rr]) + 0.f;  // -0 -> +0
-          const uint32_t u = ord_key_nz(x);  // x + 0 is never -0
-          // (non-short-circuit: no branch)
-          wave_append_all(rs[rr], count[rr], (key < (uint32_t)n_t[rr]) & (u > tau[rr]), u, key);
-        }
-        // Ask for a cut once a store has fewer than kCutRequest free slots:
-        // every lane writes the wavefront's own byte, so no branch and no
-        // clearing.
-        bool need = false;
-#pragma unroll
-        for (int rr = 0; rr < NR; ++rr) need |= count[rr] > (uint32_t)(cap - kCutRequest);
-        ((DSAI_LDS uint8_t*)&cut_req[(it_a >> 1) % 3])[wave] = need ? 1u : 0u;
-      };
       // One fragment buffer, refilled with tile it + 1 as tile it's products
       // are issued (registers for the store's bookkeeping).  Even steps
       // reduce the previous (odd) tile into part_b and read the request
@@ -274,13 +292,7 @@ __device__ __forceinline__ void score_select_body(
         ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
         sc.mma_fetch(fcur, buf(par ^ 1), cur);
-        if (red) {
-#pragma unroll
-          for (int rr = 0; rr < NR; ++rr) {
-            if (par == 0) part_b[rr] = sc.reduce_half(old, rr);
-            else part[rr] = sc.reduce_half(old, rr);
-          }
-        }
+        if (red) reduce_into(par ^ 1, old);
         // Issue order: each matrix-core product followed by a few vector
         // instructions (the record, the reduction), so that a wavefront
         // whose products wait for the matrix core still has vector work
@@ -314,8 +326,7 @@ __device__ __forceinline__ void score_select_body(
           if (want) break;
         }
         // drain: record tiles it - 2 (reduced in the last step) and it - 1
-#pragma unroll
-        for (int rr = 0; rr < NR; ++rr) part_b[rr] = sc.reduce_half(acc1, rr);
+        reduce_into(1, acc1);
         record2(it - 2);
         if (it >= ntiles) break;
         __syncthreads();  // every wavefront drained; tiles it and it + 1 are staged
