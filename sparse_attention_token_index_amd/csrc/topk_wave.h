@@ -109,6 +109,39 @@ __device__ __forceinline__ void hist_add(lds_u32* hist, uint32_t bin) {
   __hip_atomic_fetch_add(&hist[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
+// hist_add for lanes where `in` holds.  The branch is deliberate: behind it
+// the compiler waits for each atomic before issuing the next, and that is
+// faster here than straight-line atomics going out back to back (the keys
+// of a store crowd into few bins; measured: a cut took 45K cycles with
+// back-to-back atomics against 27K with this form).
+__device__ __forceinline__ void hist_add_if(lds_u32* hist, uint32_t bin, bool in) {
+  if (in) __hip_atomic_fetch_add(&hist[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// Entry i of a store of n >= 1 entries, or entry 0 for i past the end (a
+// load with no branch; the caller ignores those lanes).
+__device__ __forceinline__ uint32_t load_clamped(const lds_u32* key, uint32_t i, uint32_t n) {
+  return key[i < n ? i : 0u];
+}
+
+// One 64-entry chunk of an in-place compaction, with no branch: the kept
+// lanes go to wpos.. in lane order, every other lane into the slots right
+// after them (below wpos + 64: entries this pass has already read, since a
+// chunk keeps at most what it read; the caller runs no chunk that starts
+// past the store's entries, so those slots lie below the entry count
+// rounded up to 64, within a store whose capacity is a multiple of 64).
+template <typename IdxT>
+__device__ __forceinline__ void compact_put(const RowStore<IdxT>& rs, uint32_t& wpos, bool keep,
+                                            uint32_t u, uint32_t x) {
+  const uint64_t mk = ballot(keep);
+  const uint32_t below = lanes_below(mk);
+  const uint32_t nk = (uint32_t)__popcll(mk);
+  const uint32_t p = wpos + (keep ? below : nk + (uint32_t)lane_id() - below);
+  rs.key[p] = u;
+  rs.idx[p] = (IdxT)x;
+  wpos = uniform(wpos + nk);
+}
+
 __device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b) {
   return a > 0xFFFFFFFFu - b ? 0xFFFFFFFFu : a + b;
 }
@@ -128,14 +161,13 @@ __device__ __forceinline__ uint2 select_in_range(const lds_u32* key, uint32_t n,
       uint32_t u[kSelBatch];
 #pragma unroll
       for (int j = 0; j < kSelBatch; ++j) {
-        const uint32_t i = base + j * kWave + lane;
-        u[j] = i < n ? key[i] : 0u;
+        u[j] = load_clamped(key, base + j * kWave + lane, n);
         if constexpr (FLOAT_KEYS) u[j] = ord_key(__uint_as_float(u[j]));
       }
 #pragma unroll
       for (int j = 0; j < kSelBatch; ++j) {
         const uint32_t i = base + j * kWave + lane;
-        if (i < n && u[j] >= lo && u[j] <= hi) hist_add(hist, (u[j] - lo) >> shift);
+        hist_add_if(hist, (u[j] - lo) >> shift, (i < n) & (u[j] >= lo) & (u[j] <= hi));
       }
     }
     wave_lds_sync();
@@ -164,17 +196,11 @@ __device__ __noinline__ uint2 wave_radix_select(lds_u32* key, lds_u32* hist, lds
   for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
     uint32_t u[kSelBatch];
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      u[j] = i < n ? key[i] : 0u;
-    }
+    for (int j = 0; j < kSelBatch; ++j) u[j] = load_clamped(key, base + j * kWave + lane, n);
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      if (i < n) {
-        mn = min(mn, u[j]);
-        mx = max(mx, u[j]);
-      }
+    for (int j = 0; j < kSelBatch; ++j) {  // lanes past n hold entry 0: no effect
+      mn = min(mn, u[j]);
+      mx = max(mx, u[j]);
     }
   }
   mn = uniform(wave_min(mn));
@@ -187,15 +213,10 @@ __device__ __noinline__ uint2 wave_radix_select(lds_u32* key, lds_u32* hist, lds
   for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
     uint32_t u[kSelBatch];
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      u[j] = i < n ? key[i] : 0u;
-    }
+    for (int j = 0; j < kSelBatch; ++j) u[j] = load_clamped(key, base + j * kWave + lane, n);
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      if (i < n) hist_add(hist, (u[j] - mn) >> shift);
-    }
+    for (int j = 0; j < kSelBatch; ++j)
+      hist_add_if(hist, (u[j] - mn) >> shift, base + j * kWave + lane < n);
   }
   wave_lds_sync();
   const uint2 fb = find_bin(hist, k);
@@ -235,23 +256,19 @@ __device__ __noinline__ uint32_t wave_compact(RowStore<IdxT> rs, uint32_t n, uin
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
       const uint32_t i = base + j * kWave + lane;
-      u[j] = i < n ? rs.key[i] : 0u;
-      x[j] = i < n ? (uint32_t)rs.idx[i] : 0u;
+      const uint32_t ii = i < n ? i : 0u;
+      u[j] = rs.key[ii];
+      x[j] = (uint32_t)rs.idx[ii];
     }
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
+      if (base + j * kWave >= n) break;  // (uniform) no chunk past the entries
       const uint32_t i = base + j * kWave + lane;
       const bool in = i < n;
-      const bool eq = in && (u[j] == v);
+      const bool eq = in & (u[j] == v);
       const uint64_t meq = ballot(eq);
-      const bool keep = (in && u[j] > v) || (eq && (eq_seen + lanes_below(meq)) < take_eq);
-      const uint64_t mk = ballot(keep);
-      if (keep) {
-        const uint32_t p = wpos + lanes_below(mk);
-        rs.key[p] = u[j];
-        rs.idx[p] = (IdxT)x[j];
-      }
-      wpos = uniform(wpos + (uint32_t)__popcll(mk));
+      const bool keep = (in & (u[j] > v)) | (eq & ((eq_seen + lanes_below(meq)) < take_eq));
+      compact_put(rs, wpos, keep, u[j], x[j]);
       eq_seen = uniform(eq_seen + (uint32_t)__popcll(meq));
     }
   }
@@ -270,20 +287,15 @@ __device__ __noinline__ uint32_t wave_compact_ge(RowStore<IdxT> rs, uint32_t n, 
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
       const uint32_t i = base + j * kWave + lane;
-      u[j] = i < n ? rs.key[i] : 0u;
-      x[j] = i < n ? (uint32_t)rs.idx[i] : 0u;
+      const uint32_t ii = i < n ? i : 0u;
+      u[j] = rs.key[ii];
+      x[j] = (uint32_t)rs.idx[ii];
     }
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
+      if (base + j * kWave >= n) break;  // (uniform) no chunk past the entries
       const uint32_t i = base + j * kWave + lane;
-      const bool keep = i < n && u[j] >= t;
-      const uint64_t mk = ballot(keep);
-      if (keep) {
-        const uint32_t p = wpos + lanes_below(mk);
-        rs.key[p] = u[j];
-        rs.idx[p] = (IdxT)x[j];
-      }
-      wpos = uniform(wpos + (uint32_t)__popcll(mk));
+      compact_put(rs, wpos, (i < n) & (u[j] >= t), u[j], x[j]);
     }
   }
   wave_lds_sync();
@@ -315,17 +327,11 @@ __device__ __noinline__ uint2 wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_t k
   for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
     uint32_t u[kSelBatch];
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      u[j] = i < n ? rs.key[i] : 0u;
-    }
+    for (int j = 0; j < kSelBatch; ++j) u[j] = load_clamped(rs.key, base + j * kWave + lane, n);
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {
-      const uint32_t i = base + j * kWave + lane;
-      if (i < n) {
-        mn = min(mn, u[j]);
-        mx = max(mx, u[j]);
-      }
+    for (int j = 0; j < kSelBatch; ++j) {  // lanes past n hold entry 0: no effect
+      mn = min(mn, u[j]);
+      mx = max(mx, u[j]);
     }
   }
   const uint32_t lo = uniform(wave_min(mn));
@@ -339,15 +345,10 @@ __device__ __noinline__ uint2 wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_t k
     for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
       uint32_t u[kSelBatch];
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) {
-        const uint32_t i = base + j * kWave + lane;
-        u[j] = i < n ? rs.key[i] : lo;
-      }
+      for (int j = 0; j < kSelBatch; ++j) u[j] = load_clamped(rs.key, base + j * kWave + lane, n);
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) {
-        const uint32_t i = base + j * kWave + lane;
-        if (i < n) hist_add(rs.hist, (u[j] - lo) >> shift);
-      }
+      for (int j = 0; j < kSelBatch; ++j)
+        hist_add_if(rs.hist, (u[j] - lo) >> shift, base + j * kWave + lane < n);
     }
     wave_lds_sync();
     const uint2 fb = find_bin(rs.hist, k);
@@ -363,14 +364,11 @@ __device__ __noinline__ uint2 wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_t k
       for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
         uint32_t u[kSelBatch];
 #pragma unroll
-        for (int j = 0; j < kSelBatch; ++j) {
-          const uint32_t i = base + j * kWave + lane;
-          u[j] = i < n ? rs.key[i] : 0u;
-        }
+        for (int j = 0; j < kSelBatch; ++j) u[j] = load_clamped(rs.key, base + j * kWave + lane, n);
 #pragma unroll
         for (int j = 0; j < kSelBatch; ++j) {
           const uint32_t i = base + j * kWave + lane;
-          if (i < n && u[j] >= t && u[j] <= bin_hi) hist_add(rs.hist, (u[j] - t) >> shift2);
+          hist_add_if(rs.hist, (u[j] - t) >> shift2, (i < n) & (u[j] >= t) & (u[j] <= bin_hi));
         }
       }
       wave_lds_sync();
