@@ -205,6 +205,48 @@ struct TileScorer {
     }
   }
 
+  // The last kSpare k-steps of each tile read a second set of fragment
+  // registers, one set per tile parity.
+  static constexpr int kSpare = KS >= 4 ? 2 : 1;
+  using Spare = bf16x8[kSpare];
+
+  // mma_fetch with the last kSpare k-steps double-buffered: the next tile's
+  // fragments for those k-steps go into `spare_next` before this tile's
+  // first product (its registers were last read by the previous tile's
+  // products), so the step's last LDS read is issued kSpare k-steps before
+  // its last product and has landed by the barrier that follows.
+  __device__ __forceinline__ void mma_fetch_spare(Frag& bf, const Spare& spare_cur, Spare& spare_next,
+                                                  const lds_char* next, Acc& acc) const {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[rr][m] = floatx16{};
+#pragma unroll
+    for (int s = 0; s < kSpare; ++s)
+      spare_next[s] = *reinterpret_cast<const DSAI_LDS bf16x8*>(next + frag_offset(KS - kSpare + s));
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const bf16x8 b = j < KS - kSpare ? bf[j] : spare_cur[j - (KS - kSpare)];
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[rr][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rr][m][j], b, acc[rr][m], 0, 0, 0);
+      if (j < KS - kSpare) bf[j] = *reinterpret_cast<const DSAI_LDS bf16x8*>(next + frag_offset(j));
+    }
+  }
+
+  // fetch() for mma_fetch_spare: k-steps before the last kSpare into bf,
+  // the last kSpare into spare.
+  __device__ __forceinline__ void fetch_spare(const lds_char* tile, Frag& bf, Spare& spare) const {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const bf16x8 v = *reinterpret_cast<const DSAI_LDS bf16x8*>(tile + frag_offset(j));
+      if (j < KS - kSpare) bf[j] = v;
+      else spare[j - (KS - kSpare)] = v;
+    }
+  }
+
   __device__ __forceinline__ void mma(const lds_char* tile, Acc& acc) const {
     Frag bf;
     fetch(tile, bf);

@@ -165,6 +165,7 @@ __device__ __forceinline__ void score_select_body(
   auto buf = [&](int p) { return smem + p * L::kTileBytes; };
   Acc acc0, acc1;
   Frag f0;  // one fragment buffer, refilled as each tile's products are issued
+  typename Scorer::Spare sp0, sp1;  // the last k-steps' fragments of even / odd tiles
   float part[NR];    // reduce_half of the even tile of the pair awaiting its record
   float part_b[NR];  // ... and of its odd tile
   // Tiles are recorded two at a time: one cross-half exchange leaves tile
@@ -216,7 +217,8 @@ __device__ __forceinline__ void score_select_body(
       // Step `it` (parity par): tile it's products (the fragment registers
       // refilled with tile it + 1 as they are issued); the reduction of tile
       // it - 1; in odd steps the record of tiles it - 3 and it - 2.
-      auto step = [&](int it, int par, Acc& cur, const Acc& old, bool fin, bool red) {
+      auto step = [&](int it, int par, Acc& cur, const Acc& old, const typename Scorer::Spare& spc,
+                      typename Scorer::Spare& spn, bool fin, bool red) {
         __syncthreads();
         // Scheduling fences: the compiler may not hoist the next iteration's
         // products above this barrier or sink this one's below the next,
@@ -225,27 +227,27 @@ __device__ __forceinline__ void score_select_body(
         if (fin) record2(it - 3);
         ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
-        sc.mma_fetch(f0, buf(par ^ 1), cur);
+        sc.mma_fetch_spare(f0, spc, spn, buf(par ^ 1), cur);
         if (red) reduce_into(par ^ 1, old);
         __builtin_amdgcn_sched_barrier(0);
       };
       ld.load((uint32_t)(2 * G::kTileKeys));
       __syncthreads();
-      sc.fetch(buf(0), f0);
-      step(0, 0, acc0, acc1, false, false);
+      sc.fetch_spare(buf(0), f0, sp0);
+      step(0, 0, acc0, acc1, sp0, sp1, false, false);
       if (ntiles == 1) {
         reduce_into(0, acc0);
         reduce_into(1, acc0);  // the pair's odd half: keys past the row, never read
         record2(0);
       } else {
-        step(1, 1, acc1, acc0, false, true);
+        step(1, 1, acc1, acc0, sp1, sp0, false, true);
         int it = 2;
         for (; it + 1 < ntiles; it += 2) {
-          step(it, 0, acc0, acc1, false, true);
-          step(it + 1, 1, acc1, acc0, true, true);
+          step(it, 0, acc0, acc1, sp0, sp1, false, true);
+          step(it + 1, 1, acc1, acc0, sp1, sp0, true, true);
         }
         if (it < ntiles) {  // an odd number of tiles: tile it is the last
-          step(it, 0, acc0, acc1, false, true);
+          step(it, 0, acc0, acc1, sp0, sp1, false, true);
           record2(it - 2);
           reduce_into(0, acc0);
           reduce_into(1, acc0);  // (slots past the last tile, within the store)
@@ -282,7 +284,8 @@ __device__ __forceinline__ void score_select_body(
       // reduce the previous (odd) tile into part_b and read the request
       // word; odd steps record the previous pair and reduce the even tile
       // into part.
-      auto step = [&](int it, int par, Frag& fcur, Acc& cur, const Acc& old, bool fin,
+      auto step = [&](int it, int par, Frag& fcur, Acc& cur, const Acc& old,
+                      const typename Scorer::Spare& spc, typename Scorer::Spare& spn, bool fin,
                       bool red) -> bool {
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
@@ -291,12 +294,14 @@ __device__ __forceinline__ void score_select_body(
         if (fin) record2(it - 3);
         ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
-        sc.mma_fetch(fcur, buf(par ^ 1), cur);
+        sc.mma_fetch_spare(fcur, spc, spn, buf(par ^ 1), cur);
         if (red) reduce_into(par ^ 1, old);
         // Issue order: each matrix-core product followed by a few vector
         // instructions (the record, the reduction), so that a wavefront
         // whose products wait for the matrix core still has vector work
         // queued behind them rather than in one block after the last.
+        // (Pinning the fragment reads into the first half as well measured
+        // slower: 28.9 against 28.2 ms.)
 #pragma unroll
         for (int g = 0; g < Scorer::KS * Scorer::MT * NR; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -310,18 +315,18 @@ __device__ __forceinline__ void score_select_body(
       for (;;) {
         ld.load((uint32_t)(s + 2) * G::kTileKeys);
         __syncthreads();
-        sc.fetch(buf(0), f0);  // s is even
+        sc.fetch_spare(buf(0), f0, sp0);  // s is even
         // Steps go in pairs (products in acc0, then acc1), so a run always
         // ends with its last products in acc1; a pair may run one tile past
         // the last (zero keys past the range, never recorded).  The first
         // pair of a run (nothing to record yet, no request to read) is
         // peeled, so the flags of the steady-state steps are constants.
-        step(s, 0, f0, acc0, acc1, false, false);
-        step(s + 1, 1, f0, acc1, acc0, false, true);
+        step(s, 0, f0, acc0, acc1, sp0, sp1, false, false);
+        step(s + 1, 1, f0, acc1, acc0, sp1, sp0, false, true);
         int it = s + 2;
         while (it < ntiles) {
-          const bool want = step(it, 0, f0, acc0, acc1, false, true);
-          step(it + 1, 1, f0, acc1, acc0, true, true);
+          const bool want = step(it, 0, f0, acc0, acc1, sp0, sp1, false, true);
+          step(it + 1, 1, f0, acc1, acc0, sp1, sp0, true, true);
           it += 2;
           if (want) break;
         }
