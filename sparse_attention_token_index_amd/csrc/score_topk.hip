@@ -102,6 +102,18 @@ __device__ __forceinline__ void score_select_body(
   const int n_max = min(Skv, (t_last + 1) / ratio);
   const int ntiles = (n_max + G::kTileKeys - 1) / G::kTileKeys;
 
+  // The first two key tiles' loads go out before the query rows' loads, so
+  // staging them waits for those two loads only, while the query rows are
+  // still in flight.
+  TileLoader<D, kThreads> ld, ld1;
+  const int64_t kbytes = ((int64_t)Skv * B - b) * D * 2;  // < 2^32 (checked on the host)
+  ld.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
+  ld1.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
+  if (ntiles > 0) {
+    ld.load(0u);
+    ld1.load((uint32_t)G::kTileKeys);
+  }
+
   Scorer sc;
   sc.init_offsets();
   RowStore<IdxT> rs[NR];
@@ -124,19 +136,17 @@ __device__ __forceinline__ void score_select_body(
 
   if (!DENSE && threadIdx.x < 3) cut_req[threadIdx.x] = 0u;  // published by the loop's first barrier
   uint32_t count[NR], tau[NR];       // filter store: entries, running threshold
+  uint32_t kmax[NR];                 // filter store: this lane's largest appended key
   // a bin-edge cut may keep a few entries past k; one that would keep more
   // than a quarter of the store's slack cuts exactly instead
   const uint32_t max_keep = (uint32_t)topk + (uint32_t)(cap - topk) / 4u;
   float smin[NR], smax[NR];           // dense store: this lane's extreme scores
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
-    count[rr] = tau[rr] = 0u;
+    count[rr] = tau[rr] = kmax[rr] = 0u;
     smin[rr] = __builtin_inff();
     smax[rr] = -__builtin_inff();
   }
-  TileLoader<D, kThreads> ld;
-  const int64_t kbytes = ((int64_t)Skv * B - b) * D * 2;  // < 2^32 (checked on the host)
-  ld.init(k + (int64_t)b * D, (uint32_t)(B * D), (uint32_t)(kbytes > 0 ? kbytes : 0));
 
   // Keys stream in 32-key tiles through two LDS buffers, one barrier per
   // tile.  Every wavefront runs all of the block's tiles, so the
@@ -186,7 +196,9 @@ __device__ __forceinline__ void score_select_body(
       } else {
         const uint32_t u = ord_key_nz(x);  // x + 0 is never -0
         // (non-short-circuit: no branch)
-        wave_append_all(rs[rr], count[rr], vis & (u > tau[rr]), u, key);
+        const bool pass = vis & (u > tau[rr]);
+        wave_append_all(rs[rr], count[rr], pass, u, key);
+        kmax[rr] = max(kmax[rr], pass ? u : 0u);  // running maximum of the store's keys
       }
     }
     if constexpr (!DENSE) {
@@ -209,10 +221,8 @@ __device__ __forceinline__ void score_select_body(
     }
   };
   if (ntiles > 0) {
-    ld.load(0u);
     ld.store(buf(0));
-    ld.load((uint32_t)G::kTileKeys);
-    ld.store(buf(1));
+    ld1.store(buf(1));
     if constexpr (DENSE) {
       // Step `it` (parity par): tile it's products (the fragment registers
       // refilled with tile it + 1 as they are issued); the reduction of tile
@@ -338,7 +348,9 @@ __device__ __forceinline__ void score_select_body(
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr) {
           if (count[rr] > cut_at) {
-            const uint2 c = wave_cut(rs[rr], count[rr], (uint32_t)topk, max_keep);
+            // after the first cut every key lies in [threshold, running max]
+            const uint2 c = wave_cut(rs[rr], count[rr], (uint32_t)topk, max_keep, tau[rr],
+                                     kmax[rr]);
             count[rr] = uniform(c.x);
             tau[rr] = uniform(c.y);
           }

@@ -316,22 +316,29 @@ __device__ __noinline__ uint32_t wave_compact_ge(RowStore<IdxT> rs, uint32_t n, 
 // runs instead (to exactly k, ties to the earlier entries), without a side
 // list: `side` may be memory other wavefronts are using.  Returns (entries
 // kept, new threshold), so the caller's threshold can stay in a register.
+// [lo_bound, hi_bound], when lo_bound is not 0, is a range known to hold
+// every key (the previous threshold and a running maximum), which saves the
+// min/max pass.
 constexpr uint32_t kCutRefine = 64;
 
 template <typename IdxT>
 __device__ __noinline__ uint2 wave_cut(RowStore<IdxT> rs, uint32_t n, uint32_t k,
-                                       uint32_t max_keep) {
+                                       uint32_t max_keep, uint32_t lo_bound, uint32_t hi_bound) {
   const int lane = lane_id();
   wave_lds_sync();
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
-    uint32_t u[kSelBatch];
+  uint32_t mn = lo_bound, mx = hi_bound;
+  if (lo_bound == 0u) {
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+    for (uint32_t base = 0; base < n; base += kWave * kSelBatch) {
+      uint32_t u[kSelBatch];
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) u[j] = load_clamped(rs.key, base + j * kWave + lane, n);
+      for (int j = 0; j < kSelBatch; ++j) u[j] = load_clamped(rs.key, base + j * kWave + lane, n);
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {  // lanes past n hold entry 0: no effect
-      mn = min(mn, u[j]);
-      mx = max(mx, u[j]);
+      for (int j = 0; j < kSelBatch; ++j) {  // lanes past n hold entry 0: no effect
+        mn = min(mn, u[j]);
+        mx = max(mx, u[j]);
+      }
     }
   }
   const uint32_t lo = uniform(wave_min(mn));
