@@ -337,8 +337,14 @@ def cpu_baseline(case, budget_s=20.0):
               f"{blocks.size} evenly spaced 1024-row blocks, shuffled), each against all its "
               f"visible keys in score order, fp64 NumPy, {spent:.1f} s; extrapolated to the "
               f"whole workload by visible (query, key) pairs")
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": case.B * case.S / step_s, "unit": "query tokens/s", "cores": int(cores),
-            "kind": "oracle", "sample": sample}
+            "kind": "oracle", "sample": sample, "cpu": cpu}
 
 
 # ---------------------------------------------------------------------------
@@ -441,14 +447,15 @@ def main():
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start, end = ev(), ev()
-    start.record()
-    for _ in range(args.steps):
+    marks = [ev() for _ in range(args.steps + 1)]   # one event between steps
+    marks[0].record()
+    for i in range(args.steps):
         step()
-    end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     # The fused kernel alone: the same step in index order skips only the
     # row sort, so its launches (one per step) time the kernel by itself.
     q, k, w, oi, osc = held
@@ -483,6 +490,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms_median": float(np.median(step_ms)),
+        "step_ms_min": float(np.min(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -614,6 +623,7 @@ def main():
         "expand_q65536_cold_frac_hbm": gbs(ebb, exb_ms) / PEAK_HBM_GBS,
         "decode_graph_ms": graph_ms,
         "decode_tokens_per_s": pc.Q / (graph_ms * 1e-3),
+        "select_tokens_per_s": pc.Q / (sel_ms * 1e-3),   # index_scores + topk_pools (+ ids)
     }
 
     # the cache write's k_norm (LayerNorm with a bias) over the 65536 cache rows
