@@ -64,6 +64,22 @@ extern "C" {
  * (zero-padded to 32 or 64 on the matrix cores), dim 32, 64 or 128. */
 #define DSAI_MAX_HEADS 64
 
+/* Rank the filter store's cuts keep (dsai_config.cuts); rows longer than
+ * the dense store only.  Either way the rows are the exact top k:
+ *   DSAI_CUTS_ESTIMATED  a cut after n of a row's N keys keeps k n / N plus
+ *                        six standard deviations of that count and 32
+ *                        (the share of the top k the first n keys hold when
+ *                        key order says nothing about the scores); a row
+ *                        that ends with fewer than k entries although it
+ *                        has k keys makes its block of rows run its keys
+ *                        again with cuts to k (about twice that block's
+ *                        time);
+ *   DSAI_CUTS_TOPK       every cut keeps k: for callers whose key order
+ *                        predicts the scores (e.g. scores that fall along
+ *                        the sequence), where estimated cuts would rerun. */
+#define DSAI_CUTS_ESTIMATED 0
+#define DSAI_CUTS_TOPK 1
+
 /* Order of the entries of a top-k row (dsai_config.order). */
 #define DSAI_ORDER_SCORE 0 /* score descending, lower index first among equal scores */
 #define DSAI_ORDER_INDEX 1 /* ascending index (the same set, no sorting pass)          */
@@ -82,6 +98,8 @@ typedef struct dsai_config {
   int order;      /* DSAI_ORDER_SCORE (default 0) or DSAI_ORDER_INDEX: order of
                      the entries of each dsai_score_topk / dsai_topk_pools /
                      dsai_select row (padding is always at the tail)         */
+  int cuts;       /* DSAI_CUTS_ESTIMATED (default 0) or DSAI_CUTS_TOPK: rank
+                     the filter store's cuts keep (same results)             */
 } dsai_config;
 
 typedef struct dsai_context* dsai_handle;
@@ -89,7 +107,8 @@ typedef struct dsai_context* dsai_handle;
 /* Validate `cfg` and create a handle in *out.  Refuses (DSAI_ERR_INVALID_ARG)
  * kpool outside 1..8, index_topk not a positive multiple of kpool,
  * index_topk / kpool > DSAI_MAX_TOPK, heads < 1, first_key < 0,
- * chunk_rows < 0, order not DSAI_ORDER_SCORE / DSAI_ORDER_INDEX;
+ * chunk_rows < 0, order not DSAI_ORDER_SCORE / DSAI_ORDER_INDEX, cuts not
+ * DSAI_CUTS_ESTIMATED / DSAI_CUTS_TOPK;
  * DSAI_ERR_UNSUPPORTED for heads > 64 or dim not 32/64/128;
  * DSAI_ERR_NULLPTR for a NULL cfg or out.  Makes no HIP call. */
 int dsai_create(const dsai_config* cfg, dsai_handle* out);

@@ -42,6 +42,8 @@ EXPORTS = (
 DSAI_OK = 0
 DSAI_ORDER_SCORE = 0  # rows by score descending, lower index first on ties
 DSAI_ORDER_INDEX = 1  # rows by ascending index (same set, no sorting pass)
+DSAI_CUTS_ESTIMATED = 0  # filter-store cuts keep an estimated rank (rerun if short)
+DSAI_CUTS_TOPK = 1  # filter-store cuts keep k (key order that predicts the scores)
 DSAI_MAX_KPOOL = 8
 DSAI_MAX_TOPK = 8192
 DSAI_STATIC_SCRATCH_BYTES = 16 << 20  # scores array of dsai_select_expand_static
@@ -56,7 +58,7 @@ class DsaiError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int), ("dim", ctypes.c_int), ("kpool", ctypes.c_int),
                 ("index_topk", ctypes.c_int), ("first_key", ctypes.c_int),
-                ("chunk_rows", ctypes.c_int), ("order", ctypes.c_int)]
+                ("chunk_rows", ctypes.c_int), ("order", ctypes.c_int), ("cuts", ctypes.c_int)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -153,9 +155,10 @@ class Indexer:
     """One configured handle of the selection library (dsai_create)."""
 
     def __init__(self, heads: int, dim: int, kpool: int = 1, index_topk: int = 1,
-                 first_key: int = 0, chunk_rows: int = 0, order: int = DSAI_ORDER_SCORE):
+                 first_key: int = 0, chunk_rows: int = 0, order: int = DSAI_ORDER_SCORE,
+                 cuts: int = DSAI_CUTS_ESTIMATED):
         self._lib = load_library()
-        self.cfg = _Config(heads, dim, kpool, index_topk, first_key, chunk_rows, order)
+        self.cfg = _Config(heads, dim, kpool, index_topk, first_key, chunk_rows, order, cuts)
         h = ctypes.c_void_p()
         st = self._lib.dsai_create(ctypes.byref(self.cfg), ctypes.byref(h))
         self._check(st, "dsai_create")

@@ -43,6 +43,7 @@ int check_config(const dsai_config& c) {
   if (select_k(c) > DSAI_MAX_TOPK) return DSAI_ERR_INVALID_ARG;
   if (c.first_key < 0 || c.chunk_rows < 0) return DSAI_ERR_INVALID_ARG;
   if (c.order != DSAI_ORDER_SCORE && c.order != DSAI_ORDER_INDEX) return DSAI_ERR_INVALID_ARG;
+  if (c.cuts != DSAI_CUTS_ESTIMATED && c.cuts != DSAI_CUTS_TOPK) return DSAI_ERR_INVALID_ARG;
   if (c.heads > DSAI_MAX_HEADS) return DSAI_ERR_UNSUPPORTED;
   if (c.dim != 32 && c.dim != 64 && c.dim != 128) return DSAI_ERR_UNSUPPORTED;
   return DSAI_OK;
@@ -267,6 +268,7 @@ static int score_topk_one(dsai_handle h, const void* index_q, const void* index_
   a.H = h->cfg.heads; a.D = h->cfg.dim; a.ratio = compress_ratio; a.topk = topk;
   a.chunk_rows = h->cfg.chunk_rows;
   a.sort = sort;
+  a.est_cuts = h->cfg.cuts == DSAI_CUTS_ESTIMATED;
   a.out_idx = out_idx; a.out_score = out_score;
   // one launch on the caller's stream whatever cfg.chunk_rows is
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -366,6 +368,7 @@ int dsai_score_topk_packed(dsai_handle h, const void* index_q, const void* index
     a.w = weights;
     a.H = (int)H; a.D = (int)D; a.ratio = compress_ratio; a.topk = topk;
     a.out_idx = out_idx; a.out_score = out_score;
+    a.est_cuts = h->cfg.cuts == DSAI_CUTS_ESTIMATED;
     for (size_t g0 = 0; g0 < order.size() && le == hipSuccess; g0 += dsai::kPackedMax) {
       const size_t g1 = std::min(order.size(), g0 + (size_t)dsai::kPackedMax);
       int64_t skv_max = 0;

@@ -15,6 +15,7 @@ struct ScoreTopkArgs {
   int H, D, ratio, topk;
   int64_t chunk_rows;  // 0: all rows in one launch
   bool sort;           // score-descending rows (else ascending index order)
+  bool est_cuts = true;  // filter store: cuts to an estimated rank (else to k)
   const int32_t* sup = nullptr;  // [B, S, topk] supplied indices (dense plan only;
                                  // may alias out_idx): their scores, no selection
   int32_t* out_idx;    // [B, S, topk]
@@ -102,6 +103,7 @@ struct PackedTopkArgs {
   int H, D, ratio, topk;
   int32_t* out_idx;   // [Tq, topk], ascending index order
   float* out_score;
+  bool est_cuts = true;  // filter store: cuts to an estimated rank (else to k)
 };
 hipError_t launch_score_topk_packed(const PackedTopkArgs& a, const PackedSeqs& seqs,
                                     const ScoreSelectPlan& p, hipStream_t st);

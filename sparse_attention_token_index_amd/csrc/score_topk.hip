@@ -20,8 +20,12 @@
 //   filter  otherwise: keys beating the row's running threshold are appended
 //           (order key and index); when a store fills, every wavefront of
 //           the block whose store is past half its slack cuts it together
-//           (a bin-edge cut: at least k entries kept, none of the top k
-//           lost), which raises the thresholds.
+//           (a bin-edge cut to a rank: k, or by default the share of the top
+//           k that the keys seen so far are expected to hold, with a margin;
+//           every key dropped ranks below every key kept), which raises the
+//           thresholds.  A row that ends with fewer than k entries although
+//           it has k keys lost some of its top k to an estimated cut: its
+//           block then runs its keys again with cuts to k.
 // After the last tile the row's top k is selected exactly and written in
 // ascending index order; no score goes to device memory.  With supplied
 // indices (dense store only) the row's entries are read from its store
@@ -50,6 +54,21 @@ constexpr int64_t kStaticLds = 128;
 // one that raised it.
 constexpr int kCutRequest = 6 * 32;
 
+// Rank a filter-store cut keeps when it estimates.  If the order of a row's
+// N keys says nothing about their scores, the number of the row's final top
+// k among the first n keys is hypergeometric: mean k n / N, variance at most
+// that mean times (1 - n / N).  A cut to that mean plus six standard
+// deviations and 32 loses none of the top k except with negligible
+// probability; when it does, the row ends short and the block reruns
+// exactly.  Exact cuts, and cuts once every key is seen, keep k.
+__device__ __forceinline__ uint32_t cut_rank(uint32_t k, uint32_t n, uint32_t N, bool exact) {
+  if (exact || n >= N) return k;
+  const float f = (float)n / (float)N;
+  const float mu = (float)k * f;
+  const float m = mu + 6.f * __builtin_sqrtf(mu * (1.f - f)) + 32.f;
+  return m < (float)k ? (uint32_t)m + 1u : k;
+}
+
 template <int D, int NW>
 struct ScoreLds {
   static constexpr int kTileBytes = TileGeom<D>::kTileBytes;
@@ -58,18 +77,23 @@ struct ScoreLds {
   static constexpr int kDenseRegion = kTiles > NW * kDenseScratch ? kTiles : NW * kDenseScratch;
 };
 
-// The body of the two kernels below: sup == nullptr selects, else the
-// supplied entries are read from the dense store.
+// The body of the kernels below: sup == nullptr selects, else the supplied
+// entries are read from the dense store.  est: the filter store's cuts keep
+// an estimated rank (cut_rank) instead of k.
 template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
 __device__ __forceinline__ void score_select_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup, int bid) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score, const int32_t* sup, int bid,
+    bool est) {
   extern __shared__ __align__(16) char smem_raw[];
   // filter store: cut requests, one 8-byte word per tile modulo 3, byte w
   // written by wavefront w after recording that tile (1: its store is nearly
   // full)
   __shared__ uint64_t cut_req[3];
+  // filter store with estimated cuts: set by a wavefront whose row ended
+  // with fewer than k entries (the block then runs its keys again, exactly)
+  __shared__ uint32_t short_rows;
   lds_char* smem = (lds_char*)smem_raw;
   using G = TileGeom<D>;
   using L = ScoreLds<D, NW>;
@@ -135,11 +159,12 @@ __device__ __forceinline__ void score_select_body(
   }
 
   if (!DENSE && threadIdx.x < 3) cut_req[threadIdx.x] = 0u;  // published by the loop's first barrier
+  if (!DENSE && threadIdx.x == 3) short_rows = 0u;
   uint32_t count[NR], tau[NR];       // filter store: entries, running threshold
   uint32_t kmax[NR];                 // filter store: this lane's largest appended key
-  // a bin-edge cut may keep a few entries past k; one that would keep more
-  // than a quarter of the store's slack cuts exactly instead
-  const uint32_t max_keep = (uint32_t)topk + (uint32_t)(cap - topk) / 4u;
+  // a bin-edge cut may keep a few entries past its rank; one that would keep
+  // more than a quarter of the store's slack cuts exactly instead
+  const uint32_t slack_keep = (uint32_t)(cap - topk) / 4u;
   float smin[NR], smax[NR];           // dense store: this lane's extreme scores
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
@@ -321,7 +346,8 @@ __device__ __forceinline__ void score_select_body(
         // (uniform and with no branch: `&`, not `&&`)
         return (it >= s + 4) & (uniform((uint32_t)req | (uint32_t)(req >> 32)) != 0u);
       };
-      const uint32_t cut_at = min((uint32_t)(topk + cap) / 2u, (uint32_t)(cap - kCutRequest - 32));
+      const uint32_t cut_full = (uint32_t)(cap - kCutRequest - 32);
+      bool exact = !est;  // cuts to the top k (else to an estimated rank)
       for (;;) {
         ld.load((uint32_t)(s + 2) * G::kTileKeys);
         __syncthreads();
@@ -343,14 +369,40 @@ __device__ __forceinline__ void score_select_body(
         // drain: record tiles it - 2 (reduced in the last step) and it - 1
         reduce_into(1, acc1);
         record2(it - 2);
-        if (it >= ntiles) break;
+        if (it >= ntiles) {
+          if (exact) break;
+          // Every key the estimated cuts dropped ranks below every entry
+          // kept, so a store that ends with at least k entries (or with
+          // all of its row's keys) holds the row's top k.  If a row of the
+          // block ended short, the block runs its keys again with exact
+          // cuts.
+          bool short_row = false;
+#pragma unroll
+          for (int rr = 0; rr < NR; ++rr)
+            short_row |= count[rr] < (uint32_t)min(topk, n_t[rr]);
+          if (short_row) short_rows = 1u;
+          __syncthreads();  // every wavefront is past its last tile
+          if (short_rows == 0u) break;
+          exact = true;
+#pragma unroll
+          for (int rr = 0; rr < NR; ++rr) count[rr] = tau[rr] = kmax[rr] = 0u;
+          ld.load(0u);
+          ld.store(buf(0));
+          ld.load((uint32_t)G::kTileKeys);
+          ld.store(buf(1));
+          s = 0;
+          continue;
+        }
         __syncthreads();  // every wavefront drained; tiles it and it + 1 are staged
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr) {
-          if (count[rr] > cut_at) {
+          // a store past half its slack over the cut's rank cuts (a nearly
+          // full one always does)
+          const uint32_t kc = cut_rank((uint32_t)topk, (uint32_t)min(n_t[rr], it * G::kTileKeys),
+                                       (uint32_t)n_t[rr], exact);
+          if (count[rr] > min((kc + (uint32_t)cap) / 2u, cut_full)) {
             // after the first cut every key lies in [threshold, running max]
-            const uint2 c = wave_cut(rs[rr], count[rr], (uint32_t)topk, max_keep, tau[rr],
-                                     kmax[rr]);
+            const uint2 c = wave_cut(rs[rr], count[rr], kc, kc + slack_keep, tau[rr], kmax[rr]);
             count[rr] = uniform(c.x);
             tau[rr] = uniform(c.y);
           }
@@ -393,10 +445,10 @@ template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_select_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int S, int Skv, int B, int H, int ratio, int topk, int row_begin, int row_end, int R, int cap,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score, int est) {
   score_select_body<HP, D, NW, NR, DENSE, IdxT>(q, k, w, S, Skv, B, H, ratio, topk, row_begin,
                                                 row_end, R, cap, out_idx, out_score, nullptr,
-                                                (int)blockIdx.x);
+                                                (int)blockIdx.x, est != 0);
 }
 
 // Packed sequences: the workgroup's sequence is the number of sequence
@@ -407,7 +459,7 @@ template <int HP, int D, int NW, int NR, bool DENSE, typename IdxT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_select_packed_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int H, int ratio, int topk, int R, int cap, int32_t* __restrict__ out_idx,
-    float* __restrict__ out_score, const PackedSeqs seqs) {
+    float* __restrict__ out_score, const PackedSeqs seqs, int est) {
   const int bid = (int)blockIdx.x;
   int i = 0;
 #pragma unroll
@@ -416,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   score_select_body<HP, D, NW, NR, DENSE, IdxT>(
       q + q0 * H * D, k + (int64_t)seqs.k0[i] * D, w + q0 * H, seqs.S[i], seqs.Skv[i], 1, H, ratio,
       topk, 0, seqs.S[i], R, cap, out_idx + q0 * topk, out_score + q0 * topk, nullptr,
-      bid - seqs.blk_begin[i]);
+      bid - seqs.blk_begin[i], est != 0);
 }
 
 // Scores at supplied indices through the dense store (its own kernel, so
@@ -428,7 +480,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     int32_t* out_idx, float* __restrict__ out_score, const int32_t* sup) {
   score_select_body<HP, D, NW, NR, true, uint16_t>(q, k, w, S, Skv, B, H, ratio, topk, row_begin,
                                                    row_end, R, cap, out_idx, out_score, sup,
-                                                   (int)blockIdx.x);
+                                                   (int)blockIdx.x, false);
 }
 
 namespace {
@@ -529,7 +581,7 @@ static hipError_t launch_t(const ScoreTopkArgs& a, const ScoreSelectPlan& p, hip
       hipLaunchKernelGGL((score_select_kernel<HP, D, NW, NR, DENSE, IdxT>), dim3((unsigned)blocks),
                          dim3(NW * 64), p.lds_bytes, sc, a.q, a.k, a.w, (int)a.S, (int)a.Skv,
                          (int)a.B, a.H, a.ratio, a.topk, (int)r0, (int)r1, R, p.cap, a.out_idx,
-                         a.out_score);
+                         a.out_score, a.est_cuts ? 1 : 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -561,7 +613,7 @@ static hipError_t launch_packed_t(const PackedTopkArgs& a, const PackedSeqs& seq
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((score_select_packed_kernel<HP, D, NW, NR, DENSE, IdxT>), dim3((unsigned)blocks),
                      dim3(NW * 64), p.lds_bytes, st, a.q, a.k, a.w, a.H, a.ratio, a.topk,
-                     p.rows_per_block, p.cap, a.out_idx, a.out_score, seqs);
+                     p.rows_per_block, p.cap, a.out_idx, a.out_score, seqs, a.est_cuts ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -36,6 +36,17 @@ def test_header_declares_the_binding_exports():
     assert declared_symbols() == sorted(dsai.EXPORTS)
 
 
+def test_config_struct_matches_the_header():
+    """The binding's ctypes mirror of dsai_config has the header's int
+    fields, in the header's order."""
+    import sparse_attention_token_index_amd as dsai
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct dsai_config \{(.*?)\} dsai_config;", text, re.S).group(1)
+    fields = re.findall(r"\bint\s+([a-z_]+)\s*;", body)
+    assert fields == [f for f, _ in dsai._Config._fields_]
+    assert all(t is ctypes.c_int for _, t in dsai._Config._fields_)
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_symbols():
         assert hasattr(lib, name), name
@@ -50,9 +61,9 @@ def test_exports_are_c_symbols():
     assert set(declared_symbols()) <= exported
 
 
-def _cfg(heads=64, dim=128, kpool=4, index_topk=512, first_key=0, chunk_rows=0, order=0):
+def _cfg(heads=64, dim=128, kpool=4, index_topk=512, first_key=0, chunk_rows=0, order=0, cuts=0):
     import sparse_attention_token_index_amd as dsai
-    return dsai._Config(heads, dim, kpool, index_topk, first_key, chunk_rows, order)
+    return dsai._Config(heads, dim, kpool, index_topk, first_key, chunk_rows, order, cuts)
 
 
 def _create(lib, **kw):
@@ -76,6 +87,9 @@ def _create(lib, **kw):
     ({"order": 1}, OK),
     ({"order": 2}, INVALID),
     ({"order": -1}, INVALID),
+    ({"cuts": 1}, OK),
+    ({"cuts": 2}, INVALID),
+    ({"cuts": -1}, INVALID),
     ({"heads": 65}, UNSUPPORTED),
     ({"dim": 96}, UNSUPPORTED),
     ({"dim": 256}, UNSUPPORTED),

@@ -338,6 +338,55 @@ def test_filter_store_block_cuts(dsai, heads, dim):
     compare(case, first[0], first[1], rows, full)
 
 
+def _trend_inputs(case, falling):
+    """Integer inputs whose scores follow the key position: key s is the
+    trend (Skv - 1 - s) // 64 (falling) or s // 64 (rising) plus a random
+    0..7, in every dimension plus a random 0 or 1; q in 0..2 and weights in
+    {1/4, 1/2, 1}, all non-negative, so the score rises with the key's
+    value.  Every fp32 step is exact (dot products below 2^14)."""
+    rng = np.random.default_rng(case.seed + 700)
+    s = np.arange(case.Skv)
+    trend = (case.Skv - 1 - s) // 64 if falling else s // 64
+    c = trend + rng.integers(0, 8, case.Skv)
+    k = (c[:, None, None] + rng.integers(0, 2, (case.Skv, case.B, case.D))).astype(np.float32)
+    q = rng.integers(0, 3, (case.S, case.B, case.H, case.D)).astype(np.float32)
+    w = rng.choice([0.25, 0.5, 1.0], (case.S, case.B, case.H)).astype(np.float32)
+    assert k.max() <= 256   # integers exact in bf16
+    return {"q_bits": SY.f32_to_bf16_bits(q), "k_bits": SY.f32_to_bf16_bits(k), "w": w}
+
+
+@pytest.mark.parametrize("trend", ["falling", "rising", "random"])
+def test_filter_store_estimated_cuts(dsai, trend):
+    """Rows longer than the dense store, cut to an estimated rank (the
+    default) or to k: the same bits either way.  With scores that fall
+    along the key sequence the estimated cuts drop part of the top k, the
+    rows end short and their blocks run again with cuts to k; rising scores
+    never do; random (Gaussian) inputs are the common case.  The integer
+    cases also match the oracle bit for bit on sampled rows."""
+    case = SY.IndexerCase(f"est_cuts_{trend}", B=1, S=8192, Skv=8192, H=4, D=32,
+                          compress_ratio=1, topk=2048, w_var=1 / 4, seed=71)
+    log(f"[gpu] estimated cuts, {trend} scores {case}")
+    inp = SY.indexer_inputs(case) if trend == "random" else _trend_inputs(case, trend == "falling")
+    q, k = to_gpu_bf16(inp["q_bits"]), to_gpu_bf16(inp["k_bits"])
+    w = torch.from_numpy(inp["w"]).cuda()
+    outs = []
+    for cuts in (dsai.DSAI_CUTS_ESTIMATED, dsai.DSAI_CUTS_TOPK):
+        ix = dsai.Indexer(heads=case.H, dim=case.D, cuts=cuts)
+        idx, sc = ix.score_topk(q, k, w, 1, case.topk)
+        torch.cuda.synchronize()
+        outs.append((idx.cpu().numpy(), sc.cpu().numpy()))
+    (ei, es), (ti, ts) = outs
+    assert np.array_equal(ei, ti), np.argwhere(ei != ti)[:5]
+    assert np.array_equal(es.view(np.uint32), ts.view(np.uint32))
+    rows = sorted(set(range(0, 4)) | set(range(2044, 2052)) | set(range(0, case.S, 97)) |
+                  set(range(case.S - 4, case.S)))
+    if trend == "random":
+        _, _, full = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
+        compare(case, ei, es, rows, full)
+    else:
+        _exact_rows(case, ei, es, inp, rows)
+
+
 def test_filter_store_wide_indices(dsai):
     """Skv > 65536: the filtering store keeps 32-bit indices."""
     case = SY.IndexerCase("wide_idx", B=1, S=70000, Skv=70000, H=4, D=32, compress_ratio=1,
