@@ -582,6 +582,22 @@ def main():
     kpb_ms = timed_cold(lambda: pix.kpool_compress(kn_b, gate_b, valid_b, ape, pool_k=pk_b,
                                                    pool_tok=pt_b, pool_valid=pv_b), reps)
     kbb = kpool_bytes(NB, pc.D, pc.KP, pc.first_key)
+    # cold kpool against the token count (the first n of the 2^20 rows): a
+    # least-squares line ms = fixed + bytes / marginal rate separates the
+    # per-launch start-up from the streaming rate
+    sweep_n, sweep_ms, sweep_b = [], [], []
+    for lg in range(16, 21):
+        n = 1 << lg
+        pn = pix.pool_count(n)
+        sweep_ms.append(timed_cold(lambda: pix.kpool_compress(
+            kn_b[:n], gate_b[:n], valid_b[:n], ape, pool_k=pk_b[:pn], pool_tok=pt_b[:pn],
+            pool_valid=pv_b[:pn]), reps))
+        sweep_n.append(n)
+        sweep_b.append(kpool_bytes(n, pc.D, pc.KP, pc.first_key))
+    slope, icpt = np.polyfit(np.array(sweep_b, dtype=np.float64), np.array(sweep_ms), 1)
+    kpool_sweep = {"tokens": sweep_n, "bytes": sweep_b, "cold_ms": sweep_ms,
+                   "fixed_us": float(icpt) * 1e3,
+                   "marginal_GBps": float(1.0 / slope / 1e6) if slope > 0 else None}
     del kn_b, gate_b, valid_b, pk_b, pt_b, pv_b
     QB = 65536
     ids_b = torch.randint(-1, P, (QB, sel), generator=g, device=dev, dtype=torch.int32)
@@ -614,6 +630,7 @@ def main():
         "kpool_cold_frac_hbm": gbs(kb, kp_ms) / PEAK_HBM_GBS,
         "kpool_2p20_cold_ms": kpb_ms, "kpool_2p20_bytes": kbb,
         "kpool_2p20_cold_GBps": gbs(kbb, kpb_ms), "kpool_2p20_cold_frac_hbm": gbs(kbb, kpb_ms) / PEAK_HBM_GBS,
+        "kpool_cold_sweep": kpool_sweep,
         "select_expand_ms": sel_ms,
         "select_expand_TFLOPs": select_flops(pc, P) / (sel_ms * 1e-3) / 1e12,
         "select_expand_static_ms": st_ms,

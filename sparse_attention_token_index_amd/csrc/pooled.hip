@@ -290,26 +290,33 @@ __global__ __launch_bounds__(1024) void topk_rows_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 // topk_pools for rows of at most 1024 * 32 pools: one 1024-thread workgroup
 // per row holds the row in registers (thread t owns pools [t*ITEMS,
-// (t+1)*ITEMS)) and finds the select_k-th largest key with a block-wide radix
-// select: a histogram of (key - lo) >> shift over 2048 bins (LDS atomics), a
-// suffix search for the bin holding rank k, and at most three such passes
-// (11 bits each) inside the chosen bin's range.  That gives the threshold key
-// T and how many entries equal to T to keep (the lowest pool ids).  Selected
-// entries are written in pool-id order after two block scans; for the
-// score order with select_k <= kRankSortMax, each selected entry's rank under
-// (score desc, pool id asc) is counted against the others in LDS.
+// (t+1)*ITEMS)) and finds the select_k-th largest key with a block-wide
+// select: a histogram of the keys over 2048 float-linear bins of [min, max]
+// (LDS atomics), a suffix search for the bin holding rank k, and the
+// threshold among that bin's keys by direct counting (a crowded bin: at most
+// three radix passes of 11 bits inside its range).  That gives the threshold
+// key T and how many entries equal to T to keep (the lowest pool ids).  For
+// the score order with select_k <= kRankSortMax, when the entries above T
+// and every entry equal to T fit the LDS list, they are appended to it in
+// any order and each one's rank under (score desc, pool id asc) is counted
+// against the others; ranks past select_k (surplus equal keys) are dropped.
+// Otherwise one block scan places the selected entries in pool-id order
+// (ranked the same way for the score order, else written as they are).
+// Each phase has LDS words of its own, so a barrier separates only a
+// phase's writes from its reads.
 // ---------------------------------------------------------------------------
 constexpr int kBlockSelThreads = 1024;
 constexpr int kBlockSelWaves = kBlockSelThreads / kWave;
-constexpr int kBlockSelBins = 2048;
+constexpr int kBlockSelBinBits = 11;
+constexpr int kBlockSelBins = 1 << kBlockSelBinBits;
 constexpr int kRankSortMax = 512;
 
 // Block-wide inclusive prefix sum of one value per thread; `red` holds
-// kBlockSelWaves words.  Returns (inclusive, total).
+// kBlockSelWaves words that no thread reads after the last barrier before
+// the call (one barrier inside).  Returns (inclusive, total).
 __device__ __forceinline__ uint2 block_incl_scan(uint32_t x, uint32_t* red) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(x);
-  __syncthreads();  // earlier readers of `red` are done
   if (lane == kWave - 1) red[wave] = incl;
   __syncthreads();
   uint32_t base = 0u, total = 0u;
@@ -327,12 +334,15 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     const float* __restrict__ scores, int P, int sel, int score_order, int32_t* __restrict__ ids,
     float* __restrict__ out_scores, int32_t* __restrict__ tokens, int KP, int first_key) {
   __shared__ uint32_t hist[kBlockSelBins];
-  __shared__ uint32_t red[kBlockSelWaves];
-  __shared__ uint32_t found[2];
+  __shared__ uint32_t red_mm[3 * kBlockSelWaves];  // per-wave min, max, count
+  __shared__ uint32_t red_h[kBlockSelWaves];       // the histograms' scans
+  __shared__ uint32_t red_s[kBlockSelWaves];       // the placement scan
+  __shared__ uint32_t found[3];
   __shared__ uint2 staged[kRankSortMax];
   __shared__ uint32_t cand[kBlockSelThreads];
-  __shared__ uint32_t ncand;
+  __shared__ uint32_t ncand, nstage;
   const int t = threadIdx.x;
+  const int lane = lane_id(), wave = t >> 6;
   const float* srow = scores + (int64_t)blockIdx.x * P;
   int32_t* orow = ids + (int64_t)blockIdx.x * sel;
   float* osc = out_scores + (int64_t)blockIdx.x * sel;
@@ -345,6 +355,15 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     if (trow)
       for (int j = 0; j < KP; ++j) trow[(int64_t)i * KP + j] = id >= 0 ? first_key + id * KP + j : -1;
   };
+
+  // The first histogram's bins and the append counters start at zero (the
+  // barrier after the loads publishes them).
+  hist[2 * t] = 0u;
+  hist[2 * t + 1] = 0u;
+  if (t == 0) {
+    ncand = 0u;
+    nstage = 0u;
+  }
 
   // Load; -inf (an invalid pool) and slots past P never count.
   uint32_t u[ITEMS];
@@ -387,22 +406,24 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
   // Per-wave count / min / max, combined after one barrier.
   const uint32_t wcnt = wave_reduce(nloc, [](uint32_t x, uint32_t y) { return x + y; });
   const uint32_t wmin = wave_min(kmin), wmax = wave_max(kmax);
-  if ((t & (kWave - 1)) == 0) {
-    red[t >> 6] = wmin;
-    hist[t >> 6] = wmax;                    // hist is free until the first histogram pass
-    hist[kBlockSelWaves + (t >> 6)] = wcnt;
+  if (lane == 0) {
+    red_mm[wave] = wmin;
+    red_mm[kBlockSelWaves + wave] = wmax;
+    red_mm[2 * kBlockSelWaves + wave] = wcnt;
   }
   __syncthreads();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, nvalid = 0u;
 #pragma unroll
   for (int w = 0; w < kBlockSelWaves; ++w) {
-    lo = min(lo, red[w]);
-    hi = max(hi, hist[w]);
-    nvalid += hist[kBlockSelWaves + w];
+    lo = min(lo, red_mm[w]);
+    hi = max(hi, red_mm[kBlockSelWaves + w]);
+    nvalid += red_mm[2 * kBlockSelWaves + w];
   }
 
-  // Threshold key T and the number of entries equal to T to keep.
-  uint32_t T = 0u, need_eq = 0u;
+  // Threshold key T, how many entries equal to T to keep, and (when known)
+  // how many entries equal T in all.
+  constexpr uint32_t kUnknown = 0xFFFFFFFFu;
+  uint32_t T = 0u, need_eq = 0u, neq = kUnknown;
   const uint32_t k = (uint32_t)sel;
   bool resolved = false;
   uint32_t span = hi - lo, rem = k;
@@ -413,22 +434,17 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     const float base_h = 0.5f * ord_to_float(lo);
     const float fspan = 0.5f * ord_to_float(hi) - base_h;
     const float scale = fspan > 0.f ? fminf((float)kBlockSelBins / fspan, 3.4e38f) : 0.f;
-    auto fbin = [&](uint32_t key) {
-      const float d = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, ord_to_float(key)), base_h), scale);
-      return (uint32_t)fminf(fmaxf(d, 0.f), (float)(kBlockSelBins - 1));
-    };
-    __syncthreads();
-    hist[2 * t] = 0u;
-    hist[2 * t + 1] = 0u;
-    if (t == 0) ncand = 0u;
-    __syncthreads();
+    uint32_t bn[ITEMS];
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j)
-      if (u[j] != 0u) atomicAdd(&hist[fbin(u[j])], 1u);
+    for (int j = 0; j < ITEMS; ++j) {
+      const float d = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, ord_to_float(u[j])), base_h), scale);
+      bn[j] = (uint32_t)fminf(fmaxf(d, 0.f), (float)(kBlockSelBins - 1));
+      if (u[j] != 0u) atomicAdd(&hist[bn[j]], 1u);
+    }
     __syncthreads();
     {
       const uint32_t h0 = hist[2 * t], h1 = hist[2 * t + 1];
-      const uint2 sc = block_incl_scan(h0 + h1, red);
+      const uint2 sc = block_incl_scan(h0 + h1, red_h);
       const uint32_t after = sc.y - sc.x;
       if (h1 + after >= rem && after < rem) {
         found[0] = (uint32_t)(2 * t + 1);
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     if (ncb <= (uint32_t)kBlockSelThreads) {
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j)
-        if (u[j] != 0u && fbin(u[j]) == fb) cand[atomicAdd(&ncand, 1u)] = u[j];
+        if (u[j] != 0u && bn[j] == fb) cand[atomicAdd(&ncand, 1u)] = u[j];
       __syncthreads();
       if ((uint32_t)t < ncb) {
         const uint32_t me = cand[t];
@@ -455,39 +471,42 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
           gt += o > me ? 1u : 0u;
           eq += o == me ? 1u : 0u;
         }
-        if (gt < rem && rem <= gt + eq) {  // every thread holding the threshold key agrees
+        // every thread holding the threshold key agrees; its bin holds
+        // every key equal to it, so eq counts them all
+        if (gt < rem && rem <= gt + eq) {
           found[0] = me;
           found[1] = rem - gt;
+          found[2] = eq;
         }
       }
       __syncthreads();
       T = found[0];
       need_eq = found[1];
+      neq = found[2];
       resolved = true;
     } else {
       // many keys in one bin: continue with the radix rounds on its key range
       uint32_t bl = 0xFFFFFFFFu, bh = 0u;
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
-        if (u[j] != 0u && fbin(u[j]) == fb) {
+        if (u[j] != 0u && bn[j] == fb) {
           bl = min(bl, u[j]);
           bh = max(bh, u[j]);
         }
       }
       bl = wave_min(bl);
       bh = wave_max(bh);
-      __syncthreads();
-      if ((t & (kWave - 1)) == 0) {
-        red[t >> 6] = bl;
-        hist[t >> 6] = bh;
+      if (lane == 0) {  // red_mm's readers passed three barriers since
+        red_mm[wave] = bl;
+        red_mm[kBlockSelWaves + wave] = bh;
       }
       __syncthreads();
       lo = 0xFFFFFFFFu;
       hi = 0u;
 #pragma unroll
       for (int w = 0; w < kBlockSelWaves; ++w) {
-        lo = min(lo, red[w]);
-        hi = max(hi, hist[w]);
+        lo = min(lo, red_mm[w]);
+        hi = max(hi, red_mm[kBlockSelWaves + w]);
       }
       span = hi - lo;
     }
@@ -500,8 +519,8 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
         break;
       }
       const int bits = 32 - __builtin_clz(span);
-      const int shift = bits > 11 ? bits - 11 : 0;
-      __syncthreads();  // readers of hist / red / found from the last round are done
+      const int shift = bits > kBlockSelBinBits ? bits - kBlockSelBinBits : 0;
+      __syncthreads();  // readers of hist / found from the last round are done
       hist[2 * t] = 0u;
       hist[2 * t + 1] = 0u;
       __syncthreads();
@@ -513,7 +532,7 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
       __syncthreads();
       // suffix sums: S(b) = entries in bins >= b; find b with S(b) >= rem > S(b + 1)
       const uint32_t h0 = hist[2 * t], h1 = hist[2 * t + 1];
-      const uint2 sc = block_incl_scan(h0 + h1, red);
+      const uint2 sc = block_incl_scan(h0 + h1, red_h);
       const uint32_t after = sc.y - sc.x;  // entries in bins above 2t + 1
       if (h1 + after >= rem && after < rem) {
         found[0] = (uint32_t)(2 * t + 1);
@@ -526,9 +545,10 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
       const uint32_t b = found[0];
       rem -= found[1];
       lo += b << shift;
-      if (shift == 0) {
+      if (shift == 0) {  // bins of one key: bin b holds every key equal to T
         T = lo;
         need_eq = rem;
+        neq = hist[b];
         break;
       }
       const uint32_t width = (1u << shift) - 1u;
@@ -536,57 +556,80 @@ __global__ __launch_bounds__(kBlockSelThreads) void block_select_kernel(
     }
   }
 
-  // Selection in pool-id order: keys above T, and the first need_eq keys
-  // equal to T.  One block scan of (equal count << 16 | above count) places
-  // every selected key: its slot = keys above T before it + min(keys equal
-  // to T before it, need_eq).  (Counts fit 16 bits: at most 32768 pools.)
+  // The row's entries: keys above T (every valid key if the row has at most
+  // k), and the first need_eq keys equal to T (pool-id order).
   const bool cut = nvalid > k;
-  uint32_t ab_loc = 0u, eq_loc = 0u;
-#pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    ab_loc += (u[j] != 0u && (!cut || u[j] > T)) ? 1u : 0u;
-    eq_loc += (cut && u[j] == T) ? 1u : 0u;
-  }
-  const uint2 ss = block_incl_scan((eq_loc << 16) | ab_loc, red);
-  const uint32_t ab_before = (ss.x - ((eq_loc << 16) | ab_loc)) & 0xFFFFu;
-  uint32_t eq_before = (ss.x - ((eq_loc << 16) | ab_loc)) >> 16;
-  const uint32_t nsel = (ss.y & 0xFFFFu) + min(ss.y >> 16, need_eq);  // min(nvalid, sel)
-  uint32_t nab = 0u;
+  const uint32_t nsel = cut ? k : nvalid;  // min(nvalid, sel)
   const bool rank_sort = score_order && sel <= kRankSortMax;
+  const bool direct = rank_sort && (!cut || (neq != kUnknown && k - need_eq + neq <= kRankSortMax));
+  uint32_t nst = nsel;  // entries on the ranking list
+  if (direct) {
+    // Append the keys above T and all keys equal to T, in any order (one
+    // LDS atomic per wavefront); the ranks put the equal ones in pool-id
+    // order and drop those past k.
+    uint32_t mine = 0u;
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    const bool above = u[j] != 0u && (!cut || u[j] > T);
-    const bool eq = cut && u[j] == T;
-    const bool s = above || (eq && eq_before < need_eq);
-    if (s) {
-      const uint32_t pos = ab_before + nab + min(eq_before, need_eq);
-      if (rank_sort) {
-        staged[pos] = make_uint2(u[j], (uint32_t)(p0 + j));
-      } else {
-        put(pos, p0 + j, ord_to_float(u[j]));
-      }
+    for (int j = 0; j < ITEMS; ++j) mine += (u[j] != 0u && (!cut || u[j] >= T)) ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan(mine);
+    uint32_t base = 0u;
+    if (lane == kWave - 1) base = atomicAdd(&nstage, incl);
+    uint32_t pos = lane_value(base, kWave - 1) + incl - mine;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (u[j] != 0u && (!cut || u[j] >= T)) staged[pos++] = make_uint2(u[j], (uint32_t)(p0 + j));
+    nst = cut ? k - need_eq + neq : nvalid;
+  } else {
+    // Placement in pool-id order: one block scan of (equal count << 16 |
+    // above count) gives every selected key its slot = keys above T before
+    // it + min(keys equal to T before it, need_eq).  (Counts fit 16 bits:
+    // at most 32768 pools.)
+    uint32_t ab_loc = 0u, eq_loc = 0u;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      ab_loc += (u[j] != 0u && (!cut || u[j] > T)) ? 1u : 0u;
+      eq_loc += (cut && u[j] == T) ? 1u : 0u;
     }
-    nab += above ? 1u : 0u;
-    eq_before += eq ? 1u : 0u;
+    const uint2 ss = block_incl_scan((eq_loc << 16) | ab_loc, red_s);
+    const uint32_t ab_before = (ss.x - ((eq_loc << 16) | ab_loc)) & 0xFFFFu;
+    uint32_t eq_before = (ss.x - ((eq_loc << 16) | ab_loc)) >> 16;
+    uint32_t nab = 0u;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const bool above = u[j] != 0u && (!cut || u[j] > T);
+      const bool eq = cut && u[j] == T;
+      const bool s = above || (eq && eq_before < need_eq);
+      if (s) {
+        const uint32_t pos = ab_before + nab + min(eq_before, need_eq);
+        if (rank_sort) {
+          staged[pos] = make_uint2(u[j], (uint32_t)(p0 + j));
+        } else {
+          put(pos, p0 + j, ord_to_float(u[j]));
+        }
+      }
+      nab += above ? 1u : 0u;
+      eq_before += eq ? 1u : 0u;
+    }
   }
   if (rank_sort) {
-    // rank of each staged entry: `tpe` consecutive threads split the
-    // comparisons against the others, then sum their counts
+    // rank of each listed entry under (score desc, pool id asc): `tpe`
+    // consecutive threads split the comparisons against the others, then
+    // sum their counts; ranks below nsel are written
     __syncthreads();
     int tpe = kBlockSelThreads / kRankSortMax;
-    while (tpe * 2 * (int)nsel <= kBlockSelThreads && tpe < kWave) tpe *= 2;
+    while (tpe * 2 * (int)nst <= kBlockSelThreads && tpe < kWave) tpe *= 2;
     const uint32_t e = (uint32_t)(t / tpe), part = (uint32_t)(t % tpe);
     uint32_t r = 0u;
     uint2 me = make_uint2(0u, 0u);
-    if (e < nsel) {
+    if (e < nst) {
       me = staged[e];
-      for (uint32_t i = part; i < nsel; i += (uint32_t)tpe) {
+#pragma unroll 4
+      for (uint32_t i = part; i < nst; i += (uint32_t)tpe) {
         const uint2 o = staged[i];
         r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
       }
     }
     for (int off = 1; off < tpe; off <<= 1) r += (uint32_t)__shfl_xor((int)r, off);
-    if (e < nsel && part == 0u) {
+    if (e < nst && part == 0u && r < nsel) {
       put(r, (int32_t)me.y, ord_to_float(me.x));
     }
   }

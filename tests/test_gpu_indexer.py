@@ -28,9 +28,9 @@ def to_gpu_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def run_gpu(dsai, case, inp, chunk_rows=None, out=None):
+def run_gpu(dsai, case, inp, chunk_rows=None, out=None, cuts=0):
     ix = dsai.Indexer(heads=case.H, dim=case.D,
-                      chunk_rows=case.chunk_rows if chunk_rows is None else chunk_rows)
+                      chunk_rows=case.chunk_rows if chunk_rows is None else chunk_rows, cuts=cuts)
     q = to_gpu_bf16(inp["q_bits"])
     k = to_gpu_bf16(inp["k_bits"])
     w = torch.from_numpy(inp["w"]).cuda()
@@ -424,6 +424,12 @@ def test_config_parity(dsai, name):
         rows = sorted(set(_sample_rows(case)) | set(range(0, case.S, 64)))
     else:
         rows = _sample_rows(case)
+    if name == "long":   # estimated cuts (the default) and cuts to k: the same bits
+        log(f"[gpu] config parity {name}: cuts to k")
+        tidx, tsc = run_gpu(dsai, case, inp, cuts=dsai.DSAI_CUTS_TOPK)
+        assert np.array_equal(tidx, gidx)
+        assert np.array_equal(tsc.view(np.uint32), gsc.view(np.uint32))
+        del tidx, tsc
     log(f"[gpu] config parity {name}: oracle on {len(rows)} rows x {case.B} batches")
     _, _, full = oracle_rows(case, rows, inp["q_bits"][rows], inp["k_bits"], inp["w"][rows])
     compare(case, gidx, gsc, rows, full)

@@ -152,6 +152,9 @@ def test_topk_pools_exact_on_fp32_scores(dsai, Q, P, KP, index_topk, order):
         s[7, 1::2] = 0.0
         s[8, :] = 3.0e38                                      # the largest finite scores
         s[8, ::3] = -3.0e38
+    if Q > 9:   # one outlier stretches the range: the rest crowd one bin (radix rounds), ties
+        s[9] = (np.round(rng.standard_normal(P) * 64) / 64).astype(np.float32)
+        s[9, P // 3] = 1.0e30
     ix = dsai.Indexer(heads=32, dim=128, kpool=KP, index_topk=index_topk,
                       order=dsai.DSAI_ORDER_SCORE if order == "score" else dsai.DSAI_ORDER_INDEX)
     ids, vals = ix.topk_pools(torch.from_numpy(s).cuda())
