@@ -187,3 +187,42 @@ def test_packed_backward_exact(dsai):
         assert np.array_equal(bits(sq)[:, 0], bits(gq)[q0:q1]), i
         assert np.array_equal(bits(sk)[:, 0], bits(gk)[k0:k1]), i
         assert np.array_equal(sw.cpu().numpy()[:, 0], gw.cpu().numpy()[q0:q1]), i
+
+
+def test_packed_estimated_cuts_rerun(dsai):
+    """Sequences long enough for the filter store, with integer scores that
+    fall (or rise) along their keys: in the packed launch the estimated cuts
+    of the falling ones drop part of the top k, and those blocks run their
+    keys again with cuts to k.  Every row equals one dsai_score_topk call per
+    sequence with cuts to k, bit for bit."""
+    log("[gpu] packed estimated cuts")
+    rng = np.random.default_rng(77)
+    lens = [7000, 50, 5200, 0, 300, 6100]
+    H, D, topk = 4, 32, 2048
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    k = np.empty((T, D), np.float32)
+    for i, n in enumerate(lens):
+        s = np.arange(n)
+        trend = (n - 1 - s) // 64 if i % 2 == 0 else s // 64
+        c = trend + rng.integers(0, 8, n)
+        k[cu[i]:cu[i + 1]] = c[:, None] + rng.integers(0, 2, (n, D))
+    assert k.max() <= 256   # integers exact in bf16
+    q = rng.integers(0, 3, (T, H, D)).astype(np.float32)
+    w = rng.choice([0.25, 0.5, 1.0], (T, H)).astype(np.float32)
+    qg, kg = bf16(SY.f32_to_bf16_bits(q)), bf16(SY.f32_to_bf16_bits(k))
+    wg = torch.from_numpy(w).cuda()
+    ix = dsai.Indexer(heads=H, dim=D)   # estimated cuts (the default)
+    gi, gs = ix.score_topk_packed(qg, kg, wg, cu, cu, 1, topk)
+    torch.cuda.synchronize()
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
+    ref = dsai.Indexer(heads=H, dim=D, cuts=dsai.DSAI_CUTS_TOPK)
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if a == b:
+            continue
+        si, ss = ref.score_topk(qg[a:b, None].contiguous(), kg[a:b, None].contiguous(),
+                                wg[a:b, None].contiguous(), 1, topk)
+        torch.cuda.synchronize()
+        assert np.array_equal(si.cpu().numpy()[0], gi[a:b]), i
+        assert np.array_equal(ss.cpu().numpy()[0].view(np.uint32), gs[a:b].view(np.uint32)), i
