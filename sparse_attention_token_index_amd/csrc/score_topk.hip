@@ -29,9 +29,9 @@
 // After the last tile the row's top k is selected exactly and written in
 // ascending index order; no score goes to device memory.  With supplied
 // indices (dense store only) the row's entries are read from its store
-// instead of selected.  (Score-descending
-// order is produced by the row sort.)  Blocks are numbered heaviest (largest
-// t) first so the causal imbalance is absorbed by the dispatcher.
+// instead of selected.  (Score-descending order is produced by the row
+// sort.)  Blocks are numbered heaviest (largest t) first so the causal
+// imbalance is absorbed by the dispatcher.
 #include "internal.h"
 #include "score_tile.h"
 #include "topk_wave.h"
@@ -46,7 +46,8 @@ constexpr int kDenseScratch = 2048;
 // (one 256-bin histogram; the bin-edge cut needs no side list).
 constexpr int kCutScratch = 1024;
 
-// Static LDS of the filter-store kernels (cut requests), rounded up.
+// Static LDS of the filter-store kernels (cut requests, the short-row flag),
+// rounded up.
 constexpr int64_t kStaticLds = 128;
 
 // A filter store asks for a cut once fewer than this many slots are free:
