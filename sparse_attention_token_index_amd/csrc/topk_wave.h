@@ -492,23 +492,33 @@ __device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, ui
   const int lane = lane_id();
   const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
   const uint32_t ngroups = (n + 255u) >> 8;  // 256 keys per group, 4 per lane
+  const uint32_t nfull = n >> 8;               // groups with no slot past the row
   float a = smin, b = smax;
   uint32_t rem = k;
   for (int level = 0; level < 3; ++level) {
     if (!(a < b)) return make_uint2(__float_as_uint(a), rem);
     const FloatBins bins(a, b);
+    // Every key of a full group counts at level 0 ([a, b] is the row's
+    // range); otherwise slots past the row and keys outside [a, b] add 0
+    // (branch-free: bins() lands in [0, 255] for any bits).
+    const bool lvl0 = level == 0;
     clear_hist(hist);
     for (uint32_t gi = 0; gi < ngroups; ++gi) {
       const u32x4 u = k4[gi * 64u + lane];
       const uint32_t i0 = gi * 256u + 4u * lane;
+      if (lvl0 & (gi < nfull)) {  // (uniform)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // branch-free: a slot past the row (any bits; bins() lands in
-        // [0, 255] for every input) adds 0
-        const float x = __uint_as_float(u[e]);
-        const bool in = i0 + e < n && (level == 0 || (x >= a && x <= b));
-        __hip_atomic_fetch_add(&hist[bins(x)], in ? 1u : 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_fetch_add(&hist[bins(__uint_as_float(u[e]))], 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = __uint_as_float(u[e]);
+          const bool in = i0 + e < n && (lvl0 || (x >= a && x <= b));
+          __hip_atomic_fetch_add(&hist[bins(x)], in ? 1u : 0u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+        }
       }
     }
     wave_lds_sync();
@@ -517,27 +527,36 @@ __device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, ui
     rem -= fb.y;
     wave_lds_sync();
     if (cnt <= 256u) {
-      // gather the bin's keys (as order keys) into the side list
+      // gather the bin's scores into the side list, then turn them into
+      // order keys there (only the bin's few entries are converted)
       uint32_t ns = 0u;
       for (uint32_t gi = 0; gi < ngroups; ++gi) {
         const u32x4 u = k4[gi * 64u + lane];
         const uint32_t i0 = gi * 256u + 4u * lane;
-        uint32_t m = 0u, ok[4];
+        uint32_t m = 0u;
+        const uint32_t ux[4] = {u[0], u[1], u[2], u[3]};
+        if (lvl0 & (gi < nfull)) {  // (uniform)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = __uint_as_float(u[e]);
-          const bool in = i0 + e < n && x >= a && x <= b && bins(x) == fb.x;
-          m |= in ? (1u << e) : 0u;
-          ok[e] = ord_key(x);
+          for (int e = 0; e < 4; ++e) m |= bins(__uint_as_float(u[e])) == fb.x ? (1u << e) : 0u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = __uint_as_float(u[e]);
+            const bool in = i0 + e < n && (lvl0 || (x >= a && x <= b)) && bins(x) == fb.x;
+            m |= in ? (1u << e) : 0u;
+          }
         }
-        ns = wave_append4(side, ns, m, ok);
+        ns = wave_append4(side, ns, m, ux);
       }
       wave_lds_sync();
       uint32_t lo = 0xFFFFFFFFu, hi = 0u;
       for (uint32_t i = lane; i < ns; i += kWave) {
-        lo = min(lo, side[i]);
-        hi = max(hi, side[i]);
+        const uint32_t o = ord_key(__uint_as_float(side[i]));
+        side[i] = o;
+        lo = min(lo, o);
+        hi = max(hi, o);
       }
+      wave_lds_sync();
       lo = wave_min(lo);
       hi = wave_max(hi);
       uint2 r = make_uint2(lo, rem);
