@@ -150,7 +150,10 @@ int dsai_last_hip_error(dsai_handle h);
  * cfg.chunk_rows does not apply to the selection: the one launch covers
  * every row, its workgroups numbered from the last (longest) rows to the
  * first, so no chunk boundary leaves the GPU idle while a chunk's longest
- * rows finish.
+ * rows finish.  Rows longer than the kernel's dense store (about 4600 keys
+ * at dim 128) keep a filter store whose cuts follow cfg.cuts; the results
+ * are the same with either setting, only the time differs (see
+ * DSAI_CUTS_ESTIMATED).
  *
  * Scores at supplied indices (the page's optional topk_indices
  * [batch, seqlen, topk] int32, and pytorch_extract_topk_scores): when
