@@ -260,10 +260,13 @@ __device__ __forceinline__ void score_select_body(
         // products above this barrier or sink this one's below the next,
         // which would put a reduction right behind the products it reads.
         __builtin_amdgcn_sched_barrier(0);
+        // The fragment reads come first: LDS operations issue in program
+        // order, so behind the record's stores and the tile store (which
+        // waits for the tile's global load) they would start late.
+        sc.mma_fetch_spare(f0, spc, spn, buf(par ^ 1), cur);
         if (fin) record2(it - 3);
         ld.store(buf(par));
         ld.load((uint32_t)(it + 3) * G::kTileKeys);
-        sc.mma_fetch_spare(f0, spc, spn, buf(par ^ 1), cur);
         if (red) reduce_into(par ^ 1, old);
         __builtin_amdgcn_sched_barrier(0);
       };
