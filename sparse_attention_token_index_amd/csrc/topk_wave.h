@@ -464,91 +464,189 @@ struct FloatBins {
 // so equal scores have equal bits).  Slots up to the next multiple of 256 are
 // readable.
 
-// Appends the lanes' flagged values (up to four per lane, bit e of `m`:
-// element e) to side[ns...] in (lane, element) order; returns the new count.
-__device__ __forceinline__ uint32_t wave_append4(lds_u32* side, uint32_t ns, uint32_t m,
-                                                 const uint32_t (&val)[4]) {
-  const uint32_t c = (uint32_t)__builtin_popcount(m);
-  const uint32_t incl = wave_incl_scan(c);
-  uint32_t p = ns + incl - c;
+// The dense store's final phase works on groups of 64 consecutive keys, key
+// 64 g + lane in lane `lane`, four groups (one 256-key group of the store,
+// which holds whole 256-key groups) at a time.  The phase runs beside the
+// other wavefront of the SIMD, which is in its key loop, so it is bound by
+// its own instruction count: a group's kept keys are placed by one ballot
+// and the count of kept lanes below, with the running position in a scalar
+// register (no wave scan); loads take immediate offsets from one address
+// (no clamp: only the row's last 256 keys are masked); lanes that store
+// nothing store to a dummy LDS word or with an offset past the output row's
+// buffer range (the hardware drops such a store), so no group has a branch.
+constexpr uint32_t kFinBatch = 4;
+
+// Byte offset that puts a buffer store past any output row's range.
+constexpr int kDropOffset = 0x7FFFFFF0;
+
+// Scores of the 256 keys from slot `base` (a multiple of 256, below the
+// store's capacity).
+__device__ __forceinline__ void dense_load_batch(const lds_u32* key, uint32_t base,
+                                                 float (&x)[kFinBatch]) {
+  const lds_u32* p = key + base + (uint32_t)lane_id();
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if ((m >> e) & 1u) side[p++] = val[e];
-  }
-  return ns + lane_value(incl, kWave - 1);
+  for (uint32_t j = 0; j < kFinBatch; ++j) x[j] = __uint_as_float(p[j * kWave]);
 }
 
-// The k-th largest score among the dense row's n scores (as fp32 bits, .x)
-// and how many scores equal to it belong to the top k (.y).  [smin, smax]:
-// the row's smallest and largest score.  Histograms over float-linear bins
-// of the candidate range spread a row's scores evenly, so the bin holding
-// rank k usually has a few dozen keys: their order keys are gathered into
-// the side list and the exact one is found among them.  A bin with more than
-// 256 keys narrows the range to that bin and repeats; after three levels the
-// exact radix select over the whole row finishes the search.
-__device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, uint32_t k,
+// An output row of `topk` entries as two buffer resources whose range is
+// the row, so a store with kDropOffset writes nothing.
+struct RowOut {
+  __amdgpu_buffer_rsrc_t idx, score;
+  __device__ __forceinline__ RowOut(int32_t* out_idx, float* out_score, int topk) {
+    idx = __builtin_amdgcn_make_buffer_rsrc((void*)out_idx, (short)0, topk * 4, 0x00020000);
+    score = __builtin_amdgcn_make_buffer_rsrc((void*)out_score, (short)0, topk * 4, 0x00020000);
+  }
+  // entry p (dropped when `keep` is false)
+  __device__ __forceinline__ void put(bool keep, uint32_t p, int32_t id, float x) const {
+    const int off = keep ? (int)(p * 4u) : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)id, idx, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), score, off, 0, 0);
+  }
+};
+
+// FloatBins with the clamp as one median instruction.
+__device__ __forceinline__ uint32_t bin_of(const FloatBins& bins, float x) {
+  const float d = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, x), bins.base_h), bins.scale);
+  return (uint32_t)__builtin_amdgcn_fmed3f(d, 0.f, 255.f);
+}
+
+// Histogram of the row's n scores over `bins` (level 0: every key counts).
+__device__ __forceinline__ void dense_hist_all(const lds_u32* key, uint32_t n,
+                                               const FloatBins& bins, lds_u32* hist) {
+  const uint32_t lane = (uint32_t)lane_id();
+  const uint32_t nfull = n & ~255u;
+  for (uint32_t base = 0; base < nfull; base += kWave * kFinBatch) {
+    float x[kFinBatch];
+    dense_load_batch(key, base, x);
+#pragma unroll
+    for (uint32_t j = 0; j < kFinBatch; ++j)
+      __hip_atomic_fetch_add(&hist[bin_of(bins, x[j])], 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WAVEFRONT);
+  }
+  if (nfull < n) {
+    float x[kFinBatch];
+    dense_load_batch(key, nfull, x);
+#pragma unroll
+    for (uint32_t j = 0; j < kFinBatch; ++j) {
+      // lanes past the row add 0 to a bin of their own (no conflict)
+      const bool in = nfull + j * kWave + lane < n;
+      __hip_atomic_fetch_add(&hist[in ? bin_of(bins, x[j]) : lane], in ? 1u : 0u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    }
+  }
+}
+
+// Gather the scores of bin `fb` into side[] (order irrelevant); the other
+// lanes write to hist[lane] (no longer read).  Returns the count.
+__device__ __forceinline__ uint32_t dense_gather_all(const lds_u32* key, uint32_t n,
+                                                     const FloatBins& bins, uint32_t fb,
+                                                     lds_u32* hist, lds_u32* side) {
+  const uint32_t lane = (uint32_t)lane_id();
+  uint32_t ns = 0u;
+  for (uint32_t base = 0; base < n; base += kWave * kFinBatch) {
+    float x[kFinBatch];
+    dense_load_batch(key, base, x);
+#pragma unroll
+    for (uint32_t j = 0; j < kFinBatch; ++j) {
+      const bool inb = (base + j * kWave + lane < n) & (bin_of(bins, x[j]) == fb);
+      const uint64_t m = ballot(inb);
+      *(inb ? &side[ns + lanes_below(m)] : &hist[lane]) = __float_as_uint(x[j]);
+      ns = uniform(ns + (uint32_t)__popcll(m));
+    }
+  }
+  return ns;
+}
+
+// The k-th largest score among the dense row's n > k scores (as fp32 bits,
+// .x), how many scores equal to it belong to the top k (.y), and 1 in .z
+// when that is every score equal to it (the top k is then exactly the
+// scores >= .x).  [smin, smax]: the row's smallest and largest score.
+// Histograms over float-linear bins of the candidate range spread a row's
+// scores evenly, so the bin holding rank k usually has a few dozen keys:
+// they are gathered into the side list and, up to 64 of them, each lane
+// ranks one against the others (count greater, count equal); up to 256 go
+// through a radix select.  A bin with more than 256 keys narrows the range
+// to that bin and repeats; after three levels the exact radix select over
+// the whole row finishes the search.
+__device__ __forceinline__ uint3 dense_select(const lds_u32* key, uint32_t n, uint32_t k,
                                               float smin, float smax, lds_u32* hist,
                                               lds_u32* side) {
-  const int lane = lane_id();
-  const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
-  const uint32_t ngroups = (n + 255u) >> 8;  // 256 keys per group, 4 per lane
-  const uint32_t nfull = n >> 8;               // groups with no slot past the row
+  const uint32_t lane = (uint32_t)lane_id();
   float a = smin, b = smax;
   uint32_t rem = k;
   for (int level = 0; level < 3; ++level) {
-    if (!(a < b)) return make_uint2(__float_as_uint(a), rem);
+    if (!(a < b)) return make_uint3(__float_as_uint(a), rem, 0u);
     const FloatBins bins(a, b);
-    // Every key of a full group counts at level 0 ([a, b] is the row's
-    // range); otherwise slots past the row and keys outside [a, b] add 0
-    // (branch-free: bins() lands in [0, 255] for any bits).
-    const bool lvl0 = level == 0;
+    const bool lvl0 = level == 0;  // [a, b] is the row's range: every key counts
     clear_hist(hist);
-    for (uint32_t gi = 0; gi < ngroups; ++gi) {
-      const u32x4 u = k4[gi * 64u + lane];
-      const uint32_t i0 = gi * 256u + 4u * lane;
-      if (lvl0 & (gi < nfull)) {  // (uniform)
+    if (lvl0) {
+      dense_hist_all(key, n, bins, hist);
+    } else {
+      for (uint32_t base = 0; base < n; base += kWave * kFinBatch) {
+        float x[kFinBatch];
+        dense_load_batch(key, base, x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __hip_atomic_fetch_add(&hist[bins(__uint_as_float(u[e]))], 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = __uint_as_float(u[e]);
-          const bool in = i0 + e < n && (lvl0 || (x >= a && x <= b));
-          __hip_atomic_fetch_add(&hist[bins(x)], in ? 1u : 0u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+        for (uint32_t j = 0; j < kFinBatch; ++j) {
+          const bool in = (base + j * kWave + lane < n) & (x[j] >= a) & (x[j] <= b);
+          __hip_atomic_fetch_add(&hist[in ? bin_of(bins, x[j]) : lane], in ? 1u : 0u,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
         }
       }
     }
     wave_lds_sync();
     const uint2 fb = find_bin(hist, rem);
     const uint32_t cnt = uniform(hist[fb.x]);
-    rem -= fb.y;
+    rem -= fb.y;  // rank inside the bin: 1 <= rem <= cnt
     wave_lds_sync();
     if (cnt <= 256u) {
-      // gather the bin's scores into the side list, then turn them into
-      // order keys there (only the bin's few entries are converted)
+      // gather the bin's scores into the side list (order is irrelevant);
+      // the other lanes write to the histogram, which is no longer read
+      // (the paths below clear it before they use it)
       uint32_t ns = 0u;
-      for (uint32_t gi = 0; gi < ngroups; ++gi) {
-        const u32x4 u = k4[gi * 64u + lane];
-        const uint32_t i0 = gi * 256u + 4u * lane;
-        uint32_t m = 0u;
-        const uint32_t ux[4] = {u[0], u[1], u[2], u[3]};
-        if (lvl0 & (gi < nfull)) {  // (uniform)
+      if (lvl0) {
+        ns = dense_gather_all(key, n, bins, fb.x, hist, side);
+      } else {
+        for (uint32_t base = 0; base < n; base += kWave * kFinBatch) {
+          float x[kFinBatch];
+          dense_load_batch(key, base, x);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) m |= bins(__uint_as_float(u[e])) == fb.x ? (1u << e) : 0u;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = __uint_as_float(u[e]);
-            const bool in = i0 + e < n && (lvl0 || (x >= a && x <= b)) && bins(x) == fb.x;
-            m |= in ? (1u << e) : 0u;
+          for (uint32_t j = 0; j < kFinBatch; ++j) {
+            const bool inb = (base + j * kWave + lane < n) & (x[j] >= a) & (x[j] <= b) &
+                             (bin_of(bins, x[j]) == fb.x);
+            const uint64_t m = ballot(inb);
+            *(inb ? &side[ns + lanes_below(m)] : &hist[lane]) = __float_as_uint(x[j]);
+            ns = uniform(ns + (uint32_t)__popcll(m));
           }
         }
-        ns = wave_append4(side, ns, m, ux);
       }
       wave_lds_sync();
+      if (ns <= (uint32_t)kWave) {
+        // lane L ranks side entry L against all of them
+        const bool own = lane < ns;
+        const float o = __uint_as_float(side[own ? lane : 0u]);
+        const DSAI_LDS u32x4* s4 = reinterpret_cast<const DSAI_LDS u32x4*>(side);
+        uint32_t gt = 0u, eq = 0u;
+#pragma unroll 4
+        for (uint32_t j = 0; j < ns; j += 4u) {
+          const u32x4 s = s4[j >> 2];  // the same address in every lane
+#pragma unroll
+          for (uint32_t e = 0; e < 4u; ++e) {
+            const float y = __uint_as_float(s[e]);
+            const bool ok = j + e < ns;
+            gt += (ok & (y > o)) ? 1u : 0u;
+            eq += (ok & (y == o)) ? 1u : 0u;
+          }
+        }
+        // the rem-th largest value v: fewer than rem entries above it, at
+        // least rem at or above it (every lane holding v qualifies)
+        const uint64_t hm = ballot(own & (gt < rem) & (rem <= gt + eq));
+        const int src = (int)__ffsll((unsigned long long)hm) - 1;
+        const uint32_t vb = lane_value(__float_as_uint(o), src);
+        const uint32_t take = rem - lane_value(gt, src);
+        wave_lds_sync();  // the side list is read before anything reuses it
+        return make_uint3(vb, take, take == lane_value(eq, src) ? 1u : 0u);
+      }
+      // more than 64: order keys, then a radix select inside the bin
       uint32_t lo = 0xFFFFFFFFu, hi = 0u;
       for (uint32_t i = lane; i < ns; i += kWave) {
         const uint32_t o = ord_key(__uint_as_float(side[i]));
@@ -561,100 +659,94 @@ __device__ __forceinline__ uint2 dense_select(const lds_u32* key, uint32_t n, ui
       hi = wave_max(hi);
       uint2 r = make_uint2(lo, rem);
       if (lo != hi) r = select_in_range(side, ns, hist, lo, hi, 32 - __clz(hi - lo), rem);
-      return make_uint2(__float_as_uint(ord_to_float(r.x)), r.y);
+      return make_uint3(__float_as_uint(ord_to_float(r.x)), r.y, 0u);
     }
     // narrow to the bin's score range
     float lo = 3.4e38f, hi = -3.4e38f;
-    for (uint32_t gi = 0; gi < ngroups; ++gi) {
-      const u32x4 u = k4[gi * 64u + lane];
-      const uint32_t i0 = gi * 256u + 4u * lane;
+    for (uint32_t base = 0; base < n; base += kWave * kFinBatch) {
+      float x[kFinBatch];
+      dense_load_batch(key, base, x);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = __uint_as_float(u[e]);
-        if (i0 + e < n && x >= a && x <= b && bins(x) == fb.x) {
-          lo = fminf(lo, x);
-          hi = fmaxf(hi, x);
-        }
+      for (uint32_t j = 0; j < kFinBatch; ++j) {
+        const bool inb = (base + j * kWave + lane < n) & (x[j] >= a) & (x[j] <= b) &
+                         (bin_of(bins, x[j]) == fb.x);
+        lo = fminf(lo, inb ? x[j] : 3.4e38f);
+        hi = fmaxf(hi, inb ? x[j] : -3.4e38f);
       }
     }
     a = wave_fmin(lo);
     b = wave_fmax(hi);
   }
-  if (!(a < b)) return make_uint2(__float_as_uint(a), rem);
+  if (!(a < b)) return make_uint3(__float_as_uint(a), rem, 0u);
   const uint32_t oa = ord_key(a), ob = ord_key(b);
   const uint2 r = select_in_range<true>(key, n, hist, oa, ob, 32 - __clz(ob - oa), rem);
-  return make_uint2(__float_as_uint(ord_to_float(r.x)), r.y);
+  return make_uint3(__float_as_uint(ord_to_float(r.x)), r.y, 0u);
 }
 
-// Write the dense row's top k in index order (scores > v, then the first
-// `take_eq` scores == v), then (-1, -inf) padding up to `topk` slots.  With
-// n <= k every visible key is written.  smin / smax: this lane's smallest
-// and largest score (the wave's extremes are reduced here).  Each lane
-// handles four consecutive keys per group of 256; two wave scans place the
-// kept ones.
+// Write the kept keys of the dense row in index order: keys with score > v,
+// and the first `take_eq` keys with score == v (ALL_EQ: every key with score
+// >= v).  Returns the number written.
+template <bool ALL_EQ>
+__device__ __forceinline__ uint32_t dense_emit(const lds_u32* key, uint32_t n, float v,
+                                               uint32_t take_eq, const RowOut& out) {
+  const uint32_t lane = (uint32_t)lane_id();
+  uint32_t wpos = 0u, eq_seen = 0u;
+  for (uint32_t base = 0; base < n; base += kWave * kFinBatch) {
+    float x[kFinBatch];
+    dense_load_batch(key, base, x);
+    const uint32_t i0 = base + lane;
+#pragma unroll
+    for (uint32_t j = 0; j < kFinBatch; ++j) {
+      const uint32_t i = i0 + j * kWave;
+      const bool valid = i < n;
+      bool keep;
+      if constexpr (ALL_EQ) {
+        keep = valid & (x[j] >= v);
+      } else {
+        const bool eqv = valid & (x[j] == v);
+        const uint64_t meq = ballot(eqv);
+        keep = (valid & (x[j] > v)) | (eqv & ((eq_seen + lanes_below(meq)) < take_eq));
+        eq_seen = uniform(eq_seen + (uint32_t)__popcll(meq));
+      }
+      const uint64_t mk = ballot(keep);
+      out.put(keep, wpos + lanes_below(mk), (int32_t)i, x[j]);
+      wpos = uniform(wpos + (uint32_t)__popcll(mk));
+    }
+  }
+  return wpos;
+}
+
+// Write the dense row's top k in index order, then (-1, -inf) padding up to
+// `topk` slots.  With n <= k every visible key is written.  smin / smax:
+// this lane's smallest and largest score (the wave's extremes are reduced
+// here).
 __device__ __forceinline__ void dense_finish(const lds_u32* key, uint32_t n, uint32_t k,
                                              float smin, float smax, lds_u32* hist,
                                              lds_u32* side, int topk,
                                              int32_t* __restrict__ out_idx,
                                              float* __restrict__ out_score) {
-  const int lane = lane_id();
+  const uint32_t lane = (uint32_t)lane_id();
+  const RowOut out(out_idx, out_score, topk);
   uint32_t wpos = n;
   if (n <= k) {
-    for (uint32_t i = lane; i < n; i += kWave) {
-      out_idx[i] = (int32_t)i;
-      out_score[i] = __uint_as_float(key[i]);
+    for (uint32_t base = 0; base < n; base += kWave * kFinBatch) {
+      float x[kFinBatch];
+      dense_load_batch(key, base, x);
+#pragma unroll
+      for (uint32_t j = 0; j < kFinBatch; ++j) {
+        const uint32_t i = base + j * kWave + lane;
+        out.put(i < n, i, (int32_t)i, x[j]);
+      }
     }
   } else {
     wave_lds_sync();
-    const uint2 sel = dense_select(key, n, k, wave_fmin(smin), wave_fmax(smax), hist, side);
+    const uint3 sel = dense_select(key, n, k, wave_fmin(smin), wave_fmax(smax), hist, side);
     const float v = __uint_as_float(sel.x);
-    const uint32_t take_eq = sel.y;
-    const DSAI_LDS u32x4* k4 = reinterpret_cast<const DSAI_LDS u32x4*>(key);
-    const uint32_t ngroups = (n + 255u) >> 8;
-    wpos = 0u;
-    uint32_t eq_seen = 0u;
-    for (uint32_t gi = 0; gi < ngroups; ++gi) {
-      const u32x4 u = k4[gi * 64u + lane];
-      const uint32_t i0 = gi * 256u + 4u * lane;
-      uint32_t keep = 0u, eqm = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool valid = i0 + e < n;
-        const float x = __uint_as_float(u[e]);
-        keep |= (valid && x > v) ? (1u << e) : 0u;
-        eqm |= (valid && x == v) ? (1u << e) : 0u;
-      }
-      if (ballot(eqm != 0u)) {  // equal keys: the first take_eq of them (index order) are kept
-        const uint32_t ne = (uint32_t)__builtin_popcount(eqm);
-        const uint32_t incl = wave_incl_scan(ne);
-        uint32_t r = eq_seen + incl - ne;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((eqm >> e) & 1u) {
-            keep |= r < take_eq ? (1u << e) : 0u;
-            ++r;
-          }
-        }
-        eq_seen += lane_value(incl, kWave - 1);
-      }
-      const uint32_t nk = (uint32_t)__builtin_popcount(keep);
-      const uint32_t kincl = wave_incl_scan(nk);
-      uint32_t p = wpos + kincl - nk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((keep >> e) & 1u) {
-          out_idx[p] = (int32_t)(i0 + e);
-          out_score[p] = __uint_as_float(u[e]);
-          ++p;
-        }
-      }
-      wpos += lane_value(kincl, kWave - 1);
-    }
+    wpos = sel.z ? dense_emit<true>(key, n, v, sel.y, out)
+                 : dense_emit<false>(key, n, v, sel.y, out);
   }
-  for (uint32_t p = wpos + lane; p < (uint32_t)topk; p += kWave) {
-    out_idx[p] = -1;
-    out_score[p] = -__builtin_inff();
-  }
+  for (uint32_t p = wpos; p < (uint32_t)topk; p += kWave)
+    out.put(p + lane < (uint32_t)topk, p + lane, -1, -__builtin_inff());
 }
 
 // The row's top k (index order) from a store holding `count` entries.
