@@ -71,6 +71,10 @@ def expected(idx, sc):
     (2048, "normal"), (2049, "normal"), (8192, "normal"),
     (512, "ties"), (2048, "ties"), (2048, "equal"), (300, "zeros"), (2048, "wide"),
     (2048, "clustered"), (8192, "ties"),
+    # rows of at most 512 entries (one wavefront per row): its tie fallback
+    # (a bucket of more than 64 entries) and the range extremes
+    (512, "equal"), (100, "equal"), (512, "wide"), (200, "clustered"), (33, "ties"),
+    (129, "zeros"), (65, "normal"),
 ])
 def test_sort_rows_matches_stable_host_sort(ix, k, kind):
     rng = np.random.default_rng(1000 + k + len(kind))
