@@ -26,7 +26,10 @@ Measured in the same run and reported in `breakdown` (not part of `value`):
     expand, its static-scratch form, and the whole decode chain replayed
     from a HIP graph;
   * the cache write's k_norm (cold), scores at supplied indices, packed
-    sequences and the backward (prefill workload).
+    sequences and the backward (prefill workload);
+  * a library bf16 GEMM (torch.matmul, 8192^3) on the same box: the dense
+    bf16 rate the box's clock allows under matrix-core load, beside the
+    fused kernel's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
   --step-only             run and time only the headline step (profiling runs)
@@ -717,6 +720,24 @@ def main():
         "backward_TFLOPs": 6.0 * pcase.H * pcase.D * bw_entries / (bw_ms * 1e-3) / 1e12,
         "backward_key_adds_G_per_s": pcase.D * bw_entries / (bw_ms * 1e-3) / 1e9,
     }
+    # The same box's practical dense bf16 rate: a library GEMM (torch.matmul,
+    # hipBLASLt) of 8192^3 on contiguous operands, beside the fused kernel's
+    # rate.  Context for the fraction of the published peak, which the box's
+    # clock under matrix-core load caps for every kernel.
+    del bw_ws, bw_out, bw_g
+    torch.cuda.empty_cache()
+    gn = 8192
+    ga = torch.randn(gn, gn, device=dev, dtype=torch.bfloat16)
+    gb = torch.randn(gn, gn, device=dev, dtype=torch.bfloat16)
+    gc = torch.empty(gn, gn, device=dev, dtype=torch.bfloat16)
+    g_ms = timed(lambda: torch.matmul(ga, gb, out=gc), 10)
+    g_tf = 2.0 * gn ** 3 / (g_ms * 1e-3) / 1e12
+    bd["reference_gemm"] = {
+        "what": "torch.matmul bf16 8192x8192x8192 (hipBLASLt), same box",
+        "ms": g_ms, "TFLOPs": g_tf, "frac": g_tf / PEAK_BF16_TFLOPS,
+        "fused_kernel_vs_gemm_rate": achieved / g_tf,
+    }
+    del ga, gb, gc
     result["breakdown"] = bd
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case)
