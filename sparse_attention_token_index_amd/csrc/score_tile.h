@@ -151,6 +151,69 @@ struct TileScorer {
     }
   }
 
+  // LDS bytes load_row_staged needs: the padded query row as a tile of HP
+  // key-row slots (the key tiles' layout).
+  static constexpr int kStageBytes = HP * G::kRowBytes;
+
+  // load_row through LDS.  Each fragment load instruction of load_row
+  // gathers 16 bytes from each of 64 head rows, so it requests 64 cache
+  // lines, and the 8 k-steps request each line again.  Here each load
+  // instruction reads 64 consecutive 16-byte chunks of the row (whole cache
+  // lines), the chunks go to `stage` (kStageBytes of LDS private to the
+  // wavefront, free until the caller reuses it) in the key tiles' layout,
+  // and the fragments are read back from there, conflict-free under that
+  // layout's swizzle.  The weights are read as 16-byte groups of 4 heads when
+  // `w4` holds (H a multiple of 4 and wrow 16-byte aligned).
+  __device__ __forceinline__ void load_row_staged(int rr, const uint16_t* __restrict__ qrow,
+                                                  const float* __restrict__ wrow, int H,
+                                                  bool active, bool w4, lds_char* stage) {
+    const int lane = lane_id();
+    const int g = lane >> 5;
+    constexpr int kCh = D / 8;
+    constexpr int kPer = HP * kCh / kWave;
+    u32x4 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ch = i * kWave + lane;
+      const int h = ch / kCh, x = ch % kCh;
+      v[i] = (active && h < H) ? *reinterpret_cast<const u32x4*>(qrow + (int64_t)h * D + 8 * x)
+                               : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (w4) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int h0 = 32 * m + 8 * a + 4 * g;
+          const floatx4 f = (active && h0 < H) ? *reinterpret_cast<const floatx4*>(wrow + h0)
+                                               : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[rr][m][4 * a + e] = f[e];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int hw = 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+          wv[rr][m][r] = (active && hw < H) ? wrow[hw] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ch = i * kWave + lane;
+      *reinterpret_cast<DSAI_LDS u32x4*>(stage + G::chunk_offset(ch / kCh, ch % kCh)) = v[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        qf[rr][m][j] = *reinterpret_cast<const DSAI_LDS bf16x8*>(stage + 32 * m * G::kRowBytes +
+                                                                 frag_offset(j));
+  }
+
   // One-row form (NR == 1).
   __device__ __forceinline__ void load_query(const uint16_t* __restrict__ qrow,
                                              const float* __restrict__ wrow, int H, bool active) {

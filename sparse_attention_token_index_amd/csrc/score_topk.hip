@@ -141,6 +141,8 @@ __device__ __forceinline__ void score_select_body(
 
   Scorer sc;
   sc.init_offsets();
+  // 16-byte weight loads when every row's weights are 16-byte aligned
+  const bool w4 = (H & 3) == 0 && ((uintptr_t)w & 15u) == 0;
   RowStore<IdxT> rs[NR];
   int t[NR], n_t[NR];
   bool active[NR];
@@ -156,7 +158,15 @@ __device__ __forceinline__ void score_select_body(
     rs[rr] = RowStore<IdxT>{(lds_u32*)mine, (DSAI_LDS IdxT*)(mine + cap * 4), scratch, side,
                             kSideCap};
     const int64_t row = (int64_t)(active[rr] ? t[rr] : 0) * B + b;
-    sc.load_row(rr, q + row * H * D, w + row * H, H, active[rr]);
+    // dense store: the query row comes in through the row's store (the key
+    // loop writes it only after the row's fragments are in registers); the
+    // filter kernels keep the direct loads (their registers are fuller)
+    bool staged = false;
+    if constexpr (DENSE) staged = row_bytes >= Scorer::kStageBytes;
+    if (staged)
+      sc.load_row_staged(rr, q + row * H * D, w + row * H, H, active[rr], w4, mine);
+    else
+      sc.load_row(rr, q + row * H * D, w + row * H, H, active[rr]);
   }
 
   if (!DENSE && threadIdx.x < 3) cut_req[threadIdx.x] = 0u;  // published by the loop's first barrier

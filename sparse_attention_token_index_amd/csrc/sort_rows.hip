@@ -5,9 +5,9 @@
 //
 // Bucket path (the common case).  The row's real entries are spread over
 // NB = 256 * ITEMS buckets by a monotone map of the score onto [0, NB)
-// (linear in the score between the row's maximum and minimum, so higher
-// scores land in lower buckets); a counting pass and a scan give every bucket
-// its output range, the entries are scattered into their bucket's range, and
+// (BucketMap: higher scores land in lower buckets); a counting pass and a
+// scan give every bucket its output range, the entries are scattered into
+// their bucket's range, and
 // each entry's final slot inside its bucket is its rank there under
 // (score descending, index ascending), counted by comparing it with the
 // bucket's other entries.  With about one entry per bucket this costs a few
@@ -19,8 +19,6 @@
 // agrees are skipped.  Stability gives the index order among equal scores
 // because rows arrive in ascending index order (the selection kernels write
 // them that way).
-#include <float.h>
-
 #include "internal.h"
 #include "device_common.h"
 
@@ -78,17 +76,42 @@ __device__ __forceinline__ void store_run(uint32_t* w, const uint32_t (&v)[ITEMS
   }
 }
 
-// Monotone non-increasing map of a score onto [0, nb): every step (halving,
-// subtraction, scaling, clamping) is monotone under round-to-nearest, so a
-// higher score never lands in a higher bucket.  Halving keeps the difference
-// of any two finite scores finite.
-__device__ __forceinline__ uint32_t bucket_of(uint32_t key, float top_half, float scale,
-                                              uint32_t nb) {
+// Monotone non-increasing map of a row's scores onto [0, nb) buckets.  A top
+// k's scores crowd just above the row's smallest (the selection threshold),
+// the more so when a few large scores stretch the range, so the map is
+// log-linear in the distance from the smallest: with d = s/2 - min/2 and
+// c = (max - min) / 32, the bucket follows the float bits of d + c, counted
+// from those of c and scaled onto the nb buckets: about linear (a fixed step)
+// for d below c, logarithmic (equal buckets per octave) above it.  Each step
+// (halving, subtracting, adding c, the bits of a non-negative float, the
+// integer-to-float conversion, scaling, truncation, clamping) is monotone,
+// so a higher score never lands in a higher bucket; halving keeps the
+// difference of any two finite scores finite.  On top-k rows of the
+// 65536-token workload (5 % of keys x4) a map linear in the score put 20-37
+// entries in the fullest bucket, this one about 10; on rows nearer a
+// Gaussian's upper half the two spread alike.
+struct BucketMap {
+  float hmin;     // min / 2
+  float c;        // the offset: (max - min) / 32, halved like d
+  float scale;    // buckets per unit of bits(d + c) - bits(c)
+  uint32_t cbits;
+  __device__ __forceinline__ BucketMap(float smin, float smax, uint32_t nb) {
+    hmin = __fmul_rn(0.5f, smin);
+    const float rh = __fsub_rn(__fmul_rn(0.5f, smax), hmin);
+    c = __fmul_rn(rh, 0.0625f);  // exact: a power of two
+    cbits = __float_as_uint(c);
+    const uint32_t span = __float_as_uint(__fadd_rn(rh, c)) - cbits;
+    scale = (float)nb / ((float)span + 1.0f);
+  }
   // explicit roundings: both call sites must map a key to the same bucket
-  const float d = __fmul_rn(__fsub_rn(top_half, __fmul_rn(0.5f, ord_to_float(key))), scale);
-  const uint32_t b = (uint32_t)fminf(d, (float)(nb - 1u));  // d >= 0 for a real entry
-  return b < nb ? b : nb - 1u;
-}
+  __device__ __forceinline__ uint32_t operator()(uint32_t key, uint32_t nb) const {
+    const float d = __fsub_rn(__fmul_rn(0.5f, ord_to_float(key)), hmin);
+    const uint32_t b = __float_as_uint(__fadd_rn(d, c)) - cbits;
+    const float x = __fmul_rn((float)b, scale);
+    const uint32_t i = (uint32_t)fminf(x, (float)(nb - 1u));
+    return nb - 1u - (i < nb ? i : nb - 1u);
+  }
+};
 
 __device__ __forceinline__ uint32_t blocked_addr(uint32_t p, int items) {
   return p + p / (uint32_t)items;  // one pad word per thread block of items: odd stride
@@ -254,15 +277,13 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
     kmax = max(kmax, red[kSortWaves + w]);
     nv += red[2 * kSortWaves + w];
   }
-  const float top_half = 0.5f * ord_to_float(kmax);
-  const float range = top_half - 0.5f * ord_to_float(kmin);
-  const float scale = (nv > 0u && range > 0.f) ? fminf((float)NB / range, FLT_MAX) : 0.f;
+  const BucketMap bmap(ord_to_float(kmin), ord_to_float(kmax), NB);
 
   // Count entries per bucket.
   uint32_t bkt[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    bkt[i] = bucket_of(key[i], top_half, scale, NB);
+    bkt[i] = bmap(key[i], NB);
     if (val[i] >= 0) atomicAdd(&start[bkt[i]], 1u);
   }
   __syncthreads();
@@ -328,7 +349,7 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
       const uint2 e = kv[p];
       key[i] = e.x;
       val[i] = (int32_t)e.y;
-      const uint32_t b = bucket_of(key[i], top_half, scale, NB);
+      const uint32_t b = bmap(key[i], NB);
       const uint32_t lo = b > 0u ? start[b - 1u] : 0u, n = start[b] - lo;
       if (n > 1u) {
         s0[i] = lo;
