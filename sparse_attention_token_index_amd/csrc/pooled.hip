@@ -115,6 +115,14 @@ constexpr int kPoolTilesPerBlock = 16;
 constexpr int kPoolRows = 8;
 
 template <int HP, int D>
+struct PoolScoresLds {
+  static constexpr int kStage = kPoolRows * TileScorer<HP, D>::kStageBytes;
+  static constexpr int kTiles = 2 * TileGeom<D>::kTileBytes;
+  static constexpr int kRegion = kStage > kTiles ? kStage : kTiles;
+  static constexpr int kBytes = kRegion + kPoolTilesPerBlock * TileGeom<D>::kTileKeys;
+};
+
+template <int HP, int D>
 __global__ __launch_bounds__(kPoolRows * 64) __attribute__((amdgpu_waves_per_eu(2))) void
 pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                      const uint16_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_valid,
@@ -124,10 +132,11 @@ pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   using Scorer = TileScorer<HP, D>;
   using Acc = typename Scorer::Acc;
   using Frag = typename Scorer::Frag;
+  using L = PoolScoresLds<HP, D>;
   constexpr int kPer = kPoolTilesPerBlock * G::kTileKeys;
-  __shared__ __align__(16) char tiles_raw[2 * G::kTileBytes];
-  __shared__ uint8_t valid_s[kPer];
-  lds_char* tiles = (lds_char*)tiles_raw;
+  extern __shared__ __align__(16) char smem_raw[];
+  lds_char* tiles = (lds_char*)smem_raw;
+  DSAI_LDS uint8_t* valid_s = (DSAI_LDS uint8_t*)(tiles + L::kRegion);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = lane_id();
   const int pb = blockIdx.x % pool_blocks;  // consecutive blocks share a pool range
@@ -140,13 +149,19 @@ pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   const int np_row = max(0, min(np, lim - p0));  // this block's pools the row sees
   const int ntiles = (np + G::kTileKeys - 1) / G::kTileKeys;
 
-  Scorer sc;
-  sc.load_query(q + (int64_t)(active ? row : 0) * H * D, w + (int64_t)(active ? row : 0) * H, H,
-                active);
-  for (int i = threadIdx.x; i < kPer; i += kPoolRows * 64) valid_s[i] = i < np ? pool_valid[p0 + i] : 0;
   TileLoader<D, kPoolRows * 64> lda, ldb;  // even and odd tiles
   lda.init(pool_k + (int64_t)p0 * D, (uint32_t)D, (uint32_t)((int64_t)np * D * 2));
   ldb.init(pool_k + (int64_t)p0 * D, (uint32_t)D, (uint32_t)((int64_t)np * D * 2));
+  lda.load(0u);
+  ldb.load((uint32_t)G::kTileKeys);
+  Scorer sc;
+  sc.init_offsets();
+  const bool w4 = (H & 3) == 0 && ((uintptr_t)w & 15u) == 0;
+  sc.load_row_staged(0, q + (int64_t)(active ? row : 0) * H * D,
+                     w + (int64_t)(active ? row : 0) * H, H, active, w4,
+                     tiles + wave * Scorer::kStageBytes);
+  for (int i = threadIdx.x; i < kPer; i += kPoolRows * 64) valid_s[i] = i < np ? pool_valid[p0 + i] : 0;
+  __syncthreads();
   float* srow = scores + (int64_t)row * P + p0;
 
   auto buf = [&](int it) { return tiles + (it & 1) * G::kTileBytes; };
@@ -169,8 +184,6 @@ pooled_scores_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   };
   Acc acc0, acc1;
   Frag f0, f1;
-  lda.load(0u);
-  ldb.load((uint32_t)G::kTileKeys);
   lda.store(buf(0));
   lda.load((uint32_t)(2 * G::kTileKeys));
   ldb.store(buf(1));
@@ -198,8 +211,12 @@ static hipError_t launch_scores_t(const PooledScoresArgs& a, hipStream_t st) {
   const int64_t pool_blocks = (a.P + per_block - 1) / per_block;
   const int64_t blocks = pool_blocks * ((a.Q + kPoolRows - 1) / kPoolRows);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  constexpr int lds = PoolScoresLds<HP, D>::kBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)pooled_scores_kernel<HP, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pooled_scores_kernel<HP, D>), dim3((unsigned)blocks), dim3(kPoolRows * 64),
-                     0, st, a.q, a.w, a.pool_k, a.pool_valid, a.limit, (int)a.Q, (int)a.P, a.H,
+                     lds, st, a.q, a.w, a.pool_k, a.pool_valid, a.limit, (int)a.Q, (int)a.P, a.H,
                      (int)pool_blocks, a.scores);
   return hipGetLastError();
 }
