@@ -391,15 +391,17 @@ __device__ __forceinline__ void bucket_sort_row(int32_t* __restrict__ ri, float*
   }
 }
 
-// Each workgroup sorts rows blockIdx.x, blockIdx.x + gridDim.x, ...; the next
-// row's entries are loaded while the current row is sorted.
-template <int ITEMS>
-__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(ITEMS <= 8 ? 6 : 1))) void sort_rows_kernel(int32_t* __restrict__ idx,
-                                                                 float* __restrict__ score,
-                                                                 int topk, int rows) {
+// Each workgroup sorts rows blockIdx.x, blockIdx.x + gridDim.x, ...; with PF
+// the next row's entries are loaded while the current row is sorted (their
+// registers cost one wavefront per SIMD at 2048-entry rows, which pays only
+// where each workgroup has a second row).
+template <int ITEMS, bool PF>
+__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(
+    ITEMS <= 4 ? 6 : ITEMS <= 8 ? (PF ? 5 : 6) : 1))) void sort_rows_kernel(int32_t* __restrict__ idx,
+                                                                    float* __restrict__ score,
+                                                                    int topk, int rows) {
   extern __shared__ __align__(16) uint32_t sort_smem[];
   const int t = threadIdx.x;
-  uint32_t nk[ITEMS];
   int32_t nval[ITEMS];
   float nsc[ITEMS];
   auto load = [&](int row) {
@@ -422,23 +424,27 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(IT
       val[i] = nval[i];
       key[i] = val[i] >= 0 ? ord_key(nsc[i]) : 0u;
     }
-    if (row + (int)gridDim.x < rows) load(row + gridDim.x);
+    if (PF && row + (int)gridDim.x < rows) load(row + gridDim.x);
     bucket_sort_row<ITEMS>(idx + (int64_t)row * topk, score + (int64_t)row * topk, topk,
                            sort_smem, key, val);
+    if (!PF && row + (int)gridDim.x < rows) load(row + gridDim.x);
   }
 }
 
-// Workgroups for `rows` rows (each takes every grid-th row), from the
-// resident set R (the runtime's occupancy for this kernel, its registers and
-// `lds` bytes of LDS, times the CUs).  Workgroups that outlive the resident
+// The resident set R of a sort kernel: the runtime's occupancy for it (its
+// registers and `lds` bytes of LDS) times the CUs.  The launch takes one
+// workgroup per row up to 8 rows per slot, else one per two rows (each
+// workgroup takes every grid-th row).  Workgroups that outlive the resident
 // set are started by the dispatcher as slots free up, which balances the last
 // round and keeps the workgroups of a CU out of step with each other.  Up to
 // 8 rows per slot each workgroup sorts one row (a persistent grid of R would
 // give some slots one row more than others: 3 against 2.67 at 4096 rows);
 // beyond that each sorts two, the second row's loads in flight during the
-// first's sort.  Measured on MI355X: 4096 rows of 2048, 42 -> 37 us; 32768
-// rows of 512, 95 -> 80 us, against a persistent grid of R.
-static unsigned sort_groups(const void* kern, int64_t rows, size_t lds) {
+// first's sort (the PF kernel).  Measured on MI355X: 4096 rows of 2048,
+// 42 -> 37 us; 32768 rows of 512, 95 -> 80 us, against a persistent grid of
+// R; 65536 rows of 2048, 0.570 -> 0.518 ms with the PF kernel at five
+// wavefronts per SIMD (no spills) instead of six.
+static int64_t sort_resident(const void* kern, size_t lds) {
   static int cus_cache[64];
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
@@ -473,8 +479,7 @@ static unsigned sort_groups(const void* kern, int64_t rows, size_t lds) {
       per_cu_cache[dev][slot] = per_cu;
     }
   }
-  const int64_t resident = (int64_t)cus * per_cu;
-  return (unsigned)(rows <= 8 * resident ? rows : (rows + 1) / 2);
+  return (int64_t)cus * per_cu;
 }
 
 hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, hipStream_t st) {
@@ -483,14 +488,18 @@ hipError_t launch_sort_rows(int32_t* idx, float* score, int64_t rows, int topk, 
 #define DSAI_ITEMS(n)                                                                          \
   if (topk <= kSortThreads * n) {                                                              \
     const size_t lds = 4 * (size_t)SortLayout<n>::kWords;                                      \
-    hipError_t e = hipFuncSetAttribute((const void*)sort_rows_kernel<n>,                       \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+    const void* one = (const void*)sort_rows_kernel<n, false>;                                 \
+    const void* two = (const void*)sort_rows_kernel<n, true>;                                  \
+    hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (e == hipSuccess)                                                                       \
+      e = hipFuncSetAttribute(two, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);      \
     if (e != hipSuccess) return e;                                                             \
-    hipLaunchKernelGGL(sort_rows_kernel<n>,                                                    \
-                       dim3(sort_groups((const void*)sort_rows_kernel<n>, rows, lds)),         \
-                       dim3(kSortThreads),                                                     \
-                       lds, st, idx, score,                                                    \
-                       topk, (int)rows);                                                       \
+    if (rows <= 8 * sort_resident(one, lds))                                                   \
+      hipLaunchKernelGGL((sort_rows_kernel<n, false>), dim3((unsigned)rows), dim3(kSortThreads), \
+                         lds, st, idx, score, topk, (int)rows);                                \
+    else                                                                                       \
+      hipLaunchKernelGGL((sort_rows_kernel<n, true>), dim3((unsigned)((rows + 1) / 2)),        \
+                         dim3(kSortThreads), lds, st, idx, score, topk, (int)rows);            \
     return hipGetLastError();                                                                  \
   }
   DSAI_ITEMS(1) DSAI_ITEMS(2) DSAI_ITEMS(4) DSAI_ITEMS(8) DSAI_ITEMS(16) DSAI_ITEMS(32)
